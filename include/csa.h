@@ -1,0 +1,261 @@
+/*
+ * csa.h - C ABI of the CSA / HCA compressed-attention library for MI355X
+ * (gfx950).
+ *
+ * The calls follow the method described on the page "DeepSeek V4 深度解析"
+ * (section 2, "核心技術創新": the three CSA steps and the HCA paragraph) and
+ * the page at wmrh.cn/news/726125 ("V4 改进一", and the FP4 paragraph):
+ *
+ *   csa_kv_compress      CSA step 1: every m raw tokens' KV -> one entry,
+ *                        softmax weights from per-token logits plus per-slot
+ *                        position biases over an overlapping window.
+ *   csa_indexer_score    CSA step 2: low-rank lightning-indexer scores of each
+ *                        query against the visible entries (BF16 scores).
+ *   csa_topk_select      CSA step 2: the top-k entries of each query.
+ *   csa_sparse_mqa_attn  CSA step 3 / HCA: shared-KV multi-query attention over
+ *                        the selected (CSA) or all visible (HCA) entries
+ *                        together with the sliding window of raw tokens.
+ *   csa_swa_merge        the exact log-sum-exp combination of two partial
+ *                        attentions, so the window branch and the compressed
+ *                        branch can run separately.
+ *   csa_quantize, csa_dequantize, csa_mxfp4_to_fp8
+ *                        the storage formats: mixed-precision KV entries
+ *                        (RoPE dims BF16, the rest FP8) and the FP4 indexer
+ *                        operands with their lossless FP4 -> FP8 regrouping.
+ *
+ * Conventions
+ *  - Every pointer passed to a compute call is a DEVICE pointer unless stated,
+ *    and the structs themselves (csa_tensor, csa_batch) live in host memory.
+ *  - Calls are stream ordered and asynchronous: they enqueue kernels on
+ *    `stream` and return.  The library never synchronises the host, never
+ *    allocates device memory and keeps no pointer after a call returns.  The
+ *    caller owns every buffer.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is enqueued and the call returns a non-zero csa_status.
+ *    csa_last_error() gives a thread-local description.  Device-resident
+ *    metadata (offsets, positions, top-k indices) cannot be checked on the
+ *    host: kernels clamp every such value to the extents of the tensors they
+ *    were given, so bad metadata gives wrong results but never an
+ *    out-of-bounds access.
+ *  - Results are deterministic: the same inputs give the same bits, and a
+ *    request's results do not depend on its position in the batch or on the
+ *    other requests (no atomics in value reductions).
+ *  - Layouts are dense and row major.
+ *
+ * Readings where the pages are silent (fixed here; see the individual calls):
+ *  - entry i covers raw positions (i+1)m-w .. (i+1)m-1; slots before position 0
+ *    are left out of the softmax;
+ *  - entry i is visible to the query at position t iff (i+1)m-1 <= t, i.e.
+ *    n_c(t) = floor((t+1)/m) entries;
+ *  - the window of the query at t is positions max(0, t-W+1) .. t;
+ *  - one softmax over the union of entries and window tokens, key = value.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARGUMENT = 1, /* a null pointer, bad size or bad format      */
+  CSA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. a dim)       */
+  CSA_ERR_WORKSPACE = 3,        /* workspace missing or too small               */
+  CSA_ERR_HIP = 4               /* a HIP launch failed; see csa_last_error()    */
+} csa_status;
+
+typedef enum csa_format {
+  CSA_F32 = 0,       /* float32                                                */
+  CSA_BF16 = 1,      /* bfloat16 bit patterns (uint16)                          */
+  CSA_FP8_MIXED = 2, /* 512-dim KV entry: [448 e4m3fn | 64 bf16] with 4 e8m0
+                        scales for the e4m3 blocks [0,128) [128,256) [256,384)
+                        [384,448); scale = smallest 2^e with amax <= 448*2^e    */
+  CSA_MXFP4 = 3      /* OCP MX: e2m1 elements, two per byte (element 2i in the
+                        low nibble of byte i), one e8m0 scale per 32 elements,
+                        X = 2^(floor(log2 amax) - 2), saturating to +-6          */
+} csa_format;
+
+/* A matrix of `rows` vectors of `dim` logical elements (device memory).
+ *   CSA_F32      data  = float   [rows][dim]
+ *   CSA_BF16     data  = uint16  [rows][dim]
+ *   CSA_FP8_MIXED dim = 512;  data = uint8 e4m3fn [rows][448],
+ *                scale = uint8 e8m0 [rows][4],  rope = uint16 bf16 [rows][64]
+ *   CSA_MXFP4    data  = uint8 [rows][dim/2],   scale = uint8 e8m0 [rows][dim/32]
+ * Unused pointers must be NULL. */
+typedef struct csa_tensor {
+  int32_t fmt;
+  int32_t dim;
+  int64_t rows;
+  void* data;
+  void* scale;
+  void* rope;
+} csa_tensor;
+
+/* A batch of requests (host struct; the arrays are DEVICE memory, int64).
+ *   queries of request r      : rows q_off[r] .. q_off[r+1]-1 of the query
+ *                               tensors; query i of r sits at position
+ *                               q_pos[r] + i
+ *   compressed entries of r   : rows kv_off[r] .. kv_off[r+1]-1 of the entry
+ *                               (and indexer-key) tensor; local entry j is row
+ *                               kv_off[r] + j
+ *   raw (window) rows of r    : rows raw_off[r] .. raw_off[r+1]-1 of the raw
+ *                               tensor, holding positions raw_pos[r] ..
+ *                               (may be NULL when no window is used)
+ * n_q = q_off[n_req] and max_kv >= every kv_off[r+1]-kv_off[r] are host-side
+ * copies used to size launch grids. */
+typedef struct csa_batch {
+  int32_t n_req;
+  int32_t reserved;
+  int64_t n_q;
+  int64_t max_kv;
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* kv_off;
+  const int64_t* raw_off;
+  const int64_t* raw_pos;
+} csa_batch;
+
+/* ---------------------------------------------------------------------------
+ * csa_kv_compress - CSA step 1 (and HCA at m' = 128).
+ * Page "DeepSeek V4 深度解析", section 2, CSA step 1: m raw tokens -> one entry
+ * by a softmax-weighted sum with one learned weight per raw token plus a
+ * position bias, adjacent blocks overlapping.
+ *
+ * Computes entries entry_begin .. entry_begin+n_entries-1 of one sequence into
+ * rows 0 .. n_entries-1 of `out`.  Entry i, slot s in [0, w): p = (i+1)m-w+s;
+ * slots with p < 0 are dropped; weights = softmax over the valid slots of
+ * logits[p - x_pos0] + slot_bias[s] (fp32); entry = sum weight_s * x[p - x_pos0]
+ * accumulated in fp32, then stored as F32, BF16 (round to nearest-even) or
+ * FP8_MIXED (dim 512).
+ *   x          raw rows, F32 or BF16, positions x_pos0 .. x_pos0 + x->rows - 1;
+ *              must hold every valid slot of the requested entries
+ *   logits     float [x->rows], aligned with x
+ *   slot_bias  float [w]
+ *   1 <= m <= w <= 1024; out->rows >= n_entries; out->dim == x->dim
+ * ------------------------------------------------------------------------- */
+csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_pos0,
+                           const float* slot_bias, int32_t m, int32_t w,
+                           int64_t entry_begin, int64_t n_entries, const csa_tensor* out,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_indexer_score - CSA step 2, the lightning indexer.
+ * Page "DeepSeek V4 深度解析", section 2, CSA step 2 (a light low-rank
+ * relevance score per query and compressed entry) and the FP4 paragraph
+ * (indexer QK in FP4; BF16 scores).
+ *
+ * For query row q (request r, position t) and local entry j < n_vis =
+ * min(floor((t+1)/m), kv_off[r+1]-kv_off[r]):
+ *   S[q][j] = sum_h w[q][h] * ReLU(qi[q*n_heads+h] . ki[kv_off[r]+j])
+ * (relu = 0 drops the ReLU), accumulated in fp32 and stored as F32 or
+ * BF16 (round to nearest-even) at scores + q*ld + j.  Columns j >= n_vis are
+ * not written.
+ *   qi        rows = n_q * n_heads, fmt F32 | BF16 | MXFP4 (dim % 32 == 0)
+ *   ki        entry keys, same fmt and dim as qi
+ *   head_w    float [n_q][n_heads] or NULL (all weights 1)
+ *   scores    [n_q][ld] of score_fmt (F32 | BF16), ld >= batch->max_kv
+ * ------------------------------------------------------------------------- */
+csa_status csa_indexer_score(const csa_tensor* qi, int32_t n_heads, const float* head_w,
+                             const csa_tensor* ki, const csa_batch* batch, int32_t m,
+                             int32_t relu, void* scores, int32_t score_fmt, int64_t ld,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_topk_select - CSA step 2, top-k selection.
+ * Page "DeepSeek V4 深度解析", section 2, CSA step 2 (each query keeps the k
+ * most relevant entries: 1024 Pro, 512 Flash).
+ *
+ * Row q's candidates are its n_vis visible entries (as in csa_indexer_score).
+ * Keeps the min(k, n_vis) largest scores, ties broken by the lower entry
+ * index, and writes them in ascending index order to idx[q][0..], padding
+ * the row with -1.  Exact (radix select on the order-preserving integer image
+ * of the scores); scores must not be NaN.
+ *   scores  [n_q][ld] F32 | BF16;  idx int32 [n_q][k];  1 <= k <= 4096
+ * ------------------------------------------------------------------------- */
+csa_status csa_topk_select(const void* scores, int32_t score_fmt, int64_t ld,
+                           const csa_batch* batch, int32_t m, int32_t k, int32_t* idx,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_sparse_mqa_attn - CSA step 3 / HCA dense attention.
+ * Page "DeepSeek V4 深度解析", section 2: CSA step 3 (a sliding-window branch
+ * of the latest 128 uncompressed tokens, attended together with the selected
+ * entries) and the HCA paragraph (no selection, dense attention, same window,
+ * shared-KV multi-query attention).
+ *
+ * Query row q of request r at position t has heads q_rows[q*n_heads + h].
+ * Key set: the entries idx[q][0..k) that are >= 0 (CSA), or, when idx is NULL,
+ * every visible entry j < n_vis (HCA); plus, when raw != NULL and window > 0,
+ * the raw rows of positions max(0, t-window+1) .. t that request r holds.
+ * Each key is also its value.  One softmax over the union:
+ *   o[q][h] = sum_key softmax(scale * q_h . key) * key,
+ *   lse[q][h] = natural log-sum-exp of the scaled logits (optional).
+ * A row whose key set is empty gets o = 0 and lse = -inf.
+ *   q         rows = n_q*n_heads, dim D (128 | 512), F32 or BF16
+ *   kv        entries: F32 (D 128), BF16, or FP8_MIXED (D 512); may be NULL
+ *             for a window-only call
+ *   raw       window rows, F32 or BF16, dim D; may be NULL
+ *   compute   F32 q, kv and raw use fp32 matrix cores; otherwise all operands
+ *             are bf16 (FP8_MIXED rows dequantised to bf16 exactly) with
+ *             fp32 accumulation
+ *   out       [n_q*n_heads][D] F32 or BF16;  lse float [n_q*n_heads] or NULL
+ *   n_heads   a multiple of 32, or 8 or 16
+ * ------------------------------------------------------------------------- */
+csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads, const csa_tensor* kv,
+                               const int32_t* idx, int32_t k, const csa_tensor* raw,
+                               int32_t window, const csa_batch* batch, int32_t m, float scale,
+                               void* out, int32_t out_fmt, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_swa_merge - combination of the window branch and the compressed branch.
+ * Page "DeepSeek V4 深度解析", section 2, CSA step 3 (the two are attended
+ * together): a softmax over the union of two disjoint key sets equals
+ *   M = max(a, b),  o = (e^(a-M) o_a + e^(b-M) o_b) / (e^(a-M) + e^(b-M)),
+ *   lse = M + log(e^(a-M) + e^(b-M))
+ * with a = lse_a[r], b = lse_b[r] (fp32 arithmetic).  A side with lse = -inf
+ * contributes nothing; both -inf gives o = 0, lse = -inf.
+ *   o_a, o_b  float [rows][dim];  lse_a, lse_b float [rows]
+ *   out       [rows][dim] F32 or BF16;  lse_out float [rows] or NULL
+ * ------------------------------------------------------------------------- */
+csa_status csa_swa_merge(const float* o_a, const float* lse_a, const float* o_b,
+                         const float* lse_b, int64_t rows, int32_t dim, void* out,
+                         int32_t out_fmt, float* lse_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Storage formats.  Page "DeepSeek V4 深度解析", section 2 (KV cache: RoPE
+ * dims BF16, the rest FP8) and the FP4 quantisation paragraph of section 4
+ * (FP4 -> FP8 is lossless while the block max/min ratio is bounded).
+ *
+ * csa_quantize: src (F32 | BF16) -> dst of the same rows and dim:
+ *   BF16 (from F32, nearest-even), FP8_MIXED (dim 512), MXFP4 (dim % 32 == 0).
+ * csa_dequantize: src of any format -> float [rows][dim] (exact).
+ * csa_mxfp4_to_fp8: MXFP4 rows -> e4m3fn codes uint8 [rows][dim] with one
+ *   power-of-two group scale per row, g = max block exponent - 6, stored as an
+ *   e8m0 byte in group_scale[rows]; lossless[r] = 1 iff the row's block
+ *   exponents span at most 14 (then the conversion is exact).
+ * ------------------------------------------------------------------------- */
+csa_status csa_quantize(const csa_tensor* src, const csa_tensor* dst, hipStream_t stream);
+csa_status csa_dequantize(const csa_tensor* src, float* dst, hipStream_t stream);
+csa_status csa_mxfp4_to_fp8(const csa_tensor* src, uint8_t* fp8, uint8_t* group_scale,
+                            uint8_t* lossless, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Introspection (host only).
+ * ------------------------------------------------------------------------- */
+int csa_abi_version(void);
+const char* csa_status_string(csa_status s);
+/* Description of the last error on the calling thread ("" if none). */
+const char* csa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

@@ -1,0 +1,78 @@
+"""ctypes view of libcsa.so (include/csa.h).  Argument marshalling only."""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+CSA_OK = 0
+CSA_F32, CSA_BF16, CSA_FP8_MIXED, CSA_MXFP4 = 0, 1, 2, 3
+
+EXPORTED = (
+    "csa_kv_compress", "csa_indexer_score", "csa_topk_select", "csa_sparse_mqa_attn",
+    "csa_swa_merge", "csa_quantize", "csa_dequantize", "csa_mxfp4_to_fp8",
+    "csa_abi_version", "csa_status_string", "csa_last_error",
+)
+
+
+class CsaTensor(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("dim", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("rope", ctypes.c_void_p)]
+
+
+class CsaBatch(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_q", ctypes.c_int64), ("max_kv", ctypes.c_int64),
+                ("q_off", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+                ("kv_off", ctypes.c_void_p), ("raw_off", ctypes.c_void_p),
+                ("raw_pos", ctypes.c_void_p)]
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load():
+    """Load libcsa.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise CsaError(f"{LIB_PATH} not found: build it with "
+                       "`python -m long_context_compressed_kv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    T = ctypes.POINTER(CsaTensor)
+    B = ctypes.POINTER(CsaBatch)
+    sig = {
+        "csa_kv_compress": [T, P, I64, P, I32, I32, I64, I64, T, P],
+        "csa_indexer_score": [T, I32, P, T, B, I32, I32, P, I32, I64, P],
+        "csa_topk_select": [P, I32, I64, B, I32, I32, P, P],
+        "csa_sparse_mqa_attn": [T, I32, T, P, I32, T, I32, B, I32, F32, P, I32, P, P],
+        "csa_swa_merge": [P, P, P, P, I64, I32, P, I32, P, P],
+        "csa_quantize": [T, T, P],
+        "csa_dequantize": [T, P, P],
+        "csa_mxfp4_to_fp8": [T, P, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.csa_abi_version.restype = ctypes.c_int
+    lib.csa_abi_version.argtypes = []
+    lib.csa_status_string.restype = ctypes.c_char_p
+    lib.csa_status_string.argtypes = [ctypes.c_int]
+    lib.csa_last_error.restype = ctypes.c_char_p
+    lib.csa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def check(status, what):
+    if status != CSA_OK:
+        lib = load()
+        raise CsaError(f"{what}: {lib.csa_status_string(status).decode()} "
+                       f"({lib.csa_last_error().decode()})")

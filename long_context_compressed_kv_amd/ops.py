@@ -1,0 +1,233 @@
+"""Python binding of the CSA/HCA library: the C-ABI calls with torch tensors.
+
+Argument marshalling only: every step runs in libcsa.so's HIP kernels, on the
+current torch stream.  Torch provides device memory and streams.
+"""
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import CSA_BF16, CSA_F32, CSA_FP8_MIXED, CSA_MXFP4, CsaBatch, CsaTensor, check
+
+F32, BF16, FP8_MIXED, MXFP4 = CSA_F32, CSA_BF16, CSA_FP8_MIXED, CSA_MXFP4
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+@dataclass
+class KV:
+    """A matrix of `rows` vectors of `dim` elements in one storage format.
+
+    F32 / BF16 : data float32 / bfloat16 [rows, dim]
+    FP8_MIXED  : data uint8 [rows, 448] (e4m3fn), scale uint8 [rows, 4] (e8m0),
+                 rope bfloat16 [rows, 64]; dim 512
+    MXFP4      : data uint8 [rows, dim/2] (two e2m1 per byte), scale uint8
+                 [rows, dim/32] (e8m0)
+    """
+    fmt: int
+    dim: int
+    data: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+    rope: Optional[torch.Tensor] = None
+
+    @property
+    def rows(self):
+        return self.data.shape[0]
+
+    def c(self):
+        _need_cuda(self.data, self.scale, self.rope)
+        return CsaTensor(self.fmt, self.dim, self.rows, _ptr(self.data), _ptr(self.scale),
+                         _ptr(self.rope))
+
+    def narrow(self, start, length):
+        """Rows start .. start+length-1 (a view)."""
+        f = lambda t: None if t is None else t.narrow(0, start, length)
+        return KV(self.fmt, self.dim, f(self.data), f(self.scale), f(self.rope))
+
+    @staticmethod
+    def empty(fmt, rows, dim, device="cuda"):
+        if fmt == F32:
+            return KV(fmt, dim, torch.empty(rows, dim, dtype=torch.float32, device=device))
+        if fmt == BF16:
+            return KV(fmt, dim, torch.empty(rows, dim, dtype=torch.bfloat16, device=device))
+        if fmt == FP8_MIXED:
+            assert dim == 512
+            return KV(fmt, dim, torch.empty(rows, 448, dtype=torch.uint8, device=device),
+                      torch.empty(rows, 4, dtype=torch.uint8, device=device),
+                      torch.empty(rows, 64, dtype=torch.bfloat16, device=device))
+        if fmt == MXFP4:
+            assert dim % 32 == 0
+            return KV(fmt, dim, torch.empty(rows, dim // 2, dtype=torch.uint8, device=device),
+                      torch.empty(rows, dim // 32, dtype=torch.uint8, device=device))
+        raise ValueError(fmt)
+
+
+def dense(t):
+    """A float32 / bfloat16 tensor [..., dim] as a KV view of its rows."""
+    fmt = {torch.float32: F32, torch.bfloat16: BF16}[t.dtype]
+    return KV(fmt, t.shape[-1], t.reshape(-1, t.shape[-1]))
+
+
+@dataclass
+class Batch:
+    """Requests of a call (see csa_batch in include/csa.h).  Offsets and
+    positions are int64 device tensors; n_q and max_kv are host ints."""
+    q_off: torch.Tensor
+    q_pos: torch.Tensor
+    kv_off: Optional[torch.Tensor]
+    raw_off: Optional[torch.Tensor]
+    raw_pos: Optional[torch.Tensor]
+    n_q: int
+    max_kv: int
+
+    @property
+    def n_req(self):
+        return self.q_pos.shape[0]
+
+    def c(self):
+        for t in (self.q_off, self.q_pos, self.kv_off, self.raw_off, self.raw_pos):
+            if t is not None:
+                _need_cuda(t)
+                assert t.dtype == torch.int64
+        return CsaBatch(self.n_req, 0, self.n_q, self.max_kv, _ptr(self.q_off), _ptr(self.q_pos),
+                        _ptr(self.kv_off), _ptr(self.raw_off), _ptr(self.raw_pos))
+
+    @staticmethod
+    def make(q_counts, q_pos, kv_counts=None, raw_counts=None, raw_pos=None, device="cuda"):
+        """Build from per-request host lists."""
+        def off(c):
+            o = [0]
+            for x in c:
+                o.append(o[-1] + int(x))
+            return torch.tensor(o, dtype=torch.int64, device=device)
+        i64 = lambda v: torch.tensor([int(x) for x in v], dtype=torch.int64, device=device)
+        return Batch(off(q_counts), i64(q_pos),
+                     off(kv_counts) if kv_counts is not None else None,
+                     off(raw_counts) if raw_counts is not None else None,
+                     i64(raw_pos) if raw_pos is not None else None,
+                     int(sum(int(x) for x in q_counts)),
+                     int(max([int(x) for x in kv_counts] or [0])) if kv_counts is not None else 0)
+
+
+# ----------------------------------------------------------------------------- calls
+
+
+def kv_compress(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out: KV):
+    """CSA step 1: entries entry_begin .. +n_entries of one sequence into out[0:n]."""
+    _need_cuda(logits, slot_bias)
+    lib = _lib.load()
+    xc, oc = x.c(), out.c()
+    check(lib.csa_kv_compress(ctypes.byref(xc), _ptr(logits), int(x_pos0), _ptr(slot_bias),
+                              int(m), int(w), int(entry_begin), int(n_entries),
+                              ctypes.byref(oc), _stream()), "csa_kv_compress")
+    return out
+
+
+def indexer_score(qi: KV, n_heads, ki: KV, batch: Batch, m, scores, score_fmt,
+                  head_w=None, relu=True):
+    """CSA step 2: indexer scores [n_q, ld] (columns beyond each row's visible
+    entries are left untouched)."""
+    _need_cuda(scores, head_w)
+    lib = _lib.load()
+    qc, kc, bc = qi.c(), ki.c(), batch.c()
+    check(lib.csa_indexer_score(ctypes.byref(qc), int(n_heads), _ptr(head_w), ctypes.byref(kc),
+                                ctypes.byref(bc), int(m), 1 if relu else 0, _ptr(scores),
+                                int(score_fmt), int(scores.shape[1]), _stream()),
+          "csa_indexer_score")
+    return scores
+
+
+def topk_select(scores, score_fmt, batch: Batch, m, k, idx=None):
+    """CSA step 2: int32 [n_q, k] ascending entry indices, -1 padded."""
+    _need_cuda(scores)
+    if idx is None:
+        idx = torch.empty(batch.n_q, k, dtype=torch.int32, device=scores.device)
+    lib = _lib.load()
+    bc = batch.c()
+    check(lib.csa_topk_select(_ptr(scores), int(score_fmt), int(scores.shape[1]),
+                              ctypes.byref(bc), int(m), int(k), _ptr(idx), _stream()),
+          "csa_topk_select")
+    return idx
+
+
+def sparse_mqa_attn(q: KV, n_heads, kv: Optional[KV], idx, k, raw: Optional[KV], window,
+                    batch: Batch, m, out, out_fmt, lse=None, scale=None):
+    """CSA step 3 / HCA: attention over selected (idx) or all visible entries
+    (idx=None) plus the window; out [n_q*H, D], lse [n_q*H] (optional)."""
+    _need_cuda(idx, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.dim)
+    lib = _lib.load()
+    qc, bc = q.c(), batch.c()
+    kvc = kv.c() if kv is not None else None
+    rc = raw.c() if raw is not None else None
+    check(lib.csa_sparse_mqa_attn(ctypes.byref(qc), int(n_heads),
+                                  ctypes.byref(kvc) if kvc is not None else None,
+                                  _ptr(idx), int(k),
+                                  ctypes.byref(rc) if rc is not None else None, int(window),
+                                  ctypes.byref(bc), int(m), float(scale), _ptr(out),
+                                  int(out_fmt), _ptr(lse), _stream()),
+          "csa_sparse_mqa_attn")
+    return out
+
+
+def swa_merge(o_a, lse_a, o_b, lse_b, out, out_fmt, lse_out=None):
+    """Log-sum-exp combination of two partial attentions."""
+    _need_cuda(o_a, lse_a, o_b, lse_b, out, lse_out)
+    lib = _lib.load()
+    check(lib.csa_swa_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), int(o_a.shape[0]),
+                            int(o_a.shape[1]), _ptr(out), int(out_fmt), _ptr(lse_out), _stream()),
+          "csa_swa_merge")
+    return out
+
+
+def quantize(src: KV, dst: KV):
+    lib = _lib.load()
+    sc, dc = src.c(), dst.c()
+    check(lib.csa_quantize(ctypes.byref(sc), ctypes.byref(dc), _stream()), "csa_quantize")
+    return dst
+
+
+def dequantize(src: KV, out=None):
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty(src.rows, src.dim, dtype=torch.float32, device=src.data.device)
+    _need_cuda(out)
+    sc = src.c()
+    check(lib.csa_dequantize(ctypes.byref(sc), _ptr(out), _stream()), "csa_dequantize")
+    return out
+
+
+def mxfp4_to_fp8(src: KV):
+    lib = _lib.load()
+    dev = src.data.device
+    fp8 = torch.empty(src.rows, src.dim, dtype=torch.uint8, device=dev)
+    g = torch.empty(src.rows, dtype=torch.uint8, device=dev)
+    ok = torch.empty(src.rows, dtype=torch.uint8, device=dev)
+    sc = src.c()
+    check(lib.csa_mxfp4_to_fp8(ctypes.byref(sc), _ptr(fp8), _ptr(g), _ptr(ok), _stream()),
+          "csa_mxfp4_to_fp8")
+    return fp8, g, ok
+
+
+def abi_version():
+    return _lib.load().csa_abi_version()

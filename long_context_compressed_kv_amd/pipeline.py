@@ -1,0 +1,181 @@
+"""One CSA or HCA layer as a sequence of library calls (plumbing only).
+
+Prefill (one sequence):
+  CSA: kv_compress (new entries into the cache) -> indexer_score -> topk_select
+       -> sparse_mqa_attn over the selected entries and the window, one softmax
+  HCA: kv_compress -> sparse_mqa_attn over all visible entries and the window
+Decode (a batch of requests, one query each):
+  CSA: indexer_score -> topk_select -> sparse_mqa_attn(selected entries)
+       and sparse_mqa_attn(window) -> swa_merge
+  HCA: sparse_mqa_attn(visible entries) and sparse_mqa_attn(window) -> swa_merge
+(page "DeepSeek V4 深度解析", section 2: the three CSA steps and HCA).
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+from . import ops
+from .ops import BF16, F32, KV, Batch
+
+INDEXER_HEADS = 4
+
+
+def _score_dtype(fmt):
+    return torch.bfloat16 if fmt == BF16 else torch.float32
+
+
+def _out_dtype(fmt):
+    return torch.bfloat16 if fmt == BF16 else torch.float32
+
+
+@dataclass
+class Buffers:
+    """Reusable device buffers of a layer call (allocated on first use)."""
+    store: dict = field(default_factory=dict)
+
+    def get(self, name, shape, dtype, device="cuda"):
+        t = self.store.get(name)
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+            t = torch.empty(shape, dtype=dtype, device=device)
+            self.store[name] = t
+        return t
+
+
+# ---------------------------------------------------------------- prefill
+
+
+@dataclass
+class PrefillLayer:
+    """A prefill of T query tokens at positions pos0 .. pos0+T-1 of one sequence.
+
+    raw   : raw KV rows for positions raw_pos0 .. pos0+T-1 (history + chunk)
+    z     : compression logits aligned with raw; bias: slot biases [w]
+    cache : entry tensor with room for all entries up to pos0+T (rows
+            0 .. n_cached-1 already filled)
+    q     : [T*H, D] attention queries; qi: [T*4, 64] indexer queries;
+            ki: [>= n_entries, 64] indexer keys (CSA only)
+    """
+    csa: bool
+    H: int
+    m: int
+    w: int
+    k: int
+    window: int
+    raw: KV
+    z: torch.Tensor
+    bias: torch.Tensor
+    raw_pos0: int
+    pos0: int
+    T: int
+    cache: KV
+    n_cached: int
+    q: KV
+    qi: Optional[KV] = None
+    ki: Optional[KV] = None
+    score_fmt: int = F32
+    out_fmt: int = F32
+    buf: Buffers = field(default_factory=Buffers)
+
+    def __post_init__(self):
+        dev = self.q.data.device
+        self.n_entries = (self.pos0 + self.T) // self.m
+        self.first_new = self.pos0 // self.m
+        assert self.first_new == self.n_cached, "cache must hold every entry before the chunk"
+        assert self.cache.rows >= self.n_entries
+        self.batch = Batch.make([self.T], [self.pos0], kv_counts=[self.n_entries],
+                                raw_counts=[self.raw.rows], raw_pos=[self.raw_pos0], device=dev)
+
+    def compress(self):
+        n_new = self.n_entries - self.first_new
+        ops.kv_compress(self.raw, self.z, self.raw_pos0, self.bias, self.m, self.w,
+                        self.first_new, n_new, self.cache.narrow(self.first_new, max(n_new, 0)))
+
+    def select(self):
+        ld = self.n_entries
+        scores = self.buf.get("scores", (self.T, ld), _score_dtype(self.score_fmt))
+        ops.indexer_score(self.qi, INDEXER_HEADS, self.ki, self.batch, self.m, scores,
+                          self.score_fmt)
+        idx = self.buf.get("idx", (self.T, self.k), torch.int32)
+        ops.topk_select(scores, self.score_fmt, self.batch, self.m, self.k, idx)
+        return scores, idx
+
+    def attend(self, idx):
+        out = self.buf.get("out", (self.T * self.H, self.q.dim), _out_dtype(self.out_fmt))
+        lse = self.buf.get("lse", (self.T * self.H,), torch.float32)
+        ops.sparse_mqa_attn(self.q, self.H, self.cache, idx, self.k if idx is not None else 0,
+                            self.raw, self.window, self.batch, self.m, out, self.out_fmt, lse)
+        return out, lse
+
+    def run(self):
+        self.compress()
+        scores = idx = None
+        if self.csa:
+            scores, idx = self.select()
+        out, lse = self.attend(idx)
+        return {"out": out, "lse": lse, "idx": idx, "scores": scores}
+
+
+# ---------------------------------------------------------------- decode
+
+
+@dataclass
+class DecodeLayer:
+    """One decode step of a batch: request r has one query at position ctx[r],
+    entries kv_off[r] .. of `cache`, and window rows swa_off[r] .. of `swa`
+    holding positions swa_pos[r] .. ctx[r]."""
+    csa: bool
+    H: int
+    m: int
+    k: int
+    window: int
+    ctx: list
+    n_entries: list
+    swa_len: list
+    cache: KV
+    swa: KV
+    q: KV
+    qi: Optional[KV] = None
+    ki: Optional[KV] = None
+    score_fmt: int = BF16
+    out_fmt: int = BF16
+    buf: Buffers = field(default_factory=Buffers)
+
+    def __post_init__(self):
+        dev = self.q.data.device
+        B = len(self.ctx)
+        self.B = B
+        swa_pos = [int(c) - int(s) + 1 for c, s in zip(self.ctx, self.swa_len)]
+        self.batch = Batch.make([1] * B, self.ctx, kv_counts=self.n_entries,
+                                raw_counts=self.swa_len, raw_pos=swa_pos, device=dev)
+        self.ld = max(int(x) for x in self.n_entries)
+
+    def select(self):
+        scores = self.buf.get("scores", (self.B, self.ld), _score_dtype(self.score_fmt))
+        ops.indexer_score(self.qi, INDEXER_HEADS, self.ki, self.batch, self.m, scores,
+                          self.score_fmt)
+        idx = self.buf.get("idx", (self.B, self.k), torch.int32)
+        ops.topk_select(scores, self.score_fmt, self.batch, self.m, self.k, idx)
+        return scores, idx
+
+    def attend(self, idx):
+        rows, D = self.B * self.H, self.q.dim
+        o_c = self.buf.get("o_c", (rows, D), torch.float32)
+        l_c = self.buf.get("l_c", (rows,), torch.float32)
+        o_w = self.buf.get("o_w", (rows, D), torch.float32)
+        l_w = self.buf.get("l_w", (rows,), torch.float32)
+        ops.sparse_mqa_attn(self.q, self.H, self.cache, idx, self.k if idx is not None else 0,
+                            None, 0, self.batch, self.m, o_c, F32, l_c)
+        ops.sparse_mqa_attn(self.q, self.H, None, None, 0, self.swa, self.window, self.batch,
+                            self.m, o_w, F32, l_w)
+        out = self.buf.get("out", (rows, D), _out_dtype(self.out_fmt))
+        lse = self.buf.get("lse", (rows,), torch.float32)
+        ops.swa_merge(o_c, l_c, o_w, l_w, out, self.out_fmt, lse)
+        return out, lse
+
+    def run(self):
+        scores = idx = None
+        if self.csa:
+            scores, idx = self.select()
+        out, lse = self.attend(idx)
+        return {"out": out, "lse": lse, "idx": idx, "scores": scores}

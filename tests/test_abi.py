@@ -1,0 +1,125 @@
+"""The C ABI library loads, exports every call declared in include/csa.h, and
+rejects bad arguments on the host before launching anything (no GPU needed:
+validation fails before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_compressed_kv_amd import _lib
+from long_context_compressed_kv_amd._lib import CsaBatch, CsaTensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+BAD_ARG, UNSUPPORTED = 1, 2
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:csa_status|int|const char\*)\s+(csa_\w+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_calls():
+    names = declared_symbols()
+    for n in ("csa_kv_compress", "csa_indexer_score", "csa_topk_select",
+              "csa_sparse_mqa_attn", "csa_swa_merge"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(declared_symbols()) == set(_lib.EXPORTED)
+
+
+def test_version_and_strings(lib):
+    assert lib.csa_abi_version() == 1
+    assert lib.csa_status_string(0) == b"ok"
+    assert lib.csa_status_string(3) == b"workspace too small"
+
+
+def _t(fmt, dim, rows, data=FAKE, scale=None, rope=None):
+    return CsaTensor(fmt, dim, rows, data, scale, rope)
+
+
+def test_kv_compress_validation(lib):
+    x = _t(0, 128, 64)
+    out = _t(0, 128, 16)
+    z = b = FAKE
+    call = lambda xx, oo, m, w, e0, n, pos0=0: lib.csa_kv_compress(
+        ctypes.byref(xx), z, pos0, b, m, w, e0, n, ctypes.byref(oo), None)
+    assert call(x, out, 4, 2, 0, 4) == BAD_ARG              # w < m
+    assert call(x, out, 4, 2000, 0, 4) == BAD_ARG           # w too large
+    assert call(x, out, 4, 8, 0, 17) == BAD_ARG             # more entries than output rows
+    assert call(x, out, 4, 8, 0, 16, pos0=1) == BAD_ARG     # raw rows miss position 0
+    assert call(x, out, 4, 8, 0, 17) == BAD_ARG
+    assert call(_t(0, 128, 64), _t(1, 64, 16), 4, 8, 0, 4) == BAD_ARG   # dim mismatch
+    assert call(_t(2, 512, 64), _t(0, 512, 16), 4, 8, 0, 4) == BAD_ARG  # mixed without scales
+    assert call(_t(2, 512, 64, scale=FAKE, rope=FAKE), _t(0, 512, 16), 4, 8, 0, 4) == UNSUPPORTED
+    assert call(_t(0, 96, 64), _t(0, 96, 16), 4, 8, 0, 4) == UNSUPPORTED  # not a power of two
+    assert call(x, out, 4, 8, 0, 0) == 0                    # nothing to do, nothing launched
+    assert b"raw rows" in lib.csa_last_error() or lib.csa_last_error() == b""
+
+
+def _batch(n_q=4, n_req=1, max_kv=16):
+    return CsaBatch(n_req, 0, n_q, max_kv, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_indexer_validation(lib):
+    qi, ki = _t(1, 64, 16), _t(1, 64, 32)
+    bt = _batch()
+    f = lambda qi_, h, ki_, b_, ld, sf=1: lib.csa_indexer_score(
+        ctypes.byref(qi_), h, None, ctypes.byref(ki_), ctypes.byref(b_), 4, 1, FAKE, sf, ld, None)
+    assert f(qi, 2, ki, bt, 16) == UNSUPPORTED               # 2 heads
+    assert f(qi, 4, _t(0, 64, 32), bt, 16) == UNSUPPORTED    # format mismatch
+    assert f(qi, 4, ki, bt, 8) == BAD_ARG                    # ld < max_kv
+    assert f(_t(1, 64, 12), 4, ki, bt, 16) == BAD_ARG        # rows != n_q * heads
+    assert f(qi, 4, ki, bt, 16, sf=2) == UNSUPPORTED         # score format
+    assert f(_t(3, 64, 16, scale=None), 4, _t(3, 64, 32), bt, 16) == BAD_ARG  # MXFP4 without scales
+
+
+def test_topk_validation(lib):
+    bt = _batch()
+    f = lambda k, ld, sf=1: lib.csa_topk_select(FAKE, sf, ld, ctypes.byref(bt), 4, k, FAKE, None)
+    assert f(0, 16) == BAD_ARG
+    assert f(5000, 16) == BAD_ARG
+    assert f(8, 15) == BAD_ARG
+    assert f(8, 16, sf=2) == UNSUPPORTED
+
+
+def test_attn_validation(lib):
+    bt = _batch(n_q=2)
+    q = _t(1, 128, 2 * 64)
+    kv = _t(1, 128, 100)
+    f = lambda qq, h, kk, of=1, m=4, k=8: lib.csa_sparse_mqa_attn(
+        ctypes.byref(qq), h, ctypes.byref(kk) if kk is not None else None, None, k, None, 0,
+        ctypes.byref(bt), m, 0.1, FAKE, of, None, None)
+    assert f(q, 48, kv) == BAD_ARG                  # rows != n_q * heads
+    assert f(_t(1, 128, 2 * 48), 48, kv) == UNSUPPORTED   # 48 heads
+    assert f(q, 64, _t(1, 256, 100)) == BAD_ARG     # kv dim mismatch
+    assert f(_t(1, 256, 128), 64, None) == UNSUPPORTED   # D = 256
+    assert f(q, 64, kv, of=2) == UNSUPPORTED        # out format
+    assert f(q, 64, kv, m=0) == BAD_ARG
+    assert f(q, 64, _t(2, 128, 100, scale=FAKE, rope=FAKE)) == BAD_ARG  # mixed needs D 512
+    assert f(_t(0, 128, 128), 64, kv) == UNSUPPORTED   # f32 q with bf16 kv
+
+
+def test_merge_and_codec_validation(lib):
+    assert lib.csa_swa_merge(FAKE, FAKE, FAKE, FAKE, 4, 6, FAKE, 1, None, None) == BAD_ARG
+    assert lib.csa_swa_merge(FAKE, FAKE, FAKE, FAKE, 4, 8, FAKE, 3, None, None) == UNSUPPORTED
+    assert lib.csa_swa_merge(None, FAKE, FAKE, FAKE, 4, 8, FAKE, 1, None, None) == BAD_ARG
+    assert lib.csa_swa_merge(None, None, None, None, 0, 8, None, 1, None, None) == 0
+    src, dst = _t(0, 512, 4), _t(2, 512, 4, scale=FAKE, rope=FAKE)
+    assert lib.csa_quantize(ctypes.byref(src), ctypes.byref(_t(2, 512, 5, scale=FAKE, rope=FAKE)), None) == BAD_ARG
+    assert lib.csa_quantize(ctypes.byref(dst), ctypes.byref(src), None) == UNSUPPORTED
+    assert lib.csa_quantize(ctypes.byref(_t(0, 40, 4)), ctypes.byref(_t(3, 40, 4, scale=FAKE)), None) == BAD_ARG
+    assert lib.csa_mxfp4_to_fp8(ctypes.byref(src), FAKE, FAKE, FAKE, None) == BAD_ARG

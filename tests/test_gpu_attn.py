@@ -1,0 +1,206 @@
+"""csa_sparse_mqa_attn and csa_swa_merge against the oracle's attention.
+
+The selected-entry lists come from the oracle (or from seeded draws), so the
+comparison isolates the attention step."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_compressed_kv_amd import ops
+from long_context_compressed_kv_amd.ops import BF16, F32, KV, Batch
+from oracle import csa as ref
+
+from gpu_inputs import dev_f32, dev_kv, ref_vals, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _prefill_case(rng, T, H, D, n_ent, m, k, window, q_fmt, kv_fmt, out_fmt, sparse,
+                  pos0=0, raw_hist=0):
+    raw = rng.standard_normal((raw_hist + T, D)).astype(np.float32)
+    ent = rng.standard_normal((n_ent, D)).astype(np.float32)
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    raw_pos0 = pos0 - raw_hist
+    qd, kvd, rd = dev_kv(q.reshape(-1, D), q_fmt), dev_kv(ent, kv_fmt), dev_kv(raw, q_fmt)
+    qv, ev, rv = ref_vals(q, q_fmt), ref_vals(ent, kv_fmt), ref_vals(raw, q_fmt)
+    idx = None
+    if sparse:
+        idx = np.full((T, k), -1, np.int64)
+        for i in range(T):
+            t = pos0 + i
+            nv = min((t + 1) // m, n_ent)
+            cnt = min(k, nv) if i % 5 else max(0, min(k, nv) - 3)    # some short rows
+            sel = np.sort(rng.choice(nv, cnt, replace=False)) if cnt else np.zeros(0, np.int64)
+            idx[i, :cnt] = sel
+    batch = Batch.make([T], [pos0], kv_counts=[n_ent], raw_counts=[raw_hist + T],
+                       raw_pos=[raw_pos0])
+    out = torch.empty(T * H, D, device="cuda",
+                      dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16)
+    lse = torch.empty(T * H, device="cuda")
+    idx_d = torch.from_numpy(idx.astype(np.int32)).cuda() if sparse else None
+    ops.sparse_mqa_attn(qd, H, kvd, idx_d, k if sparse else 0, rd, window, batch, m, out,
+                        F32 if out_fmt == "f32" else BF16, lse)
+    torch.cuda.synchronize()
+    g, gl = to_np(out).reshape(T, H, D), to_np(lse).reshape(T, H)
+    sc = 1 / math.sqrt(D)
+    err, lerr = 0.0, 0.0
+    for i in range(T):
+        t = pos0 + i
+        nv = min((t + 1) // m, n_ent)
+        keys_e = ev[idx[i][idx[i] >= 0]] if sparse else ev[:nv]
+        pos = ref.window_positions(t, window)
+        keys = np.concatenate([keys_e, rv[pos - raw_pos0]])
+        o, l = ref.attend(qv[i], keys, sc)
+        err = max(err, np.max(np.abs(g[i] - o)))
+        lerr = max(lerr, np.max(np.abs(gl[i] - l)))
+    return err, lerr
+
+
+@pytest.mark.parametrize("T,H,D,n_ent,m,k,window,qf,kvf,of,sparse,pos0,hist", [
+    (67, 16, 128, 16, 4, 8, 128, "f32", "f32", "f32", True, 0, 0),     # fp32 CSA, H=16
+    (67, 16, 128, 16, 4, 8, 128, "f32", "f32", "f32", False, 0, 0),
+    (29, 16, 128, 90, 4, 40, 128, "f32", "f32", "f32", True, 330, 128),
+    (301, 64, 128, 18, 16, 0, 128, "bf16", "bf16", "bf16", False, 0, 0),  # HCA-like
+    (45, 64, 128, 40, 4, 24, 32, "bf16", "bf16", "f32", True, 0, 0),
+    (21, 64, 512, 130, 4, 100, 16, "bf16", "fp8_mixed", "bf16", True, 500, 16),
+    (9, 128, 512, 277, 4, 200, 128, "bf16", "fp8_mixed", "bf16", True, 1100, 128),
+    (40, 64, 512, 9, 4, 0, 16, "bf16", "fp8_mixed", "f32", False, 0, 0),
+    (33, 32, 512, 20, 2, 12, 8, "bf16", "bf16", "bf16", True, 0, 0),
+])
+def test_attn_prefill(T, H, D, n_ent, m, k, window, qf, kvf, of, sparse, pos0, hist):
+    rng = np.random.default_rng(T * 7 + H + D)
+    err, lerr = _prefill_case(rng, T, H, D, n_ent, m, k, window, qf, kvf, of, sparse,
+                              pos0=pos0, raw_hist=hist)
+    # bf16 compute (bf16 operands and probabilities, fp32 accumulation) is held
+    # to the bf16 bound whatever the output format; fp32 compute to 1e-4
+    tol = TOL["bf16"] if qf == "bf16" else TOL["f32"]
+    assert err <= tol, err
+    assert lerr <= (1e-4 if qf == "f32" else 2e-2), lerr
+
+
+def test_attn_chunk_with_history():
+    """Queries at positions 1000.. with 128 history rows in the raw buffer."""
+    rng = np.random.default_rng(3)
+    err, lerr = _prefill_case(rng, 40, 128, 512, 260, 4, 64, 128, "bf16", "fp8_mixed", "bf16",
+                              True, pos0=1000, raw_hist=128)
+    assert err <= 2e-2 and lerr <= 2e-2
+
+
+def _decode_case(rng, ctxs, H, D, m, k, window, kv_fmt):
+    B = len(ctxs)
+    n_ent = [(c + 1) // m for c in ctxs]
+    swa_len = [min(window, c + 1) for c in ctxs]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len]
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    idx = np.full((B, k), -1, np.int64)
+    for r in range(B):
+        cnt = min(k, n_ent[r])
+        idx[r, :cnt] = np.sort(rng.choice(n_ent[r], cnt, replace=False))
+    ent_all, swa_all = np.concatenate(ents), np.concatenate(swas)
+    kvd, sd, qd = dev_kv(ent_all, kv_fmt), dev_kv(swa_all, "bf16"), dev_kv(q.reshape(-1, D), "bf16")
+    batch = Batch.make([1] * B, ctxs, kv_counts=n_ent, raw_counts=swa_len,
+                       raw_pos=[c - s + 1 for c, s in zip(ctxs, swa_len)])
+    rows = B * H
+    oc, lc = torch.empty(rows, D, device="cuda"), torch.empty(rows, device="cuda")
+    ow, lw = torch.empty(rows, D, device="cuda"), torch.empty(rows, device="cuda")
+    ou, lu = torch.empty(rows, D, device="cuda"), torch.empty(rows, device="cuda")
+    idx_d = torch.from_numpy(idx.astype(np.int32)).cuda()
+    ops.sparse_mqa_attn(qd, H, kvd, idx_d, k, None, 0, batch, m, oc, F32, lc)
+    ops.sparse_mqa_attn(qd, H, None, None, 0, sd, window, batch, m, ow, F32, lw)
+    ops.sparse_mqa_attn(qd, H, kvd, idx_d, k, sd, window, batch, m, ou, F32, lu)
+    om, lm = torch.empty(rows, D, device="cuda"), torch.empty(rows, device="cuda")
+    ops.swa_merge(oc, lc, ow, lw, om, F32, lm)
+    torch.cuda.synchronize()
+    sc = 1 / math.sqrt(D)
+    qv = ref_vals(q, "bf16")
+    errs = []
+    for r in range(B):
+        ev, sv = ref_vals(ents[r], kv_fmt), ref_vals(swas[r], "bf16")
+        keys = np.concatenate([ev[idx[r][idx[r] >= 0]], sv[-min(window, ctxs[r] + 1):]])
+        o, l = ref.attend(qv[r], keys, sc)
+        sl = slice(r * H, (r + 1) * H)
+        errs.append(max(np.max(np.abs(to_np(om[sl]) - o)), np.max(np.abs(to_np(ou[sl]) - o)),
+                        np.max(np.abs(to_np(lm[sl]) - l))))
+    return max(errs), (om, ou)
+
+
+def test_attn_decode_split_merge_equals_union():
+    rng = np.random.default_rng(4)
+    err, (om, ou) = _decode_case(rng, [5000, 131, 40, 2047, 700], 64, 512, 4, 64, 128, "fp8_mixed")
+    assert err <= 2e-2
+    # split + merge and the one-kernel union round the probabilities to bf16
+    # against different running maxima: both are within the bf16 bound
+    assert torch.max(torch.abs(om - ou)).item() <= 2e-2
+
+
+def test_attn_window_only_and_empty_rows():
+    """No entries and window 0 for some rows: o = 0, lse = -inf."""
+    H, D = 32, 128
+    q = dev_kv(np.random.default_rng(1).standard_normal((2 * H, D)).astype(np.float32), "bf16")
+    batch = Batch.make([2], [0], kv_counts=[0], raw_counts=[2], raw_pos=[0])
+    out = torch.full((2 * H, D), 7.0, device="cuda")
+    lse = torch.zeros(2 * H, device="cuda")
+    kv = dev_kv(np.zeros((1, D), np.float32), "bf16")
+    ops.sparse_mqa_attn(q, H, kv, None, 0, None, 0, batch, 4, out, F32, lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isinf(lse)) and torch.all(lse < 0)
+
+
+def test_swa_merge_random_and_infinite():
+    rng = np.random.default_rng(9)
+    rows, D = 1000, 512
+    oa, ob = rng.standard_normal((rows, D)), rng.standard_normal((rows, D))
+    la, lb = rng.standard_normal(rows) * 5, rng.standard_normal(rows) * 5
+    la[:10] = -np.inf
+    lb[5:15] = -np.inf
+    out = torch.empty(rows, D, device="cuda")
+    lo = torch.empty(rows, device="cuda")
+    ops.swa_merge(dev_f32(oa), dev_f32(la), dev_f32(ob), dev_f32(lb), out, F32, lo)
+    outb = torch.empty(rows, D, device="cuda", dtype=torch.bfloat16)
+    ops.swa_merge(dev_f32(oa), dev_f32(la), dev_f32(ob), dev_f32(lb), outb, BF16)
+    torch.cuda.synchronize()
+    fa, fb = oa.astype(np.float32).astype(np.float64), ob.astype(np.float32).astype(np.float64)
+    la32, lb32 = la.astype(np.float32).astype(np.float64), lb.astype(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        o, l = ref.merge(fa, la32, fb, lb32)
+    both = np.isinf(la32) & np.isinf(lb32)
+    o[both] = 0.0
+    g, gl = to_np(out), to_np(lo)
+    assert np.max(np.abs(g - o)) <= 1e-5
+    assert np.all(np.isneginf(gl[both]))
+    assert np.max(np.abs(gl[~both] - l[~both])) <= 1e-5
+    assert np.max(np.abs(to_np(outb) - o)) <= 2e-2
+
+
+def test_attn_deterministic_and_batch_invariant():
+    """A request's output is bitwise the same alone and inside a batch."""
+    rng = np.random.default_rng(10)
+    H, D, m, k = 64, 512, 4, 32
+    ctxs = [900, 300, 1500]
+    n_ent = [(c + 1) // m for c in ctxs]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    q = rng.standard_normal((3, H, D)).astype(np.float32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for n in n_ent]).astype(np.int32)
+
+    def run(order):
+        e = np.concatenate([ents[r] for r in order])
+        kvd = dev_kv(e, "fp8_mixed")
+        qd = dev_kv(q[order].reshape(-1, D), "bf16")
+        b = Batch.make([1] * len(order), [ctxs[r] for r in order],
+                       kv_counts=[n_ent[r] for r in order])
+        out = torch.empty(len(order) * H, D, device="cuda")
+        ops.sparse_mqa_attn(qd, H, kvd, torch.from_numpy(idx[order]).cuda(), k, None, 0, b, m,
+                            out, F32)
+        torch.cuda.synchronize()
+        return out.view(len(order), H, D)
+
+    a = run([0, 1, 2])
+    b = run([2, 0, 1])
+    c = run([1])
+    assert torch.equal(a[0], b[1]) and torch.equal(a[2], b[0]) and torch.equal(a[1], c[0])
+    assert torch.equal(a, run([0, 1, 2]))
