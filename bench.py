@@ -1,0 +1,435 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA/HCA compressed-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
+
+A step is one pass of a layer's whole path over one batch of synthetic
+inputs already resident in HBM:
+  1  CSA prefill, fp32, 4096 tokens:   compress -> indexer -> top-k -> attention
+  2  HCA prefill, bf16, 65536 tokens:  compress -> dense attention (default)
+  3  CSA decode, 32 x 128K context:    indexer -> top-k -> attention x2 -> merge
+  4  CSA chunked prefill, 8192 tokens at 1M: compress -> MXFP4 indexer -> top-k
+                                       -> attention
+  5  4-layer C/H/C/H decode, 64 requests, 4K-1M contexts
+Prints one JSON line (throughput, roofline of the dominant kernel, and the CPU
+oracle timed on a bounded sample of the same workload).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from long_context_compressed_kv_amd import ops  # noqa: E402
+from long_context_compressed_kv_amd.ops import BF16, F32, FP8_MIXED, KV, MXFP4  # noqa: E402
+from long_context_compressed_kv_amd.pipeline import DecodeLayer, PrefillLayer  # noqa: E402
+
+PEAK = {"hbm": 8000.0, "bf16": 2500.0, "f32": 157.3, "fp4": 10100.0}   # GB/s, TFLOP/s
+FMT = {"f32": F32, "bf16": BF16, "fp8_mixed": FP8_MIXED, "mxfp4": MXFP4}
+ENTRY_BYTES = {"fp8_mixed": 580, "bf16": 1024, "f32": 2048}
+IDX_KEY_BYTES = {"mxfp4": 34, "bf16": 128, "f32": 256}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def src_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_compressed_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ inputs on the GPU
+
+
+class Gen:
+    """Seeded synthetic draws made directly on the device (plumbing)."""
+
+    def __init__(self, seed):
+        self.g = torch.Generator(device="cuda")
+        self.g.manual_seed(seed)
+
+    def normal(self, shape, std=1.0):
+        t = torch.randn(shape, generator=self.g, device="cuda", dtype=torch.float32)
+        return t.mul_(std) if std != 1.0 else t
+
+    def kv(self, rows, dim, fmt, std=1.0, chunk=1 << 20):
+        """rows x dim draws stored in `fmt` (quantised by the library)."""
+        if fmt == "f32":
+            return KV(F32, dim, self.normal((rows, dim), std))
+        if fmt == "bf16":
+            return KV(BF16, dim, self.normal((rows, dim), std).to(torch.bfloat16))
+        out = KV.empty(FMT[fmt], rows, dim)
+        for r0 in range(0, rows, chunk):
+            n = min(chunk, rows - r0)
+            ops.quantize(KV(F32, dim, self.normal((n, dim), std)), out.narrow(r0, n))
+        return out
+
+
+# ------------------------------------------------------------------ workloads
+
+
+def attn_pairs_prefill(pos0, T, m, n_ent, window, k=None):
+    """Sum over queries of (attended entries + window tokens)."""
+    t = np.arange(pos0, pos0 + T, dtype=np.int64)
+    nv = np.minimum((t + 1) // m, n_ent)
+    ent = np.minimum(nv, k) if k is not None else nv
+    win = np.minimum(window, t + 1)
+    return int(ent.sum() + win.sum()), int(nv.sum())
+
+
+class Prefill:
+    def __init__(self, wid, copies=1):
+        self.wl = wl = synth.WORKLOADS[wid]
+        gen = Gen(1000 + wid)
+        D, H, T = wl.dim, wl.heads, wl.seq
+        csa = wl.kind == "csa_prefill"
+        hist = min(wl.pos0, max(wl.window, wl.w - wl.m))
+        raw_pos0 = wl.pos0 - hist
+        n_ent = (wl.pos0 + T) // wl.m
+        cache = gen.kv(n_ent, D, wl.kv_fmt)          # rows before pos0/m act as the cached prefix
+        raw = gen.kv(hist + T, D, wl.act_fmt)
+        z, bias = gen.normal((hist + T,)), gen.normal((wl.w,))
+        q = gen.kv(T * H, D, wl.act_fmt)
+        qi = gen.kv(T * 4, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
+        ki = gen.kv(n_ent, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
+        self.layer = PrefillLayer(csa=csa, H=H, m=wl.m, w=wl.w, k=wl.k, window=wl.window,
+                                  raw=raw, z=z, bias=bias, raw_pos0=raw_pos0, pos0=wl.pos0, T=T,
+                                  cache=cache, n_cached=wl.pos0 // wl.m, q=q, qi=qi, ki=ki,
+                                  score_fmt=FMT[wl.score_fmt], out_fmt=FMT[wl.out_fmt])
+        self.tokens = T
+        self.csa = csa
+        pairs, nv_sum = attn_pairs_prefill(wl.pos0, T, wl.m, n_ent, wl.window,
+                                           wl.k if csa else None)
+        self.attn_flops = 4.0 * D * H * pairs
+        self.idx_flops = 2.0 * 4 * 64 * nv_sum if csa else 0.0
+        cdt = "f32" if wl.act_fmt == "f32" else "bf16"
+        self.dominant = {"name": "attention", "bound": "mfma", "unit": "TFLOP/s",
+                         "work": self.attn_flops, "peak": PEAK[cdt],
+                         "per_unit": f"4*D*H = {4 * D * H} flop per (query, key) pair; "
+                                     f"{pairs} pairs per launch",
+                         "sha": src_sha("attn.hip", "common.h")}
+
+    def step(self, ev=None):
+        L = self.layer
+        L.compress()
+        idx = None
+        if self.csa:
+            _, idx = L.select()
+        if ev is not None:
+            ev[0].record()
+        L.attend(idx)
+        if ev is not None:
+            ev[1].record()
+
+    def dominant_launch(self):
+        self.layer.attend(self.layer.buf.store.get("idx") if self.csa else None)
+
+
+class Decode:
+    """One decode step over one or more layers; `copies` input sets rotated so
+    successive steps do not find their data in the last-level cache."""
+
+    def __init__(self, wid, copies=3):
+        self.wl = wl = synth.WORKLOADS[wid]
+        gen = Gen(2000 + wid)
+        ctxs = [int(c) for c in synth.decode_contexts(wl)]
+        B, D, H = len(ctxs), wl.dim, wl.heads
+        specs = wl.layers if wl.kind == "mixed_decode" else [("csa", wl.m, wl.k)]
+        self.copies = []
+        self.bytes_idx = 0.0
+        self.bytes_step = 0.0
+        for c in range(copies):
+            layers = []
+            for kind, m, k in specs:
+                csa = kind == "csa"
+                n_ent = [(t + 1) // m for t in ctxs]
+                swa_len = [min(wl.window, t + 1) for t in ctxs]
+                cache = gen.kv(sum(n_ent), D, wl.kv_fmt)
+                swa = gen.kv(sum(swa_len), D, "bf16")
+                q = gen.kv(B * H, D, "bf16")
+                qi = gen.kv(B * 4, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
+                ki = gen.kv(sum(n_ent), 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
+                layers.append(DecodeLayer(csa=csa, H=H, m=m, k=k, window=wl.window, ctx=ctxs,
+                                          n_entries=n_ent, swa_len=swa_len, cache=cache,
+                                          swa=swa, q=q, qi=qi, ki=ki,
+                                          score_fmt=FMT[wl.score_fmt], out_fmt=FMT[wl.out_fmt]))
+                if c == 0:
+                    nsum = sum(n_ent)
+                    kb = IDX_KEY_BYTES[wl.idx_fmt]
+                    sb = 2 if wl.score_fmt == "bf16" else 4
+                    if csa:
+                        self.bytes_idx += nsum * kb + nsum * sb + B * 4 * kb
+                        sel = sum(min(k, n) for n in n_ent)
+                    else:
+                        sel = nsum
+                    # entries read + window rows + q in + out
+                    self.bytes_step += (nsum * (kb + sb) if csa else 0) + \
+                        sel * ENTRY_BYTES[wl.kv_fmt] + sum(swa_len) * D * 2 + 2 * B * H * D * 2
+            self.copies.append(layers)
+        self.tokens = B
+        self.has_csa = any(s[0] == "csa" for s in specs)
+        self.dominant = {"name": "indexer", "bound": "hbm", "unit": "GB/s",
+                         "work": self.bytes_idx, "peak": PEAK["hbm"],
+                         "per_unit": f"{IDX_KEY_BYTES[wl.idx_fmt]} B key + "
+                                     f"{2 if wl.score_fmt == 'bf16' else 4} B score per "
+                                     f"(request, visible entry)",
+                         "sha": src_sha("indexer.hip", "common.h")}
+        self.graphs = None
+
+    def step_copy(self, c):
+        for L in self.copies[c]:
+            L.run()
+
+    def dominant_copy(self, c):
+        for L in self.copies[c]:
+            if L.csa:
+                ops.indexer_score(L.qi, 4, L.ki, L.batch, L.m, L.buf.store["scores"], L.score_fmt)
+
+    def capture(self):
+        """One graph per input copy for the whole step, and one per copy for
+        the dominant kernel alone."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        self.g_step, self.g_dom = [], []
+        with torch.cuda.stream(s):
+            for c in range(len(self.copies)):
+                self.step_copy(c)          # allocate buffers outside capture
+            torch.cuda.synchronize()
+            for c in range(len(self.copies)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    self.step_copy(c)
+                self.g_step.append(g)
+                g2 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g2, stream=s):
+                    self.dominant_copy(c)
+                self.g_dom.append(g2)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+
+def cpu_baseline(wid, budget_s=15.0):
+    """The oracle as it stands, single-threaded BLAS, on a bounded sample of the
+    workload: the full compression it needs plus as many queries (prefill) or
+    requests (decode) as fit in about `budget_s` seconds."""
+    from threadpoolctl import threadpool_limits
+    from oracle import codecs
+    from oracle import csa as ref
+    wl = synth.WORKLOADS[wid]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        done = 0
+        if wl.kind in ("csa_prefill", "hca_prefill"):
+            # a chunk far into the sequence: its first 256 tokens are the sample
+            seq = wl.seq if wl.pos0 == 0 else min(wl.seq, 256)
+            inp = synth.prefill_inputs(wl, seq=seq)
+            t_gen = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            vals = {"f32": lambda a: a.astype(np.float64),
+                    "bf16": lambda a: codecs.bf16_round(a).astype(np.float64),
+                    "mxfp4": lambda a: codecs.dequantize_mxfp4(*codecs.quantize_mxfp4(a))}
+            rawv = vals[wl.act_fmt](inp["raw"])
+            e0, n_ent = inp["first_new_entry"], inp["n_entries"]
+            new = ref.compress_entries(rawv, inp["z"], inp["raw_pos0"], inp["bias"], wl.m,
+                                       wl.w, e0, n_ent)
+            newv = ref.load_entries(ref.store_entries(new, wl.kv_fmt), wl.kv_fmt)
+            if e0 > 0:
+                ki = vals[wl.idx_fmt](inp["ki"])
+            rng = np.random.default_rng(0)
+            for i in rng.permutation(inp["seq"]):
+                t = inp["pos0"] + int(i)
+                q = vals[wl.act_fmt](inp["q"][i])
+                if wl.kind == "hca_prefill":
+                    ref.hca_query(t, q, newv, wl.m, rawv, inp["raw_pos0"], wl.window)
+                elif e0 == 0:
+                    ref.csa_query(t, q, newv, vals[wl.idx_fmt](inp["qi"][i]),
+                                  vals[wl.idx_fmt](inp["ki"]), wl.k, wl.m, rawv,
+                                  inp["raw_pos0"], wl.window, score_fmt=wl.score_fmt)
+                else:
+                    # selection first, then only the selected cached rows are decoded
+                    nv = min((t + 1) // wl.m, n_ent)
+                    keys = ref.score_keys(ref.indexer_scores(vals[wl.idx_fmt](inp["qi"][i]),
+                                                             ki[:nv]), wl.score_fmt)
+                    idx = ref.topk_indices(keys, wl.k)
+                    sel = idx[idx >= 0]
+                    old = sel[sel < e0]
+                    ent = np.concatenate([
+                        ref.load_entries(ref.store_entries(inp["cache"][old], wl.kv_fmt), wl.kv_fmt),
+                        newv[sel[sel >= e0] - e0]])
+                    pos = ref.window_positions(t, wl.window)
+                    ref.attend(q, np.concatenate([ent, rawv[pos - inp["raw_pos0"]]]),
+                               1.0 / math.sqrt(wl.dim))
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            sample = f"{done} of {wl.seq} query tokens (all heads) plus the compression of " \
+                     f"{n_ent - e0} entries; input draws excluded ({t_gen:.1f}s)"
+        else:
+            ctxs = synth.decode_contexts(wl)
+            specs = wl.layers if wl.kind == "mixed_decode" else [("csa", wl.m, wl.k)]
+            for r in range(len(ctxs)):
+                for li, (kind, m, k) in enumerate(specs):
+                    d = synth.decode_request(wl, r, int(ctxs[r]), m, kind == "csa", layer=li)
+                    cv = codecs.dequantize_kv_mixed(*codecs.quantize_kv_mixed(d["cache"]))
+                    q = codecs.bf16_round(d["q"]).astype(np.float64)
+                    sw = codecs.bf16_round(d["swa"]).astype(np.float64)
+                    if kind == "csa":
+                        qf = (lambda a: codecs.dequantize_mxfp4(*codecs.quantize_mxfp4(a))) \
+                            if wl.idx_fmt == "mxfp4" else \
+                            (lambda a: codecs.bf16_round(a).astype(np.float64))
+                        ref.csa_query(d["t"], q, cv, qf(d["qi"]), qf(d["ki"]), k, m, sw,
+                                      d["swa_pos0"], wl.window, score_fmt=wl.score_fmt)
+                    else:
+                        ref.hca_query(d["t"], q, cv, m, sw, d["swa_pos0"], wl.window)
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            sample = f"{done} of {len(ctxs)} requests through all {len(specs)} layers " \
+                     f"(input draws and cache quantisation included)"
+        el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s" if "prefill" in wl.kind else "requests/s",
+            "cores": 1, "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
+
+
+# ------------------------------------------------------------------ main
+
+
+def traffic_for(dom, wid):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on this kernel source and workload; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(str(wid))
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("sha") != dom["sha"]:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (three "
+                         "times): the reference for scaling HBM byte counters")
+    args = ap.parse_args()
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("this benchmark runs on one GPU only: the path has no multi-GPU part "
+              "(requests shard across GPUs with no communication)", file=sys.stderr)
+        sys.exit(2)
+    wid = args.config
+    wl = synth.WORKLOADS[wid]
+    torch.cuda.init()
+    t0 = time.time()
+    decode = wl.kind in ("csa_decode", "mixed_decode")
+    w = Decode(wid) if decode else Prefill(wid)
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: inputs ready in {time.time() - t0:.1f}s")
+
+    dom = w.dominant
+    if decode:
+        w.capture()
+        nc = len(w.copies)
+        for i in range(args.warmup):
+            w.g_step[i % nc].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            w.g_step[i % nc].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        # dominant kernel alone, same rotation
+        reps = max(args.steps, 30)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for i in range(reps):
+            w.g_dom[i % nc].replay()
+        d1.record()
+        torch.cuda.synchronize()
+        n_launch = sum(1 for L in w.copies[0] if L.csa)
+        dom_ms = d0.elapsed_time(d1) / reps / n_launch
+        work = dom["work"] / n_launch
+    else:
+        for _ in range(args.warmup):
+            w.step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            w.step(evs[i])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        work = dom["work"]
+    log(f"step {ms:.4f} ms, dominant kernel ({dom['name']}) {dom_ms:.4f} ms per launch")
+
+    if dom["unit"] == "GB/s":
+        achieved = work / (dom_ms * 1e-3) / 1e9
+    else:
+        achieved = work / (dom_ms * 1e-3) / 1e12
+    value = w.tokens / (ms * 1e-3)
+    roof = {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": dom["peak"],
+            "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4),
+            "traffic": traffic_for(dom, wid), "kernel": dom["name"],
+            "work_per_launch": dom["per_unit"], "launch_ms": round(dom_ms, 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wid)
+    metric = "CSA/HCA layer tokens/s (prefill + decode) at 128K-1M ctx; % HBM/MFMA peak"
+    line = {
+        "metric": metric, "value": round(value, 2),
+        "unit": "tokens/s" if not decode else "decode tokens/s (requests x steps)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f32": "f32"}.get(wl.act_fmt, "bf16"),
+        "data": "synthetic", "roofline": roof, "cpu_baseline": cpu,
+        "config": {"workload": wl.name, "tokens_per_step": w.tokens, "heads": wl.heads,
+                   "dim": wl.dim, "parallelism": "single GPU"},
+    }
+    if decode:
+        line["config"]["step_bytes_algorithmic"] = int(w.bytes_step)
+        line["config"]["step_hbm_frac"] = round(w.bytes_step / (ms * 1e-3) / 8e12, 4)
+        line["config"]["graph_replay"] = True
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
