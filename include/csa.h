@@ -201,17 +201,32 @@ csa_status csa_topk_select(const void* scores, int32_t score_fmt, int64_t ld,
  *   q         rows = n_q*n_heads, dim D (128 | 512), F32 or BF16
  *   kv        entries: F32 (D 128), BF16, or FP8_MIXED (D 512); may be NULL
  *             for a window-only call
- *   raw       window rows, F32 or BF16, dim D; may be NULL
+ *   raw       window rows, F32 or BF16 (q's format), dim D; may be NULL
  *   compute   F32 q, kv and raw use fp32 matrix cores; otherwise all operands
  *             are bf16 (FP8_MIXED rows dequantised to bf16 exactly) with
- *             fp32 accumulation
+ *             fp32 accumulation and bf16 probabilities
+ *   scale     > 0 (the pages fix none; 1/sqrt(D) is the usual choice)
  *   out       [n_q*n_heads][D] F32 or BF16;  lse float [n_q*n_heads] or NULL
- *   n_heads   a multiple of 32, or 8 or 16
+ *   n_heads   8, 16 or a multiple of 32 up to 128 (8 and 16 need a single
+ *             request and no split)
+ *   split_keys 0: each query's keys are processed by one workgroup.  > 0
+ *             (decode): a query's key list is cut into chunks of about
+ *             split_keys keys (at most 64 chunks) processed in parallel and
+ *             merged by log-sum-exp; needs `workspace` (device memory,
+ *             caller-owned, contents not preserved) of at least
+ *             csa_attn_workspace_size(n_q, n_heads, D, max_keys, split_keys)
+ *             bytes, where max_keys = (k if idx else batch->max_kv) + window.
+ *             Calls sharing one workspace must not overlap.
  * ------------------------------------------------------------------------- */
 csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads, const csa_tensor* kv,
                                const int32_t* idx, int32_t k, const csa_tensor* raw,
                                int32_t window, const csa_batch* batch, int32_t m, float scale,
-                               void* out, int32_t out_fmt, float* lse, hipStream_t stream);
+                               void* out, int32_t out_fmt, float* lse, int32_t split_keys,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes csa_sparse_mqa_attn needs for split_keys > 0 (0 otherwise). */
+size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t dim, int64_t max_keys,
+                               int32_t split_keys);
 
 /* ---------------------------------------------------------------------------
  * csa_swa_merge - combination of the window branch and the compressed branch.

@@ -1,40 +1,56 @@
-// Exact combination of two partial attentions over disjoint key sets by their
+// Exact combination of partial attentions over disjoint key sets by their
 // log-sum-exp (the window branch and the compressed branch are attended
-// together: page "DeepSeek V4 深度解析", section 2, CSA step 3).
-//
-// Memory bound: one wave per row, float4 per lane.
-#include "common.h"
+// together: page "DeepSeek V4 深度解析", section 2, CSA step 3):
+//   M = max_p lse_p,  w_p = e^(lse_p - M),  o = sum_p w_p o_p / sum_p w_p,
+//   lse = M + log(sum_p w_p).
+// A part with lse = -inf contributes nothing; if all are -inf, o = 0 and
+// lse = -inf.  Memory bound: one wave per row, float4 per lane, parts summed
+// in a fixed order.
+#include "merge.h"
 
 using namespace csa;
 
 namespace {
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void swa_merge_kernel(const float* __restrict__ o_a,
-                                                        const float* __restrict__ lse_a,
-                                                        const float* __restrict__ o_b,
-                                                        const float* __restrict__ lse_b,
-                                                        int64_t rows, int dim, void* out,
-                                                        float* lse_out) {
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ o0,
+                                                        const float* __restrict__ l0,
+                                                        int64_t stride_o, int64_t stride_l,
+                                                        int nparts, const int* __restrict__ cnt,
+                                                        int rows_per_q, int64_t rows, int dim,
+                                                        void* out, float* lse_out) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  const float a = lse_a[row], b = lse_b[row];
-  const float mx = fmaxf(a, b);
-  float wa = 0.0f, wb = 0.0f;
-  if (mx != -INFINITY) {
-    wa = expf(a - mx);
-    wb = expf(b - mx);
+  int n = nparts;
+  if (cnt != nullptr) {
+    n = cnt[row / rows_per_q];
+    n = n < 1 ? 1 : (n > nparts ? nparts : n);
   }
-  const float den = wa + wb;
+  auto part_o = [&](int p) {
+    return reinterpret_cast<const float*>(reinterpret_cast<const char*>(o0) + p * stride_o) + row * dim;
+  };
+  const float lv = lane < n
+      ? *(reinterpret_cast<const float*>(reinterpret_cast<const char*>(l0) + lane * stride_l) + row)
+      : -INFINITY;
+  const float mx = wave_max(lv);
+  const float w = (mx == -INFINITY || lv == -INFINITY) ? 0.0f : expf(lv - mx);
+  const float den = wave_sum(w);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  const float ca = wa * inv, cb = wb * inv;
   if (lse_out != nullptr && lane == 0) lse_out[row] = den > 0.0f ? mx + logf(den) : -INFINITY;
   for (int d = lane * 4; d < dim; d += 256) {
-    const float4 x = *reinterpret_cast<const float4*>(o_a + row * dim + d);
-    const float4 y = *reinterpret_cast<const float4*>(o_b + row * dim + d);
-    const float r0 = ca * x.x + cb * y.x, r1 = ca * x.y + cb * y.y;
-    const float r2 = ca * x.z + cb * y.z, r3 = ca * x.w + cb * y.w;
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    for (int p = 0; p < n; ++p) {
+      const float wp = __shfl(w, p);
+      if (wp != 0.0f) {
+        const float4 x = *reinterpret_cast<const float4*>(part_o(p) + d);
+        r0 = fmaf(wp, x.x, r0);
+        r1 = fmaf(wp, x.y, r1);
+        r2 = fmaf(wp, x.z, r2);
+        r3 = fmaf(wp, x.w, r3);
+      }
+    }
+    r0 *= inv; r1 *= inv; r2 *= inv; r3 *= inv;
     if constexpr (OUT_BF16) {
       uint2 u;
       u.x = pack_bf16x2(r0, r1);
@@ -49,6 +65,32 @@ __global__ __launch_bounds__(256) void swa_merge_kernel(const float* __restrict_
 
 }  // namespace
 
+csa_status launch_lse_merge_bytes(const float* o0, const float* l0, int64_t stride_o_bytes,
+                                  int64_t stride_l_bytes, int nparts, const int* cnt,
+                                  int rows_per_q, int64_t rows, int dim, void* out, int out_fmt,
+                                  float* lse_out, hipStream_t stream) {
+  const int64_t blocks = (rows + 3) / 4;
+  if (blocks > 0x7fffffff || nparts < 1 || nparts > 64)
+    return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "merge: bad row or part count");
+  if (out_fmt == CSA_BF16)
+    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, o0,
+                       l0, stride_o_bytes, stride_l_bytes, nparts, cnt, rows_per_q, rows, dim,
+                       out, lse_out);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, o0,
+                       l0, stride_o_bytes, stride_l_bytes, nparts, cnt, rows_per_q, rows, dim,
+                       out, lse_out);
+  return csa_host::check_launch("lse merge");
+}
+
+csa_status launch_lse_merge(const float* o0, const float* l0, int64_t stride_o_elems,
+                            int64_t stride_l_elems, int nparts, const int* cnt, int rows_per_q,
+                            int64_t rows, int dim, void* out, int out_fmt, float* lse_out,
+                            hipStream_t stream) {
+  return launch_lse_merge_bytes(o0, l0, stride_o_elems * 4, stride_l_elems * 4, nparts, cnt,
+                                rows_per_q, rows, dim, out, out_fmt, lse_out, stream);
+}
+
 using namespace csa_host;
 
 extern "C" csa_status csa_swa_merge(const float* o_a, const float* lse_a, const float* o_b,
@@ -62,13 +104,9 @@ extern "C" csa_status csa_swa_merge(const float* o_a, const float* lse_a, const 
     return fail(CSA_ERR_INVALID_ARGUMENT, "csa_swa_merge: null pointer");
   if (out_fmt != CSA_F32 && out_fmt != CSA_BF16)
     return fail(CSA_ERR_UNSUPPORTED, "csa_swa_merge: out must be F32 or BF16");
-  const int64_t blocks = (rows + 3) / 4;
-  if (blocks > 0x7fffffff) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_swa_merge: too many rows");
-  if (out_fmt == CSA_BF16)
-    hipLaunchKernelGGL(swa_merge_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, o_a,
-                       lse_a, o_b, lse_b, rows, dim, out, lse_out);
-  else
-    hipLaunchKernelGGL(swa_merge_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, o_a,
-                       lse_a, o_b, lse_b, rows, dim, out, lse_out);
-  return check_launch("csa_swa_merge");
+  // the two parts are addressed as base + p * (distance between them)
+  const int64_t so = (int64_t)((intptr_t)o_b - (intptr_t)o_a);
+  const int64_t sl = (int64_t)((intptr_t)lse_b - (intptr_t)lse_a);
+  return launch_lse_merge_bytes(o_a, lse_a, so, sl, 2, nullptr, 1, rows, dim, out, out_fmt,
+                                lse_out, stream);
 }

@@ -169,14 +169,28 @@ def topk_select(scores, score_fmt, batch: Batch, m, k, idx=None):
     return idx
 
 
+def attn_workspace_size(n_q, n_heads, dim, max_keys, split_keys):
+    return int(_lib.load().csa_attn_workspace_size(int(n_q), int(n_heads), int(dim),
+                                                   int(max_keys), int(split_keys)))
+
+
 def sparse_mqa_attn(q: KV, n_heads, kv: Optional[KV], idx, k, raw: Optional[KV], window,
-                    batch: Batch, m, out, out_fmt, lse=None, scale=None):
+                    batch: Batch, m, out, out_fmt, lse=None, scale=None, split_keys=0,
+                    workspace=None):
     """CSA step 3 / HCA: attention over selected (idx) or all visible entries
-    (idx=None) plus the window; out [n_q*H, D], lse [n_q*H] (optional)."""
-    _need_cuda(idx, out, lse)
+    (idx=None) plus the window; out [n_q*H, D], lse [n_q*H] (optional).
+    split_keys > 0 cuts each query's keys into parallel chunks merged by
+    log-sum-exp (decode); `workspace` is then a uint8 device tensor of at least
+    attn_workspace_size(...) bytes (allocated here when None)."""
+    _need_cuda(idx, out, lse, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(q.dim)
     lib = _lib.load()
+    if split_keys and workspace is None:
+        max_keys = (k if idx is not None else batch.max_kv) + (window if raw is not None else 0)
+        workspace = torch.empty(max(attn_workspace_size(batch.n_q, n_heads, q.dim, max_keys,
+                                                        split_keys), 1),
+                                dtype=torch.uint8, device=q.data.device)
     qc, bc = q.c(), batch.c()
     kvc = kv.c() if kv is not None else None
     rc = raw.c() if raw is not None else None
@@ -185,7 +199,9 @@ def sparse_mqa_attn(q: KV, n_heads, kv: Optional[KV], idx, k, raw: Optional[KV],
                                   _ptr(idx), int(k),
                                   ctypes.byref(rc) if rc is not None else None, int(window),
                                   ctypes.byref(bc), int(m), float(scale), _ptr(out),
-                                  int(out_fmt), _ptr(lse), _stream()),
+                                  int(out_fmt), _ptr(lse), int(split_keys), _ptr(workspace),
+                                  int(workspace.numel()) if workspace is not None else 0,
+                                  _stream()),
           "csa_sparse_mqa_attn")
     return out
 

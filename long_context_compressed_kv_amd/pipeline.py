@@ -5,9 +5,9 @@ Prefill (one sequence):
        -> sparse_mqa_attn over the selected entries and the window, one softmax
   HCA: kv_compress -> sparse_mqa_attn over all visible entries and the window
 Decode (a batch of requests, one query each):
-  CSA: indexer_score -> topk_select -> sparse_mqa_attn(selected entries)
-       and sparse_mqa_attn(window) -> swa_merge
-  HCA: sparse_mqa_attn(visible entries) and sparse_mqa_attn(window) -> swa_merge
+  CSA: indexer_score -> topk_select -> sparse_mqa_attn(selected entries and
+       window, split into key chunks merged by log-sum-exp)
+  HCA: sparse_mqa_attn(visible entries and window, split the same way)
 (page "DeepSeek V4 深度解析", section 2: the three CSA steps and HCA).
 """
 from dataclasses import dataclass, field
@@ -139,6 +139,7 @@ class DecodeLayer:
     ki: Optional[KV] = None
     score_fmt: int = BF16
     out_fmt: int = BF16
+    split_keys: int = 128
     buf: Buffers = field(default_factory=Buffers)
 
     def __post_init__(self):
@@ -159,18 +160,18 @@ class DecodeLayer:
         return scores, idx
 
     def attend(self, idx):
+        """One attention call over entries and window together, its keys cut
+        into chunks of `split_keys` run in parallel and merged by log-sum-exp."""
         rows, D = self.B * self.H, self.q.dim
-        o_c = self.buf.get("o_c", (rows, D), torch.float32)
-        l_c = self.buf.get("l_c", (rows,), torch.float32)
-        o_w = self.buf.get("o_w", (rows, D), torch.float32)
-        l_w = self.buf.get("l_w", (rows,), torch.float32)
-        ops.sparse_mqa_attn(self.q, self.H, self.cache, idx, self.k if idx is not None else 0,
-                            None, 0, self.batch, self.m, o_c, F32, l_c)
-        ops.sparse_mqa_attn(self.q, self.H, None, None, 0, self.swa, self.window, self.batch,
-                            self.m, o_w, F32, l_w)
         out = self.buf.get("out", (rows, D), _out_dtype(self.out_fmt))
         lse = self.buf.get("lse", (rows,), torch.float32)
-        ops.swa_merge(o_c, l_c, o_w, l_w, out, self.out_fmt, lse)
+        max_keys = (self.k if idx is not None else self.ld) + self.window
+        ws = self.buf.get("ws", (max(ops.attn_workspace_size(self.B, self.H, D, max_keys,
+                                                               self.split_keys), 1),),
+                          torch.uint8)
+        ops.sparse_mqa_attn(self.q, self.H, self.cache, idx, self.k if idx is not None else 0,
+                            self.swa, self.window, self.batch, self.m, out, self.out_fmt, lse,
+                            split_keys=self.split_keys, workspace=ws)
         return out, lse
 
     def run(self):

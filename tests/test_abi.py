@@ -19,7 +19,7 @@ FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:csa_status|int|const char\*)\s+(csa_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:csa_status|int|size_t|const char\*)\s+(csa_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -100,9 +100,9 @@ def test_attn_validation(lib):
     bt = _batch(n_q=2)
     q = _t(1, 128, 2 * 64)
     kv = _t(1, 128, 100)
-    f = lambda qq, h, kk, of=1, m=4, k=8: lib.csa_sparse_mqa_attn(
+    f = lambda qq, h, kk, of=1, m=4, k=8, split=0, ws=None, wsb=0, sc=0.1: lib.csa_sparse_mqa_attn(
         ctypes.byref(qq), h, ctypes.byref(kk) if kk is not None else None, None, k, None, 0,
-        ctypes.byref(bt), m, 0.1, FAKE, of, None, None)
+        ctypes.byref(bt), m, sc, FAKE, of, None, split, ws, wsb, None)
     assert f(q, 48, kv) == BAD_ARG                  # rows != n_q * heads
     assert f(_t(1, 128, 2 * 48), 48, kv) == UNSUPPORTED   # 48 heads
     assert f(q, 64, _t(1, 256, 100)) == BAD_ARG     # kv dim mismatch
@@ -111,6 +111,13 @@ def test_attn_validation(lib):
     assert f(q, 64, kv, m=0) == BAD_ARG
     assert f(q, 64, _t(2, 128, 100, scale=FAKE, rope=FAKE)) == BAD_ARG  # mixed needs D 512
     assert f(_t(0, 128, 128), 64, kv) == UNSUPPORTED   # f32 q with bf16 kv
+    assert f(q, 64, kv, sc=0.0) == BAD_ARG             # scale must be positive
+    assert f(q, 64, kv, split=64) == 3                 # split-K without workspace
+    need = lib.csa_attn_workspace_size(2, 64, 128, 16, 64)
+    assert need > 2 * 64 * 129 * 4
+    assert f(q, 64, kv, split=64, ws=FAKE, wsb=need - 1) == 3
+    assert f(_t(1, 128, 2 * 16), 16, kv, split=64, ws=FAKE, wsb=need) == UNSUPPORTED
+    assert lib.csa_attn_workspace_size(2, 64, 128, 16, 0) == 0
 
 
 def test_merge_and_codec_validation(lib):

@@ -138,6 +138,44 @@ def test_attn_decode_split_merge_equals_union():
     assert torch.max(torch.abs(om - ou)).item() <= 2e-2
 
 
+@pytest.mark.parametrize("split_keys,kv_fmt,sparse", [(32, "fp8_mixed", True), (64, "fp8_mixed", False),
+                                                     (128, "bf16", True), (1, "fp8_mixed", True)])
+def test_attn_decode_split_k(split_keys, kv_fmt, sparse):
+    """Split-K over key chunks merged by log-sum-exp equals the oracle."""
+    rng = np.random.default_rng(40 + split_keys)
+    H, D, m, k, window = 64, 512, 4, 100, 128
+    ctxs = [3000, 50, 999, 400, 127, 20000]
+    B = len(ctxs)
+    n_ent = [(c + 1) // m for c in ctxs]
+    swa_len = [min(window, c + 1) for c in ctxs]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len]
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    idx = np.full((B, k), -1, np.int64)
+    for r in range(B):
+        cnt = min(k, n_ent[r]) - (3 if r == 1 else 0)
+        idx[r, :cnt] = np.sort(rng.choice(n_ent[r], cnt, replace=False))
+    kvd = dev_kv(np.concatenate(ents), kv_fmt)
+    sd, qd = dev_kv(np.concatenate(swas), "bf16"), dev_kv(q.reshape(-1, D), "bf16")
+    batch = Batch.make([1] * B, ctxs, kv_counts=n_ent, raw_counts=swa_len,
+                       raw_pos=[c - s + 1 for c, s in zip(ctxs, swa_len)])
+    out = torch.empty(B * H, D, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(B * H, device="cuda")
+    idx_d = torch.from_numpy(idx.astype(np.int32)).cuda() if sparse else None
+    ops.sparse_mqa_attn(qd, H, kvd, idx_d, k if sparse else 0, sd, window, batch, m, out, BF16,
+                        lse, split_keys=split_keys)
+    torch.cuda.synchronize()
+    qv, sc = ref_vals(q, "bf16"), 1 / math.sqrt(D)
+    worst = 0.0
+    for r in range(B):
+        ev, sv = ref_vals(ents[r], kv_fmt), ref_vals(swas[r], "bf16")
+        ke = ev[idx[r][idx[r] >= 0]] if sparse else ev
+        o, l = ref.attend(qv[r], np.concatenate([ke, sv]), sc)
+        sl = slice(r * H, (r + 1) * H)
+        worst = max(worst, np.max(np.abs(to_np(out[sl]) - o)), np.max(np.abs(to_np(lse[sl]) - l)))
+    assert worst <= 2e-2, worst
+
+
 def test_attn_window_only_and_empty_rows():
     """No entries and window 0 for some rows: o = 0, lse = -inf."""
     H, D = 32, 128
