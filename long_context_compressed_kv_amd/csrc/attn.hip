@@ -20,6 +20,10 @@
 // and a combine pass merges them (the same merge as csa_swa_merge).
 //
 // Per tile and wave (bf16):
+// Staging maps consecutive threads to consecutive groups of 4 keys at the
+// same 8 dims, so the transposed V^T writes of a wave spread over the LDS
+// banks and each key row is still read in 128-byte pieces.
+//
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, keys on M, queries on N;
 //                      lane (q = l%32, half = l/32) gets 16 keys of query q,
 //                      key = 8*(i/4) + 4*half + (i%4) for register i
@@ -297,8 +301,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         stg[i][0] = v;
       } else {
         constexpr int DG = D / 8;
-        const int k4 = u / DG;
-        const int d = (u - k4 * DG) * 8;
+        const int k4 = u & (KT / 4 - 1);          // key group fastest: V^T writes spread over banks
+        const int d = (u / (KT / 4)) * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint4 v = make_uint4(0, 0, 0, 0);
@@ -330,8 +334,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<float4*>(klds + key * KSTR + d) = stg[i][0];
       } else {
         constexpr int DG = D / 8;
-        const int k4 = u / DG;
-        const int d = (u - k4 * DG) * 8;
+        const int k4 = u & (KT / 4 - 1);          // key group fastest: V^T writes spread over banks
+        const int d = (u / (KT / 4)) * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           *reinterpret_cast<uint4*>(klds + (k4 * 4 + j) * KSTR + d) = stg[i][j];
@@ -372,8 +376,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<float4*>(klds + key * KSTR + d) = v;
       } else {
         constexpr int DG = D / 8;
-        const int k4 = u / DG;
-        const int d = (u - k4 * DG) * 8;
+        const int k4 = u & (KT / 4 - 1);          // key group fastest: V^T writes spread over banks
+        const int d = (u / (KT / 4)) * 8;
         uint4 v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

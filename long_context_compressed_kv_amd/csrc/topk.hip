@@ -4,16 +4,24 @@
 // selection cheaper).
 //
 // Exact and deterministic.  Scores are mapped to order-preserving unsigned
-// keys (-0 folded onto +0).  One workgroup per query row:
-//   1. radix select, 8 bits per pass from the top (2 passes for BF16 keys,
-//      4 for F32): per-wave LDS histograms of the digit among the keys that
-//      match the prefix found so far -> the exact k-th largest key tau, the
-//      number of keys above it, and how many tau-ties are still needed;
-//   2. one ordered pass: key > tau, or key == tau among the first `need`
-//      ties by index; output position = (#greater before) + min(#ties
-//      before, need), from a block-wide exclusive scan, so the indices come
-//      out in ascending order with no sort.
-// Rows with at most k candidates skip 1. and keep everything.
+// keys (-0 folded onto +0); a row keeps the min(k, n) largest keys, ties
+// broken by the lower index, written in ascending index order.  One
+// workgroup (16 waves) per query row:
+//   1. threshold estimate: rows longer than half the LDS candidate capacity take
+//      a strided sample of 4096 keys and use its order statistic of rank
+//      ~2k*4096/n (an exact radix select over the sample in LDS), so about
+//      2k keys of the row lie at or above it;
+//   2. one streaming pass over the row (16-byte loads, waves on contiguous
+//      segments) appends every key >= the estimate, with its index, to the
+//      wave's LDS segment; positions come from wave prefix sums, so the
+//      candidates stay in index order and no atomics are used;
+//   3. exact radix select of the k-th largest key among the candidates (LDS
+//      histograms), then an ordered scan writes key > tau, or key == tau among
+//      the first `need` ties, at position (#greater before) + min(#ties
+//      before, need).
+// When the estimate misses (fewer than k candidates, or a wave segment
+// overflows), the row is redone exactly over global memory with the same
+// radix select and ordered scan.
 #include "common.h"
 
 using namespace csa;
@@ -22,24 +30,26 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kEPT = 8;                      // consecutive elements per thread per chunk
-constexpr int kChunk = kThreads * kEPT;
+constexpr int kCap = 4096;                   // LDS candidates per row
+constexpr int kBudget = kCap / kWaves;       // per wave segment
+constexpr int kSample = 4096;
 
-template <bool BF16>
-__device__ __forceinline__ uint32_t order_key(const void* row, int64_t j) {
-  if constexpr (BF16) {
-    uint32_t b = static_cast<const uint16_t*>(row)[j];
-    if (b == 0x8000u) b = 0;
-    return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
-  } else {
-    uint32_t b = __float_as_uint(static_cast<const float*>(row)[j]);
-    if (b == 0x80000000u) b = 0;
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  }
+__device__ __forceinline__ uint32_t order_bf16(uint32_t b) {
+  if (b == 0x8000u) b = 0;
+  return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+__device__ __forceinline__ uint32_t order_f32(uint32_t b) {
+  if (b == 0x80000000u) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Inclusive scan of one int over the block; returns the exclusive prefix and
-// the block total.
+template <bool BF16>
+__device__ __forceinline__ uint32_t key_at(const void* row, int64_t j) {
+  if constexpr (BF16) return order_bf16(static_cast<const uint16_t*>(row)[j]);
+  else return order_f32(__float_as_uint(static_cast<const float*>(row)[j]));
+}
+
+// Exclusive scan of v over the block; total returned through `total`.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -62,22 +72,139 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return before + x - v;
 }
 
+// Exclusive scan of v over one wave.
+__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, 63);
+  return x - v;
+}
+
+struct Shared {
+  uint32_t hist[kWaves][256];
+  uint32_t wsum[kWaves];
+  uint32_t sel_digit, sel_remain, overflow;
+  uint32_t cnt[kWaves];
+  uint32_t cand_key[kCap];
+  int32_t cand_idx[kCap];
+};
+
+// Radix select of the rank-th largest key among `count` keys produced by
+// get(i).  Returns the key; `remain` = how many keys equal to it are needed to
+// reach rank (so rank - remain keys are strictly greater).
+template <int KBITS, typename Get>
+__device__ uint32_t radix_select(Shared& sh, int64_t count, uint32_t rank, Get get, uint32_t& remain) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  uint32_t prefix = 0;
+  remain = rank;
+  for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
+    for (int i = tid; i < kWaves * 256; i += kThreads) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
+    const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
+    for (int64_t j = tid; j < count; j += kThreads) {
+      const uint32_t key = get(j);
+      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 4l..4l+3; suffix counts from the top digit down
+      uint32_t c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t s = 0;
+        for (int w = 0; w < kWaves; ++w) s += sh.hist[w][4 * tid + i];
+        c[i] = s;
+      }
+      const uint32_t s = c[0] + c[1] + c[2] + c[3];
+      uint32_t x = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(x, o);
+        if (tid + o < 64) x += y;
+      }
+      uint32_t acc = x - s;                  // keys with a digit above this lane's group
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (acc < remain && remain <= acc + c[i]) {
+          sh.sel_digit = 4 * tid + i;
+          sh.sel_remain = remain - acc;
+        }
+        acc += c[i];
+      }
+    }
+    __syncthreads();
+    prefix |= sh.sel_digit << shift;
+    remain = sh.sel_remain;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Ordered emission over `count` keys in index order: writes the selected
+// ones' indices idx_of(i) to out[0..k).
+template <typename Get, typename Idx>
+__device__ void emit_ordered(Shared& sh, int64_t count, uint32_t tau, uint32_t need_eq, int k,
+                             Get get, Idx idx_of, int32_t* out) {
+  constexpr int EPT = 8;
+  const int tid = threadIdx.x;
+  uint32_t base_gt = 0, base_eq = 0;
+  for (int64_t c0 = 0; c0 < count; c0 += (int64_t)kThreads * EPT) {
+    const int64_t j0 = c0 + (int64_t)tid * EPT;
+    uint32_t keys[EPT];
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int64_t j = j0 + e;
+      const bool valid = j < count;
+      keys[e] = valid ? get(j) : 0u;
+      gt += (valid && keys[e] > tau) ? 1u : 0u;
+      eq += (valid && keys[e] == tau) ? 1u : 0u;
+    }
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.wsum, total);
+    uint32_t g_before = base_gt + (ex >> 16);
+    uint32_t e_before = base_eq + (ex & 0xffffu);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int64_t j = j0 + e;
+      if (j >= count) break;
+      if (keys[e] > tau) {
+        const uint32_t pos = g_before + (e_before < need_eq ? e_before : need_eq);
+        if (pos < (uint32_t)k) out[pos] = idx_of(j);
+        ++g_before;
+      } else if (keys[e] == tau) {
+        if (e_before < need_eq && g_before + e_before < (uint32_t)k) out[g_before + e_before] = idx_of(j);
+        ++e_before;
+      }
+    }
+    base_gt += total >> 16;
+    base_eq += total & 0xffffu;
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__ scores, int64_t ld,
                                                         BatchDev b, int m, int k,
                                                         int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[kWaves][256];
-  __shared__ uint32_t merged[256];
-  __shared__ uint32_t wsum[kWaves];
-  __shared__ uint32_t sel_digit, sel_remain;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ESZ;                // elements per 16-byte vector
+  constexpr int KBITS = BF16 ? 16 : 32;
 
   const int64_t q = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int lane = tid & 63;
   const QueryMeta qm = query_meta(b, q, m);
   const int64_t n = qm.n_vis < ld ? qm.n_vis : ld;    // never past the row
-  const void* row = BF16 ? (const void*)(static_cast<const uint16_t*>(scores) + q * ld)
-                         : (const void*)(static_cast<const float*>(scores) + q * ld);
+  const char* row = static_cast<const char*>(scores) + q * ld * ESZ;
   int32_t* out = idx + q * (int64_t)k;
 
   if (n <= k) {
@@ -85,92 +212,118 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     return;
   }
 
-  // ---- 1. radix select of the k-th largest key
-  constexpr int kBits = BF16 ? 16 : 32;
-  uint32_t prefix = 0;
-  uint32_t remain = (uint32_t)k;   // how many keys still to take among those matching prefix
-  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
+  // ---- 1. threshold estimate (short rows: every key is a candidate; a
+  // wave's segment then holds at most ~n/16 + 8 keys, inside its budget)
+  uint32_t tau_hat = 0;
+  if (n > kCap / 2) {
+    for (int i = tid; i < kSample; i += kThreads) sh.cand_key[i] = key_at<BF16>(row, (int64_t)i * n / kSample);
     __syncthreads();
-    const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
-    for (int64_t j = tid; j < n; j += kThreads) {
-      const uint32_t key = order_key<BF16>(row, j);
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t c = 0;
-      for (int w = 0; w < kWaves; ++w) c += hist[w][tid];
-      merged[tid] = c;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // suffix sums from the top digit down: lane l owns digits 4l..4l+3
-      const int lane = tid;
-      const uint32_t c0 = merged[4 * lane], c1 = merged[4 * lane + 1];
-      const uint32_t c2 = merged[4 * lane + 2], c3 = merged[4 * lane + 3];
-      const uint32_t s = c0 + c1 + c2 + c3;
-      // exclusive count of all digits above this lane's group
-      uint32_t x = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(x, o);
-        if (lane + o < 64) x += y;
-      }
-      const uint32_t above = x - s;   // keys with a digit > 4l+3
-      // the selected digit d satisfies above(d) < remain <= above(d) + count(d)
-      uint32_t acc = above;
-      const uint32_t cs[4] = {c3, c2, c1, c0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (acc < remain && remain <= acc + cs[i]) {
-          sel_digit = 4 * lane + 3 - i;
-          sel_remain = remain - acc;
-        }
-        acc += cs[i];
-      }
-    }
-    __syncthreads();
-    prefix |= sel_digit << shift;
-    remain = sel_remain;
-    __syncthreads();
+    int64_t r = (2 * (int64_t)k * kSample + n - 1) / n + 8;
+    if (r > kSample) r = kSample;
+    uint32_t rem;
+    tau_hat = radix_select<KBITS>(sh, kSample, (uint32_t)r,
+                                  [&](int64_t i) { return sh.cand_key[i]; }, rem);
   }
-  const uint32_t tau = prefix;
-  const uint32_t need_eq = remain;     // ties at tau still to take
+  if (tid == 0) sh.overflow = 0;
+  __syncthreads();
 
-  // ---- 2. ordered emission
-  uint32_t base_gt = 0, base_eq = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
-    const int64_t j0 = c0 + (int64_t)tid * kEPT;
-    uint32_t keys[kEPT];
-    uint32_t gt = 0, eq = 0;
+  // ---- 2. stream the row, keep keys >= tau_hat in index order
+  const uintptr_t base_addr = reinterpret_cast<uintptr_t>(row);
+  const int64_t off = (int64_t)((base_addr & 15u) / ESZ);          // elements before the row in its first vector
+  const char* vbase = reinterpret_cast<const char*>(base_addr & ~(uintptr_t)15u);
+  const int64_t nvec = (off + n + EPV - 1) / EPV;
+  const int64_t per_wave = (nvec + kWaves - 1) / kWaves;
+  const int64_t v_lo = wave * per_wave;
+  const int64_t v_hi = v_lo + per_wave < nvec ? v_lo + per_wave : nvec;
+  uint32_t wcount = 0;
+  bool wover = false;
+  for (int64_t v0 = v_lo; v0 < v_hi; v0 += 64) {
+    const int64_t v = v0 + lane;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (v < v_hi) {
+      // whole vectors inside the row use one 16-byte load; the row's partial
+      // first and last vectors read only their in-row elements
+      const char* vp = vbase + v * 16;
+      if (vp >= row && vp + 16 <= row + n * ESZ) {
+        raw = *reinterpret_cast<const uint4*>(vp);
+      } else {
+        uint32_t t4[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
-      const int64_t j = j0 + e;
-      keys[e] = j < n ? order_key<BF16>(row, j) : 0u;
-      const bool valid = j < n;
-      gt += (valid && keys[e] > tau) ? 1u : 0u;
-      eq += (valid && keys[e] == tau) ? 1u : 0u;
-    }
-    uint32_t total;
-    const uint32_t ex = block_exclusive_scan((gt << 16) | eq, wsum, total);
-    uint32_t g_before = base_gt + (ex >> 16);
-    uint32_t e_before = base_eq + (ex & 0xffffu);
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
-      const int64_t j = j0 + e;
-      if (j >= n) break;
-      if (keys[e] > tau) {
-        const uint32_t pos = g_before + (e_before < need_eq ? e_before : need_eq);
-        if (pos < (uint32_t)k) out[pos] = (int32_t)j;
-        ++g_before;
-      } else if (keys[e] == tau) {
-        if (e_before < need_eq && g_before + e_before < (uint32_t)k) out[g_before + e_before] = (int32_t)j;
-        ++e_before;
+        for (int e = 0; e < EPV; ++e) {
+          const int64_t j = v * EPV + e - off;
+          if (j >= 0 && j < n) {
+            uint32_t bits;
+            if constexpr (BF16) bits = static_cast<const uint16_t*>(static_cast<const void*>(row))[j];
+            else bits = __float_as_uint(static_cast<const float*>(static_cast<const void*>(row))[j]);
+            t4[e * ESZ / 4] |= bits << (8 * ((e * ESZ) & 3));
+          }
+        }
+        raw = make_uint4(t4[0], t4[1], t4[2], t4[3]);
       }
     }
-    base_gt += total >> 16;
-    base_eq += total & 0xffffu;
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t flags = 0;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const int64_t j = v * EPV + e - off;
+      uint32_t key;
+      if constexpr (BF16) key = order_bf16((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      else key = order_f32(w4[e]);
+      const bool ok = v < v_hi && j >= 0 && j < n && key >= tau_hat;
+      flags |= ok ? (1u << e) : 0u;
+    }
+    const uint32_t c = __builtin_popcount(flags);
+    uint32_t total;
+    const uint32_t pos = wave_exclusive_scan(c, total);
+    if (!wover && wcount + total <= (uint32_t)kBudget) {
+      uint32_t slot = wave * kBudget + wcount + pos;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        if (flags & (1u << e)) {
+          uint32_t key;
+          if constexpr (BF16) key = order_bf16((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          else key = order_f32(w4[e]);
+          sh.cand_key[slot] = key;
+          sh.cand_idx[slot] = (int32_t)(v * EPV + e - off);
+          ++slot;
+        }
+      }
+    } else {
+      wover = true;
+    }
+    wcount += total;
+  }
+  if (lane == 0) {
+    sh.cnt[wave] = wover ? 0 : wcount;
+    if (wover) sh.overflow = 1;
+  }
+  __syncthreads();
+  uint32_t ccount = 0;
+  for (int w = 0; w < kWaves; ++w) ccount += sh.cnt[w];
+
+  if (!sh.overflow && ccount >= (uint32_t)k) {
+    // ---- 3. exact selection among the candidates (segments in wave order)
+    uint32_t segoff[kWaves + 1];
+    segoff[0] = 0;
+    for (int w = 0; w < kWaves; ++w) segoff[w + 1] = segoff[w] + sh.cnt[w];
+    auto slot_of = [&](int64_t i) {
+      int w = 0;
+#pragma unroll
+      for (int s = 1; s < kWaves; ++s) w += (uint32_t)i >= segoff[s] ? 1 : 0;
+      return w * kBudget + (int)((uint32_t)i - segoff[w]);
+    };
+    uint32_t need;
+    const uint32_t tau = radix_select<KBITS>(sh, ccount, (uint32_t)k,
+                                             [&](int64_t i) { return sh.cand_key[slot_of(i)]; }, need);
+    emit_ordered(sh, ccount, tau, need, k, [&](int64_t i) { return sh.cand_key[slot_of(i)]; },
+                 [&](int64_t i) { return sh.cand_idx[slot_of(i)]; }, out);
+  } else {
+    // ---- exact fallback over global memory
+    uint32_t need;
+    const uint32_t tau = radix_select<KBITS>(sh, n, (uint32_t)k,
+                                             [&](int64_t j) { return key_at<BF16>(row, j); }, need);
+    emit_ordered(sh, n, tau, need, k, [&](int64_t j) { return key_at<BF16>(row, j); },
+                 [&](int64_t j) { return (int32_t)j; }, out);
   }
 }
 
@@ -195,14 +348,16 @@ extern "C" csa_status csa_topk_select(const void* scores, int32_t score_fmt, int
   if (idx == nullptr || (scores == nullptr && batch->max_kv > 0))
     return fail(CSA_ERR_INVALID_ARGUMENT, "csa_topk_select: null pointer");
   if (batch->n_q > 0x7fffffff) return fail(CSA_ERR_UNSUPPORTED, "csa_topk_select: too many rows");
+  if (ld > ((int64_t)1 << 31)) return fail(CSA_ERR_UNSUPPORTED, "csa_topk_select: rows above 2^31 scores");
   // there is no entry tensor here: the kernel clamps each row's candidates to ld
   const BatchDev b{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, nullptr, nullptr,
                    (int64_t)1 << 62, 0};
+  const size_t smem = sizeof(Shared);
   if (score_fmt == CSA_BF16)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)batch->n_q), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)batch->n_q), dim3(kThreads), smem, stream,
                        scores, ld, b, m, k, idx);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)batch->n_q), dim3(kThreads), 0, stream,
-                       scores, ld, b, m, k, idx);
+    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)batch->n_q), dim3(kThreads), smem,
+                       stream, scores, ld, b, m, k, idx);
   return check_launch("csa_topk_select");
 }
