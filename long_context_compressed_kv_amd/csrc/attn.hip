@@ -7,12 +7,15 @@
 // i.e. TOK*H query rows (heads stacked, since all heads share the keys).  The
 // rows form 32-row blocks; each block is handled by DSPLIT waves, each wave
 // owning D/DSPLIT of the head dimension (partial logits are summed through
-// LDS in a fixed order).  Keys are streamed in tiles of 32: the workgroup
-// stages a tile into LDS twice, as K[key][d] for the logits and as
-// V^T[d][key] for the value product, dequantising FP8_MIXED rows to bf16
-// (exact, the scales are powers of two).  The global loads of tile t+1 are in
-// flight while tile t is computed, and the source rows of a tile are resolved
-// once per key, one tile ahead.
+// LDS in a fixed order).  Keys are streamed in tiles of 32, staged once into
+// LDS as bf16 rows (FP8_MIXED rows dequantised on the way, exactly: the
+// scales are powers of two); since key = value, the same tile is the operand
+// of both products, read row-wise for the logits and through transposing LDS
+// reads for the values.  The global loads of tile t+1 are in flight while tile
+// t is computed (D = 128), and the source rows of a tile are resolved once per
+// key, one tile ahead, together with one 32-bit mask per query token of the
+// keys that token may see (causal entries, its own selection, its window), so
+// masking a logit is one bit test.
 //
 // Split-K (decode).  With split_keys > 0 a query's key list is cut into
 // chunks of split_keys keys handled by separate workgroups (grid y); each
@@ -20,10 +23,6 @@
 // and a combine pass merges them (the same merge as csa_swa_merge).
 //
 // Per tile and wave (bf16):
-// Staging maps consecutive threads to consecutive groups of 4 keys at the
-// same 8 dims, so the transposed V^T writes of a wave spread over the LDS
-// banks and each key row is still read in 128-byte pieces.
-//
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, keys on M, queries on N;
 //                      lane (q = l%32, half = l/32) gets 16 keys of query q,
 //                      key = 8*(i/4) + 4*half + (i%4) for register i
@@ -34,7 +33,7 @@
 //                      operands follow the key order above, so P never leaves
 //                      registers
 // fp32 inputs use v_mfma_f32_32x32x2f32 with the same structure (one key per
-// lane and instruction, so V is read straight from the K layout).
+// lane and instruction, so V is read straight from a padded K layout).
 #include <type_traits>
 
 #include "common.h"
@@ -45,7 +44,7 @@ using namespace csa;
 namespace {
 
 constexpr int KT = 32;           // keys per tile
-constexpr int kRawTag = 1 << 30;
+constexpr int kTokMax = 16;      // query tokens per workgroup (128 rows / 8 heads)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kStale = 8.0f;   // log2 headroom before the running max moves
 constexpr int kMaxSplits = 64;
@@ -77,34 +76,6 @@ struct AttnArgs {
   int* ws_cnt;       // [n_q] splits used per query
 };
 
-// ------------------------------------------------------------------ staging
-
-// 8 consecutive dims [d, d+8) of a key row as packed bf16.
-template <int KVF>
-__device__ __forceinline__ uint4 load_key8_bf16(const void* base, const uint8_t* scl,
-                                                const uint16_t* rope, int64_t row, int d, int D) {
-  if constexpr (KVF == CSA_BF16) {
-    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D + d);
-  } else {  // CSA_FP8_MIXED, D == 512
-    if (d < 448) {
-      const uint2 c = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + row * 448 + d);
-      const float s = e8m0_to_f32(scl[row * 4 + (d >> 7)]);
-      uint4 r;
-      // the products are exact, so their top 16 bits are the bf16 values
-      r.x = (__float_as_uint(e4m3_to_f32(c.x & 0xff) * s) >> 16) |
-            (__float_as_uint(e4m3_to_f32((c.x >> 8) & 0xff) * s) & 0xffff0000u);
-      r.y = (__float_as_uint(e4m3_to_f32((c.x >> 16) & 0xff) * s) >> 16) |
-            (__float_as_uint(e4m3_to_f32(c.x >> 24) * s) & 0xffff0000u);
-      r.z = (__float_as_uint(e4m3_to_f32(c.y & 0xff) * s) >> 16) |
-            (__float_as_uint(e4m3_to_f32((c.y >> 8) & 0xff) * s) & 0xffff0000u);
-      r.w = (__float_as_uint(e4m3_to_f32((c.y >> 16) & 0xff) * s) >> 16) |
-            (__float_as_uint(e4m3_to_f32(c.y >> 24) * s) & 0xffff0000u);
-      return r;
-    }
-    return *reinterpret_cast<const uint4*>(rope + row * 64 + (d - 448));
-  }
-}
-
 // Tile geometry shared by every thread of a workgroup.
 struct Geo {
   int64_t q_first, q_last, t_first, t_last;
@@ -114,15 +85,17 @@ struct Geo {
   int nE, nkeys, key_lo, key_hi;
 };
 
-// Source row and mask tag of key kk: entry rows carry their local index
-// (dense) or owning token (sparse); raw rows carry kRawTag | (p - t_first + W).
-// Also whether the key is valid for every query row of the workgroup.
+// Source row of key kk, encoded: entry rows as themselves (>= 0), raw window
+// rows r as -2 - r, no key as -1.  `lo` / `hi` give the range of token offsets
+// g (query token t_first + g) for which the key is valid: an entry j is visible
+// from the token whose position reaches (j+1)m - 1, a selected entry only to
+// its owner, a window row at position p to tokens p .. p + W - 1.
 template <bool SPARSE>
 __device__ __forceinline__ void key_meta(const AttnArgs& a, const Geo& g, int kk, int& row,
-                                         int& tag, bool& all_ok) {
+                                         int64_t& lo, int64_t& hi) {
   row = -1;
-  tag = -1;
-  all_ok = false;
+  lo = 1;
+  hi = 0;
   if (kk >= g.key_hi) return;
   if (kk < g.nE) {
     if constexpr (SPARSE) {
@@ -131,41 +104,113 @@ __device__ __forceinline__ void key_meta(const AttnArgs& a, const Geo& g, int kk
       const int j = a.idx[(g.q_first + owner) * (int64_t)a.k + slot];
       if (j >= 0 && j < g.kv_len) {
         row = (int)(g.kv_base + j);
-        tag = owner;
-        all_ok = a.tok == 1;
+        lo = owner;
+        hi = owner + 1;
       }
     } else {
       row = (int)(g.kv_base + kk);
-      tag = kk;
-      all_ok = kk < g.nvis_first;
+      lo = (int64_t)(kk + 1) * a.m - 1 - g.t_first;
+      hi = INT64_MAX;
     }
   } else {
     const int64_t p = g.wlo + (kk - g.nE);
-    row = (int)(g.raw_base + (p - g.raw_pos));
-    tag = kRawTag | (int)(p - g.t_first + a.window);
-    all_ok = p >= g.t_last - a.window + 1 && p <= g.t_first;
+    row = -2 - (int)(g.raw_base + (p - g.raw_pos));
+    lo = p - g.t_first;
+    hi = lo + a.window;
   }
 }
 
 // ------------------------------------------------------------------ kernel
 
+// bf16 key tiles are stored unpadded, [key][D], with the 16-byte chunks of row
+// r permuted by j -> j ^ f(r), f(r) = 4*(r%4) + (r/4)%4.  Both reads of a
+// tile then spread over all LDS banks: the logit operand (one chunk of 32
+// consecutive rows per instruction; f is distinct over any 16 consecutive
+// rows) and the transposed value operand (4 chunks of 8 consecutive rows).
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int j) {
+  const int f = 4 * (r & 3) + ((r >> 2) & 3);
+  return r * (D * 2) + ((j ^ f) << 4);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// 64-bit transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i%4 of the four 16-bit values addressed by
+// lanes i/4, i/4+4, i/4+8 and i/4+12 of its group, in that order.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Dequantise 16 e4m3fn codes with a power-of-two scale into 16 bf16 (exact:
+// every product has at most 4 significant bits).  v_cvt_scalef32_pk_bf16_fp8
+// converts the two codes of the low half-word of its source.
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4 c, float s, uint4& y0, uint4& y1) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], s, false));
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q] >> 16, s, false));
+  }
+  y0 = make_uint4(o[0], o[1], o[2], o[3]);
+  y1 = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// One staging slot of a bf16-compute tile: dims [d, d+16) of one key.  For an
+// FP8_MIXED entry below dim 448, x0 holds the 16 codes and x1.x the scale.
+template <int D, int KVF>
+__device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uint4& x0, uint4& x1) {
+  x0 = make_uint4(0, 0, 0, 0);
+  x1 = make_uint4(0, 0, 0, 0);
+  if (row >= 0) {
+    if constexpr (KVF == CSA_FP8_MIXED) {
+      if (d < 448) {
+        x0 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) + (int64_t)row * 448 + d);
+        x1.x = __float_as_uint(e8m0_to_f32(a.kv_scale[(int64_t)row * 4 + (d >> 7)]));
+        return true;
+      }
+      const uint4* p = reinterpret_cast<const uint4*>(a.kv_rope + (int64_t)row * 64 + (d - 448));
+      x0 = p[0];
+      x1 = p[1];
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kv) + (int64_t)row * D + d);
+      x0 = p[0];
+      x1 = p[1];
+    }
+  } else if (row != -1) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.raw) + (int64_t)(-2 - row) * D + d);
+    x0 = p[0];
+    x1 = p[1];
+  }
+  return false;
+}
+
+template <int D>
+__device__ __forceinline__ void store_slot(unsigned char* kb, int key, int d, bool fp8, uint4 x0, uint4 x1) {
+  if (fp8) fp8x16_to_bf16(x0, __uint_as_float(x1.x), x0, x1);
+  *reinterpret_cast<uint4*>(kb + swz_off<D>(key, d >> 3)) = x0;
+  *reinterpret_cast<uint4*>(kb + swz_off<D>(key, (d >> 3) + 1)) = x1;
+}
+
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM, bool PREF>
 __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   constexpr int DW = D / DSPLIT;                 // dims per wave
-  constexpr int KSTR = F32C ? D + 4 : D + 8;     // K-layout row stride (elements)
-  constexpr int VSTR = KT + 4;                   // V^T row stride (bf16 elements)
-  using kelem_t = typename std::conditional<F32C, float, uint16_t>::type;
-  // staging units: bf16 = 4 keys x 8 dims, fp32 = 1 key x 4 dims
-  constexpr int UNITS = F32C ? KT * D / 4 : (KT / 4) * (D / 8);
+  constexpr int KSTR = D + 4;                    // fp32 K-layout row stride (elements)
+  // staging units: bf16 = one key x 16 dims, fp32 = one key x 4 dims
+  constexpr int UPR = F32C ? D / 4 : D / 16;     // units per key row
+  constexpr int UNITS = KT * UPR;
   // prefetching variants run with at least 256 threads
   constexpr int UPT = PREF ? (UNITS + 255) / 256 : 1;
+  constexpr size_t KBYTES = F32C ? (size_t)KT * KSTR * 4 : (size_t)KT * D * 2;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  kelem_t* klds = reinterpret_cast<kelem_t*>(smem);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem + KT * KSTR * sizeof(kelem_t));
-  int* mrow = reinterpret_cast<int*>(smem + KT * KSTR * sizeof(kelem_t) + (F32C ? 0 : D * VSTR * 2));
-  int* mtag = mrow + 2 * KT;
-  int* mfull = mtag + 2 * KT;                     // [2], padded to 4 ints
+  unsigned char* kb = smem;                                        // key tile
+  int* mrow = reinterpret_cast<int*>(smem + KBYTES);               // [2][KT] source rows
+  uint32_t* mword = reinterpret_cast<uint32_t*>(mrow + 2 * KT);    // [2][kTokMax] key bits per token
+  int* mfull = reinterpret_cast<int*>(mword + 2 * kTokMax);        // [2], padded to 4 ints
   float* sx = reinterpret_cast<float*>(mfull + 4); // [nrb][DSPLIT][64][16] partial logits
 
   const int tid = threadIdx.x;
@@ -235,9 +280,6 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   const int h_row = row_in_wg - g_row * a.H;
   const int64_t q_row = g.q_first + g_row;
   const bool row_live = q_row <= g.q_last;
-  const int64_t t_row = g.t_first + g_row;
-  int64_t nvis_row = (t_row + 1) / a.m;
-  if (nvis_row > g.kv_len) nvis_row = g.kv_len;
   const int64_t qrow_index = q_row * a.H + h_row;    // row of the q / out tensors
 
   // queries (B operand), pre-loaded for the whole key loop
@@ -263,22 +305,55 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < NDB; ++i) acc_o[i] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // ---- staging helpers
-  using stage_t = typename std::conditional<F32C, float4, uint4>::type;
-  constexpr int SPU = F32C ? 1 : 4;               // stage registers per unit
-  stage_t stg[UPT][SPU];
-
+  // wave 0 resolves a tile's source rows and, per query token, a 32-bit mask
+  // of the keys valid for it (bit = key in tile)
+  const int ntok = (int)(g.q_last - g.q_first + 1);
   auto meta_tile = [&](int kbase, int buf) {
     if (tid < 64) {
-      int row = -1, tag = -1;
-      bool ok = true;
-      if (tid < KT) key_meta<SPARSE>(a, g, kbase + tid, row, tag, ok);
-      if (tid < KT) {
-        mrow[buf * KT + tid] = row;
-        mtag[buf * KT + tid] = tag;
+      int row = -1;
+      int64_t lo = 1, hi = 0;
+      if (tid < KT) key_meta<SPARSE>(a, g, kbase + tid, row, lo, hi);
+      if (tid < KT) mrow[buf * KT + tid] = row;
+      bool full = true;
+      for (int t = 0; t < a.tok; ++t) {
+        const uint32_t w = (uint32_t)__ballot(t < ntok && t >= lo && t < hi);
+        if (tid == 0) mword[buf * kTokMax + t] = w;
+        full = full && (t >= ntok || w == 0xffffffffu);
       }
-      const unsigned long long bal = __ballot(ok);
-      if (tid == 0) mfull[buf] = (bal & 0xffffffffull) == 0xffffffffull ? 1 : 0;
+      if (tid == 0) mfull[buf] = full ? 1 : 0;
+    }
+  };
+
+  // ---- staging: fp32 units are float4 of one key; bf16 units are 16 dims
+  // of one key (32 bytes once in LDS), consecutive threads along a key row
+  using stage_t = typename std::conditional<F32C, float4, uint4>::type;
+  constexpr int SPU = F32C ? 1 : 2;               // stage registers per unit
+  stage_t stg[UPT][SPU];
+  bool sfp8[UPT];
+
+  auto load_unit = [&](int buf, int u, stage_t* v, bool& fp8) {
+    const int key = u / UPR;
+    const int row = mrow[buf * KT + key];
+    fp8 = false;
+    if constexpr (F32C) {
+      const int d = (u - key * UPR) * 4;
+      v[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row != -1) {
+        const float* src = static_cast<const float*>(row >= 0 ? a.kv : a.raw);
+        const int r = row >= 0 ? row : -2 - row;
+        v[0] = *reinterpret_cast<const float4*>(src + (int64_t)r * D + d);
+      }
+    } else {
+      fp8 = load_slot<D, KVF>(a, row, (u - key * UPR) * 16, v[0], v[1]);
+    }
+  };
+  auto store_unit = [&](int u, const stage_t* v, bool fp8) {
+    const int key = u / UPR;
+    if constexpr (F32C) {
+      const int d = (u - key * UPR) * 4;
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(kb) + key * KSTR + d) = v[0];
+    } else {
+      store_slot<D>(kb, key, (u - key * UPR) * 16, fp8, v[0], v[1]);
     }
   };
 
@@ -286,131 +361,48 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * nthreads;
-      if constexpr (F32C) {
-        constexpr int UPR = D / 4;
-        const int key = u / UPR;
-        const int d = (u - key * UPR) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (u < UNITS) {
-          const int row = mrow[buf * KT + key];
-          if (row >= 0) {
-            const float* src = static_cast<const float*>((mtag[buf * KT + key] & kRawTag) ? a.raw : a.kv);
-            v = *reinterpret_cast<const float4*>(src + (int64_t)row * D + d);
-          }
-        }
-        stg[i][0] = v;
-      } else {
-        constexpr int DG = D / 8;
-        const int k4 = u & (KT / 4 - 1);          // key group fastest: V^T writes spread over banks
-        const int d = (u / (KT / 4)) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (u < UNITS) {
-            const int key = k4 * 4 + j;
-            const int row = mrow[buf * KT + key];
-            if (row >= 0) {
-              if (mtag[buf * KT + key] & kRawTag)
-                v = load_key8_bf16<CSA_BF16>(a.raw, nullptr, nullptr, row, d, D);
-              else
-                v = load_key8_bf16<KVF>(a.kv, a.kv_scale, a.kv_rope, row, d, D);
-            }
-          }
-          stg[i][j] = v;
-        }
-      }
+      if (u < UNITS) load_unit(buf, u, stg[i], sfp8[i]);
     }
   };
-
   auto store_tile = [&]() {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * nthreads;
-      if (u >= UNITS) continue;
-      if constexpr (F32C) {
-        constexpr int UPR = D / 4;
-        const int key = u / UPR;
-        const int d = (u - key * UPR) * 4;
-        *reinterpret_cast<float4*>(klds + key * KSTR + d) = stg[i][0];
-      } else {
-        constexpr int DG = D / 8;
-        const int k4 = u & (KT / 4 - 1);          // key group fastest: V^T writes spread over banks
-        const int d = (u / (KT / 4)) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint4*>(klds + (k4 * 4 + j) * KSTR + d) = stg[i][j];
-        // transpose 4 keys x 8 dims into V^T rows (4 keys = 8 bytes per dim)
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&stg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&stg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&stg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&stg[i][3]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          uint2 lo, hi;   // dims d+2p (low halves) and d+2p+1 (high halves)
-          lo.x = (w0[p] & 0xffffu) | (w1[p] << 16);
-          lo.y = (w2[p] & 0xffffu) | (w3[p] << 16);
-          hi.x = (w0[p] >> 16) | (w1[p] & 0xffff0000u);
-          hi.y = (w2[p] >> 16) | (w3[p] & 0xffff0000u);
-          *reinterpret_cast<uint2*>(vt + (d + 2 * p) * VSTR + k4 * 4) = lo;
-          *reinterpret_cast<uint2*>(vt + (d + 2 * p + 1) * VSTR + k4 * 4) = hi;
-        }
-      }
+      if (u < UNITS) store_unit(u, stg[i], sfp8[i]);
+    }
+  };
+  // without prefetch: every thread loads and stores units tid, tid+nthreads, ...
+  auto stage_direct = [&](int buf) {
+    for (int u = tid; u < UNITS; u += nthreads) {
+      stage_t v[SPU];
+      bool fp8;
+      load_unit(buf, u, v, fp8);
+      store_unit(u, v, fp8);
     }
   };
 
-  // without prefetch: every thread loads and stores units tid, tid+nthreads, ...
-  auto stage_direct = [&](int buf) {
-    for (int u0 = 0; u0 < UNITS; u0 += nthreads) {
-      const int u = u0 + tid;
-      if (u >= UNITS) break;
-      if constexpr (F32C) {
-        constexpr int UPR = D / 4;
-        const int key = u / UPR;
-        const int d = (u - key * UPR) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        const int row = mrow[buf * KT + key];
-        if (row >= 0) {
-          const float* src = static_cast<const float*>((mtag[buf * KT + key] & kRawTag) ? a.raw : a.kv);
-          v = *reinterpret_cast<const float4*>(src + (int64_t)row * D + d);
-        }
-        *reinterpret_cast<float4*>(klds + key * KSTR + d) = v;
-      } else {
-        constexpr int DG = D / 8;
-        const int k4 = u & (KT / 4 - 1);          // key group fastest: V^T writes spread over banks
-        const int d = (u / (KT / 4)) * 8;
-        uint4 v[4];
+  // Per-lane LDS byte offsets of the bf16 tile reads.  Logit operand: row ql,
+  // chunk j = d0/8 + 2c + half; as d0/8 is a multiple of 16, the swizzled
+  // chunk is 16*(j/16) + 2*((c%8) ^ (f/2)) + (half ^ f%2), f = f(ql).
+  // Transposed value reads (see lds_read_tr16): row 16c + 8r + tk, chunk
+  // 4*db' + tc (db' = d0/32 + db), swizzled to 16*(db'/4) + 4*((db'%4) ^ (tk%4))
+  // + (tc ^ ((2r + tk/4) % 4)), plus the byte `sub` within it; the row terms
+  // 16c and 8r and the term 16*(db'/4) are immediates.
+  int qk_off[8], tr_base[2], tr_x[4];
+  {
+    const int f = 4 * (ql & 3) + ((ql >> 2) & 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k4 * 4 + j;
-          const int row = mrow[buf * KT + key];
-          v[j] = make_uint4(0, 0, 0, 0);
-          if (row >= 0) {
-            if (mtag[buf * KT + key] & kRawTag)
-              v[j] = load_key8_bf16<CSA_BF16>(a.raw, nullptr, nullptr, row, d, D);
-            else
-              v[j] = load_key8_bf16<KVF>(a.kv, a.kv_scale, a.kv_rope, row, d, D);
-          }
-        }
+    for (int c8 = 0; c8 < 8; ++c8)
+      qk_off[c8] = ql * (D * 2) + 32 * (c8 ^ (f >> 1)) + 16 * (half ^ (f & 1)) + (d0 >> 7) * 256;
+    const int tg = lane >> 4, ts = lane & 15;
+    const int tk = 4 * (tg >> 1) + (ts >> 2);
+    const int tc = 2 * (tg & 1) + ((ts & 3) >> 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint4*>(klds + (k4 * 4 + j) * KSTR + d) = v[j];
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
+    for (int r = 0; r < 2; ++r)
+      tr_base[r] = tk * (D * 2) + 16 * (tc ^ ((2 * r + (tk >> 2)) & 3)) + (ts & 1) * 8 + (d0 >> 7) * 256;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          uint2 lo, hi;
-          lo.x = (w0[p] & 0xffffu) | (w1[p] << 16);
-          lo.y = (w2[p] & 0xffffu) | (w3[p] << 16);
-          hi.x = (w0[p] >> 16) | (w1[p] & 0xffff0000u);
-          hi.y = (w2[p] >> 16) | (w3[p] & 0xffff0000u);
-          *reinterpret_cast<uint2*>(vt + (d + 2 * p) * VSTR + k4 * 4) = lo;
-          *reinterpret_cast<uint2*>(vt + (d + 2 * p + 1) * VSTR + k4 * 4) = hi;
-        }
-      }
-    }
-  };
+    for (int x = 0; x < 4; ++x) tr_x[x] = 64 * (x ^ (tk & 3));
+  }
 
   // ---- key loop: prologue resolves (and, prefetching, loads) the first tile
   const int ntiles = (g.key_hi - g.key_lo + KT - 1) / KT;
@@ -432,18 +424,27 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     }
 
     // ---- logits S^T = K Q^T (partial over this wave's dims)
+    if constexpr (!F32C) {
+      // keep the few per-lane offsets opaque to loop-invariant hoisting, which
+      // would otherwise hold every derived address in a register of its own
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qk_off[i]));
+      asm volatile("" : "+v"(tr_base[0]), "+v"(tr_base[1]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(tr_x[i]));
+    }
     f32x16_t acc_s = f32x16_t{};
     if constexpr (F32C) {
-      const float* kp = klds + ql * KSTR + d0 + half;
+      const float* kp = reinterpret_cast<const float*>(kb) + ql * KSTR + d0 + half;
 #pragma unroll
       for (int c = 0; c < QC; ++c)
         acc_s = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[2 * c], qreg[c], acc_s, 0, 0, 0);
     } else {
-      const uint16_t* kp = klds + ql * KSTR + d0 + half * 8;
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kp + 16 * c));
-        acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], acc_s, 0, 0, 0);
+        const uint4 k8 = *reinterpret_cast<const uint4*>(kb + qk_off[c & 7] + (c >> 3) * 256);
+        acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k8), qreg[c], acc_s,
+                                                        0, 0, 0);
       }
     }
     if constexpr (DSPLIT > 1) {
@@ -472,19 +473,10 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = acc_s[i];
     if (!mfull[buf]) {
+      const uint32_t mw = mword[buf * kTokMax + g_row] >> (4 * half);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 8 * (i >> 2) + 4 * half + (i & 3);
-        const int tg = mtag[buf * KT + key];
-        bool ok;
-        if (tg < 0) ok = false;
-        else if (tg & kRawTag) {
-          const int rel = tg & (kRawTag - 1);
-          ok = rel > g_row && rel <= g_row + a.window;
-        } else if (SPARSE) ok = tg == g_row;
-        else ok = tg < nvis_row;
-        s[i] = ok ? s[i] : -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        s[i] = ((mw >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
     }
 
     // ---- online softmax (base 2, stale maximum)
@@ -516,7 +508,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     if constexpr (F32C) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const float* vp = klds + d0 + db * 32 + ql;
+        const float* vp = reinterpret_cast<const float*>(kb) + d0 + db * 32 + ql;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 8 * (i >> 2) + 4 * half + (i & 3);
@@ -524,27 +516,29 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         }
       }
     } else {
+      // contraction slot 8*half + q of instruction c holds key
+      // 16c + 8*(q/4) + 4*half + q%4, the key of p[8c + q] in this lane
       bf16x8_t pb[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         uint4 u;
-        u.x = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
-        u.y = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
-        u.z = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
-        u.w = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
+        u.x = pack_bf16x2_fast(p[8 * c + 0], p[8 * c + 1]);
+        u.y = pack_bf16x2_fast(p[8 * c + 2], p[8 * c + 3]);
+        u.z = pack_bf16x2_fast(p[8 * c + 4], p[8 * c + 5]);
+        u.w = pack_bf16x2_fast(p[8 * c + 6], p[8 * c + 7]);
         pb[c] = __builtin_bit_cast(bf16x8_t, u);
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vp = vt + (d0 + db * 32 + ql) * VSTR + 4 * half;
+        const unsigned char* v0 = kb + tr_base[0] + tr_x[db & 3] + (db >> 2) * 256;
+        const unsigned char* v1 = kb + tr_base[1] + tr_x[db & 3] + (db >> 2) * 256;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          uint4 u;
-          const uint2 x0 = *reinterpret_cast<const uint2*>(vp + 16 * c);
-          const uint2 x1 = *reinterpret_cast<const uint2*>(vp + 16 * c + 8);
-          u.x = x0.x; u.y = x0.y; u.z = x1.x; u.w = x1.y;
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u),
-                                                               pb[c], acc_o[db], 0, 0, 0);
+          const uint2 x0 = lds_read_tr16(v0 + 16 * c * (D * 2));
+          const uint2 x1 = lds_read_tr16(v1 + (16 * c + 8) * (D * 2));
+          const uint4 u = make_uint4(x0.x, x0.y, x1.x, x1.y);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u), pb[c],
+                                                               acc_o[db], 0, 0, 0);
         }
       }
     }
@@ -567,8 +561,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       const float o2 = acc_o[db][4 * r4 + 2] * inv, o3 = acc_o[db][4 * r4 + 3] * inv;
       if constexpr (OUTM == 1) {
         uint2 u;
-        u.x = pack_bf16x2(o0, o1);
-        u.y = pack_bf16x2(o2, o3);
+        u.x = pack_bf16x2_fast(o0, o1);
+        u.y = pack_bf16x2_fast(o2, o3);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + qrow_index * D + d) = u;
       } else {
         float* dst = OUTM == 2 ? a.ws_o + (split * rows_total + qrow_index) * D + d
@@ -600,12 +594,10 @@ csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
 
 template <int D, bool F32C, int DSPLIT>
 size_t attn_smem(int nrb) {
-  constexpr int KSTR = F32C ? D + 4 : D + 8;
-  const size_t kbytes = (size_t)KT * KSTR * (F32C ? 4 : 2);
-  const size_t vbytes = F32C ? 0 : (size_t)D * (KT + 4) * 2;
-  const size_t meta = (4 * KT + 4) * 4;
+  const size_t kbytes = F32C ? (size_t)KT * (D + 4) * 4 : (size_t)KT * D * 2;
+  const size_t meta = (2 * KT + 2 * kTokMax + 4) * 4;
   const size_t sxbytes = DSPLIT > 1 ? (size_t)nrb * DSPLIT * 64 * 16 * 4 : 0;
-  return kbytes + vbytes + meta + sxbytes;
+  return kbytes + meta + sxbytes;
 }
 
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM>
@@ -753,6 +745,7 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   if (D == 128 && !split && batch->n_req == 1) rows = H > 128 ? H : 128;
   else rows = H < 32 ? 32 : H;
   a.tok = rows / H > 0 ? rows / H : 1;
+  if (a.tok > kTokMax) return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: too many tokens per workgroup");
   a.nrb = rows / 32;
   if (a.tok > 1 && batch->n_req > 1)
     return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fewer than 32 heads needs a single request");

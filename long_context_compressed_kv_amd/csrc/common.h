@@ -36,6 +36,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
 }
 
+// The same for finite inputs in one instruction (v_cvt_pk_bf16_f32, round to
+// nearest-even); NaN payloads are not specified, so codecs use pack_bf16x2.
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_fast(float a, float b) {
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+
 // ---------------------------------------------------------------- e4m3fn (OCP)
 
 // Exact decode.  For a normal code the 7 magnitude bits placed at bits 20..26

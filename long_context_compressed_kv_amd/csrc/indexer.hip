@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
       if (live_o[g] && e < nvis_o[g]) {
         const int64_t off = (q0 + 2 * g + half) * a.ld + e;
         if constexpr (SBF16)
-          static_cast<uint16_t*>(a.scores)[off] = (uint16_t)f32_to_bf16(s);
+          static_cast<uint16_t*>(a.scores)[off] = (uint16_t)pack_bf16x2_fast(s, 0.0f);
         else
           static_cast<float*>(a.scores)[off] = s;
       }

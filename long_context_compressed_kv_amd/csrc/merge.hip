@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
     r0 *= inv; r1 *= inv; r2 *= inv; r3 *= inv;
     if constexpr (OUT_BF16) {
       uint2 u;
-      u.x = pack_bf16x2(r0, r1);
-      u.y = pack_bf16x2(r2, r3);
+      u.x = pack_bf16x2_fast(r0, r1);
+      u.y = pack_bf16x2_fast(r2, r3);
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + row * dim + d) = u;
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(out) + row * dim + d) =
