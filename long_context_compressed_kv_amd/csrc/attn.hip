@@ -68,12 +68,16 @@ struct AttnArgs {
   void* out;
   float* lse;
   int tok;           // query tokens per workgroup
+  int hg;            // heads per workgroup (a head group)
+  int ngroups;       // head groups per token (H / hg)
   int nrb;           // 32-row blocks per workgroup
   int split_keys;    // 0: one workgroup per token group; else keys per split
   int max_splits;
   float* ws_o;       // [max_splits][n_q*H][D]
   float* ws_lse;     // [max_splits][n_q*H]
   int* ws_cnt;       // [n_q] splits used per query
+  int* ws_start;     // [n_q + 1] first work item of each query (split-K)
+  int* ws_item_q;    // [n_q * max_splits] query of each work item (split-K)
 };
 
 // Tile geometry shared by every thread of a workgroup.
@@ -84,6 +88,96 @@ struct Geo {
   int64_t wlo;          // first window position
   int nE, nkeys, key_lo, key_hi;
 };
+
+// Geometry of the token group starting at query q_first: its request, the
+// entries it sees (selected or all visible) and its window, in key order
+// [entries | window rows].
+template <bool SPARSE>
+__device__ Geo make_geo(const AttnArgs& a, int64_t q_first) {
+  Geo g;
+  g.q_first = q_first;
+  g.q_last = g.q_first + a.tok - 1;
+  if (g.q_last >= a.n_q) g.q_last = a.n_q - 1;
+  const int req = find_request(a.b.q_off, a.b.n_req, g.q_first);
+  const QueryMeta qm0 = query_meta(a.b, g.q_first, a.m);
+  g.t_first = qm0.t;
+  g.t_last = g.t_first + (g.q_last - g.q_first);
+  g.kv_base = qm0.kv_base;
+  g.raw_base = qm0.raw_base;
+  g.raw_pos = qm0.raw_pos;
+  g.kv_len = a.b.kv_off != nullptr && a.b.kv_rows > 0
+                 ? clamp64(a.b.kv_off[req + 1], qm0.kv_base, a.b.kv_rows) - qm0.kv_base
+                 : 0;
+  g.nvis_first = qm0.n_vis;
+  if constexpr (SPARSE) {
+    g.nE = a.kv != nullptr ? (int)(g.q_last - g.q_first + 1) * a.k : 0;
+  } else {
+    const int64_t nc = (g.t_last + 1) / a.m;
+    g.nE = a.kv != nullptr ? (int)(nc < g.kv_len ? nc : g.kv_len) : 0;
+  }
+  int64_t whi = -1;
+  g.wlo = 0;
+  if (a.raw != nullptr && a.window > 0 && qm0.raw_len > 0) {
+    g.wlo = g.t_first - a.window + 1;
+    if (g.wlo < 0) g.wlo = 0;
+    if (g.wlo < qm0.raw_pos) g.wlo = qm0.raw_pos;
+    whi = g.t_last;
+    if (whi > qm0.raw_pos + qm0.raw_len - 1) whi = qm0.raw_pos + qm0.raw_len - 1;
+  }
+  const int nW = whi >= g.wlo ? (int)(whi - g.wlo + 1) : 0;
+  g.nkeys = g.nE + nW;
+  g.key_lo = 0;
+  g.key_hi = g.nkeys;
+  return g;
+}
+
+// Keys per split of a query with nkeys keys (a multiple of the tile).
+__device__ __forceinline__ int split_chunk(const AttnArgs& a, int nkeys) {
+  int chunk = a.split_keys;
+  const int need = (nkeys + a.max_splits - 1) / a.max_splits;
+  if (need > chunk) chunk = need;
+  return (chunk + KT - 1) / KT * KT;
+}
+
+// Split-K work list: splits per query, their prefix sums and the query of
+// every (query, split) item, so the attention grid visits only real items.
+template <bool SPARSE>
+__global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int64_t q0 = 0; q0 < a.n_q; q0 += 1024) {
+    const int64_t q = q0 + tid;
+    int ns = 0;
+    if (q < a.n_q) {
+      const Geo g = make_geo<SPARSE>(a, q);
+      const int chunk = split_chunk(a, g.nkeys);
+      ns = g.nkeys > 0 ? (g.nkeys + chunk - 1) / chunk : 1;
+      a.ws_cnt[q] = ns;
+    }
+    int x = ns;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int start = before + x - ns;
+    if (q < a.n_q) {
+      a.ws_start[q] = start;
+      for (int i = 0; i < ns; ++i) a.ws_item_q[start + i] = (int)q;
+    }
+    __syncthreads();
+    if (tid == 1023) carry = start + ns;
+    __syncthreads();
+  }
+  if (tid == 0) a.ws_start[a.n_q] = carry;
+}
 
 // Source row of key kk, encoded: entry rows as themselves (>= 0), raw window
 // rows r as -2 - r, no key as -1.  `lo` / `hi` give the range of token offsets
@@ -202,8 +296,9 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   // staging units: bf16 = one key x 16 dims, fp32 = one key x 4 dims
   constexpr int UPR = F32C ? D / 4 : D / 16;     // units per key row
   constexpr int UNITS = KT * UPR;
-  // prefetching variants run with at least 256 threads
-  constexpr int UPT = PREF ? (UNITS + 255) / 256 : 1;
+  // prefetching variants run with at least PMIN threads
+  constexpr int PMIN = D == 512 ? 512 : 256;
+  constexpr int UPT = PREF ? (UNITS + PMIN - 1) / PMIN : 1;
   constexpr size_t KBYTES = F32C ? (size_t)KT * KSTR * 4 : (size_t)KT * D * 2;
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -223,61 +318,34 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   const int dpart = wave - rb * DSPLIT;
   const int d0 = dpart * DW;
 
-  // ---- geometry of this workgroup's token group
-  Geo g;
-  g.q_first = (int64_t)blockIdx.x * a.tok;
-  g.q_last = g.q_first + a.tok - 1;
-  if (g.q_last >= a.n_q) g.q_last = a.n_q - 1;
-  const int req = find_request(a.b.q_off, a.b.n_req, g.q_first);
-  const QueryMeta qm0 = query_meta(a.b, g.q_first, a.m);
-  g.t_first = qm0.t;
-  g.t_last = g.t_first + (g.q_last - g.q_first);
-  g.kv_base = qm0.kv_base;
-  g.raw_base = qm0.raw_base;
-  g.raw_pos = qm0.raw_pos;
-  g.kv_len = a.b.kv_off != nullptr && a.b.kv_rows > 0
-                 ? clamp64(a.b.kv_off[req + 1], qm0.kv_base, a.b.kv_rows) - qm0.kv_base
-                 : 0;
-  g.nvis_first = qm0.n_vis;
-  if constexpr (SPARSE) {
-    g.nE = a.kv != nullptr ? (int)(g.q_last - g.q_first + 1) * a.k : 0;
+  // ---- work items.  Without split-K a workgroup owns one token group (x)
+  // of one head group; with split-K the grid is persistent: workgroup x takes
+  // items x, x + gridDim.x, ... of the work list, for head group y.
+  // (split-K is exactly the partial-output instantiation)
+  constexpr bool splitk = OUTM == 2;
+  const int hgrp = splitk ? (int)blockIdx.y : (int)(blockIdx.x % (unsigned)a.ngroups);
+  const int n_items = splitk ? a.ws_start[a.n_q] : 1;
+  for (int item = splitk ? (int)blockIdx.x : 0; item < n_items; item += splitk ? (int)gridDim.x : 1) {
+  int64_t q_first;
+  int split = 0;
+  if (splitk) {
+    q_first = a.ws_item_q[item];
+    split = item - a.ws_start[q_first];
   } else {
-    const int64_t nc = (g.t_last + 1) / a.m;
-    g.nE = a.kv != nullptr ? (int)(nc < g.kv_len ? nc : g.kv_len) : 0;
+    q_first = (int64_t)(blockIdx.x / (unsigned)a.ngroups) * a.tok;
   }
-  int64_t whi = -1;
-  g.wlo = 0;
-  if (a.raw != nullptr && a.window > 0 && qm0.raw_len > 0) {
-    g.wlo = g.t_first - a.window + 1;
-    if (g.wlo < 0) g.wlo = 0;
-    if (g.wlo < qm0.raw_pos) g.wlo = qm0.raw_pos;
-    whi = g.t_last;
-    if (whi > qm0.raw_pos + qm0.raw_len - 1) whi = qm0.raw_pos + qm0.raw_len - 1;
-  }
-  const int nW = whi >= g.wlo ? (int)(whi - g.wlo + 1) : 0;
-  g.nkeys = g.nE + nW;
-
-  // ---- key range of this workgroup (split-K)
-  int split = 0, nsplit = 1;
-  g.key_lo = 0;
-  g.key_hi = g.nkeys;
-  if (a.split_keys > 0) {
-    int chunk = a.split_keys;
-    const int need = (g.nkeys + a.max_splits - 1) / a.max_splits;
-    if (need > chunk) chunk = need;
-    chunk = (chunk + KT - 1) / KT * KT;
-    nsplit = g.nkeys > 0 ? (g.nkeys + chunk - 1) / chunk : 1;
-    split = blockIdx.y;
-    if (split >= nsplit) return;                   // whole workgroup: nothing to do
+  Geo g = make_geo<SPARSE>(a, q_first);
+  if (splitk) {
+    const int chunk = split_chunk(a, g.nkeys);
     g.key_lo = split * chunk;
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
-    if (split == 0 && tid == 0) a.ws_cnt[g.q_first] = nsplit;
+    __syncthreads();                 // LDS of the previous item fully consumed
   }
 
   // ---- this lane's query row
   const int row_in_wg = rb * 32 + ql;
-  const int g_row = row_in_wg / a.H;
-  const int h_row = row_in_wg - g_row * a.H;
+  const int g_row = row_in_wg / a.hg;
+  const int h_row = hgrp * a.hg + (row_in_wg - g_row * a.hg);
   const int64_t q_row = g.q_first + g_row;
   const bool row_live = q_row <= g.q_last;
   const int64_t qrow_index = q_row * a.H + h_row;    // row of the q / out tensors
@@ -371,13 +439,23 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       if (u < UNITS) store_unit(u, stg[i], sfp8[i]);
     }
   };
-  // without prefetch: every thread loads and stores units tid, tid+nthreads, ...
+  // without prefetch: every thread stages units tid, tid+nthreads, ..., in
+  // batches of SB whose loads are all issued before the first is stored
+  constexpr int SB = (D == 512 && DSPLIT == 2) ? 1 : 4;   // D = 512 over two waves: no registers to spare
   auto stage_direct = [&](int buf) {
-    for (int u = tid; u < UNITS; u += nthreads) {
-      stage_t v[SPU];
-      bool fp8;
-      load_unit(buf, u, v, fp8);
-      store_unit(u, v, fp8);
+    for (int u0 = 0; u0 < UNITS; u0 += SB * nthreads) {
+      stage_t v[SB][SPU];
+      bool fp8[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int u = u0 + tid + i * nthreads;
+        if (u < UNITS) load_unit(buf, u, v[i], fp8[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int u = u0 + tid + i * nthreads;
+        if (u < UNITS) store_unit(u, v[i], fp8[i]);
+      }
     }
   };
 
@@ -547,7 +625,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (!row_live) return;
+  if (row_live) {
   const float lse_v = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   const int64_t rows_total = a.n_q * a.H;
   float* lse_dst = OUTM == 2 ? a.ws_lse + split * rows_total : a.lse;
@@ -571,24 +649,44 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       }
     }
   }
+  }  // row_live
+  }  // work items
 }
 
 template <int D, bool F32C, int DSPLIT>
 size_t attn_smem(int nrb);
 
-// the same kernel without register prefetch (fewer than 256 threads)
+// Workgroups of one launch: one per (token group, head group), or with split-K
+// a persistent grid (as many as fit on the device at once, at most one per
+// work item) times the head groups.
+template <typename K>
+dim3 attn_grid(const AttnArgs& a, K kern, int threads, size_t smem) {
+  if (a.split_keys <= 0)
+    return dim3((unsigned)((a.n_q + a.tok - 1) / a.tok * a.ngroups), 1u);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, smem) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  int64_t n = (int64_t)cus * per_cu;
+  const int64_t items = a.n_q * (int64_t)a.max_splits;
+  if (n > items) n = items;
+  return dim3((unsigned)n, (unsigned)a.ngroups);
+}
+
+// the same kernel without register prefetch (too few threads to share it)
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM>
 csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
   const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb);
   const int threads = a.nrb * DSPLIT * 64;
-  const int64_t nblk = (a.n_q + a.tok - 1) / a.tok;
   auto kern = attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, false>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (smem > 64 * 1024 && attr != hipSuccess)
     return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
-  const unsigned gy = a.split_keys > 0 ? (unsigned)a.max_splits : 1u;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk, gy), dim3(threads), smem, stream, a);
+  hipLaunchKernelGGL(kern, attn_grid(a, kern, threads, smem), dim3(threads), smem, stream, a);
   return csa_host::check_launch("csa_sparse_mqa_attn");
 }
 
@@ -604,11 +702,13 @@ template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM>
 csa_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb);
   const int threads = a.nrb * DSPLIT * 64;
-  const int64_t nblk = (a.n_q + a.tok - 1) / a.tok;
-  if (nblk > 0x7fffffff) return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "attn: too many queries");
-  // register prefetch of the next tile only where the registers allow it
-  constexpr bool kPref = D == 128 && !F32C;
-  if (kPref && threads < 256) return launch_attn_np<D, F32C, KVF, SPARSE, DSPLIT, OUTM>(a, stream);
+  if ((a.n_q + a.tok - 1) / a.tok * a.ngroups > 0x7fffffff)
+    return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "attn: too many queries");
+  // register prefetch of the next tile (bf16 compute with registers to spare,
+  // enough threads to share it)
+  constexpr bool kPref = !F32C && (D == 128 || DSPLIT == 4);
+  if (kPref && threads < (D == 512 ? 512 : 256))
+    return launch_attn_np<D, F32C, KVF, SPARSE, DSPLIT, OUTM>(a, stream);
   auto kern = attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, kPref>;
   // the kernel's LDS ceiling is raised once per instantiation, to the most any
   // launch of it can ask for (so no attribute call happens inside a captured graph)
@@ -616,21 +716,34 @@ csa_status launch_attn(const AttnArgs& a, hipStream_t stream) {
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (smem > 64 * 1024 && attr != hipSuccess)
     return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
-  const unsigned gy = a.split_keys > 0 ? (unsigned)a.max_splits : 1u;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk, gy), dim3(threads), smem, stream, a);
+  hipLaunchKernelGGL(kern, attn_grid(a, kern, threads, smem), dim3(threads), smem, stream, a);
   return csa_host::check_launch("csa_sparse_mqa_attn");
 }
 
+csa_status launch_plan(const AttnArgs& a, bool sparse, hipStream_t s) {
+  if (sparse) hipLaunchKernelGGL(attn_split_plan<true>, dim3(1), dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL(attn_split_plan<false>, dim3(1), dim3(1024), 0, s, a);
+  return csa_host::check_launch("csa_sparse_mqa_attn (split plan)");
+}
+
+// split-K only (partial outputs to the workspace)
+template <int D, bool F32C, int KVF, int DSPLIT>
+csa_status launch_split(const AttnArgs& a, bool sparse, hipStream_t s) {
+  const csa_status st = launch_plan(a, sparse, s);
+  if (st != CSA_OK) return st;
+  if (sparse) return launch_attn<D, F32C, KVF, true, DSPLIT, 2>(a, s);
+  return launch_attn<D, F32C, KVF, false, DSPLIT, 2>(a, s);
+}
+
+// one pass per token group, final output (fp32 or bf16)
 template <int D, bool F32C, int KVF, int DSPLIT>
 csa_status launch_mode(const AttnArgs& a, bool sparse, int outm, hipStream_t s) {
   if (sparse) {
     if (outm == 0) return launch_attn<D, F32C, KVF, true, DSPLIT, 0>(a, s);
-    if (outm == 1) return launch_attn<D, F32C, KVF, true, DSPLIT, 1>(a, s);
-    return launch_attn<D, F32C, KVF, true, DSPLIT, 2>(a, s);
+    return launch_attn<D, F32C, KVF, true, DSPLIT, 1>(a, s);
   }
   if (outm == 0) return launch_attn<D, F32C, KVF, false, DSPLIT, 0>(a, s);
-  if (outm == 1) return launch_attn<D, F32C, KVF, false, DSPLIT, 1>(a, s);
-  return launch_attn<D, F32C, KVF, false, DSPLIT, 2>(a, s);
+  return launch_attn<D, F32C, KVF, false, DSPLIT, 1>(a, s);
 }
 
 int max_splits_for(int64_t max_keys, int split_keys) {
@@ -650,7 +763,9 @@ extern "C" size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t 
   if (split_keys <= 0 || n_q <= 0 || n_heads <= 0 || dim <= 0 || max_keys < 0) return 0;
   const int ns = max_splits_for(max_keys, split_keys);
   const size_t rows = (size_t)n_q * n_heads;
-  return (size_t)ns * rows * ((size_t)dim + 1) * 4 + (size_t)n_q * 4 + 256;
+  // partial outputs and lse, then per query: split count, first item (+1),
+  // and the query of every item
+  return (size_t)ns * rows * ((size_t)dim + 1) * 4 + ((size_t)n_q * (2 + (size_t)ns) + 1) * 4 + 256;
 }
 
 extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
@@ -739,12 +854,19 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   }
 
   // rows per workgroup: D = 128 packs several tokens into 128 rows (when one
-  // request and no split); otherwise one token's H rows (at least 32)
+  // request and no split), otherwise one token's H rows (at least 32).  D = 512
+  // runs two waves per 32 rows (all heads of a token in one workgroup, so its
+  // keys are staged once) or, split over keys (decode), four waves per 32 rows
+  // on at most 64 heads (a head group), which leaves registers for prefetching
   const bool split = split_keys > 0;
   int rows;
+  a.hg = H;
+  if (D == 512 && split && H % 64 == 0) a.hg = 64;
+  else if (D == 512 && split && H % 32 == 0) a.hg = 32;
   if (D == 128 && !split && batch->n_req == 1) rows = H > 128 ? H : 128;
-  else rows = H < 32 ? 32 : H;
-  a.tok = rows / H > 0 ? rows / H : 1;
+  else rows = a.hg < 32 ? 32 : a.hg;
+  a.ngroups = H / a.hg;
+  a.tok = rows / a.hg > 0 ? rows / a.hg : 1;
   if (a.tok > kTokMax) return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: too many tokens per workgroup");
   a.nrb = rows / 32;
   if (a.tok > 1 && batch->n_req > 1)
@@ -765,13 +887,19 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
     a.ws_o = reinterpret_cast<float*>(ws);
     a.ws_lse = reinterpret_cast<float*>(ws + (size_t)a.max_splits * rows_total * D * 4);
     a.ws_cnt = reinterpret_cast<int*>(ws + (size_t)a.max_splits * rows_total * (D + 1) * 4);
+    a.ws_start = a.ws_cnt + batch->n_q;
+    a.ws_item_q = a.ws_start + batch->n_q + 1;
     outm = 2;
   }
   const int kvf = has_kv ? kv->fmt : (f32c ? CSA_F32 : CSA_BF16);
   csa_status st;
-  if (f32c) st = launch_mode<128, true, CSA_F32, 1>(a, sparse, outm, stream);
+  if (f32c && split) st = launch_split<128, true, CSA_F32, 1>(a, sparse, stream);
+  else if (f32c) st = launch_mode<128, true, CSA_F32, 1>(a, sparse, outm, stream);
+  else if (D == 128 && split) st = launch_split<128, false, CSA_BF16, 1>(a, sparse, stream);
   else if (D == 128) st = launch_mode<128, false, CSA_BF16, 1>(a, sparse, outm, stream);
+  else if (kvf == CSA_FP8_MIXED && split) st = launch_split<512, false, CSA_FP8_MIXED, 4>(a, sparse, stream);
   else if (kvf == CSA_FP8_MIXED) st = launch_mode<512, false, CSA_FP8_MIXED, 2>(a, sparse, outm, stream);
+  else if (split) st = launch_split<512, false, CSA_BF16, 4>(a, sparse, stream);
   else st = launch_mode<512, false, CSA_BF16, 2>(a, sparse, outm, stream);
   if (st != CSA_OK || !split) return st;
   // combine the split partials of every query row
