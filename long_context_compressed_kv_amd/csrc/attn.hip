@@ -78,6 +78,7 @@ struct AttnArgs {
   int* ws_cnt;       // [n_q] splits used per query
   int* ws_start;     // [n_q + 1] first work item of each query (split-K)
   int* ws_item_q;    // [n_q * max_splits] query of each work item (split-K)
+  int4* ws_geo;      // [n_q][4] geometry record of each query (split-K)
 };
 
 // Tile geometry shared by every thread of a workgroup.
@@ -98,16 +99,13 @@ __device__ Geo make_geo(const AttnArgs& a, int64_t q_first) {
   g.q_first = q_first;
   g.q_last = g.q_first + a.tok - 1;
   if (g.q_last >= a.n_q) g.q_last = a.n_q - 1;
-  const int req = find_request(a.b.q_off, a.b.n_req, g.q_first);
   const QueryMeta qm0 = query_meta(a.b, g.q_first, a.m);
   g.t_first = qm0.t;
   g.t_last = g.t_first + (g.q_last - g.q_first);
   g.kv_base = qm0.kv_base;
   g.raw_base = qm0.raw_base;
   g.raw_pos = qm0.raw_pos;
-  g.kv_len = a.b.kv_off != nullptr && a.b.kv_rows > 0
-                 ? clamp64(a.b.kv_off[req + 1], qm0.kv_base, a.b.kv_rows) - qm0.kv_base
-                 : 0;
+  g.kv_len = qm0.kv_len;
   g.nvis_first = qm0.n_vis;
   if constexpr (SPARSE) {
     g.nE = a.kv != nullptr ? (int)(g.q_last - g.q_first + 1) * a.k : 0;
@@ -131,12 +129,52 @@ __device__ Geo make_geo(const AttnArgs& a, int64_t q_first) {
   return g;
 }
 
+// The geometry of a one-token group as a 64-byte record (split-K work items
+// read it with one load instead of re-resolving the request).
+__device__ __forceinline__ void store_geo(int4* dst, const Geo& g) {
+  const int64_t v[8] = {g.t_first, g.kv_base, g.raw_base, g.raw_pos, g.kv_len, g.nvis_first, g.wlo,
+                        ((int64_t)(uint32_t)g.nkeys << 32) | (uint32_t)g.nE};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(int4, make_longlong2(v[2 * i], v[2 * i + 1]));
+}
+__device__ __forceinline__ Geo load_geo(const int4* src, int64_t q) {
+  int64_t v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const longlong2 x = __builtin_bit_cast(longlong2, src[i]);
+    v[2 * i] = x.x;
+    v[2 * i + 1] = x.y;
+  }
+  Geo g;
+  g.q_first = g.q_last = q;
+  g.t_first = g.t_last = v[0];
+  g.kv_base = v[1];
+  g.raw_base = v[2];
+  g.raw_pos = v[3];
+  g.kv_len = v[4];
+  g.nvis_first = v[5];
+  g.wlo = v[6];
+  g.nE = (int)(uint32_t)v[7];
+  g.nkeys = (int)(uint32_t)(v[7] >> 32);
+  g.key_lo = 0;
+  g.key_hi = g.nkeys;
+  return g;
+}
+
 // Keys per split of a query with nkeys keys (a multiple of the tile).
 __device__ __forceinline__ int split_chunk(const AttnArgs& a, int nkeys) {
   int chunk = a.split_keys;
   const int need = (nkeys + a.max_splits - 1) / a.max_splits;
   if (need > chunk) chunk = need;
   return (chunk + KT - 1) / KT * KT;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads also waits for every
+// outstanding global load, which would drain the prefetch of the next tile at
+// each barrier inside the key loop; register uses of those loads still wait
+// for them where they are consumed.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Split-K work list: splits per query, their prefix sums and the query of
@@ -156,6 +194,7 @@ __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
       const int chunk = split_chunk(a, g.nkeys);
       ns = g.nkeys > 0 ? (g.nkeys + chunk - 1) / chunk : 1;
       a.ws_cnt[q] = ns;
+      store_geo(a.ws_geo + q * 4, g);
     }
     int x = ns;
 #pragma unroll
@@ -254,7 +293,8 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 c, float s, uint4& y0
 }
 
 // One staging slot of a bf16-compute tile: dims [d, d+16) of one key.  For an
-// FP8_MIXED entry below dim 448, x0 holds the 16 codes and x1.x the scale.
+// FP8_MIXED entry below dim 448, x0 holds the 16 codes and x1.x the e8m0 scale
+// byte (decoded only when stored, so a prefetch never waits on it).
 template <int D, int KVF>
 __device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uint4& x0, uint4& x1) {
   x0 = make_uint4(0, 0, 0, 0);
@@ -263,7 +303,7 @@ __device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uin
     if constexpr (KVF == CSA_FP8_MIXED) {
       if (d < 448) {
         x0 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) + (int64_t)row * 448 + d);
-        x1.x = __float_as_uint(e8m0_to_f32(a.kv_scale[(int64_t)row * 4 + (d >> 7)]));
+        x1.x = a.kv_scale[(int64_t)row * 4 + (d >> 7)];
         return true;
       }
       const uint4* p = reinterpret_cast<const uint4*>(a.kv_rope + (int64_t)row * 64 + (d - 448));
@@ -284,7 +324,7 @@ __device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uin
 
 template <int D>
 __device__ __forceinline__ void store_slot(unsigned char* kb, int key, int d, bool fp8, uint4 x0, uint4 x1) {
-  if (fp8) fp8x16_to_bf16(x0, __uint_as_float(x1.x), x0, x1);
+  if (fp8) fp8x16_to_bf16(x0, e8m0_to_f32(x1.x), x0, x1);
   *reinterpret_cast<uint4*>(kb + swz_off<D>(key, d >> 3)) = x0;
   *reinterpret_cast<uint4*>(kb + swz_off<D>(key, (d >> 3) + 1)) = x1;
 }
@@ -306,7 +346,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   int* mrow = reinterpret_cast<int*>(smem + KBYTES);               // [2][KT] source rows
   uint32_t* mword = reinterpret_cast<uint32_t*>(mrow + 2 * KT);    // [2][kTokMax] key bits per token
   int* mfull = reinterpret_cast<int*>(mword + 2 * kTokMax);        // [2], padded to 4 ints
-  float* sx = reinterpret_cast<float*>(mfull + 4); // [nrb][DSPLIT][64][16] partial logits
+  float* sx = reinterpret_cast<float*>(mfull + 4); // [nrb][DSPLIT][4][64] float4 partial logits
 
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -334,12 +374,12 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   } else {
     q_first = (int64_t)(blockIdx.x / (unsigned)a.ngroups) * a.tok;
   }
-  Geo g = make_geo<SPARSE>(a, q_first);
+  Geo g = splitk ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
   if (splitk) {
     const int chunk = split_chunk(a, g.nkeys);
     g.key_lo = split * chunk;
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
-    __syncthreads();                 // LDS of the previous item fully consumed
+    lds_barrier();                 // LDS of the previous item fully consumed
   }
 
   // ---- this lane's query row
@@ -486,17 +526,17 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   const int ntiles = (g.key_hi - g.key_lo + KT - 1) / KT;
   if (ntiles > 0) {
     meta_tile(g.key_lo, 0);
-    __syncthreads();
+    lds_barrier();
     if constexpr (PREF) load_tile(0);
   }
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     const int kbase = g.key_lo + tile * KT;
-    __syncthreads();                 // previous tile fully consumed
+    lds_barrier();                 // previous tile fully consumed
     if constexpr (PREF) store_tile();
     else stage_direct(buf);
     if (tile + 1 < ntiles) meta_tile(kbase + KT, buf ^ 1);
-    __syncthreads();                 // tile in LDS, next tile's sources resolved
+    lds_barrier();                 // tile in LDS, next tile's sources resolved
     if constexpr (PREF) {
       if (tile + 1 < ntiles) load_tile(buf ^ 1);   // in flight during the compute below
     }
@@ -526,19 +566,21 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       }
     }
     if constexpr (DSPLIT > 1) {
-      float* mine = sx + ((rb * DSPLIT + dpart) * 64 + lane) * 16;
+      // [rb][wave part][register quad][lane] float4s: each access of a wave is
+      // 1 KB of consecutive LDS, free of bank conflicts
+      float4* mine = reinterpret_cast<float4*>(sx) + (rb * DSPLIT + dpart) * 4 * 64 + lane;
 #pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<float4*>(mine + i) = make_float4(acc_s[i], acc_s[i + 1], acc_s[i + 2], acc_s[i + 3]);
-      __syncthreads();
+      for (int i = 0; i < 4; ++i)
+        mine[i * 64] = make_float4(acc_s[4 * i], acc_s[4 * i + 1], acc_s[4 * i + 2], acc_s[4 * i + 3]);
+      lds_barrier();
       acc_s = f32x16_t{};
 #pragma unroll
       for (int p = 0; p < DSPLIT; ++p) {
-        const float* part = sx + ((rb * DSPLIT + p) * 64 + lane) * 16;
+        const float4* part = reinterpret_cast<const float4*>(sx) + (rb * DSPLIT + p) * 4 * 64 + lane;
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(part + i);
-          acc_s[i] += v.x; acc_s[i + 1] += v.y; acc_s[i + 2] += v.z; acc_s[i + 3] += v.w;
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = part[i * 64];
+          acc_s[4 * i] += v.x; acc_s[4 * i + 1] += v.y; acc_s[4 * i + 2] += v.z; acc_s[4 * i + 3] += v.w;
         }
       }
     }
@@ -764,8 +806,9 @@ extern "C" size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t 
   const int ns = max_splits_for(max_keys, split_keys);
   const size_t rows = (size_t)n_q * n_heads;
   // partial outputs and lse, then per query: split count, first item (+1),
-  // and the query of every item
-  return (size_t)ns * rows * ((size_t)dim + 1) * 4 + ((size_t)n_q * (2 + (size_t)ns) + 1) * 4 + 256;
+  // the query of every item, and a 64-byte geometry record
+  return (size_t)ns * rows * ((size_t)dim + 1) * 4 + ((size_t)n_q * (2 + (size_t)ns) + 1) * 4 + 16 +
+         (size_t)n_q * 64 + 256;
 }
 
 extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
@@ -889,6 +932,8 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
     a.ws_cnt = reinterpret_cast<int*>(ws + (size_t)a.max_splits * rows_total * (D + 1) * 4);
     a.ws_start = a.ws_cnt + batch->n_q;
     a.ws_item_q = a.ws_start + batch->n_q + 1;
+    const uintptr_t geo = reinterpret_cast<uintptr_t>(a.ws_item_q + (size_t)batch->n_q * a.max_splits);
+    a.ws_geo = reinterpret_cast<int4*>((geo + 15) & ~(uintptr_t)15);
     outm = 2;
   }
   const int kvf = has_kv ? kv->fmt : (f32c ? CSA_F32 : CSA_BF16);

@@ -146,8 +146,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Index of the request holding flat query q (q_off is nondecreasing,
-// q_off[0] = 0).  Clamped to [0, n_req).
+// q_off[0] = 0).  Clamped to [0, n_req).  One query per request (decode)
+// resolves with one pair of loads; otherwise a binary search.
 __device__ __forceinline__ int find_request(const int64_t* q_off, int n_req, int64_t q) {
+  if (q < n_req) {
+    const int64_t a = q_off[q], b = q_off[q + 1];
+    if (a <= q && q < b) return (int)q;
+  }
   int lo = 0, hi = n_req - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -166,6 +171,7 @@ struct QueryMeta {
   int64_t t;        // absolute position of the query
   int64_t kv_base;  // first entry row of the request
   int64_t n_vis;    // visible entries
+  int64_t kv_len;   // entry rows of the request
   int64_t raw_base; // first raw row of the request
   int64_t raw_pos;  // position of raw_base
   int64_t raw_len;  // raw rows of the request
@@ -185,24 +191,33 @@ struct BatchDev {
 __device__ __forceinline__ QueryMeta query_meta(const BatchDev& b, int64_t q, int m) {
   QueryMeta r;
   const int req = find_request(b.q_off, b.n_req, q);
-  r.t = b.q_pos[req] + (q - b.q_off[req]);
+  // every load first (they are independent), then the arithmetic
+  const bool has_kv = b.kv_off != nullptr && b.kv_rows > 0;
+  const bool has_raw = b.raw_off != nullptr && b.raw_rows > 0;
+  const int64_t qpos = b.q_pos[req], qoff = b.q_off[req];
+  const int64_t kv0 = has_kv ? b.kv_off[req] : 0, kv1 = has_kv ? b.kv_off[req + 1] : 0;
+  const int64_t rw0 = has_raw ? b.raw_off[req] : 0, rw1 = has_raw ? b.raw_off[req + 1] : 0;
+  const int64_t rpos = has_raw ? b.raw_pos[req] : 0;
+  r.t = qpos + (q - qoff);
   if (r.t < 0) r.t = 0;
-  if (b.kv_off != nullptr && b.kv_rows > 0) {
-    const int64_t lo = clamp64(b.kv_off[req], 0, b.kv_rows);
-    const int64_t hi = clamp64(b.kv_off[req + 1], lo, b.kv_rows);
+  if (has_kv) {
+    const int64_t lo = clamp64(kv0, 0, b.kv_rows);
+    const int64_t hi = clamp64(kv1, lo, b.kv_rows);
     r.kv_base = lo;
+    r.kv_len = hi - lo;
     const int64_t nc = (r.t + 1) / m;
     r.n_vis = nc < hi - lo ? nc : hi - lo;
   } else {
     r.kv_base = 0;
+    r.kv_len = 0;
     r.n_vis = 0;
   }
-  if (b.raw_off != nullptr && b.raw_rows > 0) {
-    const int64_t lo = clamp64(b.raw_off[req], 0, b.raw_rows);
-    const int64_t hi = clamp64(b.raw_off[req + 1], lo, b.raw_rows);
+  if (has_raw) {
+    const int64_t lo = clamp64(rw0, 0, b.raw_rows);
+    const int64_t hi = clamp64(rw1, lo, b.raw_rows);
     r.raw_base = lo;
     r.raw_len = hi - lo;
-    r.raw_pos = b.raw_pos[req];
+    r.raw_pos = rpos;
   } else {
     r.raw_base = 0;
     r.raw_len = 0;
