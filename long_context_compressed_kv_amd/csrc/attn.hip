@@ -292,34 +292,33 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 c, float s, uint4& y0
   y1 = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// One staging slot of a bf16-compute tile: dims [d, d+16) of one key.  For an
-// FP8_MIXED entry below dim 448, x0 holds the 16 codes and x1.x the e8m0 scale
-// byte (decoded only when stored, so a prefetch never waits on it).
+// One staging slot of a bf16-compute tile: dims [d, d+16) of one key (row
+// encoded as in key_meta, never -1 here).  For an FP8_MIXED entry below dim
+// 448, x0 holds the 16 codes and x1.x the e8m0 scale byte (decoded only when
+// stored, so a prefetch never waits on it).  Returns whether x0 holds codes.
 template <int D, int KVF>
 __device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uint4& x0, uint4& x1) {
-  x0 = make_uint4(0, 0, 0, 0);
-  x1 = make_uint4(0, 0, 0, 0);
-  if (row >= 0) {
-    if constexpr (KVF == CSA_FP8_MIXED) {
-      if (d < 448) {
-        x0 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) + (int64_t)row * 448 + d);
-        x1.x = a.kv_scale[(int64_t)row * 4 + (d >> 7)];
-        return true;
-      }
-      const uint4* p = reinterpret_cast<const uint4*>(a.kv_rope + (int64_t)row * 64 + (d - 448));
-      x0 = p[0];
-      x1 = p[1];
-    } else {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kv) + (int64_t)row * D + d);
-      x0 = p[0];
-      x1 = p[1];
+  if constexpr (KVF == CSA_FP8_MIXED) {
+    if (row >= 0 && d < 448) {
+      x0 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) + (int64_t)row * 448 + d);
+      x1.x = a.kv_scale[(int64_t)row * 4 + (d >> 7)];
+      return true;
     }
-  } else if (row != -1) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.raw) + (int64_t)(-2 - row) * D + d);
+    const uint4* p = row >= 0
+        ? reinterpret_cast<const uint4*>(a.kv_rope + (int64_t)row * 64 + (d - 448))
+        : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.raw) + (int64_t)(-2 - row) * D + d);
     x0 = p[0];
     x1 = p[1];
+    return false;
+  } else {
+    // entries and window rows are both bf16 [rows, D]: one load through a select
+    const uint16_t* base = row >= 0 ? static_cast<const uint16_t*>(a.kv) + (int64_t)row * D
+                                    : static_cast<const uint16_t*>(a.raw) + (int64_t)(-2 - row) * D;
+    const uint4* p = reinterpret_cast<const uint4*>(base + d);
+    x0 = p[0];
+    x1 = p[1];
+    return false;
   }
-  return false;
 }
 
 template <int D>
@@ -421,6 +420,9 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       int row = -1;
       int64_t lo = 1, hi = 0;
       if (tid < KT) key_meta<SPARSE>(a, g, kbase + tid, row, lo, hi);
+      // a key without a source (past the range, or an unused selection slot)
+      // reads a row that always exists and stays masked
+      if (!F32C && row == -1) row = a.kv != nullptr ? 0 : -2;
       if (tid < KT) mrow[buf * KT + tid] = row;
       bool full = true;
       for (int t = 0; t < a.tok; ++t) {
@@ -438,13 +440,19 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   constexpr int SPU = F32C ? 1 : 2;               // stage registers per unit
   stage_t stg[UPT][SPU];
   bool sfp8[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    sfp8[i] = false;
+#pragma unroll
+    for (int j = 0; j < SPU; ++j) stg[i][j] = stage_t{};
+  }
 
   auto load_unit = [&](int buf, int u, stage_t* v, bool& fp8) {
     const int key = u / UPR;
     const int row = mrow[buf * KT + key];
-    fp8 = false;
     if constexpr (F32C) {
       const int d = (u - key * UPR) * 4;
+      fp8 = false;
       v[0] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (row != -1) {
         const float* src = static_cast<const float*>(row >= 0 ? a.kv : a.raw);
@@ -484,8 +492,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   constexpr int SB = (D == 512 && DSPLIT == 2) ? 1 : 4;   // D = 512 over two waves: no registers to spare
   auto stage_direct = [&](int buf) {
     for (int u0 = 0; u0 < UNITS; u0 += SB * nthreads) {
-      stage_t v[SB][SPU];
-      bool fp8[SB];
+      stage_t v[SB][SPU] = {};
+      bool fp8[SB] = {};
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         const int u = u0 + tid + i * nthreads;
@@ -521,6 +529,12 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) tr_x[x] = 64 * (x ^ (tk & 3));
   }
+
+  // The query registers are settled before the key loop: otherwise, inside
+  // the loop, their loads cannot be told apart from the prefetch in flight and
+  // every first use would wait for all outstanding loads.
+#pragma unroll
+  for (int c = 0; c < QC; ++c) asm volatile("" :: "v"(qreg[c]));
 
   // ---- key loop: prologue resolves (and, prefetching, loads) the first tile
   const int ntiles = (g.key_hi - g.key_lo + KT - 1) / KT;
