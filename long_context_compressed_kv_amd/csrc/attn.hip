@@ -73,12 +73,14 @@ struct AttnArgs {
   int nrb;           // 32-row blocks per workgroup
   int split_keys;    // 0: one workgroup per token group; else keys per split
   int max_splits;
+  int target_items;  // split-K: work items that keep the persistent grid busy
   float* ws_o;       // [max_splits][n_q*H][D]
   float* ws_lse;     // [max_splits][n_q*H]
   int* ws_cnt;       // [n_q] splits used per query
   int* ws_start;     // [n_q + 1] first work item of each query (split-K)
   int* ws_item_q;    // [n_q * max_splits] query of each work item (split-K)
   int4* ws_geo;      // [n_q][4] geometry record of each query (split-K)
+  int* ws_chunk;     // keys per split chosen by the plan (split-K)
 };
 
 // Tile geometry shared by every thread of a workgroup.
@@ -161,13 +163,6 @@ __device__ __forceinline__ Geo load_geo(const int4* src, int64_t q) {
   return g;
 }
 
-// Keys per split of a query with nkeys keys (a multiple of the tile).
-__device__ __forceinline__ int split_chunk(const AttnArgs& a, int nkeys) {
-  int chunk = a.split_keys;
-  const int need = (nkeys + a.max_splits - 1) / a.max_splits;
-  if (need > chunk) chunk = need;
-  return (chunk + KT - 1) / KT * KT;
-}
 
 // Workgroup barrier that orders LDS only.  __syncthreads also waits for every
 // outstanding global load, which would drain the prefetch of the next tile at
@@ -177,24 +172,65 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Split-K work list: splits per query, their prefix sums and the query of
-// every (query, split) item, so the attention grid visits only real items.
+// Split-K work list.  One chunk size for the whole batch: at least the
+// caller's split_keys (and enough that no query needs more than max_splits),
+// raised so the batch's keys form about target_items items; then the splits
+// of every query, their prefix sums and the query of every item, so the
+// attention grid visits only real items.
 template <bool SPARSE>
 __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
   __shared__ int wsum[16];
+  __shared__ int64_t ksum[16];
   __shared__ int carry;
+  __shared__ int chunk_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) carry = 0;
+  // pass 1: geometry records, total and longest key counts
+  int64_t tot = 0;
+  int kmax = 0;
+  for (int64_t q = tid; q < a.n_q; q += 1024) {
+    const Geo g = make_geo<SPARSE>(a, q);
+    store_geo(a.ws_geo + q * 4, g);
+    tot += g.nkeys;
+    kmax = g.nkeys > kmax ? g.nkeys : kmax;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    tot += __shfl_xor(tot, o);
+    const int m = __shfl_xor(kmax, o);
+    kmax = m > kmax ? m : kmax;
+  }
+  if (lane == 0) {
+    ksum[wave] = tot;
+    wsum[wave] = kmax;
+  }
   __syncthreads();
+  if (tid == 0) {
+    int64_t t = 0;
+    int km = 0;
+    for (int w = 0; w < 16; ++w) {
+      t += ksum[w];
+      km = wsum[w] > km ? wsum[w] : km;
+    }
+    int64_t chunk = a.split_keys;
+    const int64_t need = (km + a.max_splits - 1) / a.max_splits;
+    if (need > chunk) chunk = need;
+    const int64_t fill = a.target_items > 0 ? (t + a.target_items - 1) / a.target_items : 0;
+    if (fill > chunk) chunk = fill;
+    chunk = (chunk + KT - 1) / KT * KT;
+    chunk_s = (int)chunk;
+    *a.ws_chunk = (int)chunk;
+    carry = 0;
+  }
+  __syncthreads();
+  const int chunk = chunk_s;
+  // pass 2: splits, prefix sums, item -> query
   for (int64_t q0 = 0; q0 < a.n_q; q0 += 1024) {
     const int64_t q = q0 + tid;
     int ns = 0;
     if (q < a.n_q) {
-      const Geo g = make_geo<SPARSE>(a, q);
-      const int chunk = split_chunk(a, g.nkeys);
-      ns = g.nkeys > 0 ? (g.nkeys + chunk - 1) / chunk : 1;
+      const int nk = load_geo(a.ws_geo + q * 4, q).nkeys;
+      ns = nk > 0 ? (nk + chunk - 1) / chunk : 1;
       a.ws_cnt[q] = ns;
-      store_geo(a.ws_geo + q * 4, g);
     }
     int x = ns;
 #pragma unroll
@@ -202,6 +238,7 @@ __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
       const int y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
+    __syncthreads();
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     int before = carry;
@@ -375,7 +412,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   }
   Geo g = splitk ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
   if (splitk) {
-    const int chunk = split_chunk(a, g.nkeys);
+    const int chunk = *a.ws_chunk;
     g.key_lo = split * chunk;
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
     lds_barrier();                 // LDS of the previous item fully consumed
@@ -712,6 +749,12 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 template <int D, bool F32C, int DSPLIT>
 size_t attn_smem(int nrb);
 
+csa_status launch_plan(const AttnArgs& a, bool sparse, hipStream_t s) {
+  if (sparse) hipLaunchKernelGGL(attn_split_plan<true>, dim3(1), dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL(attn_split_plan<false>, dim3(1), dim3(1024), 0, s, a);
+  return csa_host::check_launch("csa_sparse_mqa_attn (split plan)");
+}
+
 // Workgroups of one launch: one per (token group, head group), or with split-K
 // a persistent grid (as many as fit on the device at once, at most one per
 // work item) times the head groups.
@@ -732,6 +775,21 @@ dim3 attn_grid(const AttnArgs& a, K kern, int threads, size_t smem) {
   return dim3((unsigned)n, (unsigned)a.ngroups);
 }
 
+// Launches one instantiation; with split-K the plan kernel runs first, its
+// item target set to the persistent grid of this launch.
+template <bool SPARSE, typename K>
+csa_status launch_kernel(const AttnArgs& a0, K kern, int threads, size_t smem, hipStream_t stream) {
+  AttnArgs a = a0;
+  const dim3 grid = attn_grid(a, kern, threads, smem);
+  if (a.split_keys > 0) {
+    a.target_items = (int)grid.x;
+    const csa_status st = launch_plan(a, SPARSE, stream);
+    if (st != CSA_OK) return st;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(threads), smem, stream, a);
+  return csa_host::check_launch("csa_sparse_mqa_attn");
+}
+
 // the same kernel without register prefetch (too few threads to share it)
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM>
 csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
@@ -742,8 +800,7 @@ csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (smem > 64 * 1024 && attr != hipSuccess)
     return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
-  hipLaunchKernelGGL(kern, attn_grid(a, kern, threads, smem), dim3(threads), smem, stream, a);
-  return csa_host::check_launch("csa_sparse_mqa_attn");
+  return launch_kernel<SPARSE>(a, kern, threads, smem, stream);
 }
 
 template <int D, bool F32C, int DSPLIT>
@@ -772,21 +829,12 @@ csa_status launch_attn(const AttnArgs& a, hipStream_t stream) {
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (smem > 64 * 1024 && attr != hipSuccess)
     return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
-  hipLaunchKernelGGL(kern, attn_grid(a, kern, threads, smem), dim3(threads), smem, stream, a);
-  return csa_host::check_launch("csa_sparse_mqa_attn");
-}
-
-csa_status launch_plan(const AttnArgs& a, bool sparse, hipStream_t s) {
-  if (sparse) hipLaunchKernelGGL(attn_split_plan<true>, dim3(1), dim3(1024), 0, s, a);
-  else hipLaunchKernelGGL(attn_split_plan<false>, dim3(1), dim3(1024), 0, s, a);
-  return csa_host::check_launch("csa_sparse_mqa_attn (split plan)");
+  return launch_kernel<SPARSE>(a, kern, threads, smem, stream);
 }
 
 // split-K only (partial outputs to the workspace)
 template <int D, bool F32C, int KVF, int DSPLIT>
 csa_status launch_split(const AttnArgs& a, bool sparse, hipStream_t s) {
-  const csa_status st = launch_plan(a, sparse, s);
-  if (st != CSA_OK) return st;
   if (sparse) return launch_attn<D, F32C, KVF, true, DSPLIT, 2>(a, s);
   return launch_attn<D, F32C, KVF, false, DSPLIT, 2>(a, s);
 }
@@ -821,7 +869,7 @@ extern "C" size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t 
   const size_t rows = (size_t)n_q * n_heads;
   // partial outputs and lse, then per query: split count, first item (+1),
   // the query of every item, and a 64-byte geometry record
-  return (size_t)ns * rows * ((size_t)dim + 1) * 4 + ((size_t)n_q * (2 + (size_t)ns) + 1) * 4 + 16 +
+  return (size_t)ns * rows * ((size_t)dim + 1) * 4 + ((size_t)n_q * (2 + (size_t)ns) + 2) * 4 + 16 +
          (size_t)n_q * 64 + 256;
 }
 
@@ -946,7 +994,8 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
     a.ws_cnt = reinterpret_cast<int*>(ws + (size_t)a.max_splits * rows_total * (D + 1) * 4);
     a.ws_start = a.ws_cnt + batch->n_q;
     a.ws_item_q = a.ws_start + batch->n_q + 1;
-    const uintptr_t geo = reinterpret_cast<uintptr_t>(a.ws_item_q + (size_t)batch->n_q * a.max_splits);
+    a.ws_chunk = a.ws_item_q + (size_t)batch->n_q * a.max_splits;
+    const uintptr_t geo = reinterpret_cast<uintptr_t>(a.ws_chunk + 1);
     a.ws_geo = reinterpret_cast<int4*>((geo + 15) & ~(uintptr_t)15);
     outm = 2;
   }
