@@ -6,15 +6,16 @@
 // Exact and deterministic.  Scores are mapped to order-preserving unsigned
 // keys (-0 folded onto +0); a row keeps the min(k, n) largest keys, ties
 // broken by the lower index, written in ascending index order.  One
-// workgroup (16 waves) per query row:
+// workgroup (8 or 16 waves: many rows or few) per query row:
 //   1. threshold estimate: rows longer than half the LDS candidate capacity take
 //      a strided sample of 4096 keys and use its order statistic of rank
 //      ~2k*4096/n (an exact radix select over the sample in LDS), so about
 //      2k keys of the row lie at or above it;
-//   2. one streaming pass over the row (16-byte loads, waves on contiguous
-//      segments) appends every key >= the estimate, with its index, to the
-//      wave's LDS segment; positions come from wave prefix sums, so the
-//      candidates stay in index order and no atomics are used;
+//   2. one streaming pass over the row (waves on contiguous segments, four
+//      16-byte loads in flight per lane) appends every key >= the estimate,
+//      with its index, to the wave's LDS segment; positions come from wave
+//      prefix sums, so the candidates stay in index order and no atomics are
+//      used;
 //   3. exact radix select of the k-th largest key among the candidates (LDS
 //      histograms), then an ordered scan writes key > tau, or key == tau among
 //      the first `need` ties, at position (#greater before) + min(#ties
@@ -28,11 +29,22 @@ using namespace csa;
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
 constexpr int kCap = 4096;                   // LDS candidates per row
-constexpr int kBudget = kCap / kWaves;       // per wave segment
 constexpr int kSample = 4096;
+constexpr int kU = 4;                        // 16-byte vectors in flight per lane
+
+// Inverse of the order-preserving map, as a float (the threshold test of the
+// streaming pass compares values; -0 and +0 compare equal, as their keys do).
+template <bool BF16>
+__device__ __forceinline__ float key_value(uint32_t key) {
+  if constexpr (BF16) {
+    const uint32_t b = (key & 0x8000u) ? (key & 0x7fffu) : (~key & 0xffffu);
+    return __uint_as_float(b << 16);
+  } else {
+    const uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+    return __uint_as_float(b);
+  }
+}
 
 __device__ __forceinline__ uint32_t order_bf16(uint32_t b) {
   if (b == 0x8000u) b = 0;
@@ -50,6 +62,7 @@ __device__ __forceinline__ uint32_t key_at(const void* row, int64_t j) {
 }
 
 // Exclusive scan of v over the block; total returned through `total`.
+template <int kWaves>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -85,7 +98,11 @@ __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& to
   return x - v;
 }
 
+template <int NT>
 struct Shared {
+  static constexpr int kThreads = NT;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kBudget = kCap / kWaves;       // per wave segment
   uint32_t hist[kWaves][256];
   uint32_t wsum[kWaves];
   uint32_t sel_digit, sel_remain, overflow;
@@ -97,8 +114,9 @@ struct Shared {
 // Radix select of the rank-th largest key among `count` keys produced by
 // get(i).  Returns the key; `remain` = how many keys equal to it are needed to
 // reach rank (so rank - remain keys are strictly greater).
-template <int KBITS, typename Get>
-__device__ uint32_t radix_select(Shared& sh, int64_t count, uint32_t rank, Get get, uint32_t& remain) {
+template <int KBITS, int NT, typename Get>
+__device__ uint32_t radix_select(Shared<NT>& sh, int64_t count, uint32_t rank, Get get, uint32_t& remain) {
+  constexpr int kThreads = NT, kWaves = NT / 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   uint32_t prefix = 0;
@@ -112,15 +130,18 @@ __device__ uint32_t radix_select(Shared& sh, int64_t count, uint32_t rank, Get g
       if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
     }
     __syncthreads();
+    if (tid < 256) {          // per-digit totals of the per-wave histograms
+      uint32_t s = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s += sh.hist[w][tid];
+      sh.hist[0][tid] = s;
+    }
+    __syncthreads();
     if (tid < 64) {
       // lane l owns digits 4l..4l+3; suffix counts from the top digit down
       uint32_t c[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t s = 0;
-        for (int w = 0; w < kWaves; ++w) s += sh.hist[w][4 * tid + i];
-        c[i] = s;
-      }
+      for (int i = 0; i < 4; ++i) c[i] = sh.hist[0][4 * tid + i];
       const uint32_t s = c[0] + c[1] + c[2] + c[3];
       uint32_t x = s;
 #pragma unroll
@@ -148,9 +169,10 @@ __device__ uint32_t radix_select(Shared& sh, int64_t count, uint32_t rank, Get g
 
 // Ordered emission over `count` keys in index order: writes the selected
 // ones' indices idx_of(i) to out[0..k).
-template <typename Get, typename Idx>
-__device__ void emit_ordered(Shared& sh, int64_t count, uint32_t tau, uint32_t need_eq, int k,
+template <int NT, typename Get, typename Idx>
+__device__ void emit_ordered(Shared<NT>& sh, int64_t count, uint32_t tau, uint32_t need_eq, int k,
                              Get get, Idx idx_of, int32_t* out) {
+  constexpr int kThreads = NT, kWaves = NT / 64;
   constexpr int EPT = 8;
   const int tid = threadIdx.x;
   uint32_t base_gt = 0, base_eq = 0;
@@ -167,7 +189,7 @@ __device__ void emit_ordered(Shared& sh, int64_t count, uint32_t tau, uint32_t n
       eq += (valid && keys[e] == tau) ? 1u : 0u;
     }
     uint32_t total;
-    const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.wsum, total);
+    const uint32_t ex = block_exclusive_scan<kWaves>((gt << 16) | eq, sh.wsum, total);
     uint32_t g_before = base_gt + (ex >> 16);
     uint32_t e_before = base_eq + (ex & 0xffffu);
 #pragma unroll
@@ -188,12 +210,13 @@ __device__ void emit_ordered(Shared& sh, int64_t count, uint32_t tau, uint32_t n
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__ scores, int64_t ld,
-                                                        BatchDev b, int m, int k,
-                                                        int32_t* __restrict__ idx) {
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ scores, int64_t ld,
+                                                  BatchDev b, int m, int k,
+                                                  int32_t* __restrict__ idx) {
+  constexpr int kThreads = NT, kWaves = NT / 64, kBudget = Shared<NT>::kBudget;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
+  Shared<NT>& sh = *reinterpret_cast<Shared<NT>*>(smem_raw);
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ESZ;                // elements per 16-byte vector
   constexpr int KBITS = BF16 ? 16 : 32;
@@ -216,7 +239,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
   // wave's segment then holds at most ~n/16 + 8 keys, inside its budget)
   uint32_t tau_hat = 0;
   if (n > kCap / 2) {
-    for (int i = tid; i < kSample; i += kThreads) sh.cand_key[i] = key_at<BF16>(row, (int64_t)i * n / kSample);
+    uint32_t smp[kSample / kThreads];
+#pragma unroll
+    for (int s = 0; s < kSample / kThreads; ++s) {
+      const int i = tid + s * kThreads;
+      smp[s] = key_at<BF16>(row, (int64_t)i * n / kSample);
+    }
+#pragma unroll
+    for (int s = 0; s < kSample / kThreads; ++s) sh.cand_key[tid + s * kThreads] = smp[s];
     __syncthreads();
     int64_t r = (2 * (int64_t)k * kSample + n - 1) / n + 8;
     if (r > kSample) r = kSample;
@@ -227,71 +257,98 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
   if (tid == 0) sh.overflow = 0;
   __syncthreads();
 
-  // ---- 2. stream the row, keep keys >= tau_hat in index order
-  const uintptr_t base_addr = reinterpret_cast<uintptr_t>(row);
-  const int64_t off = (int64_t)((base_addr & 15u) / ESZ);          // elements before the row in its first vector
-  const char* vbase = reinterpret_cast<const char*>(base_addr & ~(uintptr_t)15u);
+  // ---- 2. stream the row, keep keys >= tau_hat in index order.  A wave owns
+  // a contiguous run of 16-byte vectors; each lane keeps kU of them in flight
+  // (vector v0 + 64u + lane), and one packed wave scan per round places the
+  // candidates of all of them.
+  const float tau_f = n > kCap / 2 ? key_value<BF16>(tau_hat) : -INFINITY;
+  const int64_t off = (int64_t)((reinterpret_cast<uintptr_t>(row) & 15u) / ESZ);  // row elements before its first vector boundary
+  const char* vbase = row - off * ESZ;
   const int64_t nvec = (off + n + EPV - 1) / EPV;
   const int64_t per_wave = (nvec + kWaves - 1) / kWaves;
   const int64_t v_lo = wave * per_wave;
   const int64_t v_hi = v_lo + per_wave < nvec ? v_lo + per_wave : nvec;
+  const char* row_end = row + n * ESZ;
   uint32_t wcount = 0;
   bool wover = false;
-  for (int64_t v0 = v_lo; v0 < v_hi; v0 += 64) {
-    const int64_t v = v0 + lane;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (v < v_hi) {
-      // whole vectors inside the row use one 16-byte load; the row's partial
-      // first and last vectors read only their in-row elements
+  for (int64_t v0 = v_lo; v0 < v_hi; v0 += 64 * kU) {
+    uint4 raw[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t v = v0 + 64 * u + lane;
       const char* vp = vbase + v * 16;
-      if (vp >= row && vp + 16 <= row + n * ESZ) {
-        raw = *reinterpret_cast<const uint4*>(vp);
-      } else {
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (v < v_hi && vp >= row && vp + 16 <= row_end) raw[u] = *reinterpret_cast<const uint4*>(vp);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      // the row's partial first and last vectors read only their in-row elements
+      const int64_t v = v0 + 64 * u + lane;
+      const char* vp = vbase + v * 16;
+      if (v < v_hi && !(vp >= row && vp + 16 <= row_end)) {
         uint32_t t4[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const int64_t j = v * EPV + e - off;
           if (j >= 0 && j < n) {
             uint32_t bits;
-            if constexpr (BF16) bits = static_cast<const uint16_t*>(static_cast<const void*>(row))[j];
-            else bits = __float_as_uint(static_cast<const float*>(static_cast<const void*>(row))[j]);
+            if constexpr (BF16) bits = reinterpret_cast<const uint16_t*>(row)[j];
+            else bits = __float_as_uint(reinterpret_cast<const float*>(row)[j]);
             t4[e * ESZ / 4] |= bits << (8 * ((e * ESZ) & 3));
           }
         }
-        raw = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+        raw[u] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
       }
     }
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t flags = 0;
+    uint32_t flags[kU], cnt01 = 0, cnt23 = 0;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int64_t j = v * EPV + e - off;
-      uint32_t key;
-      if constexpr (BF16) key = order_bf16((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-      else key = order_f32(w4[e]);
-      const bool ok = v < v_hi && j >= 0 && j < n && key >= tau_hat;
-      flags |= ok ? (1u << e) : 0u;
-    }
-    const uint32_t c = __builtin_popcount(flags);
-    uint32_t total;
-    const uint32_t pos = wave_exclusive_scan(c, total);
-    if (!wover && wcount + total <= (uint32_t)kBudget) {
-      uint32_t slot = wave * kBudget + wcount + pos;
+    for (int u = 0; u < kU; ++u) {
+      const int64_t v = v0 + 64 * u + lane;
+      const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      uint32_t f = 0;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
-        if (flags & (1u << e)) {
-          uint32_t key;
-          if constexpr (BF16) key = order_bf16((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-          else key = order_f32(w4[e]);
-          sh.cand_key[slot] = key;
-          sh.cand_idx[slot] = (int32_t)(v * EPV + e - off);
-          ++slot;
+        const int64_t j = v * EPV + e - off;
+        float x;
+        if constexpr (BF16) x = __uint_as_float((w4[e >> 1] << (16 * (1 - (e & 1)))) & 0xffff0000u);
+        else x = __uint_as_float(w4[e]);
+        f |= (v < v_hi && j >= 0 && j < n && x >= tau_f) ? (1u << e) : 0u;
+      }
+      flags[u] = f;
+      const uint32_t c = __builtin_popcount(f);
+      if (u < 2) cnt01 |= c << (16 * u);
+      else cnt23 |= c << (16 * (u - 2));
+    }
+    uint32_t tot01, tot23;
+    const uint32_t ex01 = wave_exclusive_scan(cnt01, tot01);
+    const uint32_t ex23 = wave_exclusive_scan(cnt23, tot23);
+    const uint32_t tot[kU] = {tot01 & 0xffffu, tot01 >> 16, tot23 & 0xffffu, tot23 >> 16};
+    const uint32_t ex[kU] = {ex01 & 0xffffu, ex01 >> 16, ex23 & 0xffffu, ex23 >> 16};
+    const uint32_t round = tot[0] + tot[1] + tot[2] + tot[3];
+    if (!wover && wcount + round <= (uint32_t)kBudget) {
+      uint32_t before = wcount;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t v = v0 + 64 * u + lane;
+        const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        uint32_t slot = wave * kBudget + before + ex[u];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          if (flags[u] & (1u << e)) {
+            uint32_t key;
+            if constexpr (BF16) key = order_bf16((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            else key = order_f32(w4[e]);
+            sh.cand_key[slot] = key;
+            sh.cand_idx[slot] = (int32_t)(v * EPV + e - off);
+            ++slot;
+          }
         }
+        before += tot[u];
       }
     } else {
       wover = true;
     }
-    wcount += total;
+    wcount += round;
   }
   if (lane == 0) {
     sh.cnt[wave] = wover ? 0 : wcount;
@@ -352,12 +409,20 @@ extern "C" csa_status csa_topk_select(const void* scores, int32_t score_fmt, int
   // there is no entry tensor here: the kernel clamps each row's candidates to ld
   const BatchDev b{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, nullptr, nullptr,
                    (int64_t)1 << 62, 0};
-  const size_t smem = sizeof(Shared);
-  if (score_fmt == CSA_BF16)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)batch->n_q), dim3(kThreads), smem, stream,
-                       scores, ld, b, m, k, idx);
+  // few rows (decode): 16 waves per row; many rows: 8, so several rows share a CU
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const bool wide = batch->n_q < 2 * (int64_t)cus;
+  const dim3 grid((unsigned)batch->n_q);
+  if (score_fmt == CSA_BF16 && wide)
+    hipLaunchKernelGGL((topk_kernel<true, 1024>), grid, dim3(1024), sizeof(Shared<1024>), stream, scores, ld, b, m, k, idx);
+  else if (score_fmt == CSA_BF16)
+    hipLaunchKernelGGL((topk_kernel<true, 512>), grid, dim3(512), sizeof(Shared<512>), stream, scores, ld, b, m, k, idx);
+  else if (wide)
+    hipLaunchKernelGGL((topk_kernel<false, 1024>), grid, dim3(1024), sizeof(Shared<1024>), stream, scores, ld, b, m, k, idx);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)batch->n_q), dim3(kThreads), smem,
-                       stream, scores, ld, b, m, k, idx);
+    hipLaunchKernelGGL((topk_kernel<false, 512>), grid, dim3(512), sizeof(Shared<512>), stream, scores, ld, b, m, k, idx);
   return check_launch("csa_topk_select");
 }
