@@ -10,8 +10,9 @@
 // one query in 4 consecutive registers of one lane and the ReLU + head sum
 // needs no cross-lane traffic.  The entry keys are the B operand and are read
 // straight from HBM in operand layout (each lane: 8 bf16 dims / 32 fp4 codes
-// of one entry), so the key stream is the only large traffic: the kernel is
-// HBM bound for decode and score-write bound for long prefill.
+// of one entry); for decode a wave keeps several key tiles in flight.  The
+// key stream is the only large read: the kernel is HBM bound for decode and
+// score-write bound for long prefill.
 //   fp32  : v_mfma_f32_32x32x2f32, 32 per tile
 //   bf16  : v_mfma_f32_32x32x16_bf16, 4 per tile
 //   MXFP4 : v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 operands, e8m0 block
@@ -44,119 +45,177 @@ struct IdxArgs {
   int64_t ld;
 };
 
-template <int FMT, bool SBF16>
+// Tiles whose keys one wave loads before computing any of them when the
+// kernel streams keys (one query per request, decode).  A prefill instead
+// keeps one tile in flight and relies on occupancy, its cost being the score
+// writes.
+template <int FMT> struct Tiling;
+template <> struct Tiling<CSA_F32> { static constexpr int TB = 1; };
+template <> struct Tiling<CSA_BF16> { static constexpr int TB = 2; };
+template <> struct Tiling<CSA_MXFP4> { static constexpr int TB = 8; };
+
+// Key operand of one tile for this lane (entry e0 + rl, its half of the dims).
+template <int FMT> struct KeyOp;
+template <> struct KeyOp<CSA_F32> { float v[kDI / 2]; };
+template <> struct KeyOp<CSA_BF16> { uint4 v[kDI / 16]; };
+template <> struct KeyOp<CSA_MXFP4> { uint4 v; int scale; };
+
+// Query operand of one 8-query group for this lane (query rl/4, head rl%4).
+template <int FMT> struct QueryOp;
+template <> struct QueryOp<CSA_F32> { float v[kDI / 2]; };
+template <> struct QueryOp<CSA_BF16> { bf16x8_t v[kDI / 16]; };
+template <> struct QueryOp<CSA_MXFP4> { i32x8_t v; int scale; };
+
+template <int FMT>
+__device__ __forceinline__ void load_key(const IdxArgs& a, int64_t krow, bool ok, int half, KeyOp<FMT>& k) {
+  if constexpr (FMT == CSA_F32) {
+    const float* p = static_cast<const float*>(a.ki) + krow * kDI + half;
+#pragma unroll
+    for (int c = 0; c < kDI / 2; ++c) k.v[c] = ok ? p[2 * c] : 0.0f;
+  } else if constexpr (FMT == CSA_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(a.ki) + krow * kDI + half * 8;
+#pragma unroll
+    for (int c = 0; c < kDI / 16; ++c)
+      k.v[c] = ok ? *reinterpret_cast<const uint4*>(p + 16 * c) : make_uint4(0, 0, 0, 0);
+  } else {
+    k.v = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.ki) + krow * 32 + half * 16)
+             : make_uint4(0, 0, 0, 0);
+    k.scale = ok ? a.ki_scale[krow * 2 + half] : 127;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_query(const IdxArgs& a, int64_t arow, bool ok, int half, QueryOp<FMT>& q) {
+  if constexpr (FMT == CSA_F32) {
+    const float* p = static_cast<const float*>(a.qi) + arow * kDI + half;
+#pragma unroll
+    for (int c = 0; c < kDI / 2; ++c) q.v[c] = ok ? p[2 * c] : 0.0f;
+  } else if constexpr (FMT == CSA_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(a.qi) + arow * kDI + half * 8;
+#pragma unroll
+    for (int c = 0; c < kDI / 16; ++c) {
+      const uint4 v = ok ? *reinterpret_cast<const uint4*>(p + 16 * c) : make_uint4(0, 0, 0, 0);
+      q.v[c] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  } else {
+    q.v = i32x8_t{};
+    q.scale = 127;
+    if (ok) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.qi) + arow * 32 + half * 16);
+      q.v[0] = v.x; q.v[1] = v.y; q.v[2] = v.z; q.v[3] = v.w;
+      q.scale = a.qi_scale[arow * 2 + half];
+    }
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x16_t tile_dots(const QueryOp<FMT>& q, const KeyOp<FMT>& k) {
+  f32x16_t acc = f32x16_t{};
+  if constexpr (FMT == CSA_F32) {
+#pragma unroll
+    for (int c = 0; c < kDI / 2; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q.v[c], k.v[c], acc, 0, 0, 0);
+  } else if constexpr (FMT == CSA_BF16) {
+#pragma unroll
+    for (int c = 0; c < kDI / 16; ++c)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q.v[c], __builtin_bit_cast(bf16x8_t, k.v[c]), acc, 0, 0, 0);
+  } else {
+    i32x8_t bk{};
+    bk[0] = k.v.x; bk[1] = k.v.y; bk[2] = k.v.z; bk[3] = k.v.w;
+    // cbsz = blgp = 4: both operands e2m1; opsel 0 picks scale byte 0
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.v, bk, acc, 4, 4, 0, q.scale, 0, k.scale);
+  }
+  return acc;
+}
+
+// Grid: x = chunks of kEntriesPerWG entries, y = groups of qpg queries
+// (qpg = 8 for a single request, else 1).
+template <int FMT, bool SBF16, bool STREAM>
 __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
+  constexpr int TB = STREAM ? Tiling<FMT>::TB : 1;
+  constexpr int QGMAX = 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int rl = lane & 31;
 
-  const int64_t q0 = (int64_t)blockIdx.y * a.qpg;
-  // this lane's A row: (query q0 + rl/4, head rl%4)
-  const int qa = rl >> 2, ha = rl & 3;
-  const bool a_live = qa < a.qpg && q0 + qa < a.n_q;
-  const int64_t qa_idx = q0 + qa;
-
-  const QueryMeta qm = query_meta(a.b, q0, a.m);
+  const int qg = QGMAX;                               // query groups of this workgroup
+  const int64_t qblock = (int64_t)blockIdx.y * a.qpg * qg;
+  const QueryMeta qm = query_meta(a.b, qblock, a.m);
   const int64_t kv_base = qm.kv_base;
-  // entries this group scans: up to the largest n_vis of its queries
-  int64_t q_hi = q0 + a.qpg - 1;
+  // entries this block scans: up to the largest n_vis of its queries
+  int64_t q_hi = qblock + a.qpg * qg - 1;
   if (q_hi >= a.n_q) q_hi = a.n_q - 1;
   const QueryMeta qm_hi = query_meta(a.b, q_hi, a.m);
   const int64_t n_scan = qm_hi.n_vis < a.ld ? qm_hi.n_vis : a.ld;   // never past a row
 
-  // per-lane output queries: q_local = 2*(i/4) + half, i/4 = 0..3
-  int64_t nvis_o[4];
-  float w_o[4][kHI];
-  bool live_o[4];
+  // A operands (queries) of every group, loaded once; this lane's A row is
+  // (query rl/4 of the group, head rl%4)
+  QueryOp<FMT> aq[QGMAX];
+  const int qa = rl >> 2, ha = rl & 3;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int ql = 2 * g + half;
-    const int64_t qq = q0 + ql;
-    live_o[g] = ql < a.qpg && qq < a.n_q;
-    nvis_o[g] = live_o[g] ? query_meta(a.b, qq, a.m).n_vis : 0;
-    if (nvis_o[g] > a.ld) nvis_o[g] = a.ld;
-#pragma unroll
-    for (int h = 0; h < kHI; ++h)
-      w_o[g][h] = (live_o[g] && a.head_w != nullptr) ? a.head_w[qq * kHI + h] : 1.0f;
+  for (int gi = 0; gi < QGMAX; ++gi) {
+    const int64_t qq = qblock + (int64_t)gi * a.qpg + qa;
+    load_query<FMT>(a, qq * kHI + ha, gi < qg && qa < a.qpg && qq < a.n_q, half, aq[gi]);
   }
 
-  // A operand (queries), loaded once
-  float aq_f32[kDI / 2];
-  bf16x8_t aq_bf16[kDI / 16];
-  i32x8_t aq_fp4{};
-  int aq_scale = 127;
-  const int64_t arow = qa_idx * kHI + ha;
-  if constexpr (FMT == CSA_F32) {
-    const float* p = static_cast<const float*>(a.qi) + arow * kDI + half;
+  // visible entries of this lane's output queries (query 2g + half of group
+  // gi); the queries of a block belong to one request, at consecutive positions
+  int nv[QGMAX][4];
 #pragma unroll
-    for (int c = 0; c < kDI / 2; ++c) aq_f32[c] = a_live ? p[2 * c] : 0.0f;
-  } else if constexpr (FMT == CSA_BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(a.qi) + arow * kDI + half * 8;
-#pragma unroll
-    for (int c = 0; c < kDI / 16; ++c) {
-      const uint4 v = a_live ? *reinterpret_cast<const uint4*>(p + 16 * c) : make_uint4(0, 0, 0, 0);
-      aq_bf16[c] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  } else {
-    if (a_live) {
-      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.qi) + arow * 32 + half * 16);
-      aq_fp4[0] = v.x; aq_fp4[1] = v.y; aq_fp4[2] = v.z; aq_fp4[3] = v.w;
-      aq_scale = a.qi_scale[arow * 2 + half];
-    }
-  }
-
-  const int64_t e_wg = (int64_t)blockIdx.x * kEntriesPerWG;
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t e0 = e_wg + (int64_t)(t * kWaves + wave) * 32;
-    if (e0 >= n_scan) break;
-    const int64_t e = e0 + rl;               // this lane's entry (B column)
-    const bool e_ok = e < n_scan;
-    const int64_t krow = kv_base + e;
-    f32x16_t acc = f32x16_t{};
-    if constexpr (FMT == CSA_F32) {
-      const float* p = static_cast<const float*>(a.ki) + krow * kDI + half;
-#pragma unroll
-      for (int c = 0; c < kDI / 2; ++c)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(aq_f32[c], e_ok ? p[2 * c] : 0.0f, acc, 0, 0, 0);
-    } else if constexpr (FMT == CSA_BF16) {
-      const uint16_t* p = static_cast<const uint16_t*>(a.ki) + krow * kDI + half * 8;
-      uint4 kv[kDI / 16];
-#pragma unroll
-      for (int c = 0; c < kDI / 16; ++c)
-        kv[c] = e_ok ? *reinterpret_cast<const uint4*>(p + 16 * c) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < kDI / 16; ++c)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq_bf16[c], __builtin_bit_cast(bf16x8_t, kv[c]),
-                                                       acc, 0, 0, 0);
-    } else {
-      i32x8_t bk{};
-      int bscale = 127;
-      if (e_ok) {
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.ki) + krow * 32 + half * 16);
-        bk[0] = v.x; bk[1] = v.y; bk[2] = v.z; bk[3] = v.w;
-        bscale = a.ki_scale[krow * 2 + half];
-      }
-      // cbsz = blgp = 4: both operands e2m1; opsel 0 picks scale byte 0
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq_fp4, bk, acc, 4, 4, 0, aq_scale, 0,
-                                                            bscale);
-    }
-    // ReLU + weighted head sum, then store
+  for (int gi = 0; gi < QGMAX; ++gi)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      float s = 0.0f;
-#pragma unroll
-      for (int h = 0; h < kHI; ++h) {
-        float v = acc[4 * g + h];
-        if (a.relu) v = fmaxf(v, 0.0f);
-        s = fmaf(w_o[g][h], v, s);
+      const int ql = 2 * g + half;
+      const int64_t qq = qblock + (int64_t)gi * a.qpg + ql;
+      int64_t v = 0;
+      if (gi < qg && ql < a.qpg && qq < a.n_q) {
+        v = (qm.t + (qq - qblock) + 1) / a.m;
+        if (v > qm.kv_len) v = qm.kv_len;
+        if (v > a.ld) v = a.ld;
       }
-      if (live_o[g] && e < nvis_o[g]) {
-        const int64_t off = (q0 + 2 * g + half) * a.ld + e;
-        if constexpr (SBF16)
-          static_cast<uint16_t*>(a.scores)[off] = (uint16_t)pack_bf16x2_fast(s, 0.0f);
-        else
-          static_cast<float*>(a.scores)[off] = s;
+      nv[gi][g] = (int)v;
+    }
+
+  const int64_t e_wg = (int64_t)blockIdx.x * kEntriesPerWG;
+  for (int t0 = 0; t0 < kTilesPerWave; t0 += TB) {
+    if (e_wg + (int64_t)(t0 * kWaves + wave) * 32 >= n_scan) break;
+    // keys of TB tiles in flight together
+    KeyOp<FMT> kt[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t e = e_wg + (int64_t)((t0 + tb) * kWaves + wave) * 32 + rl;
+      load_key<FMT>(a, kv_base + e, e < n_scan, half, kt[tb]);
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t e0 = e_wg + (int64_t)((t0 + tb) * kWaves + wave) * 32;
+      if (e0 >= n_scan) break;
+      const int64_t e = e0 + rl;             // this lane's entry (B column)
+#pragma unroll
+      for (int gi = 0; gi < QGMAX; ++gi) {
+        if (gi >= qg) break;
+        const f32x16_t acc = tile_dots<FMT>(aq[gi], kt[tb]);
+        // ReLU + weighted head sum, then store; output query of register
+        // block g is 2g + half of the group
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ql = 2 * g + half;
+          const int64_t qq = qblock + (int64_t)gi * a.qpg + ql;
+          if (e >= nv[gi][g]) continue;          // also covers queries past the block
+          float s = 0.0f;
+#pragma unroll
+          for (int h = 0; h < kHI; ++h) {
+            float v = acc[4 * g + h];
+            if (a.relu) v = fmaxf(v, 0.0f);
+            const float w = a.head_w != nullptr ? a.head_w[qq * kHI + h] : 1.0f;
+            s = fmaf(w, v, s);
+          }
+          const int64_t off = qq * a.ld + e;
+          if constexpr (SBF16)
+            static_cast<uint16_t*>(a.scores)[off] = (uint16_t)pack_bf16x2_fast(s, 0.0f);
+          else
+            static_cast<float*>(a.scores)[off] = s;
+        }
       }
     }
   }
@@ -164,10 +223,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
 
 template <int FMT>
 void launch(const IdxArgs& a, bool sbf16, dim3 grid, hipStream_t s) {
-  if (sbf16)
-    hipLaunchKernelGGL((indexer_kernel<FMT, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((indexer_kernel<FMT, false>), grid, dim3(256), 0, s, a);
+  if (a.qpg == 8 && sbf16) hipLaunchKernelGGL((indexer_kernel<FMT, true, false>), grid, dim3(256), 0, s, a);
+  else if (a.qpg == 8) hipLaunchKernelGGL((indexer_kernel<FMT, false, false>), grid, dim3(256), 0, s, a);
+  else if (sbf16) hipLaunchKernelGGL((indexer_kernel<FMT, true, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((indexer_kernel<FMT, false, true>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
