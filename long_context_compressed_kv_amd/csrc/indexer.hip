@@ -18,6 +18,8 @@
 //   MXFP4 : v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 operands, e8m0 block
 //           scales per lane), 1 per tile - the products and block sums are
 //           exact, so this equals the lossless FP4 -> FP8 route.
+#include <type_traits>
+
 #include "common.h"
 
 using namespace csa;
@@ -43,6 +45,7 @@ struct IdxArgs {
   int64_t n_q;
   void* scores;
   int64_t ld;
+  int vec_out;      // score rows start 16-byte aligned: stage and write vectors
 };
 
 // Tiles whose keys one wave loads before computing any of them when the
@@ -128,94 +131,120 @@ __device__ __forceinline__ f32x16_t tile_dots(const QueryOp<FMT>& q, const KeyOp
 }
 
 // Grid: x = chunks of kEntriesPerWG entries, y = groups of qpg queries
-// (qpg = 8 for a single request, else 1).
+// (qpg = 8 for a single request, else 1); neighbouring workgroups stream
+// neighbouring key chunks.  Wave w scores the contiguous
+// entries [w*256, w*256 + 256) of its chunk, one 32-entry tile at a time.
+// A prefill (STREAM false) stages the chunk's 8 x 1024 scores in LDS and
+// writes every query row out in 16-byte vectors (when rows are 16-byte
+// aligned); decode stores each score directly.
 template <int FMT, bool SBF16, bool STREAM>
 __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
   constexpr int TB = STREAM ? Tiling<FMT>::TB : 1;
-  constexpr int QGMAX = 1;
+  using score_t = typename std::conditional<SBF16, uint16_t, float>::type;
+  constexpr int VEC = 16 / (int)sizeof(score_t);      // scores per 16-byte vector
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int rl = lane & 31;
 
-  const int qg = QGMAX;                               // query groups of this workgroup
-  const int64_t qblock = (int64_t)blockIdx.y * a.qpg * qg;
+  const int64_t qblock = (int64_t)blockIdx.y * a.qpg;
   const QueryMeta qm = query_meta(a.b, qblock, a.m);
   const int64_t kv_base = qm.kv_base;
-  // entries this block scans: up to the largest n_vis of its queries
-  int64_t q_hi = qblock + a.qpg * qg - 1;
+  // entries this group scans: up to the largest n_vis of its queries
+  int64_t q_hi = qblock + a.qpg - 1;
   if (q_hi >= a.n_q) q_hi = a.n_q - 1;
   const QueryMeta qm_hi = query_meta(a.b, q_hi, a.m);
   const int64_t n_scan = qm_hi.n_vis < a.ld ? qm_hi.n_vis : a.ld;   // never past a row
 
-  // A operands (queries) of every group, loaded once; this lane's A row is
-  // (query rl/4 of the group, head rl%4)
-  QueryOp<FMT> aq[QGMAX];
+  // visible entries of query ql of the group (one request, consecutive
+  // positions); 0 past the batch
+  auto nvis_of = [&](int ql) -> int {
+    const int64_t qq = qblock + ql;
+    if (ql >= a.qpg || qq >= a.n_q) return 0;
+    int64_t v = (qm.t + ql + 1) / a.m;
+    if (v > qm.kv_len) v = qm.kv_len;
+    if (v > a.ld) v = a.ld;
+    return (int)v;
+  };
+
+  // A operand (queries): this lane's row is (query rl/4, head rl%4)
+  QueryOp<FMT> aq;
   const int qa = rl >> 2, ha = rl & 3;
+  load_query<FMT>(a, (qblock + qa) * kHI + ha, qa < a.qpg && qblock + qa < a.n_q, half, aq);
+
+  // this lane's output queries: 2g + half for register block g
+  int nv[4];
+  float hw[4][kHI];
 #pragma unroll
-  for (int gi = 0; gi < QGMAX; ++gi) {
-    const int64_t qq = qblock + (int64_t)gi * a.qpg + qa;
-    load_query<FMT>(a, qq * kHI + ha, gi < qg && qa < a.qpg && qq < a.n_q, half, aq[gi]);
+  for (int g = 0; g < 4; ++g) {
+    const int ql = 2 * g + half;
+    nv[g] = nvis_of(ql);
+#pragma unroll
+    for (int h = 0; h < kHI; ++h)
+      hw[g][h] = (a.head_w != nullptr && nv[g] > 0) ? a.head_w[(qblock + ql) * kHI + h] : 1.0f;
   }
 
-  // visible entries of this lane's output queries (query 2g + half of group
-  // gi); the queries of a block belong to one request, at consecutive positions
-  int nv[QGMAX][4];
-#pragma unroll
-  for (int gi = 0; gi < QGMAX; ++gi)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ql = 2 * g + half;
-      const int64_t qq = qblock + (int64_t)gi * a.qpg + ql;
-      int64_t v = 0;
-      if (gi < qg && ql < a.qpg && qq < a.n_q) {
-        v = (qm.t + (qq - qblock) + 1) / a.m;
-        if (v > qm.kv_len) v = qm.kv_len;
-        if (v > a.ld) v = a.ld;
-      }
-      nv[gi][g] = (int)v;
-    }
-
   const int64_t e_wg = (int64_t)blockIdx.x * kEntriesPerWG;
+  const int e_wave = wave * (kTilesPerWave * 32);      // first entry of this wave in the chunk
+  const bool staged = !STREAM && a.vec_out;
+  score_t* stage = nullptr;
+  if constexpr (!STREAM) {
+    __shared__ __align__(16) score_t sc[8 * kEntriesPerWG];
+    stage = sc;
+  }
   for (int t0 = 0; t0 < kTilesPerWave; t0 += TB) {
-    if (e_wg + (int64_t)(t0 * kWaves + wave) * 32 >= n_scan) break;
+    if (e_wg + e_wave + t0 * 32 >= n_scan) break;
     // keys of TB tiles in flight together
     KeyOp<FMT> kt[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int64_t e = e_wg + (int64_t)((t0 + tb) * kWaves + wave) * 32 + rl;
+      const int64_t e = e_wg + e_wave + (t0 + tb) * 32 + rl;
       load_key<FMT>(a, kv_base + e, e < n_scan, half, kt[tb]);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int64_t e0 = e_wg + (int64_t)((t0 + tb) * kWaves + wave) * 32;
-      if (e0 >= n_scan) break;
-      const int64_t e = e0 + rl;             // this lane's entry (B column)
+      const int el = e_wave + (t0 + tb) * 32 + rl;     // entry within the chunk
+      const int64_t e = e_wg + el;                      // this lane's entry (B column)
+      if (e - rl >= n_scan) break;
+      const f32x16_t acc = tile_dots<FMT>(aq, kt[tb]);
+      // ReLU + weighted head sum; register block g holds the 4 heads of
+      // query 2g + half
 #pragma unroll
-      for (int gi = 0; gi < QGMAX; ++gi) {
-        if (gi >= qg) break;
-        const f32x16_t acc = tile_dots<FMT>(aq[gi], kt[tb]);
-        // ReLU + weighted head sum, then store; output query of register
-        // block g is 2g + half of the group
+      for (int g = 0; g < 4; ++g) {
+        if (e >= nv[g]) continue;                       // also covers queries past the batch
+        float s = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = 2 * g + half;
-          const int64_t qq = qblock + (int64_t)gi * a.qpg + ql;
-          if (e >= nv[gi][g]) continue;          // also covers queries past the block
-          float s = 0.0f;
-#pragma unroll
-          for (int h = 0; h < kHI; ++h) {
-            float v = acc[4 * g + h];
-            if (a.relu) v = fmaxf(v, 0.0f);
-            const float w = a.head_w != nullptr ? a.head_w[qq * kHI + h] : 1.0f;
-            s = fmaf(w, v, s);
-          }
-          const int64_t off = qq * a.ld + e;
-          if constexpr (SBF16)
-            static_cast<uint16_t*>(a.scores)[off] = (uint16_t)pack_bf16x2_fast(s, 0.0f);
-          else
-            static_cast<float*>(a.scores)[off] = s;
+        for (int h = 0; h < kHI; ++h) {
+          float v = acc[4 * g + h];
+          if (a.relu) v = fmaxf(v, 0.0f);
+          s = fmaf(hw[g][h], v, s);
         }
+        score_t o;
+        if constexpr (SBF16) o = (uint16_t)pack_bf16x2_fast(s, 0.0f);
+        else o = s;
+        if (staged) stage[(2 * g + half) * kEntriesPerWG + el] = o;
+        else static_cast<score_t*>(a.scores)[(qblock + 2 * g + half) * a.ld + e] = o;
+      }
+    }
+  }
+  if constexpr (!STREAM) {
+    if (!staged) return;
+    __syncthreads();
+    // every query row of the chunk in 16-byte vectors; a vector that crosses
+    // the query's visible end is written element by element
+    constexpr int VPR = kEntriesPerWG / VEC;          // vectors per query row
+    for (int i = threadIdx.x; i < 8 * VPR; i += 256) {
+      const int ql = i / VPR;
+      const int el = (i - ql * VPR) * VEC;
+      const int nvq = nvis_of(ql);
+      const int64_t e = e_wg + el;
+      if (e >= nvq) continue;
+      score_t* dst = static_cast<score_t*>(a.scores) + (qblock + ql) * a.ld + e;
+      const score_t* src = stage + ql * kEntriesPerWG + el;
+      if (e + VEC <= nvq) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int j = 0; j < VEC && e + j < nvq; ++j) dst[j] = src[j];
       }
     }
   }
@@ -273,6 +302,8 @@ extern "C" csa_status csa_indexer_score(const csa_tensor* qi, int32_t n_heads,
   a.scores = scores;
   a.ld = ld;
   const int64_t gy = (batch->n_q + a.qpg - 1) / a.qpg;
+  const int esz = score_fmt == CSA_BF16 ? 2 : 4;
+  a.vec_out = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && ((ld * esz) % 16 == 0) ? 1 : 0;
   const int64_t gx = (batch->max_kv + kEntriesPerWG - 1) / kEntriesPerWG;
   if (gy > 65535 || gx > 0x7fffffff)
     return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_score: problem too large for one launch");

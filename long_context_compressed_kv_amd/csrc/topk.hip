@@ -8,7 +8,8 @@
 // broken by the lower index, written in ascending index order.  One
 // workgroup (8 or 16 waves: many rows or few) per query row:
 //   1. threshold estimate: rows longer than half the LDS candidate capacity take
-//      a strided sample of 4096 keys and use its order statistic of rank
+//      a sample of 4096 keys (evenly spread runs of 8 or 4 consecutive keys,
+//      one 16-byte load each) and use its order statistic of rank
 //      ~2k*4096/n (an exact radix select over the sample in LDS), so about
 //      2k keys of the row lie at or above it;
 //   2. one streaming pass over the row (waves on contiguous segments, four
@@ -239,14 +240,29 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ score
   // wave's segment then holds at most ~n/16 + 8 keys, inside its budget)
   uint32_t tau_hat = 0;
   if (n > kCap / 2) {
-    uint32_t smp[kSample / kThreads];
+    // kSample keys in runs of SR consecutive ones (one 16-byte load each when
+    // aligned), the runs spread evenly over the row: far fewer cache lines
+    // than single scattered keys
+    constexpr int SR = 16 / ESZ;
+    constexpr int NRUN = kSample / SR;
+    for (int r0 = tid; r0 < NRUN; r0 += kThreads) {
+      const int64_t j0 = (int64_t)r0 * (n - SR) / (NRUN - 1);   // run start, j0 + SR <= n
+      uint32_t ks[SR];
+      if (((reinterpret_cast<uintptr_t>(row) + j0 * ESZ) & 15u) == 0) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + j0 * ESZ);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int s = 0; s < kSample / kThreads; ++s) {
-      const int i = tid + s * kThreads;
-      smp[s] = key_at<BF16>(row, (int64_t)i * n / kSample);
+        for (int e = 0; e < SR; ++e) {
+          if constexpr (BF16) ks[e] = order_bf16((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          else ks[e] = order_f32(w4[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < SR; ++e) ks[e] = key_at<BF16>(row, j0 + e);
+      }
+#pragma unroll
+      for (int e = 0; e < SR; ++e) sh.cand_key[r0 * SR + e] = ks[e];
     }
-#pragma unroll
-    for (int s = 0; s < kSample / kThreads; ++s) sh.cand_key[tid + s * kThreads] = smp[s];
     __syncthreads();
     int64_t r = (2 * (int64_t)k * kSample + n - 1) / n + 8;
     if (r > kSample) r = kSample;
