@@ -305,11 +305,19 @@ __device__ __forceinline__ int swz_off(int r, int j) {
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read through a 32-bit LDS address.
+__device__ __forceinline__ uint4 lds_read_b128(const lds_u8* p) {
+  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // 64-bit transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i receives element i%4 of the four 16-bit values addressed by
 // lanes i/4, i/4+4, i/4+8 and i/4+12 of its group, in that order.
-__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+__device__ __forceinline__ uint2 lds_read_tr16(const lds_u8* p) {
   const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
   return __builtin_bit_cast(uint2, v);
 }
@@ -358,11 +366,11 @@ __device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uin
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_slot(unsigned char* kb, int key, int d, bool fp8, uint4 x0, uint4 x1) {
+// A slot's two 16-byte chunks land at lds[0] and lds[1] (swizzled positions).
+__device__ __forceinline__ void store_slot(lds_u8* const* lds, bool fp8, uint4 x0, uint4 x1) {
   if (fp8) fp8x16_to_bf16(x0, e8m0_to_f32(x1.x), x0, x1);
-  *reinterpret_cast<uint4*>(kb + swz_off<D>(key, d >> 3)) = x0;
-  *reinterpret_cast<uint4*>(kb + swz_off<D>(key, (d >> 3) + 1)) = x1;
+  *(__attribute__((address_space(3))) u32x4_t*)(lds[0]) = u32x4_t{x0.x, x0.y, x0.z, x0.w};
+  *(__attribute__((address_space(3))) u32x4_t*)(lds[1]) = u32x4_t{x1.x, x1.y, x1.z, x1.w};
 }
 
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM, bool PREF>
@@ -500,15 +508,32 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       fp8 = load_slot<D, KVF>(a, row, (u - key * UPR) * 16, v[0], v[1]);
     }
   };
-  auto store_unit = [&](int u, const stage_t* v, bool fp8) {
+  // LDS destinations of a bf16 unit (tile-invariant for a given unit)
+  auto unit_dst = [&](int u, lds_u8** dst) {
     const int key = u / UPR;
+    const int j = (u - key * UPR) * 2;
+    dst[0] = (lds_u8*)kb + swz_off<D>(key, j);
+    dst[1] = (lds_u8*)kb + swz_off<D>(key, j + 1);
+  };
+  auto store_unit = [&](int u, const stage_t* v, bool fp8, lds_u8* const* dst) {
     if constexpr (F32C) {
+      const int key = u / UPR;
       const int d = (u - key * UPR) * 4;
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(kb) + key * KSTR + d) = v[0];
     } else {
-      store_slot<D>(kb, key, (u - key * UPR) * 16, fp8, v[0], v[1]);
+      store_slot(dst, fp8, v[0], v[1]);
     }
   };
+  // prefetching: each thread's units, and so their LDS destinations, are
+  // the same every tile
+  lds_u8* sdst[UPT][2];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    sdst[i][0] = sdst[i][1] = nullptr;
+    if constexpr (!F32C) {
+      if (tid + i * nthreads < UNITS) unit_dst(tid + i * nthreads, sdst[i]);
+    }
+  }
 
   auto load_tile = [&](int buf) {
 #pragma unroll
@@ -521,7 +546,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * nthreads;
-      if (u < UNITS) store_unit(u, stg[i], sfp8[i]);
+      if (u < UNITS) store_unit(u, stg[i], sfp8[i], sdst[i]);
     }
   };
   // without prefetch: every thread stages units tid, tid+nthreads, ..., in
@@ -539,7 +564,11 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         const int u = u0 + tid + i * nthreads;
-        if (u < UNITS) store_unit(u, v[i], fp8[i]);
+        if (u < UNITS) {
+          lds_u8* dst[2] = {nullptr, nullptr};
+          if constexpr (!F32C) unit_dst(u, dst);
+          store_unit(u, v[i], fp8[i], dst);
+        }
       }
     }
   };
@@ -551,20 +580,26 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   // 4*db' + tc (db' = d0/32 + db), swizzled to 16*(db'/4) + 4*((db'%4) ^ (tk%4))
   // + (tc ^ ((2r + tk/4) % 4)), plus the byte `sub` within it; the row terms
   // 16c and 8r and the term 16*(db'/4) are immediates.
-  int qk_off[8], tr_base[2], tr_x[4];
+  // The tables hold 32-bit LDS addresses with the tile's base included, so a
+  // read is one instruction with an immediate offset (the base of dynamic LDS
+  // is a link-time symbol the compiler cannot fold into an offset).
+  lds_u8* qk_ptr[8];
+  lds_u8* tr_ptr[2][4];
   {
+    lds_u8* kbl = (lds_u8*)(kb);
     const int f = 4 * (ql & 3) + ((ql >> 2) & 3);
 #pragma unroll
     for (int c8 = 0; c8 < 8; ++c8)
-      qk_off[c8] = ql * (D * 2) + 32 * (c8 ^ (f >> 1)) + 16 * (half ^ (f & 1)) + (d0 >> 7) * 256;
+      qk_ptr[c8] = kbl + ql * (D * 2) + 32 * (c8 ^ (f >> 1)) + 16 * (half ^ (f & 1)) + (d0 >> 7) * 256;
     const int tg = lane >> 4, ts = lane & 15;
     const int tk = 4 * (tg >> 1) + (ts >> 2);
     const int tc = 2 * (tg & 1) + ((ts & 3) >> 1);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
-      tr_base[r] = tk * (D * 2) + 16 * (tc ^ ((2 * r + (tk >> 2)) & 3)) + (ts & 1) * 8 + (d0 >> 7) * 256;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) tr_x[x] = 64 * (x ^ (tk & 3));
+      for (int x = 0; x < 4; ++x)
+        tr_ptr[r][x] = kbl + tk * (D * 2) + 16 * (tc ^ ((2 * r + (tk >> 2)) & 3)) + (ts & 1) * 8 +
+                       (d0 >> 7) * 256 + 64 * (x ^ (tk & 3));
   }
 
   // The query registers are settled before the key loop: otherwise, inside
@@ -597,10 +632,9 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       // keep the few per-lane offsets opaque to loop-invariant hoisting, which
       // would otherwise hold every derived address in a register of its own
 #pragma unroll
-      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qk_off[i]));
-      asm volatile("" : "+v"(tr_base[0]), "+v"(tr_base[1]));
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qk_ptr[i]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(tr_x[i]));
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(tr_ptr[i >> 2][i & 3]));
     }
     f32x16_t acc_s = f32x16_t{};
     if constexpr (F32C) {
@@ -611,7 +645,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
-        const uint4 k8 = *reinterpret_cast<const uint4*>(kb + qk_off[c & 7] + (c >> 3) * 256);
+        const uint4 k8 = lds_read_b128(qk_ptr[c & 7] + (c >> 3) * 256);
         acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k8), qreg[c], acc_s,
                                                         0, 0, 0);
       }
@@ -701,8 +735,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const unsigned char* v0 = kb + tr_base[0] + tr_x[db & 3] + (db >> 2) * 256;
-        const unsigned char* v1 = kb + tr_base[1] + tr_x[db & 3] + (db >> 2) * 256;
+        const lds_u8* v0 = tr_ptr[0][db & 3] + (db >> 2) * 256;
+        const lds_u8* v1 = tr_ptr[1][db & 3] + (db >> 2) * 256;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const uint2 x0 = lds_read_tr16(v0 + 16 * c * (D * 2));
