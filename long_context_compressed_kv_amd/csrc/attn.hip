@@ -11,16 +11,17 @@
 // LDS as bf16 rows (FP8_MIXED rows dequantised on the way, exactly: the
 // scales are powers of two); since key = value, the same tile is the operand
 // of both products, read row-wise for the logits and through transposing LDS
-// reads for the values.  The global loads of tile t+1 are in flight while tile
-// t is computed (D = 128), and the source rows of a tile are resolved once per
-// key, one tile ahead, together with one 32-bit mask per query token of the
-// keys that token may see (causal entries, its own selection, its window), so
-// masking a logit is one bit test.
+// reads for the values.  The source rows of a tile are resolved once per key,
+// ahead of the tile, together with one 32-bit mask per query token of the keys
+// that token may see (causal entries, its own selection, its window), so
+// masking a logit is one bit test.  With enough waves the global loads of a
+// later tile are in flight while a tile is computed: D = 128 keeps two key
+// buffers in LDS (one barrier per tile), D = 512 decode one.
 //
 // Split-K (decode).  With split_keys > 0 a query's key list is cut into
-// chunks of split_keys keys handled by separate workgroups (grid y); each
-// writes a normalised partial output and its log-sum-exp to the workspace,
-// and a combine pass merges them (the same merge as csa_swa_merge).
+// chunks handled by a persistent grid of workgroups; each writes a normalised
+// partial output and its log-sum-exp to the workspace, and a combine pass
+// merges them (the same merge as csa_swa_merge).
 //
 // Per tile and wave (bf16):
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, keys on M, queries on N;
@@ -47,6 +48,7 @@ constexpr int KT = 32;           // keys per tile
 constexpr int kTokMax = 16;      // query tokens per workgroup (128 rows / 8 heads)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kStale = 8.0f;   // log2 headroom before the running max moves
+constexpr int kMetaSlots = 8;    // ring of per-tile source rows and key masks
 constexpr int kMaxSplits = 64;
 
 struct AttnArgs {
@@ -366,15 +368,16 @@ __device__ __forceinline__ bool load_slot(const AttnArgs& a, int row, int d, uin
   }
 }
 
-// A slot's two 16-byte chunks land at lds[0] and lds[1] (swizzled positions).
-__device__ __forceinline__ void store_slot(lds_u8* const* lds, bool fp8, uint4 x0, uint4 x1) {
+// A slot's two 16-byte chunks land at lds[0] + ofs and lds[1] + ofs (swizzled
+// positions in the key buffer at byte offset ofs).
+__device__ __forceinline__ void store_slot(lds_u8* const* lds, int ofs, bool fp8, uint4 x0, uint4 x1) {
   if (fp8) fp8x16_to_bf16(x0, e8m0_to_f32(x1.x), x0, x1);
-  *(__attribute__((address_space(3))) u32x4_t*)(lds[0]) = u32x4_t{x0.x, x0.y, x0.z, x0.w};
-  *(__attribute__((address_space(3))) u32x4_t*)(lds[1]) = u32x4_t{x1.x, x1.y, x1.z, x1.w};
+  *(__attribute__((address_space(3))) u32x4_t*)(lds[0] + ofs) = u32x4_t{x0.x, x0.y, x0.z, x0.w};
+  *(__attribute__((address_space(3))) u32x4_t*)(lds[1] + ofs) = u32x4_t{x1.x, x1.y, x1.z, x1.w};
 }
 
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM, bool PREF>
-__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_body(const AttnArgs& a) {
   constexpr int DW = D / DSPLIT;                 // dims per wave
   constexpr int KSTR = D + 4;                    // fp32 K-layout row stride (elements)
   // staging units: bf16 = one key x 16 dims, fp32 = one key x 4 dims
@@ -385,12 +388,16 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   constexpr int UPT = PREF ? (UNITS + PMIN - 1) / PMIN : 1;
   constexpr size_t KBYTES = F32C ? (size_t)KT * KSTR * 4 : (size_t)KT * D * 2;
 
+  // double-buffered key tiles (one wave per 32 rows, at least four waves)
+  constexpr bool DBUF = PREF && DSPLIT == 1;
+  constexpr int NKB = DBUF ? 2 : 1;
+
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* kb = smem;                                        // key tile
-  int* mrow = reinterpret_cast<int*>(smem + KBYTES);               // [2][KT] source rows
-  uint32_t* mword = reinterpret_cast<uint32_t*>(mrow + 2 * KT);    // [2][kTokMax] key bits per token
-  int* mfull = reinterpret_cast<int*>(mword + 2 * kTokMax);        // [2], padded to 4 ints
-  float* sx = reinterpret_cast<float*>(mfull + 4); // [nrb][DSPLIT][4][64] float4 partial logits
+  unsigned char* kb = smem;                                        // [NKB] key tiles
+  int* mrow = reinterpret_cast<int*>(smem + NKB * KBYTES);         // [kMetaSlots][KT] source rows
+  uint32_t* mword = reinterpret_cast<uint32_t*>(mrow + kMetaSlots * KT);  // [kMetaSlots][kTokMax] key bits
+  int* mfull = reinterpret_cast<int*>(mword + kMetaSlots * kTokMax);      // [kMetaSlots]
+  float* sx = reinterpret_cast<float*>(mfull + kMetaSlots); // [nrb][DSPLIT][4][64] float4 partial logits
 
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -460,24 +467,26 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   // wave 0 resolves a tile's source rows and, per query token, a 32-bit mask
   // of the keys valid for it (bit = key in tile)
   const int ntok = (int)(g.q_last - g.q_first + 1);
-  auto meta_tile = [&](int kbase, int buf) {
-    if (tid < 64) {
+  // (done by wave `by`)
+  auto meta_tile_by = [&](int kbase, int buf, int by) {
+    if (wave == by) {
       int row = -1;
       int64_t lo = 1, hi = 0;
-      if (tid < KT) key_meta<SPARSE>(a, g, kbase + tid, row, lo, hi);
+      if (lane < KT) key_meta<SPARSE>(a, g, kbase + lane, row, lo, hi);
       // a key without a source (past the range, or an unused selection slot)
       // reads a row that always exists and stays masked
       if (!F32C && row == -1) row = a.kv != nullptr ? 0 : -2;
-      if (tid < KT) mrow[buf * KT + tid] = row;
+      if (lane < KT) mrow[buf * KT + lane] = row;
       bool full = true;
       for (int t = 0; t < a.tok; ++t) {
         const uint32_t w = (uint32_t)__ballot(t < ntok && t >= lo && t < hi);
-        if (tid == 0) mword[buf * kTokMax + t] = w;
+        if (lane == 0) mword[buf * kTokMax + t] = w;
         full = full && (t >= ntok || w == 0xffffffffu);
       }
-      if (tid == 0) mfull[buf] = full ? 1 : 0;
+      if (lane == 0) mfull[buf] = full ? 1 : 0;
     }
   };
+  auto meta_tile = [&](int kbase, int buf) { meta_tile_by(kbase, buf, 0); };
 
   // ---- staging: fp32 units are float4 of one key; bf16 units are 16 dims
   // of one key (32 bytes once in LDS), consecutive threads along a key row
@@ -492,9 +501,9 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     for (int j = 0; j < SPU; ++j) stg[i][j] = stage_t{};
   }
 
-  auto load_unit = [&](int buf, int u, stage_t* v, bool& fp8) {
+  // loads one staging unit whose source row is `row`
+  auto load_unit_row = [&](int row, int u, stage_t* v, bool& fp8) {
     const int key = u / UPR;
-    const int row = mrow[buf * KT + key];
     if constexpr (F32C) {
       const int d = (u - key * UPR) * 4;
       fp8 = false;
@@ -508,6 +517,9 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       fp8 = load_slot<D, KVF>(a, row, (u - key * UPR) * 16, v[0], v[1]);
     }
   };
+  auto load_unit = [&](int buf, int u, stage_t* v, bool& fp8) {
+    load_unit_row(mrow[buf * KT + u / UPR], u, v, fp8);
+  };
   // LDS destinations of a bf16 unit (tile-invariant for a given unit)
   auto unit_dst = [&](int u, lds_u8** dst) {
     const int key = u / UPR;
@@ -515,13 +527,13 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     dst[0] = (lds_u8*)kb + swz_off<D>(key, j);
     dst[1] = (lds_u8*)kb + swz_off<D>(key, j + 1);
   };
-  auto store_unit = [&](int u, const stage_t* v, bool fp8, lds_u8* const* dst) {
+  auto store_unit = [&](int u, const stage_t* v, bool fp8, lds_u8* const* dst, int kofs) {
     if constexpr (F32C) {
       const int key = u / UPR;
       const int d = (u - key * UPR) * 4;
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(kb) + key * KSTR + d) = v[0];
     } else {
-      store_slot(dst, fp8, v[0], v[1]);
+      store_slot(dst, kofs, fp8, v[0], v[1]);
     }
   };
   // prefetching: each thread's units, and so their LDS destinations, are
@@ -542,11 +554,27 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       if (u < UNITS) load_unit(buf, u, stg[i], sfp8[i]);
     }
   };
-  auto store_tile = [&]() {
+  // the same in two parts: source rows of this thread's units (LDS), then
+  // the loads themselves
+  auto tile_rows = [&](int buf, int* rows) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * nthreads;
-      if (u < UNITS) store_unit(u, stg[i], sfp8[i], sdst[i]);
+      rows[i] = u < UNITS ? mrow[buf * KT + u / UPR] : -1;
+    }
+  };
+  auto load_tile_rows = [&](const int* rows) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * nthreads;
+      if (u < UNITS) load_unit_row(rows[i], u, stg[i], sfp8[i]);
+    }
+  };
+  auto store_tile = [&](int kofs) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * nthreads;
+      if (u < UNITS) store_unit(u, stg[i], sfp8[i], sdst[i], kofs);
     }
   };
   // without prefetch: every thread stages units tid, tid+nthreads, ..., in
@@ -567,7 +595,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         if (u < UNITS) {
           lds_u8* dst[2] = {nullptr, nullptr};
           if constexpr (!F32C) unit_dst(u, dst);
-          store_unit(u, v[i], fp8[i], dst);
+          store_unit(u, v[i], fp8[i], dst, 0);
         }
       }
     }
@@ -608,34 +636,37 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < QC; ++c) asm volatile("" :: "v"(qreg[c]));
 
-  // ---- key loop: prologue resolves (and, prefetching, loads) the first tile
-  const int ntiles = (g.key_hi - g.key_lo + KT - 1) / KT;
-  if (ntiles > 0) {
-    meta_tile(g.key_lo, 0);
-    lds_barrier();
-    if constexpr (PREF) load_tile(0);
-  }
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const int kbase = g.key_lo + tile * KT;
-    lds_barrier();                 // previous tile fully consumed
-    if constexpr (PREF) store_tile();
-    else stage_direct(buf);
-    if (tile + 1 < ntiles) meta_tile(kbase + KT, buf ^ 1);
-    lds_barrier();                 // tile in LDS, next tile's sources resolved
-    if constexpr (PREF) {
-      if (tile + 1 < ntiles) load_tile(buf ^ 1);   // in flight during the compute below
-    }
-
-    // ---- logits S^T = K Q^T (partial over this wave's dims)
+  // ---- logits of one tile, S^T = K Q^T (partial over this wave's dims and
+  // summed over the waves of the row block); kofs = byte offset of the key
+  // buffer
+  // Keep the few per-lane offsets opaque to loop-invariant hoisting, which
+  // would otherwise hold every derived address in a register of its own.
+  auto launder_qk = [&]() {
     if constexpr (!F32C) {
-      // keep the few per-lane offsets opaque to loop-invariant hoisting, which
-      // would otherwise hold every derived address in a register of its own
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qk_ptr[i]));
+    }
+  };
+  auto launder_tr = [&]() {
+    if constexpr (!F32C) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(tr_ptr[i >> 2][i & 3]));
     }
+  };
+  // bf16 operands of the two products: K chunk of logit instruction c, and
+  // the V^T operand of value instruction c of dim block db
+  auto read_k = [&](int c, int kofs) -> uint4 {
+    return lds_read_b128(qk_ptr[c & 7] + (c >> 3) * 256 + kofs);
+  };
+  auto read_v = [&](int db, int c, int kofs) -> uint4 {
+    const lds_u8* v0 = tr_ptr[0][db & 3] + (db >> 2) * 256 + kofs;
+    const lds_u8* v1 = tr_ptr[1][db & 3] + (db >> 2) * 256 + kofs;
+    const uint2 x0 = lds_read_tr16(v0 + 16 * c * (D * 2));
+    const uint2 x1 = lds_read_tr16(v1 + (16 * c + 8) * (D * 2));
+    return make_uint4(x0.x, x0.y, x1.x, x1.y);
+  };
+
+  auto tile_logits_with = [&](auto&& kget) -> f32x16_t {
     f32x16_t acc_s = f32x16_t{};
     if constexpr (F32C) {
       const float* kp = reinterpret_cast<const float*>(kb) + ql * KSTR + d0 + half;
@@ -645,7 +676,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
-        const uint4 k8 = lds_read_b128(qk_ptr[c & 7] + (c >> 3) * 256);
+        const uint4 k8 = kget(c);
         acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k8), qreg[c], acc_s,
                                                         0, 0, 0);
       }
@@ -669,26 +700,42 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         }
       }
     }
+    return acc_s;
+  };
+  auto tile_logits = [&](int kofs) -> f32x16_t {
+    launder_qk();
+    return tile_logits_with([&](int c) { return read_k(c, kofs); });
+  };
 
-    // ---- mask (skipped when every key of the tile is valid for every row).
-    // The logits are copied out of the matrix-core result before any lane is
+  // ---- mask, online softmax and O^T += V^T P^T for one tile whose logits are
+  // acc_s; full = every key valid for every row, else mw holds this lane's
+  // key bits.
+  // vget(db, c) gives the V^T operand of value instruction c of dim block db.
+  auto tile_softmax_pv_with = [&](const f32x16_t& acc_s, int full, uint32_t mw, auto&& vget) {
+    // mask (skipped when every key of the tile is valid for every row).  The
+    // logits are copied out of the matrix-core result before any lane is
     // masked: masking the result vector in place miscompiled (rows kept keys
     // they had masked).
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = acc_s[i];
-    if (!mfull[buf]) {
-      const uint32_t mw = mword[buf * kTokMax + g_row] >> (4 * half);
+    if (!full) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         s[i] = ((mw >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
     }
 
-    // ---- online softmax (base 2, stale maximum)
+    // online softmax (base 2, stale maximum)
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;
+    {
+      // the other half of the wave holds the rest of each row: exchange
+      // halves (lanes l and l ^ 32) without going through LDS
+      const uint32_t u = __float_as_uint(tmax);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+    }
     const bool raise = tmax > m_run + kStale || (m_run == -INFINITY && tmax != -INFINITY);
     if (__any(raise)) {
       const float m_new = raise ? tmax : m_run;
@@ -709,7 +756,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) psum += p[i];
     l_run += psum;
 
-    // ---- O^T += V^T P^T
+    // O^T += V^T P^T
     if constexpr (F32C) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -734,18 +781,98 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         pb[c] = __builtin_bit_cast(bf16x8_t, u);
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const lds_u8* v0 = tr_ptr[0][db & 3] + (db >> 2) * 256;
-        const lds_u8* v1 = tr_ptr[1][db & 3] + (db >> 2) * 256;
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint2 x0 = lds_read_tr16(v0 + 16 * c * (D * 2));
-          const uint2 x1 = lds_read_tr16(v1 + (16 * c + 8) * (D * 2));
-          const uint4 u = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        for (int db = 0; db < NDB; ++db) {
+          const uint4 u = vget(db, c);
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u), pb[c],
                                                                acc_o[db], 0, 0, 0);
         }
       }
+    }
+  };
+  auto tile_softmax_pv = [&](const f32x16_t& acc_s, int full, uint32_t mw, int kofs) {
+    launder_tr();
+    tile_softmax_pv_with(acc_s, full, mw, [&](int db, int c) { return read_v(db, c, kofs); });
+  };
+
+  // this lane's key bits of the tile in ring slot `slot`
+  auto lane_mask = [&](int slot) -> uint32_t { return mword[slot * kTokMax + g_row] >> (4 * half); };
+
+  const int ntiles = (g.key_hi - g.key_lo + KT - 1) / KT;
+  if constexpr (DBUF) {
+    // ---- key loop over two key buffers, one barrier per tile: during tile t
+    // the workgroup stores tile t+1 (loaded during t-1) and loads tile t+2.
+    // The sources of four tiles are resolved at a time, one tile per wave
+    // (tiles t+4 .. t+7 during tile t, t a multiple of 4), so no wave carries
+    // more than the others into a barrier; the metadata ring holds the eight
+    // tiles t .. t+7.
+    if (ntiles > 0) {
+      if (wave < 4 && wave < ntiles) meta_tile_by(g.key_lo + wave * KT, wave, wave);
+      lds_barrier();
+      load_tile(0);
+      store_tile(0);
+      if (ntiles > 1) load_tile(1);
+      lds_barrier();
+    }
+    int full_next = mfull[0];
+    uint32_t mw_next = lane_mask(0);
+    auto step = [&](int t, auto bsel) {
+      constexpr int B = decltype(bsel)::value;   // buffer of tile t (= t mod 2)
+      constexpr int KO = B * (int)KBYTES;
+      constexpr int KS = (B ^ 1) * (int)KBYTES;
+      const int full = full_next;
+      const uint32_t mw = mw_next;
+      const int s1 = (t + 1) & (kMetaSlots - 1);
+      full_next = mfull[s1];
+      mw_next = lane_mask(s1);
+      int rows[UPT];
+      tile_rows((t + 2) & (kMetaSlots - 1), rows);
+      // the first key operands of this tile are in flight during the staging
+      // (two: more cost the third wave per SIMD its registers)
+      constexpr int KPRE = 2;
+      uint4 kr[KPRE];
+      __builtin_amdgcn_sched_barrier(0);
+      launder_qk();
+#pragma unroll
+      for (int c = 0; c < KPRE; ++c) kr[c] = read_k(c, KO);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < ntiles) store_tile(KS);
+      if (t + 2 < ntiles) load_tile_rows(rows);
+      if ((t & 3) == 0 && wave < 4) {
+        const int tt = t + 4 + wave;
+        if (tt < ntiles) meta_tile_by(g.key_lo + tt * KT, tt & (kMetaSlots - 1), wave);
+      }
+      const f32x16_t sc = tile_logits_with([&](int c) { return c < KPRE ? kr[c] : read_k(c, KO); });
+      tile_softmax_pv(sc, full, mw, KO);
+      lds_barrier();
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, B0{});
+      if (t + 1 >= ntiles) break;
+      step(t + 1, B1{});
+    }
+  } else {
+    // ---- key loop: prologue resolves (and, prefetching, loads) the first tile
+    if (ntiles > 0) {
+      meta_tile(g.key_lo, 0);
+      lds_barrier();
+      if constexpr (PREF) load_tile(0);
+    }
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int buf = tile & 1;
+      const int kbase = g.key_lo + tile * KT;
+      lds_barrier();                 // previous tile fully consumed
+      if constexpr (PREF) store_tile(0);
+      else stage_direct(buf);
+      if (tile + 1 < ntiles) meta_tile(kbase + KT, buf ^ 1);
+      lds_barrier();                 // tile in LDS, next tile's sources resolved
+      if constexpr (PREF) {
+        if (tile + 1 < ntiles) load_tile(buf ^ 1);   // in flight during the compute below
+      }
+      tile_softmax_pv(tile_logits(0), mfull[buf], lane_mask(buf), 0);
     }
   }
 
@@ -780,8 +907,21 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   }  // work items
 }
 
+template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM, bool PREF>
+__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
+  attn_body<D, F32C, KVF, SPARSE, DSPLIT, OUTM, PREF>(a);
+}
+
+// D = 128 with prefetch: registers held to three waves per SIMD, the
+// occupancy its latency hiding relies on
+template <int KVF, bool SPARSE, int OUTM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_kernel_d128(AttnArgs a) {
+  attn_body<128, false, KVF, SPARSE, 1, OUTM, true>(a);
+}
+
 template <int D, bool F32C, int DSPLIT>
-size_t attn_smem(int nrb);
+size_t attn_smem(int nrb, bool dbuf);
 
 csa_status launch_plan(const AttnArgs& a, bool sparse, hipStream_t s) {
   if (sparse) hipLaunchKernelGGL(attn_split_plan<true>, dim3(1), dim3(1024), 0, s, a);
@@ -827,7 +967,7 @@ csa_status launch_kernel(const AttnArgs& a0, K kern, int threads, size_t smem, h
 // the same kernel without register prefetch (too few threads to share it)
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM>
 csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
-  const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb);
+  const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb, false);
   const int threads = a.nrb * DSPLIT * 64;
   auto kern = attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, false>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -837,26 +977,31 @@ csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
   return launch_kernel<SPARSE>(a, kern, threads, smem, stream);
 }
 
+// LDS of one workgroup: key buffers (two when double-buffered), the metadata
+// ring, and the partial-logit exchange when a row block spans several waves
 template <int D, bool F32C, int DSPLIT>
-size_t attn_smem(int nrb) {
+size_t attn_smem(int nrb, bool dbuf) {
   const size_t kbytes = F32C ? (size_t)KT * (D + 4) * 4 : (size_t)KT * D * 2;
-  const size_t meta = (2 * KT + 2 * kTokMax + 4) * 4;
+  const size_t meta = ((size_t)kMetaSlots * (KT + kTokMax + 1)) * 4;
   const size_t sxbytes = DSPLIT > 1 ? (size_t)nrb * DSPLIT * 64 * 16 * 4 : 0;
-  return kbytes + meta + sxbytes;
+  return kbytes * (dbuf ? 2 : 1) + meta + sxbytes;
 }
 
 template <int D, bool F32C, int KVF, bool SPARSE, int DSPLIT, int OUTM>
 csa_status launch_attn(const AttnArgs& a, hipStream_t stream) {
-  const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb);
   const int threads = a.nrb * DSPLIT * 64;
   if ((a.n_q + a.tok - 1) / a.tok * a.ngroups > 0x7fffffff)
     return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "attn: too many queries");
   // register prefetch of the next tile (bf16 compute with registers to spare,
-  // enough threads to share it)
+  // enough threads to share it); with one wave per row block, double-buffered
   constexpr bool kPref = !F32C && (D == 128 || DSPLIT == 4);
   if (kPref && threads < (D == 512 ? 512 : 256))
     return launch_attn_np<D, F32C, KVF, SPARSE, DSPLIT, OUTM>(a, stream);
-  auto kern = attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, kPref>;
+  const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb, kPref && DSPLIT == 1);
+  auto kern = [] {
+    if constexpr (D == 128 && kPref && OUTM != 2) return attn_kernel_d128<KVF, SPARSE, OUTM>;
+    else return attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, kPref>;
+  }();
   // the kernel's LDS ceiling is raised once per instantiation, to the most any
   // launch of it can ask for (so no attribute call happens inside a captured graph)
   static const hipError_t attr = hipFuncSetAttribute(

@@ -20,10 +20,10 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def _prefill_case(rng, T, H, D, n_ent, m, k, window, q_fmt, kv_fmt, out_fmt, sparse,
-                  pos0=0, raw_hist=0):
-    raw = rng.standard_normal((raw_hist + T, D)).astype(np.float32)
-    ent = rng.standard_normal((n_ent, D)).astype(np.float32)
-    q = rng.standard_normal((T, H, D)).astype(np.float32)
+                  pos0=0, raw_hist=0, amp=1.0):
+    raw = (amp * rng.standard_normal((raw_hist + T, D))).astype(np.float32)
+    ent = (amp * rng.standard_normal((n_ent, D))).astype(np.float32)
+    q = (amp * rng.standard_normal((T, H, D))).astype(np.float32)
     raw_pos0 = pos0 - raw_hist
     qd, kvd, rd = dev_kv(q.reshape(-1, D), q_fmt), dev_kv(ent, kv_fmt), dev_kv(raw, q_fmt)
     qv, ev, rv = ref_vals(q, q_fmt), ref_vals(ent, kv_fmt), ref_vals(raw, q_fmt)
@@ -82,6 +82,25 @@ def test_attn_prefill(T, H, D, n_ent, m, k, window, qf, kvf, of, sparse, pos0, h
     assert lerr <= (1e-4 if qf == "f32" else 2e-2), lerr
 
 
+@pytest.mark.parametrize("T,H,D,n_ent,m,k,window,qf,kvf,sparse,pos0,hist", [
+    (67, 16, 128, 16, 4, 8, 128, "f32", "f32", True, 0, 0),
+    (301, 64, 128, 18, 16, 0, 128, "bf16", "bf16", False, 0, 0),
+    (45, 64, 128, 40, 4, 24, 32, "bf16", "bf16", True, 0, 0),
+    (21, 64, 512, 130, 4, 100, 16, "bf16", "fp8_mixed", True, 500, 16),
+])
+def test_attn_large_logits(T, H, D, n_ent, m, k, window, qf, kvf, sparse, pos0, hist):
+    """Inputs scaled by 6: logits spread over hundreds of units, so a running
+    maximum that missed part of a row would overflow the exponentials.  Errors
+    are measured relative to the scale of the values (x6) and logits (x36)."""
+    amp = 6.0
+    rng = np.random.default_rng(T * 11 + H + D)
+    err, lerr = _prefill_case(rng, T, H, D, n_ent, m, k, window, qf, kvf, "f32", sparse,
+                              pos0=pos0, raw_hist=hist, amp=amp)
+    tol = TOL["bf16"] if qf == "bf16" else TOL["f32"]
+    assert np.isfinite(err) and err <= tol * amp, err
+    assert np.isfinite(lerr) and lerr <= (1e-4 if qf == "f32" else 2e-2) * amp * amp, lerr
+
+
 def test_attn_chunk_with_history():
     """Queries at positions 1000.. with 128 history rows in the raw buffer."""
     rng = np.random.default_rng(3)
@@ -90,13 +109,13 @@ def test_attn_chunk_with_history():
     assert err <= 2e-2 and lerr <= 2e-2
 
 
-def _decode_case(rng, ctxs, H, D, m, k, window, kv_fmt):
+def _decode_case(rng, ctxs, H, D, m, k, window, kv_fmt, amp=1.0):
     B = len(ctxs)
     n_ent = [(c + 1) // m for c in ctxs]
     swa_len = [min(window, c + 1) for c in ctxs]
-    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
-    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len]
-    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    ents = [(amp * rng.standard_normal((n, D))).astype(np.float32) for n in n_ent]
+    swas = [(amp * rng.standard_normal((s, D))).astype(np.float32) for s in swa_len]
+    q = (amp * rng.standard_normal((B, H, D))).astype(np.float32)
     idx = np.full((B, k), -1, np.int64)
     for r in range(B):
         cnt = min(k, n_ent[r])
@@ -138,19 +157,21 @@ def test_attn_decode_split_merge_equals_union():
     assert torch.max(torch.abs(om - ou)).item() <= 2e-2
 
 
-@pytest.mark.parametrize("split_keys,kv_fmt,sparse", [(32, "fp8_mixed", True), (64, "fp8_mixed", False),
-                                                     (128, "bf16", True), (1, "fp8_mixed", True)])
-def test_attn_decode_split_k(split_keys, kv_fmt, sparse):
-    """Split-K over key chunks merged by log-sum-exp equals the oracle."""
-    rng = np.random.default_rng(40 + split_keys)
+@pytest.mark.parametrize("split_keys,kv_fmt,sparse,amp", [
+    (32, "fp8_mixed", True, 1.0), (64, "fp8_mixed", False, 1.0), (128, "bf16", True, 1.0),
+    (1, "fp8_mixed", True, 1.0), (64, "fp8_mixed", True, 6.0)])
+def test_attn_decode_split_k(split_keys, kv_fmt, sparse, amp):
+    """Split-K over key chunks merged by log-sum-exp equals the oracle (amp = 6:
+    logits spread over hundreds of units, errors relative to that scale)."""
+    rng = np.random.default_rng(40 + split_keys + int(amp))
     H, D, m, k, window = 64, 512, 4, 100, 128
     ctxs = [3000, 50, 999, 400, 127, 20000]
     B = len(ctxs)
     n_ent = [(c + 1) // m for c in ctxs]
     swa_len = [min(window, c + 1) for c in ctxs]
-    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
-    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len]
-    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    ents = [(amp * rng.standard_normal((n, D))).astype(np.float32) for n in n_ent]
+    swas = [(amp * rng.standard_normal((s, D))).astype(np.float32) for s in swa_len]
+    q = (amp * rng.standard_normal((B, H, D))).astype(np.float32)
     idx = np.full((B, k), -1, np.int64)
     for r in range(B):
         cnt = min(k, n_ent[r]) - (3 if r == 1 else 0)
@@ -172,8 +193,9 @@ def test_attn_decode_split_k(split_keys, kv_fmt, sparse):
         ke = ev[idx[r][idx[r] >= 0]] if sparse else ev
         o, l = ref.attend(qv[r], np.concatenate([ke, sv]), sc)
         sl = slice(r * H, (r + 1) * H)
-        worst = max(worst, np.max(np.abs(to_np(out[sl]) - o)), np.max(np.abs(to_np(lse[sl]) - l)))
-    assert worst <= 2e-2, worst
+        worst = max(worst, np.max(np.abs(to_np(out[sl]) - o)) / amp,
+                    np.max(np.abs(to_np(lse[sl]) - l)) / (amp * amp))
+    assert np.isfinite(worst) and worst <= 2e-2, worst
 
 
 def test_attn_window_only_and_empty_rows():
