@@ -388,13 +388,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   constexpr int UPT = PREF ? (UNITS + PMIN - 1) / PMIN : 1;
   constexpr size_t KBYTES = F32C ? (size_t)KT * KSTR * 4 : (size_t)KT * D * 2;
 
-  // double-buffered key tiles (one wave per 32 rows, at least four waves)
-  constexpr bool DBUF = PREF && DSPLIT == 1;
+  // double-buffered key tiles (at least four waves)
+  constexpr bool DBUF = PREF;
   constexpr int NKB = DBUF ? 2 : 1;
 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* kb = smem;                                        // [NKB] key tiles
-  int* mrow = reinterpret_cast<int*>(smem + NKB * KBYTES);         // [kMetaSlots][KT] source rows
+  // bf16 keys: the metadata also holds each key's row address
+  constexpr bool ADDR = !F32C && KVF != CSA_FP8_MIXED;
+  const uint16_t** maddr = reinterpret_cast<const uint16_t**>(smem + NKB * KBYTES);  // [kMetaSlots][KT]
+  int* mrow = reinterpret_cast<int*>(smem + NKB * KBYTES + (ADDR ? kMetaSlots * KT * 8 : 0));  // [kMetaSlots][KT] source rows
   uint32_t* mword = reinterpret_cast<uint32_t*>(mrow + kMetaSlots * KT);  // [kMetaSlots][kTokMax] key bits
   int* mfull = reinterpret_cast<int*>(mword + kMetaSlots * kTokMax);      // [kMetaSlots]
   float* sx = reinterpret_cast<float*>(mfull + kMetaSlots); // [nrb][DSPLIT][4][64] float4 partial logits
@@ -414,7 +417,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   // items x, x + gridDim.x, ... of the work list, for head group y.
   // (split-K is exactly the partial-output instantiation)
   constexpr bool splitk = OUTM == 2;
-  const int hgrp = splitk ? (int)blockIdx.y : (int)(blockIdx.x % (unsigned)a.ngroups);
+  const unsigned wg = blockIdx.x;
+  const int hgrp = splitk ? (int)blockIdx.y : (int)(wg % (unsigned)a.ngroups);
   const int n_items = splitk ? a.ws_start[a.n_q] : 1;
   for (int item = splitk ? (int)blockIdx.x : 0; item < n_items; item += splitk ? (int)gridDim.x : 1) {
   int64_t q_first;
@@ -423,7 +427,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     q_first = a.ws_item_q[item];
     split = item - a.ws_start[q_first];
   } else {
-    q_first = (int64_t)(blockIdx.x / (unsigned)a.ngroups) * a.tok;
+    q_first = (int64_t)(wg / (unsigned)a.ngroups) * a.tok;
   }
   Geo g = splitk ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
   if (splitk) {
@@ -477,6 +481,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       // reads a row that always exists and stays masked
       if (!F32C && row == -1) row = a.kv != nullptr ? 0 : -2;
       if (lane < KT) mrow[buf * KT + lane] = row;
+      if constexpr (ADDR) {
+        // rows are bf16 [.., D] in either tensor; -2 - r is raw row r
+        const uint16_t* base = row >= 0 ? static_cast<const uint16_t*>(a.kv) + (int64_t)row * D
+                                        : static_cast<const uint16_t*>(a.raw) + (int64_t)(-2 - row) * D;
+        if (lane < KT) maddr[buf * KT + lane] = base;
+      }
       bool full = true;
       for (int t = 0; t < a.tok; ++t) {
         const uint32_t w = (uint32_t)__ballot(t < ntok && t >= lo && t < hi);
@@ -556,18 +566,35 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   };
   // the same in two parts: source rows of this thread's units (LDS), then
   // the loads themselves
-  auto tile_rows = [&](int buf, int* rows) {
+  // (for bf16 keys the row addresses instead of the rows)
+  using src_t = typename std::conditional<ADDR, const uint16_t*, int>::type;
+  auto tile_rows = [&](int buf, src_t* rows) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * nthreads;
-      rows[i] = u < UNITS ? mrow[buf * KT + u / UPR] : -1;
+      if constexpr (ADDR) rows[i] = maddr[buf * KT + (u < UNITS ? u / UPR : 0)];
+      else rows[i] = u < UNITS ? mrow[buf * KT + u / UPR] : -1;
     }
   };
-  auto load_tile_rows = [&](const int* rows) {
+  auto load_tile_rows = [&](const src_t* rows) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * nthreads;
-      if (u < UNITS) load_unit_row(rows[i], u, stg[i], sfp8[i]);
+      if (u < UNITS) {
+        if constexpr (ADDR) {
+          // a pointer read back from LDS is generic: named global, the loads
+          // stay global loads (a flat load would also count against the LDS
+          // wait counter)
+          typedef const __attribute__((address_space(1))) u32x4_t gu4;
+          const gu4* p = (const gu4*)(uintptr_t)(rows[i] + (u % UPR) * 16);
+          const u32x4_t v0 = p[0], v1 = p[1];
+          stg[i][0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+          stg[i][1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+          sfp8[i] = false;
+        } else {
+          load_unit_row(rows[i], u, stg[i], sfp8[i]);
+        }
+      }
     }
   };
   auto store_tile = [&](int kofs) {
@@ -826,7 +853,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       const int s1 = (t + 1) & (kMetaSlots - 1);
       full_next = mfull[s1];
       mw_next = lane_mask(s1);
-      int rows[UPT];
+      src_t rows[UPT];
       tile_rows((t + 2) & (kMetaSlots - 1), rows);
       // the first key operands of this tile are in flight during the staging
       // (two: more cost the third wave per SIMD its registers)
@@ -982,7 +1009,7 @@ csa_status launch_attn_np(const AttnArgs& a, hipStream_t stream) {
 template <int D, bool F32C, int DSPLIT>
 size_t attn_smem(int nrb, bool dbuf) {
   const size_t kbytes = F32C ? (size_t)KT * (D + 4) * 4 : (size_t)KT * D * 2;
-  const size_t meta = ((size_t)kMetaSlots * (KT + kTokMax + 1)) * 4;
+  const size_t meta = ((size_t)kMetaSlots * (KT + kTokMax + 1)) * 4 + (F32C ? 0 : (size_t)kMetaSlots * KT * 8);
   const size_t sxbytes = DSPLIT > 1 ? (size_t)nrb * DSPLIT * 64 * 16 * 4 : 0;
   return kbytes * (dbuf ? 2 : 1) + meta + sxbytes;
 }
@@ -997,7 +1024,7 @@ csa_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   constexpr bool kPref = !F32C && (D == 128 || DSPLIT == 4);
   if (kPref && threads < (D == 512 ? 512 : 256))
     return launch_attn_np<D, F32C, KVF, SPARSE, DSPLIT, OUTM>(a, stream);
-  const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb, kPref && DSPLIT == 1);
+  const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb, kPref);
   auto kern = [] {
     if constexpr (D == 128 && kPref && OUTM != 2) return attn_kernel_d128<KVF, SPARSE, OUTM>;
     else return attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, kPref>;

@@ -53,9 +53,17 @@ struct IdxArgs {
 // keeps one tile in flight and relies on occupancy, its cost being the score
 // writes.
 template <int FMT> struct Tiling;
-template <> struct Tiling<CSA_F32> { static constexpr int TB = 1; };
-template <> struct Tiling<CSA_BF16> { static constexpr int TB = 2; };
-template <> struct Tiling<CSA_MXFP4> { static constexpr int TB = 8; };
+// TPW = tiles per wave when streaming (each wave reads 16 to 32 KB of keys);
+// batches of TB tiles are double-buffered.
+template <> struct Tiling<CSA_F32> { static constexpr int TB = 1, TPW = 8; };
+template <> struct Tiling<CSA_BF16> { static constexpr int TB = 1, TPW = 8; };
+template <> struct Tiling<CSA_MXFP4> { static constexpr int TB = 8, TPW = 16; };
+
+// entries per workgroup
+template <int FMT>
+constexpr int entries_per_wg(bool stream) {
+  return kWaves * (stream ? Tiling<FMT>::TPW : kTilesPerWave) * 32;
+}
 
 // Key operand of one tile for this lane (entry e0 + rl, its half of the dims).
 template <int FMT> struct KeyOp;
@@ -139,7 +147,7 @@ __device__ __forceinline__ f32x16_t tile_dots(const QueryOp<FMT>& q, const KeyOp
 // aligned); decode stores each score directly.
 template <int FMT, bool SBF16, bool STREAM>
 __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
-  constexpr int TB = STREAM ? Tiling<FMT>::TB : 1;
+  constexpr int TB = Tiling<FMT>::TB;
   using score_t = typename std::conditional<SBF16, uint16_t, float>::type;
   constexpr int VEC = 16 / (int)sizeof(score_t);      // scores per 16-byte vector
   const int lane = threadIdx.x & 63;
@@ -173,10 +181,12 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
   load_query<FMT>(a, (qblock + qa) * kHI + ha, qa < a.qpg && qblock + qa < a.n_q, half, aq);
 
   // this lane's output queries: 2g + half for register block g
-  int nv[4];
-  float hw[4][kHI];
+  // (streaming, a group is one query: only block 0 of the lower half has one)
+  constexpr int NG = STREAM ? 1 : 4;
+  int nv[NG];
+  float hw[NG][kHI];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const int ql = 2 * g + half;
     nv[g] = nvis_of(ql);
 #pragma unroll
@@ -184,48 +194,84 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
       hw[g][h] = (a.head_w != nullptr && nv[g] > 0) ? a.head_w[(qblock + ql) * kHI + h] : 1.0f;
   }
 
-  const int64_t e_wg = (int64_t)blockIdx.x * kEntriesPerWG;
-  const int e_wave = wave * (kTilesPerWave * 32);      // first entry of this wave in the chunk
+  constexpr int TPW = STREAM ? Tiling<FMT>::TPW : kTilesPerWave;
+  const int64_t e_wg = (int64_t)blockIdx.x * entries_per_wg<FMT>(STREAM);
+  const int e_wave = wave * (TPW * 32);                // first entry of this wave in the chunk
+
+  // scores of tile t (keys k, this lane's entry e_wave + 32t + rl of the
+  // chunk) for this lane's queries
+  auto score_tile = [&](int t, const KeyOp<FMT>& k, score_t* stage, bool staged) {
+    const int el = e_wave + t * 32 + rl;               // entry within the chunk
+    const int64_t e = e_wg + el;                       // this lane's entry (B column)
+    const f32x16_t acc = tile_dots<FMT>(aq, k);
+    // ReLU + weighted head sum; register block g holds the 4 heads of
+    // query 2g + half
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (e >= nv[g]) continue;                        // also covers queries past the batch
+      float s = 0.0f;
+#pragma unroll
+      for (int h = 0; h < kHI; ++h) {
+        float v = acc[4 * g + h];
+        if (a.relu) v = fmaxf(v, 0.0f);
+        s = fmaf(hw[g][h], v, s);
+      }
+      score_t o;
+      if constexpr (SBF16) o = (uint16_t)pack_bf16x2_fast(s, 0.0f);
+      else o = s;
+      if (staged) stage[(2 * g + half) * kEntriesPerWG + el] = o;
+      else static_cast<score_t*>(a.scores)[(qblock + 2 * g + half) * a.ld + e] = o;
+    }
+  };
+
+  if constexpr (STREAM) {
+    // batches of TB tiles, the keys of batch b+1 in flight while batch b is
+    // scored
+    constexpr int NB = TPW / TB;
+    auto batch_live = [&](int b) { return e_wg + e_wave + b * TB * 32 < n_scan; };
+    auto load_batch = [&](int b, KeyOp<FMT>* k) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int64_t e = e_wg + e_wave + (b * TB + tb) * 32 + rl;
+        load_key<FMT>(a, kv_base + e, e < n_scan, half, k[tb]);
+      }
+    };
+    auto score_batch = [&](int b, const KeyOp<FMT>* k) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (e_wg + e_wave + (b * TB + tb) * 32 >= n_scan) break;
+        score_tile(b * TB + tb, k[tb], nullptr, false);
+      }
+    };
+    if (!batch_live(0)) return;
+    KeyOp<FMT> k0[TB], k1[TB];
+    load_batch(0, k0);
+    for (int b = 0; b < NB; b += 2) {
+      const bool l1 = b + 1 < NB && batch_live(b + 1);
+      if (l1) load_batch(b + 1, k1);
+      score_batch(b, k0);
+      if (!l1) break;
+      const bool l2 = b + 2 < NB && batch_live(b + 2);
+      if (l2) load_batch(b + 2, k0);
+      score_batch(b + 1, k1);
+      if (!l2) break;
+    }
+    return;
+  }
+
   const bool staged = !STREAM && a.vec_out;
   score_t* stage = nullptr;
   if constexpr (!STREAM) {
     __shared__ __align__(16) score_t sc[8 * kEntriesPerWG];
     stage = sc;
   }
-  for (int t0 = 0; t0 < kTilesPerWave; t0 += TB) {
-    if (e_wg + e_wave + t0 * 32 >= n_scan) break;
-    // keys of TB tiles in flight together
-    KeyOp<FMT> kt[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int64_t e = e_wg + e_wave + (t0 + tb) * 32 + rl;
-      load_key<FMT>(a, kv_base + e, e < n_scan, half, kt[tb]);
-    }
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int el = e_wave + (t0 + tb) * 32 + rl;     // entry within the chunk
-      const int64_t e = e_wg + el;                      // this lane's entry (B column)
-      if (e - rl >= n_scan) break;
-      const f32x16_t acc = tile_dots<FMT>(aq, kt[tb]);
-      // ReLU + weighted head sum; register block g holds the 4 heads of
-      // query 2g + half
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (e >= nv[g]) continue;                       // also covers queries past the batch
-        float s = 0.0f;
-#pragma unroll
-        for (int h = 0; h < kHI; ++h) {
-          float v = acc[4 * g + h];
-          if (a.relu) v = fmaxf(v, 0.0f);
-          s = fmaf(hw[g][h], v, s);
-        }
-        score_t o;
-        if constexpr (SBF16) o = (uint16_t)pack_bf16x2_fast(s, 0.0f);
-        else o = s;
-        if (staged) stage[(2 * g + half) * kEntriesPerWG + el] = o;
-        else static_cast<score_t*>(a.scores)[(qblock + 2 * g + half) * a.ld + e] = o;
-      }
-    }
+  // prefill: one tile at a time, occupancy hides the loads
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    if (e_wg + e_wave + t * 32 >= n_scan) break;
+    KeyOp<FMT> kt;
+    const int64_t e = e_wg + e_wave + t * 32 + rl;
+    load_key<FMT>(a, kv_base + e, e < n_scan, half, kt);
+    score_tile(t, kt, stage, staged);
   }
   if constexpr (!STREAM) {
     if (!staged) return;
@@ -304,7 +350,12 @@ extern "C" csa_status csa_indexer_score(const csa_tensor* qi, int32_t n_heads,
   const int64_t gy = (batch->n_q + a.qpg - 1) / a.qpg;
   const int esz = score_fmt == CSA_BF16 ? 2 : 4;
   a.vec_out = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && ((ld * esz) % 16 == 0) ? 1 : 0;
-  const int64_t gx = (batch->max_kv + kEntriesPerWG - 1) / kEntriesPerWG;
+  // (the kernel streams keys when one query per request: qpg == 1)
+  const bool streams = a.qpg != 8;
+  const int epw = qi->fmt == CSA_F32    ? entries_per_wg<CSA_F32>(streams)
+                  : qi->fmt == CSA_BF16 ? entries_per_wg<CSA_BF16>(streams)
+                                        : entries_per_wg<CSA_MXFP4>(streams);
+  const int64_t gx = (batch->max_kv + epw - 1) / epw;
   if (gy > 65535 || gx > 0x7fffffff)
     return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_score: problem too large for one launch");
   const dim3 grid((unsigned)gx, (unsigned)gy);
