@@ -12,6 +12,7 @@
  *   csa_indexer_score    CSA step 2: low-rank lightning-indexer scores of each
  *                        query against the visible entries (BF16 scores).
  *   csa_topk_select      CSA step 2: the top-k entries of each query.
+ *   csa_indexer_topk     the two together, without writing the scores.
  *   csa_sparse_mqa_attn  CSA step 3 / HCA: shared-KV multi-query attention over
  *                        the selected (CSA) or all visible (HCA) entries
  *                        together with the sliding window of raw tokens.
@@ -182,6 +183,31 @@ csa_status csa_indexer_score(const csa_tensor* qi, int32_t n_heads, const float*
 csa_status csa_topk_select(const void* scores, int32_t score_fmt, int64_t ld,
                            const csa_batch* batch, int32_t m, int32_t k, int32_t* idx,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_indexer_topk - CSA step 2 fused: indexer scores and top-k selection.
+ * Page "DeepSeek V4 深度解析", section 2, CSA step 2 (light indexer scores,
+ * then the k most relevant entries per query) and the FP4 paragraph.
+ *
+ * Same result, bit for bit, as csa_indexer_score (same qi, ki, head_w, m,
+ * relu, score_fmt; ld >= max_kv) followed by csa_topk_select (same k): the
+ * min(k, n_vis) best entries of each query by the score rounded to score_fmt,
+ * ties to the lower index, ascending, -1 padded.  The score matrix is never
+ * written: each query keeps a list of candidates in `workspace`, sized by
+ * csa_indexer_topk_workspace_size(n_q, k) and owned by the caller (16-byte
+ * aligned; its contents are scratch).  Rows whose candidate list misses (more
+ * than the list holds, or fewer than k) are redone exactly from recomputed
+ * scores, so the result never depends on the estimate.
+ *   qi, ki, head_w, batch, m, relu, score_fmt   as csa_indexer_score
+ *   idx    int32 [n_q][k];  1 <= k <= 4096;  rows of at most 2^20 entries
+ * Errors: CSA_ERR_WORKSPACE if workspace is NULL or short; CSA_ERR_UNSUPPORTED
+ * for max_kv > 2^20 or the formats csa_indexer_score refuses.
+ * ------------------------------------------------------------------------- */
+size_t csa_indexer_topk_workspace_size(int64_t n_q, int32_t k);
+csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* head_w,
+                            const csa_tensor* ki, const csa_batch* batch, int32_t m,
+                            int32_t relu, int32_t score_fmt, int32_t k, int32_t* idx,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * csa_sparse_mqa_attn - CSA step 3 / HCA dense attention.

@@ -9,7 +9,8 @@ CSA_OK = 0
 CSA_F32, CSA_BF16, CSA_FP8_MIXED, CSA_MXFP4 = 0, 1, 2, 3
 
 EXPORTED = (
-    "csa_kv_compress", "csa_indexer_score", "csa_topk_select", "csa_sparse_mqa_attn",
+    "csa_kv_compress", "csa_indexer_score", "csa_topk_select", "csa_indexer_topk",
+    "csa_indexer_topk_workspace_size", "csa_sparse_mqa_attn",
     "csa_swa_merge", "csa_quantize", "csa_dequantize", "csa_mxfp4_to_fp8",
     "csa_attn_workspace_size", "csa_abi_version", "csa_status_string", "csa_last_error",
 )
@@ -51,6 +52,7 @@ def load():
         "csa_kv_compress": [T, P, I64, P, I32, I32, I64, I64, T, P],
         "csa_indexer_score": [T, I32, P, T, B, I32, I32, P, I32, I64, P],
         "csa_topk_select": [P, I32, I64, B, I32, I32, P, P],
+        "csa_indexer_topk": [T, I32, P, T, B, I32, I32, I32, I32, P, P, ctypes.c_size_t, P],
         "csa_sparse_mqa_attn": [T, I32, T, P, I32, T, I32, B, I32, F32, P, I32, P, I32, P,
                                 ctypes.c_size_t, P],
         "csa_swa_merge": [P, P, P, P, I64, I32, P, I32, P, P],
@@ -62,6 +64,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.csa_indexer_topk_workspace_size.restype = ctypes.c_size_t
+    lib.csa_indexer_topk_workspace_size.argtypes = [I64, I32]
     lib.csa_attn_workspace_size.restype = ctypes.c_size_t
     lib.csa_attn_workspace_size.argtypes = [I64, I32, I32, I64, I32]
     lib.csa_abi_version.restype = ctypes.c_int

@@ -1,18 +1,7 @@
-// Lightning indexer (page "DeepSeek V4 深度解析", section 2, CSA step 2: a
-// light, low-rank relevance score of each query against every compressed
-// entry; the FP4 paragraph: the indexer QK runs in FP4 and its scores are
-// kept in BF16).
-//
-//   S[q][j] = sum_h w[q][h] * ReLU(qi[q][h] . ki[j])       (H_I = 4, d_I = 64)
-//
-// One MFMA tile is 32 (query, head) rows x 32 entries: rows are 8 queries x
-// 4 heads, so the C layout (row = 8*(i/4) + 4*half + i%4) puts the 4 heads of
-// one query in 4 consecutive registers of one lane and the ReLU + head sum
-// needs no cross-lane traffic.  The entry keys are the B operand and are read
-// straight from HBM in operand layout (each lane: 8 bf16 dims / 32 fp4 codes
-// of one entry); for decode a wave keeps several key tiles in flight.  The
-// key stream is the only large read: the kernel is HBM bound for decode and
-// score-write bound for long prefill.
+// Lightning indexer scores (page "DeepSeek V4 深度解析", section 2, CSA step
+// 2; the scoring arithmetic is in indexer_core.h).  For decode a wave keeps
+// several key tiles in flight.  The key stream is the only large read: the
+// kernel is HBM bound for decode and score-write bound for long prefill.
 //   fp32  : v_mfma_f32_32x32x2f32, 32 per tile
 //   bf16  : v_mfma_f32_32x32x16_bf16, 4 per tile
 //   MXFP4 : v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 operands, e8m0 block
@@ -20,14 +9,12 @@
 //           exact, so this equals the lossless FP4 -> FP8 route.
 #include <type_traits>
 
-#include "common.h"
+#include "indexer_core.h"
 
 using namespace csa;
 
 namespace {
 
-constexpr int kHI = 4;       // indexer heads
-constexpr int kDI = 64;      // indexer dim
 constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 8;
 constexpr int kEntriesPerWG = kWaves * kTilesPerWave * 32;
@@ -63,79 +50,6 @@ template <> struct Tiling<CSA_MXFP4> { static constexpr int TB = 8, TPW = 16; };
 template <int FMT>
 constexpr int entries_per_wg(bool stream) {
   return kWaves * (stream ? Tiling<FMT>::TPW : kTilesPerWave) * 32;
-}
-
-// Key operand of one tile for this lane (entry e0 + rl, its half of the dims).
-template <int FMT> struct KeyOp;
-template <> struct KeyOp<CSA_F32> { float v[kDI / 2]; };
-template <> struct KeyOp<CSA_BF16> { uint4 v[kDI / 16]; };
-template <> struct KeyOp<CSA_MXFP4> { uint4 v; int scale; };
-
-// Query operand of one 8-query group for this lane (query rl/4, head rl%4).
-template <int FMT> struct QueryOp;
-template <> struct QueryOp<CSA_F32> { float v[kDI / 2]; };
-template <> struct QueryOp<CSA_BF16> { bf16x8_t v[kDI / 16]; };
-template <> struct QueryOp<CSA_MXFP4> { i32x8_t v; int scale; };
-
-template <int FMT>
-__device__ __forceinline__ void load_key(const IdxArgs& a, int64_t krow, bool ok, int half, KeyOp<FMT>& k) {
-  if constexpr (FMT == CSA_F32) {
-    const float* p = static_cast<const float*>(a.ki) + krow * kDI + half;
-#pragma unroll
-    for (int c = 0; c < kDI / 2; ++c) k.v[c] = ok ? p[2 * c] : 0.0f;
-  } else if constexpr (FMT == CSA_BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(a.ki) + krow * kDI + half * 8;
-#pragma unroll
-    for (int c = 0; c < kDI / 16; ++c)
-      k.v[c] = ok ? *reinterpret_cast<const uint4*>(p + 16 * c) : make_uint4(0, 0, 0, 0);
-  } else {
-    k.v = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.ki) + krow * 32 + half * 16)
-             : make_uint4(0, 0, 0, 0);
-    k.scale = ok ? a.ki_scale[krow * 2 + half] : 127;
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ void load_query(const IdxArgs& a, int64_t arow, bool ok, int half, QueryOp<FMT>& q) {
-  if constexpr (FMT == CSA_F32) {
-    const float* p = static_cast<const float*>(a.qi) + arow * kDI + half;
-#pragma unroll
-    for (int c = 0; c < kDI / 2; ++c) q.v[c] = ok ? p[2 * c] : 0.0f;
-  } else if constexpr (FMT == CSA_BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(a.qi) + arow * kDI + half * 8;
-#pragma unroll
-    for (int c = 0; c < kDI / 16; ++c) {
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(p + 16 * c) : make_uint4(0, 0, 0, 0);
-      q.v[c] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  } else {
-    q.v = i32x8_t{};
-    q.scale = 127;
-    if (ok) {
-      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.qi) + arow * 32 + half * 16);
-      q.v[0] = v.x; q.v[1] = v.y; q.v[2] = v.z; q.v[3] = v.w;
-      q.scale = a.qi_scale[arow * 2 + half];
-    }
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ f32x16_t tile_dots(const QueryOp<FMT>& q, const KeyOp<FMT>& k) {
-  f32x16_t acc = f32x16_t{};
-  if constexpr (FMT == CSA_F32) {
-#pragma unroll
-    for (int c = 0; c < kDI / 2; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q.v[c], k.v[c], acc, 0, 0, 0);
-  } else if constexpr (FMT == CSA_BF16) {
-#pragma unroll
-    for (int c = 0; c < kDI / 16; ++c)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q.v[c], __builtin_bit_cast(bf16x8_t, k.v[c]), acc, 0, 0, 0);
-  } else {
-    i32x8_t bk{};
-    bk[0] = k.v.x; bk[1] = k.v.y; bk[2] = k.v.z; bk[3] = k.v.w;
-    // cbsz = blgp = 4: both operands e2m1; opsel 0 picks scale byte 0
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.v, bk, acc, 4, 4, 0, q.scale, 0, k.scale);
-  }
-  return acc;
 }
 
 // Grid: x = chunks of kEntriesPerWG entries, y = groups of qpg queries
@@ -178,7 +92,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
   // A operand (queries): this lane's row is (query rl/4, head rl%4)
   QueryOp<FMT> aq;
   const int qa = rl >> 2, ha = rl & 3;
-  load_query<FMT>(a, (qblock + qa) * kHI + ha, qa < a.qpg && qblock + qa < a.n_q, half, aq);
+  load_query<FMT>(a.qi, a.qi_scale, (qblock + qa) * kHI + ha, qa < a.qpg && qblock + qa < a.n_q, half, aq);
 
   // this lane's output queries: 2g + half for register block g
   // (streaming, a group is one query: only block 0 of the lower half has one)
@@ -209,13 +123,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (e >= nv[g]) continue;                        // also covers queries past the batch
-      float s = 0.0f;
-#pragma unroll
-      for (int h = 0; h < kHI; ++h) {
-        float v = acc[4 * g + h];
-        if (a.relu) v = fmaxf(v, 0.0f);
-        s = fmaf(hw[g][h], v, s);
-      }
+      const float s = head_score(acc, g, hw[g], a.relu);
       score_t o;
       if constexpr (SBF16) o = (uint16_t)pack_bf16x2_fast(s, 0.0f);
       else o = s;
@@ -233,7 +141,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t e = e_wg + e_wave + (b * TB + tb) * 32 + rl;
-        load_key<FMT>(a, kv_base + e, e < n_scan, half, k[tb]);
+        load_key<FMT>(a.ki, a.ki_scale, kv_base + e, e < n_scan, half, k[tb]);
       }
     };
     auto score_batch = [&](int b, const KeyOp<FMT>* k) {
@@ -270,7 +178,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
     if (e_wg + e_wave + t * 32 >= n_scan) break;
     KeyOp<FMT> kt;
     const int64_t e = e_wg + e_wave + t * 32 + rl;
-    load_key<FMT>(a, kv_base + e, e < n_scan, half, kt);
+    load_key<FMT>(a.ki, a.ki_scale, kv_base + e, e < n_scan, half, kt);
     score_tile(t, kt, stage, staged);
   }
   if constexpr (!STREAM) {

@@ -1,0 +1,573 @@
+// Fused lightning indexer + top-k (page "DeepSeek V4 深度解析", section 2,
+// CSA step 2: every query scores the compressed entries with the light
+// indexer and keeps the k best).  The result equals csa_indexer_score
+// followed by csa_topk_select, bit for bit, but the score matrix never goes
+// to memory: only a short list of candidates per query does.
+//
+//   1. itk_sample_kernel: each query scores a sample of its visible entries
+//      (runs of 32 consecutive entries spread evenly over the row) and takes
+//      as threshold the sample key of rank ~3k * sample / n, so that about 3k
+//      entries of the row score at least as high.  Rows of at most `cap`
+//      entries take every entry (threshold 0).
+//   2. itk_filter_kernel: the indexer's tiles (same grid and arithmetic as
+//      csa_indexer_score); an entry whose order key reaches its query's
+//      threshold is appended, (key, index), to the query's candidate list.
+//      Each workgroup reserves its span with one atomic per query.
+//   3. itk_select_kernel: per query, an exact radix select of the k-th
+//      largest candidate key, ties resolved to the lowest indices by a radix
+//      select over the tied indices, the chosen entries marked in an LDS
+//      bitmap of the row and read back in index order.
+//   4. itk_redo_kernel: a row whose candidates overflowed `cap` or fell short
+//      of k (the sample misjudged it, e.g. masses of equal scores) is redone
+//      exactly from recomputed scores; every other row exits at once.
+// The candidates arrive in no fixed order, but every step after the filter
+// depends only on the candidate set, so the output is deterministic.
+#include <type_traits>
+
+#include "indexer_core.h"
+#include "select_core.h"
+
+using namespace csa;
+
+namespace {
+
+constexpr int kWaves = 4;            // waves of the scoring kernels
+constexpr int kTilesPerWave = 8;     // tiles per wave, several queries per group
+constexpr int kBitmapMax = 1 << 20;  // longest row the select and redo kernels take
+
+struct ItkArgs {
+  const void* qi;
+  const uint8_t* qi_scale;
+  const float* head_w;
+  const void* ki;
+  const uint8_t* ki_scale;
+  BatchDev b;
+  int m;
+  int relu;
+  int qpg;            // queries per group (8 for a single request, else 1)
+  int64_t n_q;
+  int k;
+  int cap;            // candidates kept per query
+  int64_t max_n;      // rows are cut to this many entries (the batch's max_kv, at most 2^20)
+  uint32_t* tau;      // [n_q] threshold keys
+  uint32_t* cnt;      // [n_q] candidates found (may exceed cap)
+  uint32_t* redo;     // [n_q] 1 = the row is redone exactly
+  uint2* cand;        // [n_q][cap] (key, entry)
+  int32_t* idx;       // [n_q][k] result
+};
+
+// Keys per tile batch when one query per group streams its row (as in the
+// score kernel's decode mode).
+template <int FMT> struct Tiling;
+template <> struct Tiling<CSA_F32> { static constexpr int TB = 1, TPW = 8; };
+template <> struct Tiling<CSA_BF16> { static constexpr int TB = 1, TPW = 8; };
+template <> struct Tiling<CSA_MXFP4> { static constexpr int TB = 8, TPW = 16; };
+
+template <int FMT>
+constexpr int entries_per_wg(bool stream) {
+  return kWaves * (stream ? Tiling<FMT>::TPW : kTilesPerWave) * 32;
+}
+
+// Order key of a score as the score kernel would store it.
+template <bool SBF16>
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if constexpr (SBF16) return order_bf16(pack_bf16x2_fast(s, 0.0f) & 0xffffu);
+  else return order_f32(__float_as_uint(s));
+}
+
+// A group of queries as the score kernel forms it: its first query, the
+// queries' visible counts, the A operand of this lane and the head weights of
+// the lane's register blocks.
+template <int FMT, int NG>
+struct Group {
+  int64_t qblock;
+  QueryMeta qm;
+  QueryOp<FMT> aq;
+  int nv[NG];
+  float hw[NG][kHI];
+};
+
+template <int FMT, int NG>
+__device__ __forceinline__ void load_group(const ItkArgs& a, int64_t qblock, Group<FMT, NG>& gr) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int rl = lane & 31;
+  gr.qblock = qblock;
+  gr.qm = query_meta(a.b, qblock, a.m);
+  const int qa = rl >> 2, ha = rl & 3;
+  load_query<FMT>(a.qi, a.qi_scale, (qblock + qa) * kHI + ha, qa < a.qpg && qblock + qa < a.n_q, half, gr.aq);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int ql = 2 * g + half;
+    int v = 0;
+    if (ql < a.qpg && qblock + ql < a.n_q) {
+      int64_t n = (gr.qm.t + ql + 1) / a.m;
+      if (n > gr.qm.kv_len) n = gr.qm.kv_len;
+      if (n > a.max_n) n = a.max_n;
+      v = (int)n;
+    }
+    gr.nv[g] = v;
+#pragma unroll
+    for (int h = 0; h < kHI; ++h)
+      gr.hw[g][h] = (a.head_w != nullptr && v > 0) ? a.head_w[(qblock + ql) * kHI + h] : 1.0f;
+  }
+}
+
+// visible entries of query q (cut to max_n, which bounds every LDS bitmap)
+__device__ __forceinline__ int64_t visible(const ItkArgs& a, int64_t q) {
+  const int64_t n = query_meta(a.b, q, a.m).n_vis;
+  return n < a.max_n ? n : a.max_n;
+}
+
+// ------------------------------------------------------------------ 1. sample
+
+constexpr int kSampleRun = 32;       // one tile per run
+
+// Grid: one workgroup per query group.  LDS: the sample keys of the group's
+// queries, [8][S] (16-bit keys for bf16 scores, S = 4096; 32-bit for fp32,
+// S = 2048).
+template <int FMT, bool SBF16>
+__global__ __launch_bounds__(256) void itk_sample_kernel(ItkArgs a) {
+  constexpr int S = SBF16 ? 4096 : 2048;
+  constexpr int NRUN = S / kSampleRun;
+  using skey_t = typename std::conditional<SBF16, uint16_t, uint32_t>::type;
+  __shared__ skey_t sk[8][S];
+  __shared__ RadixLds<256> rx;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
+  const int64_t qblock = (int64_t)blockIdx.x * a.qpg;
+  const int nq = (int)(a.n_q - qblock < a.qpg ? a.n_q - qblock : a.qpg);
+
+  // the group's queries see n_lo .. n_lo + a few entries; only rows longer
+  // than cap are sampled, over the entries all of them see
+  const int64_t n_lo = visible(a, qblock);
+  const int64_t n_hi = visible(a, qblock + nq - 1);
+  if (n_hi > a.cap) {
+    Group<FMT, 4> gr;
+    load_group<FMT, 4>(a, qblock, gr);
+    for (int r = wave; r < NRUN; r += kWaves) {
+      const int64_t j0 = (int64_t)r * (n_lo - kSampleRun) / (NRUN - 1);   // j0 + 32 <= n_lo
+      KeyOp<FMT> kt;
+      load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + j0 + rl, true, half, kt);
+      const f32x16_t acc = tile_dots<FMT>(gr.aq, kt);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 2 * g + half;
+        if (ql < nq) sk[ql][r * kSampleRun + rl] = (skey_t)score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
+      }
+    }
+  }
+  __syncthreads();
+  for (int ql = 0; ql < nq; ++ql) {
+    const int64_t q = qblock + ql;
+    const int64_t n = visible(a, q);
+    uint32_t tau = 0;
+    if (n > a.cap) {
+      // about 3k of the row's keys reach the sample key of this rank
+      int64_t rank = (3 * (int64_t)a.k * S + n - 1) / n;
+      if (rank < 1) rank = 1;
+      if (rank > S) rank = S;
+      uint32_t rem;
+      tau = radix_select_visit<SBF16 ? 16 : 32, 256>(
+          rx, (uint32_t)rank,
+          [&](auto&& f) {
+            for (int i = tid; i < S; i += 256) f((uint32_t)sk[ql][i]);
+          },
+          rem);
+    }
+    if (tid == 0) {
+      a.tau[q] = tau;
+      a.cnt[q] = 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 2. filter
+
+// Grid: x = chunks of entries, y = query groups, as the score kernel.  Pass 1
+// scores the wave's tiles, keeping each lane's keys in registers, and counts
+// the candidates per query; one atomic per query reserves the workgroup's
+// span of the list; pass 2 writes the candidates.
+template <int FMT, bool SBF16, bool STREAM>
+__global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
+  constexpr int TB = STREAM ? Tiling<FMT>::TB : 1;
+  constexpr int TPW = STREAM ? Tiling<FMT>::TPW : kTilesPerWave;
+  constexpr int NG = STREAM ? 1 : 4;
+  __shared__ uint32_t wcnt[kWaves][8];   // candidates per (wave, query)
+  __shared__ uint32_t gbase[8];          // the workgroup's first list slot per query
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
+
+  const int64_t qblock = (int64_t)blockIdx.y * a.qpg;
+  Group<FMT, NG> gr;
+  load_group<FMT, NG>(a, qblock, gr);
+  int64_t q_hi = qblock + a.qpg - 1;
+  if (q_hi >= a.n_q) q_hi = a.n_q - 1;
+  const int64_t n_scan = visible(a, q_hi);
+  uint32_t tau[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) tau[g] = gr.nv[g] > 0 ? a.tau[qblock + 2 * g + half] : 0u;
+
+  const int64_t e_wg = (int64_t)blockIdx.x * entries_per_wg<FMT>(STREAM);
+  const int e_wave = wave * (TPW * 32);
+  if (e_wg >= n_scan) return;            // the whole workgroup: no barrier reached
+
+  // pass 1: keys of this lane's entries (one per tile), candidate flags
+  uint32_t key[TPW][NG];
+  uint32_t flags = 0;                    // bit t*NG + g
+  auto score_tile = [&](int t, const KeyOp<FMT>& k) {
+    const int64_t e = e_wg + e_wave + t * 32 + rl;
+    const f32x16_t acc = tile_dots<FMT>(gr.aq, k);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      key[t][g] = score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
+      if (e < gr.nv[g] && key[t][g] >= tau[g]) flags |= 1u << (t * NG + g);
+    }
+  };
+  auto tile_live = [&](int t) { return e_wg + e_wave + t * 32 < n_scan; };
+  if constexpr (STREAM) {
+    constexpr int NB = TPW / TB;
+    auto load_batch = [&](int b, KeyOp<FMT>* k) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int64_t e = e_wg + e_wave + (b * TB + tb) * 32 + rl;
+        load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n_scan, half, k[tb]);
+      }
+    };
+    auto score_batch = [&](int b, const KeyOp<FMT>* k) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        if (tile_live(b * TB + tb)) score_tile(b * TB + tb, k[tb]);
+    };
+    if (tile_live(0)) {
+      KeyOp<FMT> k0[TB], k1[TB];
+      load_batch(0, k0);
+#pragma unroll
+      for (int b = 0; b < NB; b += 2) {
+        const bool l1 = b + 1 < NB && tile_live((b + 1) * TB);
+        if (l1) load_batch(b + 1, k1);
+        score_batch(b, k0);
+        if (!l1) break;
+        const bool l2 = b + 2 < NB && tile_live((b + 2) * TB);
+        if (l2) load_batch(b + 2, k0);
+        score_batch(b + 1, k1);
+        if (!l2) break;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (!tile_live(t)) break;
+      KeyOp<FMT> kt;
+      const int64_t e = e_wg + e_wave + t * 32 + rl;
+      load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n_scan, half, kt);
+      score_tile(t, kt);
+    }
+  }
+
+  // candidates per (wave, query): lanes 0-31 hold query 2g, lanes 32-63
+  // query 2g + 1 of register block g
+  uint32_t wq[NG][2];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) c += (flags >> (t * NG + g)) & 1u;
+    // sums over each half of the wave
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) c += __shfl_xor(c, o);
+    wq[g][0] = __shfl(c, 0);
+    wq[g][1] = __shfl(c, 32);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      wcnt[wave][2 * g] = wq[g][0];
+      wcnt[wave][2 * g + 1] = wq[g][1];
+    }
+  }
+  __syncthreads();
+  if (tid < 2 * NG && tid < a.qpg && qblock + tid < a.n_q) {
+    uint32_t tot = 0;
+    for (int w = 0; w < kWaves; ++w) tot += wcnt[w][tid];
+    gbase[tid] = tot > 0 ? atomicAdd(&a.cnt[qblock + tid], tot) : 0u;
+  }
+  __syncthreads();
+
+  // pass 2: write the candidates (slots past cap are dropped; the count
+  // still records them, which sends the row to the exact redo)
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int ql = 2 * g + half;
+    if (ql >= a.qpg || qblock + ql >= a.n_q) continue;
+    uint32_t base = gbase[ql];
+    for (int w = 0; w < wave; ++w) base += wcnt[w][ql];
+    uint2* list = a.cand + (qblock + ql) * (int64_t)a.cap;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const bool f = (flags >> (t * NG + g)) & 1u;
+      const uint64_t m = __ballot(f);
+      const uint32_t mh = (uint32_t)(m >> (32 * half));
+      const uint32_t before = __builtin_popcount(mh & ((1u << rl) - 1u));
+      if (f) {
+        const uint32_t slot = base + before;
+        if (slot < (uint32_t)a.cap)
+          list[slot] = make_uint2(key[t][g], (uint32_t)(e_wg + e_wave + t * 32 + rl));
+      }
+      base += __builtin_popcount(mh);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 3. select
+
+// Selected entries of a row, marked in an LDS bitmap, written in index order
+// to out[0..k): each thread owns a contiguous run of bitmap words.
+template <int NT>
+__device__ void emit_bitmap(const uint32_t* bm, int nwords, uint32_t* wsum, int32_t* out, int k) {
+  const int tid = threadIdx.x;
+  const int per = (nwords + NT - 1) / NT;
+  const int w0 = tid * per;
+  const int w1 = w0 + per < nwords ? w0 + per : nwords;
+  uint32_t c = 0;
+  for (int w = w0; w < w1; ++w) c += __builtin_popcount(bm[w]);
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<NT / 64>(c, wsum, total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bm[w];
+    while (bits) {
+      const int b = __builtin_ctz(bits);
+      if (pos < (uint32_t)k) out[pos] = 32 * w + b;
+      ++pos;
+      bits &= bits - 1;
+    }
+  }
+}
+
+template <int NT>
+struct SelectLds {
+  RadixLds<NT> rx;
+  uint32_t wsum[NT / 64];
+  uint32_t n_eq;
+};
+
+// Marks the chosen entries of a row in the bitmap: every key above tau and,
+// among the keys equal to tau, the `need` with the lowest indices.  visit(f)
+// calls f(key, entry) for this thread's share of the row's keys (candidates
+// or the whole row).  The bitmap (nwords words) is cleared here.
+template <int KBITS, int NT, typename Visit>
+__device__ void mark_top(SelectLds<NT>& sh, uint32_t* bm, int nwords, uint32_t tau, uint32_t need,
+                         Visit visit) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.n_eq = 0;
+  for (int w = tid; w < nwords; w += NT) bm[w] = 0;
+  __syncthreads();
+  uint32_t my_eq = 0;
+  visit([&](uint32_t key, uint32_t e) { my_eq += key == tau ? 1u : 0u; });
+  if (my_eq) atomicAdd(&sh.n_eq, my_eq);
+  __syncthreads();
+  // the need-th lowest tied index is the need-th largest of the complements
+  uint32_t iota = 0xffffffffu;
+  if (need < sh.n_eq) {
+    uint32_t rem;
+    iota = ~radix_select_visit<32, NT>(
+        sh.rx, need,
+        [&](auto&& f) {
+          visit([&](uint32_t key, uint32_t e) {
+            if (key == tau) f(~e);
+          });
+        },
+        rem);
+  }
+  visit([&](uint32_t key, uint32_t e) {
+    if (key > tau || (key == tau && e <= iota)) atomicOr(&bm[e >> 5], 1u << (e & 31));
+  });
+  __syncthreads();
+}
+
+// Grid: one workgroup per query.
+template <bool SBF16, int NT>
+__global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
+  constexpr int KBITS = SBF16 ? 16 : 32;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SelectLds<NT>& sh = *reinterpret_cast<SelectLds<NT>*>(smem_raw);
+  uint32_t* bm = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SelectLds<NT>));
+  const int tid = threadIdx.x;
+  const int64_t q = blockIdx.x;
+  const int64_t n = visible(a, q);
+  int32_t* out = a.idx + q * (int64_t)a.k;
+  if (n <= a.k) {
+    for (int64_t j = tid; j < a.k; j += NT) out[j] = j < n ? (int32_t)j : -1;
+    if (tid == 0) a.redo[q] = 0;
+    return;
+  }
+  const uint32_t c = a.cnt[q];
+  const bool miss = c > (uint32_t)a.cap || c < (uint32_t)a.k;
+  if (tid == 0) a.redo[q] = miss ? 1u : 0u;
+  if (miss) return;
+  const uint2* list = a.cand + q * (int64_t)a.cap;
+  auto visit = [&](auto&& f) {
+    for (uint32_t i = tid; i < c; i += NT) {
+      const uint2 ce = list[i];
+      f(ce.x, ce.y);
+    }
+  };
+  uint32_t need;
+  const uint32_t tau = radix_select_visit<KBITS, NT>(
+      sh.rx, (uint32_t)a.k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need);
+  const int nwords = (int)((n + 31) / 32);
+  mark_top<KBITS, NT>(sh, bm, nwords, tau, need, visit);
+  emit_bitmap<NT>(bm, nwords, sh.wsum, out, a.k);
+}
+
+// ------------------------------------------------------------------ 4. redo
+
+// Grid: one workgroup per query; rows not flagged return at once.  The row's
+// keys are recomputed tile by tile (the query in its group's slot, so the
+// arithmetic is the score kernel's) for each pass of the selection.
+template <int FMT, bool SBF16>
+__global__ __launch_bounds__(256) void itk_redo_kernel(ItkArgs a) {
+  constexpr int KBITS = SBF16 ? 16 : 32;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SelectLds<256>& sh = *reinterpret_cast<SelectLds<256>*>(smem_raw);
+  uint32_t* bm = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SelectLds<256>));
+  const int64_t q = blockIdx.x;
+  if (a.redo[q] == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, rl = lane & 31;
+  const int64_t n = visible(a, q);
+  int32_t* out = a.idx + q * (int64_t)a.k;
+  const int64_t qblock = q / a.qpg * a.qpg;
+  const int slot = (int)(q - qblock);
+  Group<FMT, 4> gr;
+  load_group<FMT, 4>(a, qblock, gr);
+  const int gs = slot >> 1;             // register block of the query
+  const bool mine = (slot & 1) == half; // lanes of the query's half
+  // f(key, entry) for every entry of the row, each lane its own
+  auto visit = [&](auto&& f) {
+    for (int64_t t0 = (int64_t)wave * 32; t0 < n; t0 += kWaves * 32) {
+      const int64_t e = t0 + rl;
+      KeyOp<FMT> kt;
+      load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n, half, kt);
+      const f32x16_t acc = tile_dots<FMT>(gr.aq, kt);
+      float s = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (g == gs) s = head_score(acc, g, gr.hw[g], a.relu);
+      if (mine && e < n) f(score_key<SBF16>(s), (uint32_t)e);
+    }
+  };
+  uint32_t need;
+  const uint32_t tau = radix_select_visit<KBITS, 256>(
+      sh.rx, (uint32_t)a.k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need);
+  const int nwords = (int)((n + 31) / 32);
+  mark_top<KBITS, 256>(sh, bm, nwords, tau, need, visit);
+  emit_bitmap<256>(bm, nwords, sh.wsum, out, a.k);
+}
+
+template <int FMT, bool SBF16>
+csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
+  const int64_t groups = (a.n_q + a.qpg - 1) / a.qpg;
+  const bool stream = a.qpg == 1;
+  hipLaunchKernelGGL((itk_sample_kernel<FMT, SBF16>), dim3((unsigned)groups), dim3(256), 0, s, a);
+  csa_status st = csa_host::check_launch("csa_indexer_topk (sample)");
+  if (st != CSA_OK) return st;
+  const int64_t epw = entries_per_wg<FMT>(stream);
+  const dim3 fgrid((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups);
+  if (stream) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true>), fgrid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false>), fgrid, dim3(256), 0, s, a);
+  st = csa_host::check_launch("csa_indexer_topk (filter)");
+  if (st != CSA_OK) return st;
+  const size_t bm_bytes = (size_t)((max_kv < kBitmapMax ? max_kv : kBitmapMax) + 31) / 32 * 4;
+  const size_t sel_lds = sizeof(SelectLds<1024>) + bm_bytes;
+  static const hipError_t attr1 = hipFuncSetAttribute(
+      (const void*)itk_select_kernel<SBF16, 1024>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (sel_lds > 64 * 1024 && attr1 != hipSuccess)
+    return csa_host::fail(CSA_ERR_HIP, "csa_indexer_topk: cannot reserve %zu B of LDS", sel_lds);
+  hipLaunchKernelGGL((itk_select_kernel<SBF16, 1024>), dim3((unsigned)a.n_q), dim3(1024), sel_lds, s, a);
+  st = csa_host::check_launch("csa_indexer_topk (select)");
+  if (st != CSA_OK) return st;
+  const size_t redo_lds = sizeof(SelectLds<256>) + bm_bytes;
+  static const hipError_t attr2 = hipFuncSetAttribute(
+      (const void*)itk_redo_kernel<FMT, SBF16>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (redo_lds > 64 * 1024 && attr2 != hipSuccess)
+    return csa_host::fail(CSA_ERR_HIP, "csa_indexer_topk: cannot reserve %zu B of LDS", redo_lds);
+  hipLaunchKernelGGL((itk_redo_kernel<FMT, SBF16>), dim3((unsigned)a.n_q), dim3(256), redo_lds, s, a);
+  return csa_host::check_launch("csa_indexer_topk (redo)");
+}
+
+// candidates kept per query: the threshold aims at about 3k
+int64_t cap_for(int32_t k) {
+  const int64_t c = 6 * (int64_t)k;
+  return c > 4096 ? c : 4096;
+}
+
+}  // namespace
+
+using namespace csa_host;
+
+extern "C" size_t csa_indexer_topk_workspace_size(int64_t n_q, int32_t k) {
+  if (n_q <= 0 || k < 1) return 0;
+  // tau, cnt and redo per query, then the candidate lists (8-byte aligned)
+  const size_t head = ((size_t)n_q * 3 * 4 + 15) / 16 * 16;
+  return head + (size_t)n_q * (size_t)cap_for(k) * 8;
+}
+
+extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* head_w,
+                                       const csa_tensor* ki, const csa_batch* batch, int32_t m,
+                                       int32_t relu, int32_t score_fmt, int32_t k, int32_t* idx,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (batch == nullptr || !fmt_valid_tensor(qi) || !fmt_valid_tensor(ki, false))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: bad tensor or batch");
+  if (batch->n_req < 1 || batch->n_q < 0 || batch->q_off == nullptr || batch->q_pos == nullptr ||
+      batch->kv_off == nullptr)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: bad batch descriptor");
+  if (n_heads != kHI || qi->dim != kDI || ki->dim != kDI)
+    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: implemented for 4 heads of dim 64");
+  if (qi->fmt != ki->fmt || (qi->fmt != CSA_F32 && qi->fmt != CSA_BF16 && qi->fmt != CSA_MXFP4))
+    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: qi and ki must both be F32, BF16 or MXFP4");
+  if (score_fmt != CSA_F32 && score_fmt != CSA_BF16)
+    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: scores must be F32 or BF16");
+  if (qi->rows != batch->n_q * n_heads)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: qi rows must be n_q * n_heads");
+  if (m < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: m must be >= 1");
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: need 1 <= k <= 4096");
+  if (batch->max_kv < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: max_kv < 0");
+  if (batch->max_kv > kBitmapMax)
+    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: rows above 2^20 entries");
+  if (batch->n_q == 0) return CSA_OK;
+  if (batch->n_q > 0x7fffffff) return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: too many queries");
+  if (idx == nullptr) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: null idx");
+  const size_t need = csa_indexer_topk_workspace_size(batch->n_q, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "csa_indexer_topk: needs %zu workspace bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: workspace must be 16-byte aligned");
+
+  ItkArgs a{};
+  a.qi = qi->data;
+  a.qi_scale = static_cast<const uint8_t*>(qi->scale);
+  a.head_w = head_w;
+  a.ki = ki->data;
+  a.ki_scale = static_cast<const uint8_t*>(ki->scale);
+  a.b = BatchDev{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, nullptr, nullptr, ki->rows, 0};
+  a.m = m;
+  a.relu = relu ? 1 : 0;
+  a.qpg = batch->n_req == 1 ? 8 : 1;
+  a.n_q = batch->n_q;
+  a.k = k;
+  a.cap = (int)cap_for(k);
+  char* ws = static_cast<char*>(workspace);
+  a.tau = reinterpret_cast<uint32_t*>(ws);
+  a.cnt = a.tau + batch->n_q;
+  a.redo = a.cnt + batch->n_q;
+  a.cand = reinterpret_cast<uint2*>(ws + ((size_t)batch->n_q * 3 * 4 + 15) / 16 * 16);
+  a.idx = idx;
+  const int64_t groups = (batch->n_q + a.qpg - 1) / a.qpg;
+  const int64_t max_kv = batch->max_kv < ki->rows ? batch->max_kv : ki->rows;
+  a.max_n = max_kv;
+  if (groups > 0x7fffffff || (max_kv + 1023) / 1024 > 0x7fffffff || groups > 65535)
+    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: problem too large for one launch");
+  const bool sb = score_fmt == CSA_BF16;
+  if (qi->fmt == CSA_F32) return sb ? launch_all<CSA_F32, true>(a, max_kv, stream) : launch_all<CSA_F32, false>(a, max_kv, stream);
+  if (qi->fmt == CSA_BF16) return sb ? launch_all<CSA_BF16, true>(a, max_kv, stream) : launch_all<CSA_BF16, false>(a, max_kv, stream);
+  return sb ? launch_all<CSA_MXFP4, true>(a, max_kv, stream) : launch_all<CSA_MXFP4, false>(a, max_kv, stream);
+}

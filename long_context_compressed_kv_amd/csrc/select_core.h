@@ -1,0 +1,138 @@
+// Exact top-k building blocks shared by the top-k kernels (page "DeepSeek V4
+// 深度解析", section 2, CSA step 2: each query keeps its k highest-scoring
+// entries): order-preserving integer keys for fp32 / bf16 scores, scans, and
+// a radix select over keys that the caller feeds through a visitor.
+#pragma once
+
+#include "common.h"
+
+namespace csa {
+
+// Order-preserving keys: a larger score gives a larger key; -0 is folded
+// onto +0 so that they tie, as the scores compare.
+__device__ __forceinline__ uint32_t order_bf16(uint32_t b) {
+  if (b == 0x8000u) b = 0;
+  return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+__device__ __forceinline__ uint32_t order_f32(uint32_t b) {
+  if (b == 0x80000000u) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Inverse of the order-preserving map, as a float.
+template <bool BF16>
+__device__ __forceinline__ float key_value(uint32_t key) {
+  if constexpr (BF16) {
+    const uint32_t b = (key & 0x8000u) ? (key & 0x7fffu) : (~key & 0xffffu);
+    return __uint_as_float(b << 16);
+  } else {
+    const uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+    return __uint_as_float(b);
+  }
+}
+
+// Exclusive scan of v over one wave; total returned through `total`.
+__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, 63);
+  return x - v;
+}
+
+// Exclusive scan of v over the block (kWaves waves, wsum: kWaves words of
+// LDS); total returned through `total`.
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t s = wsum[w];
+    before += w < wave ? s : 0;
+    tot += s;
+  }
+  total = tot;
+  return before + x - v;
+}
+
+// LDS of a radix select: one 256-bin histogram per wave, the chosen digit and
+// the rank left inside it.
+template <int NT>
+struct RadixLds {
+  uint32_t hist[NT / 64][256];
+  uint32_t sel_digit, sel_remain;
+};
+
+// Radix select (8-bit digits, most significant first) of the rank-th largest
+// of a multiset of KBITS-bit keys.  visit(f) calls f(key) once for each key
+// this thread contributes; every thread of the block calls it (the keys of
+// all threads together form the multiset).  Returns the key; `remain` = how
+// many keys equal to it are needed to reach rank (rank - remain keys are
+// strictly greater).  1 <= rank <= the multiset's size.
+template <int KBITS, int NT, typename Visit>
+__device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit visit, uint32_t& remain) {
+  constexpr int kWaves = NT / 64;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  uint32_t prefix = 0;
+  remain = rank;
+  for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
+    for (int i = tid; i < kWaves * 256; i += NT) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
+    const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
+    visit([&](uint32_t key) {
+      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (tid < 256) {          // per-digit totals of the per-wave histograms
+      uint32_t s = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s += sh.hist[w][tid];
+      sh.hist[0][tid] = s;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 4l..4l+3; suffix counts from the top digit down
+      uint32_t c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = sh.hist[0][4 * tid + i];
+      const uint32_t s = c[0] + c[1] + c[2] + c[3];
+      uint32_t x = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(x, o);
+        if (tid + o < 64) x += y;
+      }
+      uint32_t acc = x - s;                  // keys with a digit above this lane's group
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (acc < remain && remain <= acc + c[i]) {
+          sh.sel_digit = 4 * tid + i;
+          sh.sel_remain = remain - acc;
+        }
+        acc += c[i];
+      }
+    }
+    __syncthreads();
+    prefix |= sh.sel_digit << shift;
+    remain = sh.sel_remain;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+}  // namespace csa

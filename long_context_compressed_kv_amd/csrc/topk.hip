@@ -24,7 +24,7 @@
 // When the estimate misses (fewer than k candidates, or a wave segment
 // overflows), the row is redone exactly over global memory with the same
 // radix select and ordered scan.
-#include "common.h"
+#include "select_core.h"
 
 using namespace csa;
 
@@ -34,69 +34,10 @@ constexpr int kCap = 4096;                   // LDS candidates per row
 constexpr int kSample = 4096;
 constexpr int kU = 4;                        // 16-byte vectors in flight per lane
 
-// Inverse of the order-preserving map, as a float (the threshold test of the
-// streaming pass compares values; -0 and +0 compare equal, as their keys do).
-template <bool BF16>
-__device__ __forceinline__ float key_value(uint32_t key) {
-  if constexpr (BF16) {
-    const uint32_t b = (key & 0x8000u) ? (key & 0x7fffu) : (~key & 0xffffu);
-    return __uint_as_float(b << 16);
-  } else {
-    const uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
-    return __uint_as_float(b);
-  }
-}
-
-__device__ __forceinline__ uint32_t order_bf16(uint32_t b) {
-  if (b == 0x8000u) b = 0;
-  return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
-}
-__device__ __forceinline__ uint32_t order_f32(uint32_t b) {
-  if (b == 0x80000000u) b = 0;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
 template <bool BF16>
 __device__ __forceinline__ uint32_t key_at(const void* row, int64_t j) {
   if constexpr (BF16) return order_bf16(static_cast<const uint16_t*>(row)[j]);
   else return order_f32(__float_as_uint(static_cast<const float*>(row)[j]));
-}
-
-// Exclusive scan of v over the block; total returned through `total`.
-template <int kWaves>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t s = wsum[w];
-    before += w < wave ? s : 0;
-    tot += s;
-  }
-  total = tot;
-  return before + x - v;
-}
-
-// Exclusive scan of v over one wave.
-__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
-  const int lane = threadIdx.x & 63;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  total = __shfl(x, 63);
-  return x - v;
 }
 
 template <int NT>
@@ -104,68 +45,24 @@ struct Shared {
   static constexpr int kThreads = NT;
   static constexpr int kWaves = NT / 64;
   static constexpr int kBudget = kCap / kWaves;       // per wave segment
-  uint32_t hist[kWaves][256];
+  RadixLds<NT> rx;
   uint32_t wsum[kWaves];
-  uint32_t sel_digit, sel_remain, overflow;
+  uint32_t overflow;
   uint32_t cnt[kWaves];
   uint32_t cand_key[kCap];
   int32_t cand_idx[kCap];
 };
 
 // Radix select of the rank-th largest key among `count` keys produced by
-// get(i).  Returns the key; `remain` = how many keys equal to it are needed to
-// reach rank (so rank - remain keys are strictly greater).
+// get(i) (see radix_select_visit).
 template <int KBITS, int NT, typename Get>
 __device__ uint32_t radix_select(Shared<NT>& sh, int64_t count, uint32_t rank, Get get, uint32_t& remain) {
-  constexpr int kThreads = NT, kWaves = NT / 64;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  uint32_t prefix = 0;
-  remain = rank;
-  for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kWaves * 256; i += kThreads) (&sh.hist[0][0])[i] = 0;
-    __syncthreads();
-    const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
-    for (int64_t j = tid; j < count; j += kThreads) {
-      const uint32_t key = get(j);
-      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 256) {          // per-digit totals of the per-wave histograms
-      uint32_t s = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += sh.hist[w][tid];
-      sh.hist[0][tid] = s;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 4l..4l+3; suffix counts from the top digit down
-      uint32_t c[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = sh.hist[0][4 * tid + i];
-      const uint32_t s = c[0] + c[1] + c[2] + c[3];
-      uint32_t x = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(x, o);
-        if (tid + o < 64) x += y;
-      }
-      uint32_t acc = x - s;                  // keys with a digit above this lane's group
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (acc < remain && remain <= acc + c[i]) {
-          sh.sel_digit = 4 * tid + i;
-          sh.sel_remain = remain - acc;
-        }
-        acc += c[i];
-      }
-    }
-    __syncthreads();
-    prefix |= sh.sel_digit << shift;
-    remain = sh.sel_remain;
-    __syncthreads();
-  }
-  return prefix;
+  return radix_select_visit<KBITS, NT>(
+      sh.rx, rank,
+      [&](auto&& f) {
+        for (int64_t j = threadIdx.x; j < count; j += NT) f(get(j));
+      },
+      remain);
 }
 
 // Ordered emission over `count` keys in index order: writes the selected

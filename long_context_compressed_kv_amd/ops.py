@@ -169,6 +169,32 @@ def topk_select(scores, score_fmt, batch: Batch, m, k, idx=None):
     return idx
 
 
+def indexer_topk_workspace_size(n_q, k):
+    return int(_lib.load().csa_indexer_topk_workspace_size(int(n_q), int(k)))
+
+
+def indexer_topk(qi: KV, n_heads, ki: KV, batch: Batch, m, score_fmt, k, head_w=None,
+                 relu=True, idx=None, workspace=None):
+    """CSA step 2 fused: the top-k entries of each query by indexer score
+    (score_fmt rounding), int32 [n_q, k] ascending, -1 padded, without a score
+    matrix.  `workspace` is a uint8 device tensor of at least
+    indexer_topk_workspace_size(n_q, k) bytes (allocated here when None)."""
+    _need_cuda(head_w, idx, workspace)
+    dev = qi.data.device
+    if idx is None:
+        idx = torch.empty(batch.n_q, k, dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    need = indexer_topk_workspace_size(batch.n_q, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    qc, kc, bc = qi.c(), ki.c(), batch.c()
+    check(lib.csa_indexer_topk(ctypes.byref(qc), int(n_heads), _ptr(head_w), ctypes.byref(kc),
+                               ctypes.byref(bc), int(m), 1 if relu else 0, int(score_fmt), int(k),
+                               _ptr(idx), _ptr(workspace), int(workspace.numel()), _stream()),
+          "csa_indexer_topk")
+    return idx
+
+
 def attn_workspace_size(n_q, n_heads, dim, max_keys, split_keys):
     return int(_lib.load().csa_attn_workspace_size(int(n_q), int(n_heads), int(dim),
                                                    int(max_keys), int(split_keys)))

@@ -130,3 +130,23 @@ def test_merge_and_codec_validation(lib):
     assert lib.csa_quantize(ctypes.byref(dst), ctypes.byref(src), None) == UNSUPPORTED
     assert lib.csa_quantize(ctypes.byref(_t(0, 40, 4)), ctypes.byref(_t(3, 40, 4, scale=FAKE)), None) == BAD_ARG
     assert lib.csa_mxfp4_to_fp8(ctypes.byref(src), FAKE, FAKE, FAKE, None) == BAD_ARG
+
+
+def test_indexer_topk_validation(lib):
+    qi, ki = _t(1, 64, 16), _t(1, 64, 32)
+    bt = _batch()
+    need = lib.csa_indexer_topk_workspace_size(4, 8)
+    assert need >= 4 * 3 * 4 + 4 * 4096 * 8         # per-query state and candidate lists
+    assert lib.csa_indexer_topk_workspace_size(0, 8) == 0
+    f = lambda k=8, ws=FAKE, nbytes=need, b_=bt, sf=1, qi_=qi: lib.csa_indexer_topk(
+        ctypes.byref(qi_), 4, None, ctypes.byref(ki), ctypes.byref(b_), 4, 1, sf, k, FAKE, ws,
+        nbytes, None)
+    WORKSPACE = 3
+    assert f(ws=None) == WORKSPACE
+    assert f(nbytes=need - 1) == WORKSPACE
+    assert f(k=0) == BAD_ARG
+    assert f(k=4097) == BAD_ARG
+    assert f(sf=2) == UNSUPPORTED                       # scores are F32 or BF16
+    assert f(qi_=_t(1, 64, 15)) == BAD_ARG               # rows != n_q * heads
+    assert f(b_=_batch(max_kv=(1 << 20) + 1)) == UNSUPPORTED
+    assert f(ws=ctypes.c_void_p(0x1008)) == BAD_ARG      # workspace not 16-byte aligned
