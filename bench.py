@@ -169,24 +169,24 @@ class Decode:
                 if c == 0:
                     nsum = sum(n_ent)
                     kb = IDX_KEY_BYTES[wl.idx_fmt]
-                    sb = 2 if wl.score_fmt == "bf16" else 4
                     if csa:
-                        self.bytes_idx += nsum * kb + nsum * sb + B * 4 * kb
+                        # indexer keys and queries read, selected indices written
+                        self.bytes_idx += nsum * kb + B * 4 * kb + B * k * 4
                         sel = sum(min(k, n) for n in n_ent)
                     else:
                         sel = nsum
-                    # entries read + window rows + q in + out
-                    self.bytes_step += (nsum * (kb + sb) if csa else 0) + \
+                    # index keys + entries read + window rows + q in + out
+                    self.bytes_step += (nsum * kb if csa else 0) + \
                         sel * ENTRY_BYTES[wl.kv_fmt] + sum(swa_len) * D * 2 + 2 * B * H * D * 2
             self.copies.append(layers)
         self.tokens = B
         self.has_csa = any(s[0] == "csa" for s in specs)
-        self.dominant = {"name": "indexer", "bound": "hbm", "unit": "GB/s",
+        self.dominant = {"name": "indexer_topk", "bound": "hbm", "unit": "GB/s",
                          "work": self.bytes_idx, "peak": PEAK["hbm"],
-                         "per_unit": f"{IDX_KEY_BYTES[wl.idx_fmt]} B key + "
-                                     f"{2 if wl.score_fmt == 'bf16' else 4} B score per "
-                                     f"(request, visible entry)",
-                         "sha": src_sha("indexer.hip", "common.h")}
+                         "per_unit": f"{IDX_KEY_BYTES[wl.idx_fmt]} B key per (request, visible "
+                                     f"entry), plus 4 B per selected index",
+                         "sha": src_sha("itk.hip", "indexer_core.h", "select_core.h",
+                                        "common.h")}
         self.graphs = None
 
     def step_copy(self, c):
@@ -196,7 +196,7 @@ class Decode:
     def dominant_copy(self, c):
         for L in self.copies[c]:
             if L.csa:
-                ops.indexer_score(L.qi, 4, L.ki, L.batch, L.m, L.buf.store["scores"], L.score_fmt)
+                L.select()
 
     def capture(self):
         """One graph per input copy for the whole step, and one per copy for

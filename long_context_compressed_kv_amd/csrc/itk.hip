@@ -5,10 +5,10 @@
 // to memory: only a short list of candidates per query does.
 //
 //   1. itk_sample_kernel: each query scores a sample of its visible entries
-//      (runs of 32 consecutive entries spread evenly over the row) and takes
-//      as threshold the sample key of rank ~3k * sample / n, so that about 3k
-//      entries of the row score at least as high.  Rows of at most `cap`
-//      entries take every entry (threshold 0).
+//      (runs of 32 consecutive entries spread evenly over the row, about
+//      40n/3k of them) and takes as threshold the sample key of rank
+//      ~3k * sample / n, so that about 3k entries of the row score at least
+//      as high.  Rows of at most `cap` entries take every entry (threshold 0).
 //   2. itk_filter_kernel: the indexer's tiles (same grid and arithmetic as
 //      csa_indexer_score); an entry whose order key reaches its query's
 //      threshold is appended, (key, index), to the query's candidate list.
@@ -123,16 +123,23 @@ __device__ __forceinline__ int64_t visible(const ItkArgs& a, int64_t q) {
 
 constexpr int kSampleRun = 32;       // one tile per run
 
-// Grid: one workgroup per query group.  LDS: the sample keys of the group's
-// queries, [8][S] (16-bit keys for bf16 scores, S = 4096; 32-bit for fp32,
-// S = 2048).
+// Grid: one workgroup (8 waves) per query group.  LDS: the sample keys of the
+// group's queries, [8][S] (16-bit keys for bf16 scores, S = 4096; 32-bit for
+// fp32, S = 2048).  A wave loads the keys of STB runs before scoring them.
+template <int FMT> struct SampleTiles { static constexpr int STB = 4; };
+template <> struct SampleTiles<CSA_F32> { static constexpr int STB = 2; };
+template <> struct SampleTiles<CSA_MXFP4> { static constexpr int STB = 8; };
+constexpr int kSampleThreads = 512;
+
 template <int FMT, bool SBF16>
-__global__ __launch_bounds__(256) void itk_sample_kernel(ItkArgs a) {
+__global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
   constexpr int S = SBF16 ? 4096 : 2048;
   constexpr int NRUN = S / kSampleRun;
+  constexpr int NW = kSampleThreads / 64;
+  constexpr int STB = SampleTiles<FMT>::STB;
   using skey_t = typename std::conditional<SBF16, uint16_t, uint32_t>::type;
   __shared__ skey_t sk[8][S];
-  __shared__ RadixLds<256> rx;
+  __shared__ RadixLds<kSampleThreads> rx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
   const int64_t qblock = (int64_t)blockIdx.x * a.qpg;
   const int nq = (int)(a.n_q - qblock < a.qpg ? a.n_q - qblock : a.qpg);
@@ -141,18 +148,30 @@ __global__ __launch_bounds__(256) void itk_sample_kernel(ItkArgs a) {
   // than cap are sampled, over the entries all of them see
   const int64_t n_lo = visible(a, qblock);
   const int64_t n_hi = visible(a, qblock + nq - 1);
+  // runs enough that the threshold is the sample's ~40th key (a relative
+  // spread of about 1/sqrt(40) in the candidate count), at least 16
+  int nrun = (int)((40 * n_lo + 3 * (int64_t)a.k * kSampleRun - 1) / (3 * (int64_t)a.k * kSampleRun));
+  nrun = nrun < 16 ? 16 : (nrun > NRUN ? NRUN : nrun);
+  const int ns = nrun * kSampleRun;        // sample keys
   if (n_hi > a.cap) {
     Group<FMT, 4> gr;
     load_group<FMT, 4>(a, qblock, gr);
-    for (int r = wave; r < NRUN; r += kWaves) {
-      const int64_t j0 = (int64_t)r * (n_lo - kSampleRun) / (NRUN - 1);   // j0 + 32 <= n_lo
-      KeyOp<FMT> kt;
-      load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + j0 + rl, true, half, kt);
-      const f32x16_t acc = tile_dots<FMT>(gr.aq, kt);
+    auto run_start = [&](int r) { return (int64_t)r * (n_lo - kSampleRun) / (nrun - 1); };  // + 32 <= n_lo
+    for (int r0 = wave * STB; r0 < nrun; r0 += NW * STB) {
+      KeyOp<FMT> kt[STB];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 2 * g + half;
-        if (ql < nq) sk[ql][r * kSampleRun + rl] = (skey_t)score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
+      for (int tb = 0; tb < STB; ++tb)
+        load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + run_start(r0 + tb) + rl, r0 + tb < nrun, half, kt[tb]);
+#pragma unroll
+      for (int tb = 0; tb < STB; ++tb) {
+        const int r = r0 + tb;
+        if (r >= nrun) break;
+        const f32x16_t acc = tile_dots<FMT>(gr.aq, kt[tb]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ql = 2 * g + half;
+          if (ql < nq) sk[ql][r * kSampleRun + rl] = (skey_t)score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
+        }
       }
     }
   }
@@ -163,14 +182,14 @@ __global__ __launch_bounds__(256) void itk_sample_kernel(ItkArgs a) {
     uint32_t tau = 0;
     if (n > a.cap) {
       // about 3k of the row's keys reach the sample key of this rank
-      int64_t rank = (3 * (int64_t)a.k * S + n - 1) / n;
+      int64_t rank = (3 * (int64_t)a.k * ns + n - 1) / n;
       if (rank < 1) rank = 1;
-      if (rank > S) rank = S;
+      if (rank > ns) rank = ns;
       uint32_t rem;
-      tau = radix_select_visit<SBF16 ? 16 : 32, 256>(
+      tau = radix_select_visit<SBF16 ? 16 : 32, kSampleThreads>(
           rx, (uint32_t)rank,
           [&](auto&& f) {
-            for (int i = tid; i < S; i += 256) f((uint32_t)sk[ql][i]);
+            for (int i = tid; i < ns; i += kSampleThreads) f((uint32_t)sk[ql][i]);
           },
           rem);
     }
@@ -183,43 +202,55 @@ __global__ __launch_bounds__(256) void itk_sample_kernel(ItkArgs a) {
 
 // ------------------------------------------------------------------ 2. filter
 
-// Grid: x = chunks of entries, y = query groups, as the score kernel.  Pass 1
-// scores the wave's tiles, keeping each lane's keys in registers, and counts
-// the candidates per query; one atomic per query reserves the workgroup's
-// span of the list; pass 2 writes the candidates.
+// Grid: entry chunks and query groups, as the score kernel.  Pass 1
+// scores the wave's tiles into an LDS row of keys per query of the group and
+// counts the candidates per (wave, query); one atomic per query reserves the
+// workgroup's span of the list; pass 2 rescans the LDS rows and writes the
+// candidates (each wave its own entries, so the reserved spans line up).
 template <int FMT, bool SBF16, bool STREAM>
 __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
   constexpr int TB = STREAM ? Tiling<FMT>::TB : 1;
   constexpr int TPW = STREAM ? Tiling<FMT>::TPW : kTilesPerWave;
   constexpr int NG = STREAM ? 1 : 4;
-  __shared__ uint32_t wcnt[kWaves][8];   // candidates per (wave, query)
-  __shared__ uint32_t gbase[8];          // the workgroup's first list slot per query
+  constexpr int QS = STREAM ? 1 : 8;                   // query slots of a group
+  constexpr int EW = TPW * 32;                         // entries per wave
+  using skey_t = typename std::conditional<SBF16, uint16_t, uint32_t>::type;
+  __shared__ skey_t lk[QS][kWaves * EW];
+  __shared__ uint32_t wcnt[kWaves][QS];   // candidates per (wave, query)
+  __shared__ uint32_t gbase[QS];          // the workgroup's first list slot per query
+  __shared__ uint32_t stau[QS];           // the queries' thresholds
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
 
-  const int64_t qblock = (int64_t)blockIdx.y * a.qpg;
+  // several queries per group (prefill): x = query group, y = entry chunk,
+  // so the groups reading one chunk of keys run together and share it in L2;
+  // streaming: x = entry chunk, y = query
+  const unsigned bq = STREAM ? blockIdx.y : blockIdx.x, be = STREAM ? blockIdx.x : blockIdx.y;
+  const int64_t qblock = (int64_t)bq * a.qpg;
   Group<FMT, NG> gr;
   load_group<FMT, NG>(a, qblock, gr);
   int64_t q_hi = qblock + a.qpg - 1;
   if (q_hi >= a.n_q) q_hi = a.n_q - 1;
   const int64_t n_scan = visible(a, q_hi);
+  const int64_t e_wg = (int64_t)be * (kWaves * EW);
+  const int e_wave = wave * EW;
+  if (e_wg >= n_scan) return;            // the whole workgroup: no barrier reached
+
+  // pass 1: keys into LDS, candidate counts per query in this lane
   uint32_t tau[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) tau[g] = gr.nv[g] > 0 ? a.tau[qblock + 2 * g + half] : 0u;
-
-  const int64_t e_wg = (int64_t)blockIdx.x * entries_per_wg<FMT>(STREAM);
-  const int e_wave = wave * (TPW * 32);
-  if (e_wg >= n_scan) return;            // the whole workgroup: no barrier reached
-
-  // pass 1: keys of this lane's entries (one per tile), candidate flags
-  uint32_t key[TPW][NG];
-  uint32_t flags = 0;                    // bit t*NG + g
+  uint32_t c[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) c[g] = 0;
   auto score_tile = [&](int t, const KeyOp<FMT>& k) {
-    const int64_t e = e_wg + e_wave + t * 32 + rl;
+    const int el = e_wave + t * 32 + rl;
     const f32x16_t acc = tile_dots<FMT>(gr.aq, k);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      key[t][g] = score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
-      if (e < gr.nv[g] && key[t][g] >= tau[g]) flags |= 1u << (t * NG + g);
+      const int ql = 2 * g + half;
+      const uint32_t key = score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
+      if (ql < QS) lk[ql][el] = (skey_t)key;
+      c[g] += (e_wg + el < gr.nv[g] && key >= tau[g]) ? 1u : 0u;
     }
   };
   auto tile_live = [&](int t) { return e_wg + e_wave + t * 32 < n_scan; };
@@ -240,7 +271,6 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
     if (tile_live(0)) {
       KeyOp<FMT> k0[TB], k1[TB];
       load_batch(0, k0);
-#pragma unroll
       for (int b = 0; b < NB; b += 2) {
         const bool l1 = b + 1 < NB && tile_live((b + 1) * TB);
         if (l1) load_batch(b + 1, k1);
@@ -253,7 +283,8 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       }
     }
   } else {
-#pragma unroll
+    // one tile at a time: occupancy hides the loads (more in flight per wave
+    // measured slower)
     for (int t = 0; t < TPW; ++t) {
       if (!tile_live(t)) break;
       KeyOp<FMT> kt;
@@ -262,57 +293,50 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       score_tile(t, kt);
     }
   }
-
-  // candidates per (wave, query): lanes 0-31 hold query 2g, lanes 32-63
+  // sums over each half of the wave: lanes 0-31 count query 2g, lanes 32-63
   // query 2g + 1 of register block g
-  uint32_t wq[NG][2];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    uint32_t c = 0;
+    uint32_t x = c[g];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) c += (flags >> (t * NG + g)) & 1u;
-    // sums over each half of the wave
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) c += __shfl_xor(c, o);
-    wq[g][0] = __shfl(c, 0);
-    wq[g][1] = __shfl(c, 32);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      wcnt[wave][2 * g] = wq[g][0];
-      wcnt[wave][2 * g + 1] = wq[g][1];
-    }
+    for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+    const int ql = 2 * g + half;
+    if (rl == 0 && ql < QS) wcnt[wave][ql] = x;
   }
   __syncthreads();
-  if (tid < 2 * NG && tid < a.qpg && qblock + tid < a.n_q) {
+  if (tid < QS && qblock + tid < a.n_q) {
     uint32_t tot = 0;
     for (int w = 0; w < kWaves; ++w) tot += wcnt[w][tid];
     gbase[tid] = tot > 0 ? atomicAdd(&a.cnt[qblock + tid], tot) : 0u;
+    stau[tid] = a.tau[qblock + tid];
   }
   __syncthreads();
 
-  // pass 2: write the candidates (slots past cap are dropped; the count
-  // still records them, which sends the row to the exact redo)
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int ql = 2 * g + half;
-    if (ql >= a.qpg || qblock + ql >= a.n_q) continue;
+  // pass 2: each wave writes its entries' candidates, query by query (slots
+  // past cap are dropped; the count still records them, which sends the row
+  // to the exact redo)
+  for (int ql = 0; ql < QS; ++ql) {
+    const int64_t q = qblock + ql;
+    if (q >= a.n_q || wcnt[wave][ql] == 0) continue;   // uniform over the wave
+    // visible entries of the group's query ql (consecutive positions of one
+    // request, as load_group counts them)
+    int64_t nvq = (gr.qm.t + ql + 1) / a.m;
+    if (nvq > gr.qm.kv_len) nvq = gr.qm.kv_len;
+    if (nvq > a.max_n) nvq = a.max_n;
+    const uint32_t tq = stau[ql];
     uint32_t base = gbase[ql];
     for (int w = 0; w < wave; ++w) base += wcnt[w][ql];
-    uint2* list = a.cand + (qblock + ql) * (int64_t)a.cap;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const bool f = (flags >> (t * NG + g)) & 1u;
+    uint2* list = a.cand + q * (int64_t)a.cap;
+    for (int i = 0; i < EW; i += 64) {
+      const int el = e_wave + i + lane;
+      const uint32_t key = lk[ql][el];
+      const bool f = e_wg + el < nvq && key >= tq;
       const uint64_t m = __ballot(f);
-      const uint32_t mh = (uint32_t)(m >> (32 * half));
-      const uint32_t before = __builtin_popcount(mh & ((1u << rl) - 1u));
       if (f) {
-        const uint32_t slot = base + before;
-        if (slot < (uint32_t)a.cap)
-          list[slot] = make_uint2(key[t][g], (uint32_t)(e_wg + e_wave + t * 32 + rl));
+        const uint32_t slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+        if (slot < (uint32_t)a.cap) list[slot] = make_uint2(key, (uint32_t)(e_wg + el));
       }
-      base += __builtin_popcount(mh);
+      base += __builtin_popcountll(m);
     }
   }
 }
@@ -383,8 +407,10 @@ __device__ void mark_top(SelectLds<NT>& sh, uint32_t* bm, int nwords, uint32_t t
   __syncthreads();
 }
 
-// Grid: one workgroup per query.
-template <bool SBF16, int NT>
+// Grid: one workgroup per query.  A list of at most CPT * NT candidates is
+// read once into registers (CPT per thread); a longer one is read from memory
+// at every pass.
+template <bool SBF16, int NT, int CPT>
 __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   constexpr int KBITS = SBF16 ? 16 : 32;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -404,18 +430,34 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   if (tid == 0) a.redo[q] = miss ? 1u : 0u;
   if (miss) return;
   const uint2* list = a.cand + q * (int64_t)a.cap;
-  auto visit = [&](auto&& f) {
-    for (uint32_t i = tid; i < c; i += NT) {
-      const uint2 ce = list[i];
-      f(ce.x, ce.y);
-    }
-  };
-  uint32_t need;
-  const uint32_t tau = radix_select_visit<KBITS, NT>(
-      sh.rx, (uint32_t)a.k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need);
   const int nwords = (int)((n + 31) / 32);
-  mark_top<KBITS, NT>(sh, bm, nwords, tau, need, visit);
-  emit_bitmap<NT>(bm, nwords, sh.wsum, out, a.k);
+  auto select = [&](auto&& visit) {
+    uint32_t need;
+    const uint32_t tau = radix_select_visit<KBITS, NT>(
+        sh.rx, (uint32_t)a.k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need);
+    mark_top<KBITS, NT>(sh, bm, nwords, tau, need, visit);
+    emit_bitmap<NT>(bm, nwords, sh.wsum, out, a.k);
+  };
+  if (c <= (uint32_t)(CPT * NT)) {
+    uint2 cr[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const uint32_t i = tid + j * NT;
+      cr[j] = i < c ? list[i] : make_uint2(0, 0);
+    }
+    select([&](auto&& f) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        if (tid + j * NT < c) f(cr[j].x, cr[j].y);
+    });
+  } else {
+    select([&](auto&& f) {
+      for (uint32_t i = tid; i < c; i += NT) {
+        const uint2 ce = list[i];
+        f(ce.x, ce.y);
+      }
+    });
+  }
 }
 
 // ------------------------------------------------------------------ 4. redo
@@ -462,27 +504,41 @@ __global__ __launch_bounds__(256) void itk_redo_kernel(ItkArgs a) {
   emit_bitmap<256>(bm, nwords, sh.wsum, out, a.k);
 }
 
+template <bool SBF16, int NT>
+csa_status launch_select(const ItkArgs& a, size_t bm_bytes, hipStream_t s) {
+  constexpr int CPT = 6144 / NT;         // the list of k <= 1024 fits the registers
+  auto kern = itk_select_kernel<SBF16, NT, CPT>;
+  const size_t lds = sizeof(SelectLds<NT>) + bm_bytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (lds > 64 * 1024 && attr != hipSuccess)
+    return csa_host::fail(CSA_ERR_HIP, "csa_indexer_topk: cannot reserve %zu B of LDS", lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_q), dim3(NT), lds, s, a);
+  return csa_host::check_launch("csa_indexer_topk (select)");
+}
+
 template <int FMT, bool SBF16>
 csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   const int64_t groups = (a.n_q + a.qpg - 1) / a.qpg;
   const bool stream = a.qpg == 1;
-  hipLaunchKernelGGL((itk_sample_kernel<FMT, SBF16>), dim3((unsigned)groups), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((itk_sample_kernel<FMT, SBF16>), dim3((unsigned)groups), dim3(kSampleThreads), 0, s, a);
   csa_status st = csa_host::check_launch("csa_indexer_topk (sample)");
   if (st != CSA_OK) return st;
   const int64_t epw = entries_per_wg<FMT>(stream);
-  const dim3 fgrid((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups);
+  const dim3 fgrid = stream ? dim3((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups)
+                            : dim3((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
   if (stream) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true>), fgrid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false>), fgrid, dim3(256), 0, s, a);
   st = csa_host::check_launch("csa_indexer_topk (filter)");
   if (st != CSA_OK) return st;
   const size_t bm_bytes = (size_t)((max_kv < kBitmapMax ? max_kv : kBitmapMax) + 31) / 32 * 4;
-  const size_t sel_lds = sizeof(SelectLds<1024>) + bm_bytes;
-  static const hipError_t attr1 = hipFuncSetAttribute(
-      (const void*)itk_select_kernel<SBF16, 1024>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (sel_lds > 64 * 1024 && attr1 != hipSuccess)
-    return csa_host::fail(CSA_ERR_HIP, "csa_indexer_topk: cannot reserve %zu B of LDS", sel_lds);
-  hipLaunchKernelGGL((itk_select_kernel<SBF16, 1024>), dim3((unsigned)a.n_q), dim3(1024), sel_lds, s, a);
-  st = csa_host::check_launch("csa_indexer_topk (select)");
+  // few rows (decode): 16 waves per row; many: 4, so several rows share a CU
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (a.n_q < 2 * (int64_t)cus) st = launch_select<SBF16, 1024>(a, bm_bytes, s);
+  else st = launch_select<SBF16, 256>(a, bm_bytes, s);
   if (st != CSA_OK) return st;
   const size_t redo_lds = sizeof(SelectLds<256>) + bm_bytes;
   static const hipError_t attr2 = hipFuncSetAttribute(
@@ -564,7 +620,8 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
   const int64_t groups = (batch->n_q + a.qpg - 1) / a.qpg;
   const int64_t max_kv = batch->max_kv < ki->rows ? batch->max_kv : ki->rows;
   a.max_n = max_kv;
-  if (groups > 0x7fffffff || (max_kv + 1023) / 1024 > 0x7fffffff || groups > 65535)
+  // (grid y: the queries when streaming; else the entry chunks, at most 1024)
+  if (groups > 0x7fffffff || (a.qpg == 1 && groups > 65535))
     return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: problem too large for one launch");
   const bool sb = score_fmt == CSA_BF16;
   if (qi->fmt == CSA_F32) return sb ? launch_all<CSA_F32, true>(a, max_kv, stream) : launch_all<CSA_F32, false>(a, max_kv, stream);

@@ -1,12 +1,13 @@
 """One CSA or HCA layer as a sequence of library calls (plumbing only).
 
 Prefill (one sequence):
-  CSA: kv_compress (new entries into the cache) -> indexer_score -> topk_select
+  CSA: kv_compress (new entries into the cache) -> indexer_topk (scores and
+       selection fused; or indexer_score -> topk_select with fused=False)
        -> sparse_mqa_attn over the selected entries and the window, one softmax
   HCA: kv_compress -> sparse_mqa_attn over all visible entries and the window
 Decode (a batch of requests, one query each):
-  CSA: indexer_score -> topk_select -> sparse_mqa_attn(selected entries and
-       window, split into key chunks merged by log-sum-exp)
+  CSA: indexer_topk (or indexer_score -> topk_select) -> sparse_mqa_attn(selected
+       entries and window, split into key chunks merged by log-sum-exp)
   HCA: sparse_mqa_attn(visible entries and window, split the same way)
 (page "DeepSeek V4 深度解析", section 2: the three CSA steps and HCA).
 """
@@ -42,6 +43,22 @@ class Buffers:
         return t
 
 
+def _select(L, n_q, ld):
+    """CSA step 2 for a layer L with n_q queries and rows of at most ld entries:
+    the fused call, or the score matrix and the selection over it."""
+    idx = L.buf.get("idx", (n_q, L.k), torch.int32)
+    if L.fused:
+        ws = L.buf.get("itk_ws", (max(ops.indexer_topk_workspace_size(n_q, L.k), 1),),
+                       torch.uint8)
+        ops.indexer_topk(L.qi, INDEXER_HEADS, L.ki, L.batch, L.m, L.score_fmt, L.k, idx=idx,
+                         workspace=ws)
+        return None, idx
+    scores = L.buf.get("scores", (n_q, ld), _score_dtype(L.score_fmt))
+    ops.indexer_score(L.qi, INDEXER_HEADS, L.ki, L.batch, L.m, scores, L.score_fmt)
+    ops.topk_select(scores, L.score_fmt, L.batch, L.m, L.k, idx)
+    return scores, idx
+
+
 # ---------------------------------------------------------------- prefill
 
 
@@ -75,6 +92,7 @@ class PrefillLayer:
     ki: Optional[KV] = None
     score_fmt: int = F32
     out_fmt: int = F32
+    fused: bool = True
     buf: Buffers = field(default_factory=Buffers)
 
     def __post_init__(self):
@@ -92,13 +110,8 @@ class PrefillLayer:
                         self.first_new, n_new, self.cache.narrow(self.first_new, max(n_new, 0)))
 
     def select(self):
-        ld = self.n_entries
-        scores = self.buf.get("scores", (self.T, ld), _score_dtype(self.score_fmt))
-        ops.indexer_score(self.qi, INDEXER_HEADS, self.ki, self.batch, self.m, scores,
-                          self.score_fmt)
-        idx = self.buf.get("idx", (self.T, self.k), torch.int32)
-        ops.topk_select(scores, self.score_fmt, self.batch, self.m, self.k, idx)
-        return scores, idx
+        """(scores, or None when fused; idx [T, k])"""
+        return _select(self, self.T, self.n_entries)
 
     def attend(self, idx):
         out = self.buf.get("out", (self.T * self.H, self.q.dim), _out_dtype(self.out_fmt))
@@ -140,6 +153,7 @@ class DecodeLayer:
     score_fmt: int = BF16
     out_fmt: int = BF16
     split_keys: int = 128
+    fused: bool = True
     buf: Buffers = field(default_factory=Buffers)
 
     def __post_init__(self):
@@ -152,12 +166,8 @@ class DecodeLayer:
         self.ld = max(int(x) for x in self.n_entries)
 
     def select(self):
-        scores = self.buf.get("scores", (self.B, self.ld), _score_dtype(self.score_fmt))
-        ops.indexer_score(self.qi, INDEXER_HEADS, self.ki, self.batch, self.m, scores,
-                          self.score_fmt)
-        idx = self.buf.get("idx", (self.B, self.k), torch.int32)
-        ops.topk_select(scores, self.score_fmt, self.batch, self.m, self.k, idx)
-        return scores, idx
+        """(scores, or None when fused; idx [B, k])"""
+        return _select(self, self.B, self.ld)
 
     def attend(self, idx):
         """One attention call over entries and window together, its keys cut

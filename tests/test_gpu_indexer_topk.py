@@ -63,6 +63,7 @@ def test_fused_equals_unfused_decode(fmt, score_fmt):
     ("bf16", "bf16", 512, 67, 30000, True, True),     # every row sampled
     ("f32", "f32", 100, 29, 20000, False, True),      # no ReLU: negative scores too
     ("mxfp4", "f32", 8, 70, 0, True, False),          # from position 0: short rows
+    ("bf16", "bf16", 64, 600, 20000, True, False),    # many rows: the narrow select
 ])
 def test_fused_equals_unfused_prefill(fmt, score_fmt, k, T, pos0, relu, weights):
     rng = np.random.default_rng(62 + k)
