@@ -778,13 +778,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, nm));
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) psum += p[i];
-    l_run += psum;
 
     // O^T += V^T P^T
     if constexpr (F32C) {
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) psum += p[i];
+      l_run += psum;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const float* vp = reinterpret_cast<const float*>(kb) + d0 + db * 32 + ql;
@@ -807,6 +807,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
         u.w = pack_bf16x2_fast(p[8 * c + 6], p[8 * c + 7]);
         pb[c] = __builtin_bit_cast(bf16x8_t, u);
       }
+      // the row sum of the probabilities as rounded for the product (two per
+      // dot-product instruction), so the normaliser sums the weights applied
+      float psum = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 u = __builtin_bit_cast(uint4, pb[c]);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w[j]),
+                                                 __builtin_bit_cast(bf16x2_v, 0x3f803f80u), psum, false);
+      }
+      l_run += psum;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll

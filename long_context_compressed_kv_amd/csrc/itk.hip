@@ -16,10 +16,10 @@
 //   3. itk_select_kernel: per query, an exact radix select of the k-th
 //      largest candidate key, ties resolved to the lowest indices by a radix
 //      select over the tied indices, the chosen entries marked in an LDS
-//      bitmap of the row and read back in index order.
-//   4. itk_redo_kernel: a row whose candidates overflowed `cap` or fell short
-//      of k (the sample misjudged it, e.g. masses of equal scores) is redone
-//      exactly from recomputed scores; every other row exits at once.
+//      bitmap of the row and read back in index order.  A row whose
+//      candidates overflowed `cap` or fell short of k (the sample misjudged
+//      it, e.g. masses of equal scores) is redone there exactly from
+//      recomputed scores.
 // The candidates arrive in no fixed order, but every step after the filter
 // depends only on the candidate set, so the output is deterministic.
 #include <type_traits>
@@ -33,7 +33,7 @@ namespace {
 
 constexpr int kWaves = 4;            // waves of the scoring kernels
 constexpr int kTilesPerWave = 8;     // tiles per wave, several queries per group
-constexpr int kBitmapMax = 1 << 20;  // longest row the select and redo kernels take
+constexpr int kBitmapMax = 1 << 20;  // longest row the select kernel takes
 
 struct ItkArgs {
   const void* qi;
@@ -51,7 +51,6 @@ struct ItkArgs {
   int64_t max_n;      // rows are cut to this many entries (the batch's max_kv, at most 2^20)
   uint32_t* tau;      // [n_q] threshold keys
   uint32_t* cnt;      // [n_q] candidates found (may exceed cap)
-  uint32_t* redo;     // [n_q] 1 = the row is redone exactly
   uint2* cand;        // [n_q][cap] (key, entry)
   int32_t* idx;       // [n_q][k] result
 };
@@ -370,27 +369,25 @@ template <int NT>
 struct SelectLds {
   RadixLds<NT> rx;
   uint32_t wsum[NT / 64];
-  uint32_t n_eq;
 };
 
-// Marks the chosen entries of a row in the bitmap: every key above tau and,
-// among the keys equal to tau, the `need` with the lowest indices.  visit(f)
-// calls f(key, entry) for this thread's share of the row's keys (candidates
-// or the whole row).  The bitmap (nwords words) is cleared here.
+// The exact top-k of a row whose keys visit(f) produces (f(key, entry), each
+// thread its share; every thread calls it): the k-th largest key tau by radix
+// select, ties to the lowest entries by a radix select over their
+// complemented indices, the chosen entries marked in the LDS bitmap (nwords
+// words, cleared here) and written in index order to out[0..k).
 template <int KBITS, int NT, typename Visit>
-__device__ void mark_top(SelectLds<NT>& sh, uint32_t* bm, int nwords, uint32_t tau, uint32_t need,
-                         Visit visit) {
+__device__ void select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, int32_t* out,
+                           Visit visit) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.n_eq = 0;
+  uint32_t need, n_eq;
+  const uint32_t tau = radix_select_visit<KBITS, NT>(
+      sh.rx, (uint32_t)k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need,
+      &n_eq);
   for (int w = tid; w < nwords; w += NT) bm[w] = 0;
-  __syncthreads();
-  uint32_t my_eq = 0;
-  visit([&](uint32_t key, uint32_t e) { my_eq += key == tau ? 1u : 0u; });
-  if (my_eq) atomicAdd(&sh.n_eq, my_eq);
-  __syncthreads();
   // the need-th lowest tied index is the need-th largest of the complements
   uint32_t iota = 0xffffffffu;
-  if (need < sh.n_eq) {
+  if (need < n_eq) {
     uint32_t rem;
     iota = ~radix_select_visit<32, NT>(
         sh.rx, need,
@@ -401,18 +398,23 @@ __device__ void mark_top(SelectLds<NT>& sh, uint32_t* bm, int nwords, uint32_t t
         },
         rem);
   }
+  __syncthreads();
   visit([&](uint32_t key, uint32_t e) {
     if (key > tau || (key == tau && e <= iota)) atomicOr(&bm[e >> 5], 1u << (e & 31));
   });
   __syncthreads();
+  emit_bitmap<NT>(bm, nwords, sh.wsum, out, k);
 }
 
 // Grid: one workgroup per query.  A list of at most CPT * NT candidates is
 // read once into registers (CPT per thread); a longer one is read from memory
-// at every pass.
-template <bool SBF16, int NT, int CPT>
+// at every pass.  A row whose list overflowed or fell short of k is redone
+// here exactly: its keys are recomputed tile by tile for every pass (the query
+// in its group's slot, so the arithmetic is the score kernel's).
+template <int FMT, bool SBF16, int NT, int CPT>
 __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   constexpr int KBITS = SBF16 ? 16 : 32;
+  constexpr int NW = NT / 64;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SelectLds<NT>& sh = *reinterpret_cast<SelectLds<NT>*>(smem_raw);
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SelectLds<NT>));
@@ -422,22 +424,35 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   int32_t* out = a.idx + q * (int64_t)a.k;
   if (n <= a.k) {
     for (int64_t j = tid; j < a.k; j += NT) out[j] = j < n ? (int32_t)j : -1;
-    if (tid == 0) a.redo[q] = 0;
     return;
   }
-  const uint32_t c = a.cnt[q];
-  const bool miss = c > (uint32_t)a.cap || c < (uint32_t)a.k;
-  if (tid == 0) a.redo[q] = miss ? 1u : 0u;
-  if (miss) return;
-  const uint2* list = a.cand + q * (int64_t)a.cap;
   const int nwords = (int)((n + 31) / 32);
-  auto select = [&](auto&& visit) {
-    uint32_t need;
-    const uint32_t tau = radix_select_visit<KBITS, NT>(
-        sh.rx, (uint32_t)a.k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need);
-    mark_top<KBITS, NT>(sh, bm, nwords, tau, need, visit);
-    emit_bitmap<NT>(bm, nwords, sh.wsum, out, a.k);
-  };
+  const uint32_t c = a.cnt[q];
+  if (c > (uint32_t)a.cap || c < (uint32_t)a.k) {
+    // the exact redo over the whole row
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
+    const int64_t qblock = q / a.qpg * a.qpg;
+    const int slot = (int)(q - qblock);
+    Group<FMT, 4> gr;
+    load_group<FMT, 4>(a, qblock, gr);
+    const int gs = slot >> 1;             // register block of the query
+    const bool mine = (slot & 1) == half; // lanes of the query's half
+    select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
+      for (int64_t t0 = (int64_t)wave * 32; t0 < n; t0 += NW * 32) {
+        const int64_t e = t0 + rl;
+        KeyOp<FMT> kt;
+        load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n, half, kt);
+        const f32x16_t acc = tile_dots<FMT>(gr.aq, kt);
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (g == gs) s = head_score(acc, g, gr.hw[g], a.relu);
+        if (mine && e < n) f(score_key<SBF16>(s), (uint32_t)e);
+      }
+    });
+    return;
+  }
+  const uint2* list = a.cand + q * (int64_t)a.cap;
   if (c <= (uint32_t)(CPT * NT)) {
     uint2 cr[CPT];
 #pragma unroll
@@ -445,13 +460,13 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
       const uint32_t i = tid + j * NT;
       cr[j] = i < c ? list[i] : make_uint2(0, 0);
     }
-    select([&](auto&& f) {
+    select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
 #pragma unroll
       for (int j = 0; j < CPT; ++j)
         if (tid + j * NT < c) f(cr[j].x, cr[j].y);
     });
   } else {
-    select([&](auto&& f) {
+    select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
       for (uint32_t i = tid; i < c; i += NT) {
         const uint2 ce = list[i];
         f(ce.x, ce.y);
@@ -460,54 +475,10 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ 4. redo
-
-// Grid: one workgroup per query; rows not flagged return at once.  The row's
-// keys are recomputed tile by tile (the query in its group's slot, so the
-// arithmetic is the score kernel's) for each pass of the selection.
-template <int FMT, bool SBF16>
-__global__ __launch_bounds__(256) void itk_redo_kernel(ItkArgs a) {
-  constexpr int KBITS = SBF16 ? 16 : 32;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  SelectLds<256>& sh = *reinterpret_cast<SelectLds<256>*>(smem_raw);
-  uint32_t* bm = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SelectLds<256>));
-  const int64_t q = blockIdx.x;
-  if (a.redo[q] == 0) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, rl = lane & 31;
-  const int64_t n = visible(a, q);
-  int32_t* out = a.idx + q * (int64_t)a.k;
-  const int64_t qblock = q / a.qpg * a.qpg;
-  const int slot = (int)(q - qblock);
-  Group<FMT, 4> gr;
-  load_group<FMT, 4>(a, qblock, gr);
-  const int gs = slot >> 1;             // register block of the query
-  const bool mine = (slot & 1) == half; // lanes of the query's half
-  // f(key, entry) for every entry of the row, each lane its own
-  auto visit = [&](auto&& f) {
-    for (int64_t t0 = (int64_t)wave * 32; t0 < n; t0 += kWaves * 32) {
-      const int64_t e = t0 + rl;
-      KeyOp<FMT> kt;
-      load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n, half, kt);
-      const f32x16_t acc = tile_dots<FMT>(gr.aq, kt);
-      float s = 0.0f;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        if (g == gs) s = head_score(acc, g, gr.hw[g], a.relu);
-      if (mine && e < n) f(score_key<SBF16>(s), (uint32_t)e);
-    }
-  };
-  uint32_t need;
-  const uint32_t tau = radix_select_visit<KBITS, 256>(
-      sh.rx, (uint32_t)a.k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need);
-  const int nwords = (int)((n + 31) / 32);
-  mark_top<KBITS, 256>(sh, bm, nwords, tau, need, visit);
-  emit_bitmap<256>(bm, nwords, sh.wsum, out, a.k);
-}
-
-template <bool SBF16, int NT>
+template <int FMT, bool SBF16, int NT>
 csa_status launch_select(const ItkArgs& a, size_t bm_bytes, hipStream_t s) {
   constexpr int CPT = 6144 / NT;         // the list of k <= 1024 fits the registers
-  auto kern = itk_select_kernel<SBF16, NT, CPT>;
+  auto kern = itk_select_kernel<FMT, SBF16, NT, CPT>;
   const size_t lds = sizeof(SelectLds<NT>) + bm_bytes;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -537,16 +508,8 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  if (a.n_q < 2 * (int64_t)cus) st = launch_select<SBF16, 1024>(a, bm_bytes, s);
-  else st = launch_select<SBF16, 256>(a, bm_bytes, s);
-  if (st != CSA_OK) return st;
-  const size_t redo_lds = sizeof(SelectLds<256>) + bm_bytes;
-  static const hipError_t attr2 = hipFuncSetAttribute(
-      (const void*)itk_redo_kernel<FMT, SBF16>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (redo_lds > 64 * 1024 && attr2 != hipSuccess)
-    return csa_host::fail(CSA_ERR_HIP, "csa_indexer_topk: cannot reserve %zu B of LDS", redo_lds);
-  hipLaunchKernelGGL((itk_redo_kernel<FMT, SBF16>), dim3((unsigned)a.n_q), dim3(256), redo_lds, s, a);
-  return csa_host::check_launch("csa_indexer_topk (redo)");
+  if (a.n_q < 2 * (int64_t)cus) return launch_select<FMT, SBF16, 1024>(a, bm_bytes, s);
+  return launch_select<FMT, SBF16, 256>(a, bm_bytes, s);
 }
 
 // candidates kept per query: the threshold aims at about 3k
@@ -561,8 +524,8 @@ using namespace csa_host;
 
 extern "C" size_t csa_indexer_topk_workspace_size(int64_t n_q, int32_t k) {
   if (n_q <= 0 || k < 1) return 0;
-  // tau, cnt and redo per query, then the candidate lists (8-byte aligned)
-  const size_t head = ((size_t)n_q * 3 * 4 + 15) / 16 * 16;
+  // tau and cnt per query, then the candidate lists (16-byte aligned)
+  const size_t head = ((size_t)n_q * 2 * 4 + 15) / 16 * 16;
   return head + (size_t)n_q * (size_t)cap_for(k) * 8;
 }
 
@@ -614,8 +577,7 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
   char* ws = static_cast<char*>(workspace);
   a.tau = reinterpret_cast<uint32_t*>(ws);
   a.cnt = a.tau + batch->n_q;
-  a.redo = a.cnt + batch->n_q;
-  a.cand = reinterpret_cast<uint2*>(ws + ((size_t)batch->n_q * 3 * 4 + 15) / 16 * 16);
+  a.cand = reinterpret_cast<uint2*>(ws + ((size_t)batch->n_q * 2 * 4 + 15) / 16 * 16);
   a.idx = idx;
   const int64_t groups = (batch->n_q + a.qpg - 1) / a.qpg;
   const int64_t max_kv = batch->max_kv < ki->rows ? batch->max_kv : ki->rows;

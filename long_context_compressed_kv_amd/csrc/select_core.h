@@ -82,9 +82,11 @@ struct RadixLds {
 // this thread contributes; every thread of the block calls it (the keys of
 // all threads together form the multiset).  Returns the key; `remain` = how
 // many keys equal to it are needed to reach rank (rank - remain keys are
-// strictly greater).  1 <= rank <= the multiset's size.
+// strictly greater) and, if n_equal is given, *n_equal = how many keys equal
+// it.  1 <= rank <= the multiset's size.
 template <int KBITS, int NT, typename Visit>
-__device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit visit, uint32_t& remain) {
+__device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit visit, uint32_t& remain,
+                                       uint32_t* n_equal = nullptr) {
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -130,6 +132,8 @@ __device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit vi
     __syncthreads();
     prefix |= sh.sel_digit << shift;
     remain = sh.sel_remain;
+    // after the last digit, its bin counts the keys equal to the result
+    if (shift == 0 && n_equal != nullptr) *n_equal = sh.hist[0][sh.sel_digit];
     __syncthreads();
   }
   return prefix;

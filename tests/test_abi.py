@@ -136,7 +136,7 @@ def test_indexer_topk_validation(lib):
     qi, ki = _t(1, 64, 16), _t(1, 64, 32)
     bt = _batch()
     need = lib.csa_indexer_topk_workspace_size(4, 8)
-    assert need >= 4 * 3 * 4 + 4 * 4096 * 8         # per-query state and candidate lists
+    assert need >= 4 * 2 * 4 + 4 * 4096 * 8         # per-query state and candidate lists
     assert lib.csa_indexer_topk_workspace_size(0, 8) == 0
     f = lambda k=8, ws=FAKE, nbytes=need, b_=bt, sf=1, qi_=qi: lib.csa_indexer_topk(
         ctypes.byref(qi_), 4, None, ctypes.byref(ki), ctypes.byref(b_), 4, 1, sf, k, FAKE, ws,
