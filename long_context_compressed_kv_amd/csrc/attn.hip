@@ -174,24 +174,61 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Split-K work list.  One chunk size for the whole batch: at least the
-// caller's split_keys (and enough that no query needs more than max_splits),
-// raised so the batch's keys form about target_items items; then the splits
-// of every query, their prefix sums and the query of every item, so the
-// attention grid visits only real items.
+// Sum of v over the 64 lanes of a wave (every lane active): an inclusive scan
+// by row shifts within each row of 16 lanes, then row broadcasts across rows,
+// whose last lane holds the total.
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);    // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);    // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);    // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);    // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Items a query of n keys makes at chunk c (rc about 1/c, within an ulp or
+// two): ceil(n / c) from a float estimate, corrected by one either way (n, c <
+// 2^24 keep the estimate within one), and one item for a query with no keys.
+__device__ __forceinline__ int plan_splits(int n, float fn, int c, float rc) {
+  int d = (int)ceilf(fn * rc);
+  const int lo = d * c;
+  d += (int)(lo < n) - ((int)(d > 0) & (int)(lo - c >= n));
+  return n > 0 ? d : 1;
+}
+
+// Split-K work list.  One chunk size (a multiple of the key tile) for the
+// whole batch, at least the caller's split_keys and enough that no query
+// needs more than max_splits.  With the key counts of at most kPlanQ queries
+// at hand, the chunk is the one that minimises the longest workgroup's work,
+// ceil(items / workgroups) * (chunk + kItemCost), where a query of n keys
+// makes ceil(n / chunk) items (fewer items on a tie: less to merge), and
+// kItemCost keys stand for an item's fixed costs; the candidates are every
+// tile multiple from the smallest chunk to the longest query, thinned to a
+// coarser step when candidates times queries would pass kPlanEvals.
+// Otherwise the chunk is raised so the batch's keys form about target_items
+// items.  Then the splits of every query, their prefix sums and the query of
+// every item, so the attention grid visits only real items.
+constexpr int kPlanQ = 4096;
+constexpr int kItemCost = 96;
+constexpr int kPlanEvals = 1 << 16;
 template <bool SPARSE>
 __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
   __shared__ int wsum[16];
   __shared__ int64_t ksum[16];
   __shared__ int carry;
   __shared__ int chunk_s;
+  __shared__ int nks[kPlanQ];
+  __shared__ unsigned long long best[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool keep = a.n_q <= kPlanQ;   // key counts kept in LDS
   // pass 1: geometry records, total and longest key counts
   int64_t tot = 0;
   int kmax = 0;
   for (int64_t q = tid; q < a.n_q; q += 1024) {
     const Geo g = make_geo<SPARSE>(a, q);
     store_geo(a.ws_geo + q * 4, g);
+    if (keep) nks[q] = g.nkeys;
     tot += g.nkeys;
     kmax = g.nkeys > kmax ? g.nkeys : kmax;
   }
@@ -206,31 +243,75 @@ __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
     wsum[wave] = kmax;
   }
   __syncthreads();
-  if (tid == 0) {
-    int64_t t = 0;
-    int km = 0;
-    for (int w = 0; w < 16; ++w) {
-      t += ksum[w];
-      km = wsum[w] > km ? wsum[w] : km;
+  int64_t t = 0;
+  int km = 0;
+  for (int w = 0; w < 16; ++w) {
+    t += ksum[w];
+    km = wsum[w] > km ? wsum[w] : km;
+  }
+  int64_t c_min = a.split_keys;
+  const int64_t need = (km + a.max_splits - 1) / a.max_splits;
+  if (need > c_min) c_min = need;
+  c_min = (c_min + KT - 1) / KT * KT;
+  const int64_t c_max = ((int64_t)km + KT - 1) / KT * KT;   // one item per query
+  if (keep && a.target_items > 0 && c_max > c_min) {
+    const int nq = (int)a.n_q;
+    int64_t ncand = (c_max - c_min) / KT + 1;
+    int64_t stride = 1;
+    if (ncand * nq > kPlanEvals) {
+      stride = (ncand * nq + kPlanEvals - 1) / kPlanEvals;
+      ncand = (c_max - c_min) / (KT * stride) + 1;
     }
-    int64_t chunk = a.split_keys;
-    const int64_t need = (km + a.max_splits - 1) / a.max_splits;
-    if (need > chunk) chunk = need;
+    const int step = (int)(KT * stride), c0 = (int)c_min, nc = (int)ncand;
+    // wave w takes candidates w, w + 16, ..., its lanes the queries (the
+    // key count in a register when there are at most 64); a compact loop,
+    // since the plan runs once and every new instruction is a cache miss
+    const int nreg = lane < nq ? nks[lane] : 0;
+    unsigned long long mine = ~0ull;
+    for (int j = wave; j < nc; j += 16) {
+      const int c = c0 + step * j;
+      const float rc = __builtin_amdgcn_rcpf((float)c);
+      int cnt = 0;
+      if (nq <= 64) {
+        if (lane < nq) cnt = plan_splits(nreg, (float)nreg, c, rc);
+      } else {
+        for (int q = lane; q < nq; q += 64) cnt += plan_splits(nks[q], (float)nks[q], c, rc);
+      }
+      const int items = wave_sum_dpp(cnt);
+      // a workgroup's cost: its items' keys plus a fixed cost per item (the
+      // queries, the partial output and its share of the merge), in keys
+      const int rounds = items > 0 ? (items + a.target_items - 1) / a.target_items : 1;
+      const unsigned long long span = (unsigned long long)rounds * (unsigned)(c + kItemCost);
+      const unsigned long long key = (span << 32) | (unsigned)items;
+      mine = key < mine ? key : mine;
+    }
+    if (lane == 0) best[wave] = mine;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long b = best[0];
+      for (int w = 1; w < 16; ++w) b = best[w] < b ? best[w] : b;
+      // recover the chunk from the span and the item count
+      const int64_t span = (int64_t)(b >> 32), items = (int64_t)(b & 0xffffffffull);
+      const int64_t rounds = items > 0 ? (items + a.target_items - 1) / a.target_items : 1;
+      chunk_s = (int)(span / rounds - kItemCost);
+      carry = 0;
+    }
+  } else if (tid == 0) {
+    int64_t chunk = c_min;
     const int64_t fill = a.target_items > 0 ? (t + a.target_items - 1) / a.target_items : 0;
     if (fill > chunk) chunk = fill;
-    chunk = (chunk + KT - 1) / KT * KT;
-    chunk_s = (int)chunk;
-    *a.ws_chunk = (int)chunk;
+    chunk_s = (int)((chunk + KT - 1) / KT * KT);
     carry = 0;
   }
   __syncthreads();
   const int chunk = chunk_s;
+  if (tid == 0) *a.ws_chunk = chunk;
   // pass 2: splits, prefix sums, item -> query
   for (int64_t q0 = 0; q0 < a.n_q; q0 += 1024) {
     const int64_t q = q0 + tid;
     int ns = 0;
     if (q < a.n_q) {
-      const int nk = load_geo(a.ws_geo + q * 4, q).nkeys;
+      const int nk = keep ? nks[q] : load_geo(a.ws_geo + q * 4, q).nkeys;
       ns = nk > 0 ? (nk + chunk - 1) / chunk : 1;
       a.ws_cnt[q] = ns;
     }
