@@ -5,7 +5,7 @@
 //   lse = M + log(sum_p w_p).
 // A part with lse = -inf contributes nothing; if all are -inf, o = 0 and
 // lse = -inf.  Memory bound: one wave per row, float4 per lane, parts summed
-// in a fixed order.
+// in a fixed order with several parts' loads in flight at once.
 #include "merge.h"
 
 using namespace csa;
@@ -19,7 +19,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
                                                         int nparts, const int* __restrict__ cnt,
                                                         int rows_per_q, int64_t rows, int dim,
                                                         void* out, float* lse_out) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the row is the same for the whole wave: held in scalar registers
+  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   int n = nparts;
@@ -38,17 +39,37 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   const float den = wave_sum(w);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   if (lse_out != nullptr && lane == 0) lse_out[row] = den > 0.0f ? mx + logf(den) : -INFINITY;
+  // part p's weight, read from lane p into a scalar register
+  auto weight = [&](int p) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), p));
+  };
+  // a part of weight 0 (lse = -inf) is skipped by a select, so its values
+  // never reach the sum
+  auto add = [](float& r, float wp, float x) { r = wp != 0.0f ? fmaf(wp, x, r) : r; };
   for (int d = lane * 4; d < dim; d += 256) {
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-    for (int p = 0; p < n; ++p) {
-      const float wp = __shfl(w, p);
-      if (wp != 0.0f) {
-        const float4 x = *reinterpret_cast<const float4*>(part_o(p) + d);
-        r0 = fmaf(wp, x.x, r0);
-        r1 = fmaf(wp, x.y, r1);
-        r2 = fmaf(wp, x.z, r2);
-        r3 = fmaf(wp, x.w, r3);
+    int p = 0;
+    // four parts' loads in flight before their sums, parts in a fixed order
+    for (; p + 4 <= n; p += 4) {
+      float4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4*>(part_o(p + i) + d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wp = weight(p + i);
+        add(r0, wp, x[i].x);
+        add(r1, wp, x[i].y);
+        add(r2, wp, x[i].z);
+        add(r3, wp, x[i].w);
       }
+    }
+    for (; p < n; ++p) {
+      const float4 x = *reinterpret_cast<const float4*>(part_o(p) + d);
+      const float wp = weight(p);
+      add(r0, wp, x.x);
+      add(r1, wp, x.y);
+      add(r2, wp, x.z);
+      add(r3, wp, x.w);
     }
     r0 *= inv; r1 *= inv; r2 *= inv; r3 *= inv;
     if constexpr (OUT_BF16) {
