@@ -910,6 +910,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
                                                                acc_o[db], 0, 0, 0);
         }
       }
+      // keep one instruction's V^T reads in flight ahead of each product
+      // (left alone, the scheduler waits for every read right before its use)
+      if constexpr (NDB == 4) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // LDS reads
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1); // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      }
     }
   };
   auto tile_softmax_pv = [&](const f32x16_t& acc_s, int full, uint32_t mw, int kofs) {
