@@ -21,7 +21,10 @@
 // Split-K (decode).  With split_keys > 0 a query's key list is cut into
 // chunks handled by a persistent grid of workgroups; each writes a normalised
 // partial output and its log-sum-exp to the workspace, and a combine pass
-// merges them (the same merge as csa_swa_merge).
+// merges them (the same merge as csa_swa_merge).  Selected keys number at
+// most k + window per query, so the host fixes the chunk and the work items
+// are (query, split) pairs; all visible entries vary per request, so a plan
+// kernel reads the key counts, picks the chunk and lists the items.
 //
 // Per tile and wave (bf16):
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, keys on M, queries on N;
@@ -83,6 +86,13 @@ struct AttnArgs {
   int* ws_item_q;    // [n_q * max_splits] query of each work item (split-K)
   int4* ws_geo;      // [n_q][4] geometry record of each query (split-K)
   int* ws_chunk;     // keys per split chosen by the plan (split-K)
+  // split-K without a plan (selected keys: every query has at most
+  // static_keys): chunk and splits per query fixed by the host, work item
+  // i = (query i / static_splits, split i % static_splits); 0 = planned
+  int static_chunk;
+  int static_splits;
+  int static_keys;
+  int* host_splits;  // host only: where the launch reports static_splits
 };
 
 // Tile geometry shared by every thread of a workgroup.
@@ -500,21 +510,26 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   constexpr bool splitk = OUTM == 2;
   const unsigned wg = blockIdx.x;
   const int hgrp = splitk ? (int)blockIdx.y : (int)(wg % (unsigned)a.ngroups);
-  const int n_items = splitk ? a.ws_start[a.n_q] : 1;
+  const bool fixed = splitk && a.static_chunk > 0;
+  const int n_items = splitk ? (fixed ? (int)a.n_q * a.static_splits : a.ws_start[a.n_q]) : 1;
   for (int item = splitk ? (int)blockIdx.x : 0; item < n_items; item += splitk ? (int)gridDim.x : 1) {
   int64_t q_first;
   int split = 0;
-  if (splitk) {
+  if (fixed) {
+    q_first = item / a.static_splits;
+    split = item - (int)q_first * a.static_splits;
+  } else if (splitk) {
     q_first = a.ws_item_q[item];
     split = item - a.ws_start[q_first];
   } else {
     q_first = (int64_t)(wg / (unsigned)a.ngroups) * a.tok;
   }
-  Geo g = splitk ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
+  Geo g = splitk && !fixed ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
   if (splitk) {
-    const int chunk = *a.ws_chunk;
+    const int chunk = fixed ? a.static_chunk : *a.ws_chunk;
     g.key_lo = split * chunk;
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
+    if (g.key_hi < g.key_lo) g.key_hi = g.key_lo;   // past this query's keys: an empty part
     lds_barrier();                 // LDS of the previous item fully consumed
   }
 
@@ -1086,8 +1101,32 @@ dim3 attn_grid(const AttnArgs& a, K kern, int threads, size_t smem) {
 template <bool SPARSE, typename K>
 csa_status launch_kernel(const AttnArgs& a0, K kern, int threads, size_t smem, hipStream_t stream) {
   AttnArgs a = a0;
-  const dim3 grid = attn_grid(a, kern, threads, smem);
-  if (a.split_keys > 0) {
+  dim3 grid = attn_grid(a, kern, threads, smem);
+  if (a.split_keys > 0 && SPARSE && a.static_keys > 0) {
+    // selected keys: at most static_keys per query, so the host picks the
+    // chunk with the plan's cost (rounds of items over the grid times chunk
+    // plus the per-item cost) and the items are indexed statically
+    const int64_t nk = a.static_keys, T = grid.x;
+    int64_t c_min = a.split_keys;
+    const int64_t need = (nk + a.max_splits - 1) / a.max_splits;
+    if (need > c_min) c_min = need;
+    c_min = (c_min + KT - 1) / KT * KT;
+    const int64_t c_max = c_min > (nk + KT - 1) / KT * KT ? c_min : (nk + KT - 1) / KT * KT;
+    int64_t best_c = c_min, best_cost = -1, best_items = 0;
+    for (int64_t c = c_min; c <= c_max; c += KT) {
+      const int64_t items = a.n_q * ((nk + c - 1) / c);
+      const int64_t cost = (items + T - 1) / T * (c + kItemCost);
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && items < best_items)) {
+        best_cost = cost;
+        best_items = items;
+        best_c = c;
+      }
+    }
+    a.static_chunk = (int)best_c;
+    a.static_splits = (int)((nk + best_c - 1) / best_c);
+    if (a.host_splits != nullptr) *a.host_splits = a.static_splits;
+    if ((int64_t)grid.x > best_items) grid.x = (unsigned)best_items;
+  } else if (a.split_keys > 0) {
     a.target_items = (int)grid.x;
     const csa_status st = launch_plan(a, SPARSE, stream);
     if (st != CSA_OK) return st;
@@ -1236,6 +1275,8 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   if (split_keys < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_sparse_mqa_attn: split_keys < 0");
 
   AttnArgs a{};
+  int static_splits = 0;       // reported by a fixed split-K launch
+  a.host_splits = &static_splits;
   a.q = q->data;
   a.H = H;
   a.n_q = batch->n_q;
@@ -1308,6 +1349,7 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
     a.ws_chunk = a.ws_item_q + (size_t)batch->n_q * a.max_splits;
     const uintptr_t geo = reinterpret_cast<uintptr_t>(a.ws_chunk + 1);
     a.ws_geo = reinterpret_cast<int4*>((geo + 15) & ~(uintptr_t)15);
+    if (sparse && a.tok == 1) a.static_keys = (int)max_keys;
     outm = 2;
   }
   const int kvf = has_kv ? kv->fmt : (f32c ? CSA_F32 : CSA_BF16);
@@ -1321,9 +1363,11 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   else if (split) st = launch_split<512, false, CSA_BF16, 4>(a, sparse, stream);
   else st = launch_mode<512, false, CSA_BF16, 2>(a, sparse, outm, stream);
   if (st != CSA_OK || !split) return st;
-  // combine the split partials of every query row
+  // combine the split partials of every query row (a fixed split: all of its
+  // parts, the empty ones with lse = -inf)
   const size_t rows_total = (size_t)batch->n_q * H;
+  const bool fixed = a.static_keys > 0;
   return launch_lse_merge(a.ws_o, a.ws_lse, (int64_t)rows_total * D, (int64_t)rows_total,
-                          a.max_splits, a.ws_cnt, H, (int64_t)rows_total, D, out, out_fmt, lse,
-                          stream);
+                          fixed ? static_splits : a.max_splits, fixed ? nullptr : a.ws_cnt, H,
+                          (int64_t)rows_total, D, out, out_fmt, lse, stream);
 }
