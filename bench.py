@@ -325,6 +325,82 @@ def traffic_for(dom, wid):
     return rec.get("bytes_per_launch")
 
 
+# ------------------------------------------------------- score precision study
+
+
+def score_study():
+    """How much the indexer's reduced precision changes the top-k set, and how
+    much faster selection over bf16 scores is than over fp32 scores.
+
+    Decode-shaped synthetic rows (every entry visible, one query per request):
+    the reference set is the top-k of fp32 scores of fp32 operands; the
+    others round the operands to bf16 or MXFP4 and/or the scores to bf16.
+    Recall = |set & reference| / k per row, averaged.  Times are HIP-event
+    means over repeated launches of the unfused selection (over a stored score
+    matrix) and of the fused indexer + top-k."""
+    m = 4
+    cases = [("decode_b32_ctx131072_k512", 32, 32768, 512),
+             ("decode_b16_ctx1M_k1024", 16, 262144, 1024)]
+    gen = Gen(20262)
+    out = []
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name, n_q, n_ent, k in cases:
+        batch = ops.Batch.make([1] * n_q, [n_ent * m - 1] * n_q, kv_counts=[n_ent] * n_q)
+        qi32 = KV(F32, 64, gen.normal((n_q * 4, 64), 0.125))
+        ki32 = KV(F32, 64, gen.normal((n_q * n_ent, 64), 0.125))
+        qib = KV(BF16, 64, qi32.data.to(torch.bfloat16))
+        kib = KV(BF16, 64, ki32.data.to(torch.bfloat16))
+        qi4, ki4 = KV.empty(MXFP4, n_q * 4, 64), KV.empty(MXFP4, n_q * n_ent, 64)
+        ops.quantize(qi32, qi4)
+        ops.quantize(ki32, ki4)
+        sets = {
+            "f32_operands_f32_scores": (qi32, ki32, F32),
+            "f32_operands_bf16_scores": (qi32, ki32, BF16),
+            "bf16_operands_f32_scores": (qib, kib, F32),
+            "bf16_operands_bf16_scores": (qib, kib, BF16),
+            "mxfp4_operands_bf16_scores": (qi4, ki4, BF16),
+        }
+        idx = {key: ops.indexer_topk(q, 4, kk, batch, m, sf, k).cpu().numpy()
+               for key, (q, kk, sf) in sets.items()}
+        ref = idx["f32_operands_f32_scores"]
+        recall = {}
+        for key, got in idx.items():
+            if key == "f32_operands_f32_scores":
+                continue
+            r = [len(np.intersect1d(got[i], ref[i])) / k for i in range(n_q)]
+            recall[key] = round(float(np.mean(r)), 5)
+        s32 = torch.empty(n_q, n_ent, device="cuda", dtype=torch.float32)
+        s16 = torch.empty(n_q, n_ent, device="cuda", dtype=torch.bfloat16)
+        ops.indexer_score(qib, 4, kib, batch, m, s32, F32)
+        ops.indexer_score(qib, 4, kib, batch, m, s16, BF16)
+        sel32 = timed(lambda: ops.topk_select(s32, F32, batch, m, k))
+        sel16 = timed(lambda: ops.topk_select(s16, BF16, batch, m, k))
+        fus32 = timed(lambda: ops.indexer_topk(qib, 4, kib, batch, m, F32, k))
+        fus16 = timed(lambda: ops.indexer_topk(qib, 4, kib, batch, m, BF16, k))
+        log(f"{name}: recall {recall}; select f32 {sel32:.4f} ms, bf16 {sel16:.4f} ms; "
+            f"fused f32 {fus32:.4f} ms, bf16 {fus16:.4f} ms")
+        out.append({"workload": name, "requests": n_q, "entries": n_ent, "k": k,
+                    "recall_vs_f32": recall,
+                    "select_ms": {"f32_scores": round(sel32, 5), "bf16_scores": round(sel16, 5),
+                                  "speedup": round(sel32 / sel16, 3)},
+                    "fused_indexer_topk_ms": {"f32_scores": round(fus32, 5),
+                                              "bf16_scores": round(fus16, 5),
+                                              "speedup": round(fus32 / fus16, 3)}})
+    print(json.dumps({"study": "indexer score precision (bf16 / MXFP4 vs fp32)",
+                      "data": "synthetic, N(0, 1/64) queries and keys", "cases": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,7 +411,14 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (three "
                          "times): the reference for scaling HBM byte counters")
+    ap.add_argument("--score-study", action="store_true",
+                    help="instead of the benchmark: top-k recall and selection time with "
+                         "bf16 / MXFP4 indexer precision against fp32")
     args = ap.parse_args()
+    if args.score_study:
+        torch.cuda.init()
+        score_study()
+        return
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
