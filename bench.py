@@ -401,6 +401,63 @@ def score_study():
                       "data": "synthetic, N(0, 1/64) queries and keys", "cases": out}), flush=True)
 
 
+# ------------------------------------------------- decode-time compression
+
+
+def append_bench(reps=200):
+    """One csa_kv_compress_append call per decode step and layer: 64 requests
+    at spread positions append a 512-dim bf16 token; entries go to a mixed
+    cache, the raw row to a 128-row window ring.  Algorithmic bytes per
+    request and call: the token (1024 B) and its logit / position / offset,
+    the two open entries read and written ((512 + 4) * 4 B each way), the
+    window row (1024 B), plus one 580-byte entry every m calls."""
+    n_req, D, C = 64, 512, 128
+    gen = Gen(20263)
+    out = []
+    for name, m, w in (("csa_m4_w8", 4, 8), ("hca_m128_w256", 128, 256)):
+        pos0 = torch.randint(4 * w, 1 << 16, (n_req,), generator=gen.g, device="cuda")
+        x = KV(BF16, D, gen.normal((reps + 2 * w, n_req, D)).to(torch.bfloat16).reshape(-1, D))
+        z = gen.normal((reps + 2 * w, n_req))
+        b = gen.normal((w,))
+        n_ent = (pos0.max().item() + reps + 2 * w) // m + 1
+        cache = KV.empty(FP8_MIXED, n_req * n_ent, D)
+        e_off = torch.arange(n_req, dtype=torch.int64, device="cuda") * n_ent
+        win = KV(BF16, D, torch.zeros(n_req * C, D, dtype=torch.bfloat16, device="cuda"))
+        w_off = torch.arange(n_req, dtype=torch.int64, device="cuda") * C
+        state = torch.zeros(ops.kv_append_state_size(n_req, D) // 4, device="cuda")
+        pos = torch.stack([pos0 + i for i in range(reps + 2 * w)])
+        # the first 2w calls open every request's entries (warm-up, untimed)
+        call = lambda i: ops.kv_compress_append(x.narrow(i * n_req, n_req), z[i], b, m, w, pos[i],
+                                                state, e_off, cache, win, w_off, C)
+        for i in range(2 * w):
+            call(i)
+        torch.cuda.synchronize()
+        # the timed calls as one captured graph, as a decode step would run them
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(2 * w, 2 * w + reps):
+                    call(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        per_req = 1024 + 4 + 8 + 8 + 2 * 2 * (D + 4) * 4 + 1024 + 580.0 / m
+        gbs = n_req * per_req / (us * 1e-6) / 1e9
+        log(f"append {name}: {us:.2f} us per call, {gbs:.1f} GB/s algorithmic")
+        out.append({"workload": f"decode_append_b{n_req}_{name}_d512_mixed", "us_per_call": round(us, 3),
+                    "bytes_per_call": int(n_req * per_req), "achieved_gbs": round(gbs, 2),
+                    "hbm_frac": round(gbs / PEAK["hbm"], 5)})
+    print(json.dumps({"measure": "decode-time compression (csa_kv_compress_append)",
+                      "data": "synthetic", "cases": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,7 +471,13 @@ def main():
     ap.add_argument("--score-study", action="store_true",
                     help="instead of the benchmark: top-k recall and selection time with "
                          "bf16 / MXFP4 indexer precision against fp32")
+    ap.add_argument("--kv-append", action="store_true",
+                    help="instead of the benchmark: time decode-time compression per call")
     args = ap.parse_args()
+    if args.kv_append:
+        torch.cuda.init()
+        append_bench()
+        return
     if args.score_study:
         torch.cuda.init()
         score_study()

@@ -19,6 +19,10 @@
  *   csa_swa_merge        the exact log-sum-exp combination of two partial
  *                        attentions, so the window branch and the compressed
  *                        branch can run separately.
+ *   csa_kv_compress_append
+ *                        decode-time compression through a per-request state
+ *                        (page "DeepSeek V4 深度解析", section 4, KV-cache
+ *                        management): one token per request and call.
  *   csa_quantize, csa_dequantize, csa_mxfp4_to_fp8
  *                        the storage formats: mixed-precision KV entries
  *                        (RoPE dims BF16, the rest FP8) and the FP4 indexer
@@ -109,11 +113,20 @@ typedef struct csa_tensor {
  *   raw (window) rows of r    : rows raw_off[r] .. raw_off[r+1]-1 of the raw
  *                               tensor, holding positions raw_pos[r] ..
  *                               (may be NULL when no window is used)
+ *   window_ring               : 0: the raw rows of r hold positions raw_pos[r],
+ *                               raw_pos[r] + 1, ... in order.  1: they are a
+ *                               ring of C = raw_off[r+1]-raw_off[r] rows,
+ *                               position p at row raw_off[r] + p mod C,
+ *                               holding the positions from raw_pos[r] up to
+ *                               the request's last query, at most C of them
+ *                               (as csa_kv_compress_append writes them); C
+ *                               must be at least the window plus the
+ *                               request's queries minus one
  * n_q = q_off[n_req] and max_kv >= every kv_off[r+1]-kv_off[r] are host-side
  * copies used to size launch grids. */
 typedef struct csa_batch {
   int32_t n_req;
-  int32_t reserved;
+  int32_t window_ring;
   int64_t n_q;
   int64_t max_kv;
   const int64_t* q_off;
@@ -145,6 +158,48 @@ csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_p
                            const float* slot_bias, int32_t m, int32_t w,
                            int64_t entry_begin, int64_t n_entries, const csa_tensor* out,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_kv_compress_append - decode-time compression through a state cache.
+ * Page "DeepSeek V4 深度解析", section 4, the paragraph on KV-cache management
+ * for the hybrid attention: a fixed per-request state holds the window and the
+ * tail of tokens not yet compressed, finished entries go to the compressed
+ * cache.  The entries are those of csa_kv_compress (same reading: entry i
+ * covers positions (i+1)m-w .. (i+1)m-1, slots before 0 left out), computed
+ * one token at a time.
+ *
+ * Appends one raw token to each of the n_req = x->rows requests:
+ *   x          [n_req, dim] F32 or BF16, request r's new raw row, at position
+ *              pos[r] (device int64; a negative position skips the request)
+ *   logits     float [n_req], its compression logit; slot_bias float [w]
+ *   1 <= m <= w <= 2m (so a token lies in at most two entries' windows), w <= 1024
+ *   state      device float, csa_kv_append_state_size(n_req, dim) bytes,
+ *              owned by the caller: per request the two open entries (online
+ *              softmax: running max, sum and weighted row, fp32).  An entry's
+ *              accumulator is reset at the first valid position of its window,
+ *              so no initialisation is needed when a request's tokens are
+ *              appended in order from a window start (position 0, or the first
+ *              position of the oldest entry still open after a prefill);
+ *              replaying such a tail re-emits the entries it completes
+ *   entry_off  device int64 [n_req]: entry i of request r goes to row
+ *              entry_off[r] + i of `cache` when position (i+1)m-1 is appended
+ *              (rows outside the cache are skipped)
+ *   cache      F32, BF16 or FP8_MIXED (dim 512) entries of dim = x->dim, dim in
+ *              {64, 128, 256, 512}
+ *   window     NULL, or F32 / BF16 rows of dim: the raw row also goes to row
+ *              window_off[r] + pos[r] mod window_rows (a ring of window_rows
+ *              rows per request, read by csa_sparse_mqa_attn with
+ *              csa_batch.window_ring = 1)
+ * Requests must be distinct (each owns its state and rows); calls on one
+ * stream see each other's writes in order.
+ * ------------------------------------------------------------------------- */
+size_t csa_kv_append_state_size(int64_t n_req, int32_t dim);
+csa_status csa_kv_compress_append(const csa_tensor* x, const float* logits,
+                                  const float* slot_bias, int32_t m, int32_t w,
+                                  const int64_t* pos, float* state, const int64_t* entry_off,
+                                  const csa_tensor* cache, const csa_tensor* window,
+                                  const int64_t* window_off, int32_t window_rows,
+                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * csa_indexer_score - CSA step 2, the lightning indexer.

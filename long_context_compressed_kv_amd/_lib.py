@@ -9,7 +9,7 @@ CSA_OK = 0
 CSA_F32, CSA_BF16, CSA_FP8_MIXED, CSA_MXFP4 = 0, 1, 2, 3
 
 EXPORTED = (
-    "csa_kv_compress", "csa_indexer_score", "csa_topk_select", "csa_indexer_topk",
+    "csa_kv_compress", "csa_kv_compress_append", "csa_kv_append_state_size", "csa_indexer_score", "csa_topk_select", "csa_indexer_topk",
     "csa_indexer_topk_workspace_size", "csa_sparse_mqa_attn",
     "csa_swa_merge", "csa_quantize", "csa_dequantize", "csa_mxfp4_to_fp8",
     "csa_attn_workspace_size", "csa_abi_version", "csa_status_string", "csa_last_error",
@@ -22,7 +22,7 @@ class CsaTensor(ctypes.Structure):
 
 
 class CsaBatch(ctypes.Structure):
-    _fields_ = [("n_req", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("n_req", ctypes.c_int32), ("window_ring", ctypes.c_int32),
                 ("n_q", ctypes.c_int64), ("max_kv", ctypes.c_int64),
                 ("q_off", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
                 ("kv_off", ctypes.c_void_p), ("raw_off", ctypes.c_void_p),
@@ -50,6 +50,7 @@ def load():
     B = ctypes.POINTER(CsaBatch)
     sig = {
         "csa_kv_compress": [T, P, I64, P, I32, I32, I64, I64, T, P],
+        "csa_kv_compress_append": [T, P, P, I32, I32, P, P, P, T, T, P, I32, P],
         "csa_indexer_score": [T, I32, P, T, B, I32, I32, P, I32, I64, P],
         "csa_topk_select": [P, I32, I64, B, I32, I32, P, P],
         "csa_indexer_topk": [T, I32, P, T, B, I32, I32, I32, I32, P, P, ctypes.c_size_t, P],
@@ -64,6 +65,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.csa_kv_append_state_size.restype = ctypes.c_size_t
+    lib.csa_kv_append_state_size.argtypes = [I64, I32]
     lib.csa_indexer_topk_workspace_size.restype = ctypes.c_size_t
     lib.csa_indexer_topk_workspace_size.argtypes = [I64, I32]
     lib.csa_attn_workspace_size.restype = ctypes.c_size_t

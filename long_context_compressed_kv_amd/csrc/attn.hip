@@ -99,7 +99,7 @@ struct AttnArgs {
 struct Geo {
   int64_t q_first, q_last, t_first, t_last;
   int64_t kv_base, raw_base, raw_pos, kv_len;
-  int64_t nvis_first;   // visible entries of the first token (the fewest)
+  int64_t raw_cap;      // ring capacity of the request's raw rows (0: in order)
   int64_t wlo;          // first window position
   int nE, nkeys, key_lo, key_hi;
 };
@@ -120,7 +120,7 @@ __device__ Geo make_geo(const AttnArgs& a, int64_t q_first) {
   g.raw_base = qm0.raw_base;
   g.raw_pos = qm0.raw_pos;
   g.kv_len = qm0.kv_len;
-  g.nvis_first = qm0.n_vis;
+  g.raw_cap = a.b.ring ? qm0.raw_len : 0;
   if constexpr (SPARSE) {
     g.nE = a.kv != nullptr ? (int)(g.q_last - g.q_first + 1) * a.k : 0;
   } else {
@@ -134,7 +134,12 @@ __device__ Geo make_geo(const AttnArgs& a, int64_t q_first) {
     if (g.wlo < 0) g.wlo = 0;
     if (g.wlo < qm0.raw_pos) g.wlo = qm0.raw_pos;
     whi = g.t_last;
-    if (whi > qm0.raw_pos + qm0.raw_len - 1) whi = qm0.raw_pos + qm0.raw_len - 1;
+    if (g.raw_cap > 0) {
+      // a ring holds the last raw_cap positions up to the group's last token
+      if (g.wlo < g.t_last - g.raw_cap + 1) g.wlo = g.t_last - g.raw_cap + 1;
+    } else if (whi > qm0.raw_pos + qm0.raw_len - 1) {
+      whi = qm0.raw_pos + qm0.raw_len - 1;
+    }
   }
   const int nW = whi >= g.wlo ? (int)(whi - g.wlo + 1) : 0;
   g.nkeys = g.nE + nW;
@@ -146,7 +151,7 @@ __device__ Geo make_geo(const AttnArgs& a, int64_t q_first) {
 // The geometry of a one-token group as a 64-byte record (split-K work items
 // read it with one load instead of re-resolving the request).
 __device__ __forceinline__ void store_geo(int4* dst, const Geo& g) {
-  const int64_t v[8] = {g.t_first, g.kv_base, g.raw_base, g.raw_pos, g.kv_len, g.nvis_first, g.wlo,
+  const int64_t v[8] = {g.t_first, g.kv_base, g.raw_base, g.raw_pos, g.kv_len, g.raw_cap, g.wlo,
                         ((int64_t)(uint32_t)g.nkeys << 32) | (uint32_t)g.nE};
 #pragma unroll
   for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(int4, make_longlong2(v[2 * i], v[2 * i + 1]));
@@ -166,7 +171,7 @@ __device__ __forceinline__ Geo load_geo(const int4* src, int64_t q) {
   g.raw_base = v[2];
   g.raw_pos = v[3];
   g.kv_len = v[4];
-  g.nvis_first = v[5];
+  g.raw_cap = v[5];
   g.wlo = v[6];
   g.nE = (int)(uint32_t)v[7];
   g.nkeys = (int)(uint32_t)(v[7] >> 32);
@@ -377,7 +382,7 @@ __device__ __forceinline__ void key_meta(const AttnArgs& a, const Geo& g, int kk
     }
   } else {
     const int64_t p = g.wlo + (kk - g.nE);
-    row = -2 - (int)(g.raw_base + (p - g.raw_pos));
+    row = -2 - (int)(g.raw_base + (g.raw_cap > 0 ? p % g.raw_cap : p - g.raw_pos));
     lo = p - g.t_first;
     hi = lo + a.window;
   }
@@ -1263,6 +1268,8 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
       return fail(CSA_ERR_INVALID_ARGUMENT, "csa_sparse_mqa_attn: raw must match q's format and dim");
     if (batch->raw_off == nullptr || batch->raw_pos == nullptr)
       return fail(CSA_ERR_INVALID_ARGUMENT, "csa_sparse_mqa_attn: raw given without raw_off/raw_pos");
+    if (batch->window_ring != 0 && batch->window_ring != 1)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "csa_sparse_mqa_attn: window_ring must be 0 or 1");
     if (window > (1 << 20))
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: window too large");
     if (raw->rows > 0x7fffffff)
@@ -1289,7 +1296,7 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   a.window = has_raw ? window : 0;
   a.b = BatchDev{batch->n_req, batch->q_off, batch->q_pos, has_kv ? batch->kv_off : nullptr,
                  has_raw ? batch->raw_off : nullptr, has_raw ? batch->raw_pos : nullptr,
-                 has_kv ? kv->rows : 0, has_raw ? raw->rows : 0};
+                 has_kv ? kv->rows : 0, has_raw ? raw->rows : 0, batch->window_ring};
   a.m = m;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;

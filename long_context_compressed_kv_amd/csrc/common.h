@@ -186,6 +186,7 @@ struct BatchDev {
   const int64_t* raw_pos;
   int64_t kv_rows;   // rows of the entry tensor (0 if none)
   int64_t raw_rows;  // rows of the raw tensor (0 if none)
+  int ring;          // raw rows of a request are a ring (position p at row p mod rows)
 };
 
 __device__ __forceinline__ QueryMeta query_meta(const BatchDev& b, int64_t q, int m) {

@@ -98,6 +98,7 @@ class Batch:
     raw_pos: Optional[torch.Tensor]
     n_q: int
     max_kv: int
+    window_ring: bool = False   # raw rows of a request form a ring (see csa_batch)
 
     @property
     def n_req(self):
@@ -108,7 +109,8 @@ class Batch:
             if t is not None:
                 _need_cuda(t)
                 assert t.dtype == torch.int64
-        return CsaBatch(self.n_req, 0, self.n_q, self.max_kv, _ptr(self.q_off), _ptr(self.q_pos),
+        return CsaBatch(self.n_req, int(bool(self.window_ring)), self.n_q, self.max_kv,
+                        _ptr(self.q_off), _ptr(self.q_pos),
                         _ptr(self.kv_off), _ptr(self.raw_off), _ptr(self.raw_pos))
 
     @staticmethod
@@ -140,6 +142,28 @@ def kv_compress(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, 
                               int(m), int(w), int(entry_begin), int(n_entries),
                               ctypes.byref(oc), _stream()), "csa_kv_compress")
     return out
+
+
+def kv_append_state_size(n_req, dim):
+    """Bytes of the per-request compression state csa_kv_compress_append keeps."""
+    return int(_lib.load().csa_kv_append_state_size(int(n_req), int(dim)))
+
+
+def kv_compress_append(x: KV, logits, slot_bias, m, w, pos, state, entry_off, cache: KV,
+                       window: Optional[KV] = None, window_off=None, window_rows=0):
+    """Decode-time compression: appends row r of x (at position pos[r]) to
+    request r's state; finished entries go to cache row entry_off[r] + i, and
+    with a window the raw row to window_off[r] + pos[r] % window_rows."""
+    _need_cuda(logits, slot_bias, pos, state, entry_off, window_off)
+    lib = _lib.load()
+    xc, cc = x.c(), cache.c()
+    wc = window.c() if window is not None else None
+    check(lib.csa_kv_compress_append(ctypes.byref(xc), _ptr(logits), _ptr(slot_bias), int(m),
+                                     int(w), _ptr(pos), _ptr(state), _ptr(entry_off),
+                                     ctypes.byref(cc), ctypes.byref(wc) if wc is not None else None,
+                                     _ptr(window_off), int(window_rows), _stream()),
+          "csa_kv_compress_append")
+    return cache
 
 
 def indexer_score(qi: KV, n_heads, ki: KV, batch: Batch, m, scores, score_fmt,

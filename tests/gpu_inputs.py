@@ -62,3 +62,38 @@ def to_np(t):
 
 def bits16(t):
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_mixed(out, c64, cabs, rel=2.0 ** -20):
+    """Mixed-format entries against the oracle's.
+
+    c64  : exact entries; cabs: the same weighted sum of |x| (bounds the fp32
+    accumulation error: |c_fp32 - c| <= cabs * rel, 2^-20 for the one-pass
+    weighted sum over these window sizes).
+    Scale bytes must match unless the block amax sits within that error of a
+    power-of-two bound; an e4m3 code may differ by one step, or a bf16 RoPE value
+    by one ulp, only where the exact value is within that error of the rounding
+    midpoint.  Returns the number of differing codes."""
+    err = cabs * rel
+    nope_r, scale_r, rope_r = codecs.quantize_kv_mixed(c64.astype(np.float32))
+    nope_g = out.data.cpu().numpy()
+    scale_g = out.scale.cpu().numpy()
+    rope_g = bits16(out.rope)
+    gr = codecs.bf16_to_f32(rope_g).astype(np.float64)
+    assert np.all(np.abs(gr - c64[:, 448:]) <= 0.5 * bf16_ulp(c64[:, 448:]) * 1.0001 + err[:, 448:])
+    bad_scale = scale_g != scale_r
+    for r, b in zip(*np.nonzero(bad_scale)):
+        lo, hi = b * 128, min(b * 128 + 128, 448)
+        amax = np.max(np.abs(c64[r, lo:hi]))
+        bound = 448.0 * 2.0 ** np.round(np.log2(amax / 448.0))
+        assert abs(amax - bound) <= np.max(err[r, lo:hi])
+    diff = nope_g != nope_r
+    for r, c in zip(*np.nonzero(diff)):
+        b = c // 128
+        if bad_scale[r, b]:
+            continue
+        s = codecs.e8m0_decode(scale_r[r, b])
+        a, bb = codecs.e4m3_decode(nope_g[r, c]), codecs.e4m3_decode(nope_r[r, c])
+        assert abs(int(nope_g[r, c] & 0x7F) - int(nope_r[r, c] & 0x7F)) == 1
+        assert abs(c64[r, c] - (a + bb) / 2 * s) <= err[r, c]
+    return int(diff.sum())

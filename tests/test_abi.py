@@ -74,6 +74,36 @@ def _batch(n_q=4, n_req=1, max_kv=16):
     return CsaBatch(n_req, 0, n_q, max_kv, FAKE, FAKE, FAKE, FAKE, FAKE)
 
 
+def test_kv_append_validation(lib):
+    """Arguments the host refuses before any launch (no device needed)."""
+    x, cache = _t(1, 128, 4), _t(1, 128, 64)
+    f = lambda xx, cc, m=4, w=8, win=None, woff=FAKE, wrows=0, pos=FAKE, st=FAKE: \
+        lib.csa_kv_compress_append(ctypes.byref(xx), FAKE, FAKE, m, w, pos, st, FAKE,
+                                   ctypes.byref(cc), ctypes.byref(win) if win is not None else None,
+                                   woff, wrows, None)
+    assert f(x, cache, w=9) == BAD_ARG                            # w > 2m
+    assert f(x, cache, w=3) == BAD_ARG                            # w < m
+    assert f(x, _t(1, 64, 64)) == BAD_ARG                         # dim mismatch
+    assert f(_t(1, 32, 4), _t(1, 32, 64)) == UNSUPPORTED          # dim 32
+    assert f(x, _t(2, 128, 64, scale=FAKE, rope=FAKE)) == BAD_ARG   # a mixed row has 512 dims
+    assert f(x, _t(3, 128, 64, scale=FAKE)) == UNSUPPORTED        # MXFP4 entries
+    assert f(x, cache, win=_t(1, 128, 256), wrows=0) == BAD_ARG   # ring without capacity
+    assert f(x, cache, win=_t(1, 128, 256), woff=None, wrows=128) == BAD_ARG
+    assert f(x, cache, pos=None) == BAD_ARG
+    assert f(_t(1, 128, 0), cache, pos=None) == 0                 # no requests: nothing to do
+    assert lib.csa_kv_append_state_size(3, 128) == 3 * 2 * 132 * 4
+
+
+def test_attn_window_ring_flag_validated(lib):
+    bt = _batch(n_q=2)
+    bt.window_ring = 2
+    q = _t(1, 128, 2 * 64)
+    raw = _t(1, 128, 256)
+    st = lib.csa_sparse_mqa_attn(ctypes.byref(q), 64, None, None, 0, ctypes.byref(raw), 128,
+                                 ctypes.byref(bt), 4, 0.1, FAKE, 1, None, 0, None, 0, None)
+    assert st == BAD_ARG
+
+
 def test_indexer_validation(lib):
     qi, ki = _t(1, 64, 16), _t(1, 64, 32)
     bt = _batch()
