@@ -4,22 +4,28 @@
 // followed by csa_topk_select, bit for bit, but the score matrix never goes
 // to memory: only a short list of candidates per query does.
 //
-//   1. itk_sample_kernel: each query scores a sample of its visible entries
-//      (runs of 32 consecutive entries spread evenly over the row, about
-//      40n/3k of them) and takes as threshold the sample key of rank
-//      ~3k * sample / n, so that about 3k entries of the row score at least
-//      as high.  Rows of at most `cap` entries take every entry (threshold 0).
+//   1. itk_sample_kernel (groups of several queries of one request):
+//      each query scores a sample of its visible entries (runs of 32
+//      consecutive entries spread evenly over the row, about 40n/3k of them)
+//      and takes as threshold the sample key of rank ~3k * sample / n, so that
+//      about 3k entries of the row score at least as high.  Rows of at most
+//      `cap` entries take every entry (threshold 0).
 //   2. itk_filter_kernel: the indexer's tiles (same grid and arithmetic as
-//      csa_indexer_score); an entry whose order key reaches its query's
-//      threshold is appended, (key, index), to the query's candidate list.
-//      Each workgroup reserves its span with one atomic per query.
+//      csa_indexer_score); an entry whose order key reaches its threshold is
+//      appended, (key, index), to the query's candidate list.  Each workgroup
+//      reserves its span with one atomic per query.  With one query per group
+//      (decode) there is no sample: each workgroup takes as its threshold the
+//      key of rank ~3k/n of its own entries (+1), and records the largest
+//      such threshold of the row.
 //   3. itk_select_kernel: per query, an exact radix select of the k-th
 //      largest candidate key, ties resolved to the lowest indices by a radix
 //      select over the tied indices, the chosen entries marked in an LDS
-//      bitmap of the row and read back in index order.  A row whose
-//      candidates overflowed `cap` or fell short of k (the sample misjudged
-//      it, e.g. masses of equal scores) is redone there exactly from
-//      recomputed scores.
+//      bitmap of the row and read back in index order.  Every entry left out
+//      scored below its threshold, so the list holds the exact top-k unless
+//      the k-th candidate key is below the row's (largest) threshold.  A row
+//      where that happens, or whose candidates overflowed `cap` or fell short
+//      of k (masses of equal scores), is redone there exactly from recomputed
+//      scores.
 // The candidates arrive in no fixed order, but every step after the filter
 // depends only on the candidate set, so the output is deterministic.
 #include <type_traits>
@@ -49,7 +55,7 @@ struct ItkArgs {
   int k;
   int cap;            // candidates kept per query
   int64_t max_n;      // rows are cut to this many entries (the batch's max_kv, at most 2^20)
-  uint32_t* tau;      // [n_q] threshold keys
+  uint32_t* tau;      // [n_q] threshold keys (decode: the largest of the workgroups')
   uint32_t* cnt;      // [n_q] candidates found (may exceed cap)
   uint2* cand;        // [n_q][cap] (key, entry)
   int32_t* idx;       // [n_q][k] result
@@ -203,7 +209,8 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 
 // Grid: entry chunks and query groups, as the score kernel.  Pass 1
 // scores the wave's tiles into an LDS row of keys per query of the group and
-// counts the candidates per (wave, query); one atomic per query reserves the
+// counts the candidates per (wave, query) (streaming: after the workgroup's
+// own threshold is selected from that row); one atomic per query reserves the
 // workgroup's span of the list; pass 2 rescans the LDS rows and writes the
 // candidates (each wave its own entries, so the reserved spans line up).
 template <int FMT, bool SBF16, bool STREAM>
@@ -218,6 +225,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
   __shared__ uint32_t wcnt[kWaves][QS];   // candidates per (wave, query)
   __shared__ uint32_t gbase[QS];          // the workgroup's first list slot per query
   __shared__ uint32_t stau[QS];           // the queries' thresholds
+  __shared__ RadixLds<256> frx;           // the workgroup's own threshold (streaming)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
 
   // several queries per group (prefill): x = query group, y = entry chunk,
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
   // pass 1: keys into LDS, candidate counts per query in this lane
   uint32_t tau[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) tau[g] = gr.nv[g] > 0 ? a.tau[qblock + 2 * g + half] : 0u;
+  for (int g = 0; g < NG; ++g) tau[g] = !STREAM && gr.nv[g] > 0 ? a.tau[qblock + 2 * g + half] : 0u;
   uint32_t c[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) c[g] = 0;
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       const int ql = 2 * g + half;
       const uint32_t key = score_key<SBF16>(head_score(acc, g, gr.hw[g], a.relu));
       if (ql < QS) lk[ql][el] = (skey_t)key;
-      c[g] += (e_wg + el < gr.nv[g] && key >= tau[g]) ? 1u : 0u;
+      if constexpr (!STREAM) c[g] += (e_wg + el < gr.nv[g] && key >= tau[g]) ? 1u : 0u;
     }
   };
   auto tile_live = [&](int t) { return e_wg + e_wave + t * 32 < n_scan; };
@@ -292,24 +300,64 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       score_tile(t, kt);
     }
   }
-  // sums over each half of the wave: lanes 0-31 count query 2g, lanes 32-63
-  // query 2g + 1 of register block g
+  if constexpr (STREAM) {
+    // the workgroup's own threshold: the key of rank ~3k * mine / n among its
+    // mine = n_valid entries (+1 for rounding), all of them in rows of at
+    // most cap entries
+    __syncthreads();
+    int64_t nvq = (gr.qm.t + 1) / a.m;
+    if (nvq > gr.qm.kv_len) nvq = gr.qm.kv_len;
+    if (nvq > a.max_n) nvq = a.max_n;
+    int64_t nvalid = nvq - e_wg;
+    if (nvalid > kWaves * EW) nvalid = kWaves * EW;
+    uint32_t tw = 0;
+    if (nvq > a.cap) {
+      int64_t r = (3 * (int64_t)a.k * nvalid + nvq - 1) / nvq + 1;
+      if (r < nvalid) {
+        uint32_t rem;
+        tw = radix_select_visit<SBF16 ? 16 : 32, 256>(
+            frx, (uint32_t)r,
+            [&](auto&& f) {
+              for (int i = tid; i < nvalid; i += 256) f((uint32_t)lk[0][i]);
+            },
+            rem);
+      }
+    }
+    uint32_t x = 0;
+    for (int i = 0; i < EW; i += 64) {
+      const int el = e_wave + i + lane;
+      x += __builtin_popcountll(__ballot(el < nvalid && (uint32_t)lk[0][el] >= tw));
+    }
+    if (lane == 0) wcnt[wave][0] = x;
+    __syncthreads();
+    if (tid == 0 && qblock < a.n_q) {
+      uint32_t tot = 0;
+      for (int w = 0; w < kWaves; ++w) tot += wcnt[w][0];
+      gbase[0] = tot > 0 ? atomicAdd(&a.cnt[qblock], tot) : 0u;
+      stau[0] = tw;
+      atomicMax(&a.tau[qblock], tw);
+    }
+    __syncthreads();
+  } else {
+    // sums over each half of the wave: lanes 0-31 count query 2g, lanes
+    // 32-63 query 2g + 1 of register block g
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    uint32_t x = c[g];
+    for (int g = 0; g < NG; ++g) {
+      uint32_t x = c[g];
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-    const int ql = 2 * g + half;
-    if (rl == 0 && ql < QS) wcnt[wave][ql] = x;
+      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+      const int ql = 2 * g + half;
+      if (rl == 0 && ql < QS) wcnt[wave][ql] = x;
+    }
+    __syncthreads();
+    if (tid < QS && qblock + tid < a.n_q) {
+      uint32_t tot = 0;
+      for (int w = 0; w < kWaves; ++w) tot += wcnt[w][tid];
+      gbase[tid] = tot > 0 ? atomicAdd(&a.cnt[qblock + tid], tot) : 0u;
+      stau[tid] = a.tau[qblock + tid];
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid < QS && qblock + tid < a.n_q) {
-    uint32_t tot = 0;
-    for (int w = 0; w < kWaves; ++w) tot += wcnt[w][tid];
-    gbase[tid] = tot > 0 ? atomicAdd(&a.cnt[qblock + tid], tot) : 0u;
-    stau[tid] = a.tau[qblock + tid];
-  }
-  __syncthreads();
 
   // pass 2: each wave writes its entries' candidates, query by query (slots
   // past cap are dropped; the count still records them, which sends the row
@@ -375,15 +423,19 @@ struct SelectLds {
 // thread its share; every thread calls it): the k-th largest key tau by radix
 // select, ties to the lowest entries by a radix select over their
 // complemented indices, the chosen entries marked in the LDS bitmap (nwords
-// words, cleared here) and written in index order to out[0..k).
+// words, cleared here) and written in index order to out[0..k).  The keys
+// visited must include every key of the row at or above `floor`; if tau
+// turns out below it, entries that were not visited could belong to the
+// top-k: nothing is written and false is returned.
 template <int KBITS, int NT, typename Visit>
-__device__ void select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, int32_t* out,
-                           Visit visit) {
+__device__ bool select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, int32_t* out,
+                           Visit visit, uint32_t floor = 0) {
   const int tid = threadIdx.x;
   uint32_t need, n_eq;
   const uint32_t tau = radix_select_visit<KBITS, NT>(
       sh.rx, (uint32_t)k, [&](auto&& f) { visit([&](uint32_t key, uint32_t) { f(key); }); }, need,
       &n_eq);
+  if (tau < floor) return false;          // the same in every thread
   for (int w = tid; w < nwords; w += NT) bm[w] = 0;
   // the need-th lowest tied index is the need-th largest of the complements
   uint32_t iota = 0xffffffffu;
@@ -404,6 +456,7 @@ __device__ void select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, i
   });
   __syncthreads();
   emit_bitmap<NT>(bm, nwords, sh.wsum, out, k);
+  return true;
 }
 
 // Grid: one workgroup per query.  A list of at most CPT * NT candidates is
@@ -428,7 +481,8 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   }
   const int nwords = (int)((n + 31) / 32);
   const uint32_t c = a.cnt[q];
-  if (c > (uint32_t)a.cap || c < (uint32_t)a.k) {
+  const uint32_t floor = a.tau[q];
+  auto redo = [&]() {
     // the exact redo over the whole row
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
     const int64_t qblock = q / a.qpg * a.qpg;
@@ -450,6 +504,9 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
         if (mine && e < n) f(score_key<SBF16>(s), (uint32_t)e);
       }
     });
+  };
+  if (c > (uint32_t)a.cap || c < (uint32_t)a.k) {
+    redo();
     return;
   }
   const uint2* list = a.cand + q * (int64_t)a.cap;
@@ -460,19 +517,27 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
       const uint32_t i = tid + j * NT;
       cr[j] = i < c ? list[i] : make_uint2(0, 0);
     }
-    select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
+    if (!select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
 #pragma unroll
-      for (int j = 0; j < CPT; ++j)
-        if (tid + j * NT < c) f(cr[j].x, cr[j].y);
-    });
+          for (int j = 0; j < CPT; ++j)
+            if (tid + j * NT < c) f(cr[j].x, cr[j].y);
+        }, floor))
+      redo();
   } else {
-    select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
-      for (uint32_t i = tid; i < c; i += NT) {
-        const uint2 ce = list[i];
-        f(ce.x, ce.y);
-      }
-    });
+    if (!select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
+          for (uint32_t i = tid; i < c; i += NT) {
+            const uint2 ce = list[i];
+            f(ce.x, ce.y);
+          }
+        }, floor))
+      redo();
   }
+}
+
+// the per-query threshold and count words, cleared before a streaming filter
+__global__ __launch_bounds__(256) void itk_clear_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 template <int FMT, bool SBF16, int NT>
@@ -492,8 +557,13 @@ template <int FMT, bool SBF16>
 csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   const int64_t groups = (a.n_q + a.qpg - 1) / a.qpg;
   const bool stream = a.qpg == 1;
-  hipLaunchKernelGGL((itk_sample_kernel<FMT, SBF16>), dim3((unsigned)groups), dim3(kSampleThreads), 0, s, a);
-  csa_status st = csa_host::check_launch("csa_indexer_topk (sample)");
+  // tau and cnt are adjacent: 2 n_q words
+  if (stream)
+    hipLaunchKernelGGL(itk_clear_kernel, dim3((unsigned)((2 * a.n_q + 255) / 256)), dim3(256), 0, s, a.tau,
+                       2 * a.n_q);
+  else
+    hipLaunchKernelGGL((itk_sample_kernel<FMT, SBF16>), dim3((unsigned)groups), dim3(kSampleThreads), 0, s, a);
+  csa_status st = csa_host::check_launch(stream ? "csa_indexer_topk (clear)" : "csa_indexer_topk (sample)");
   if (st != CSA_OK) return st;
   const int64_t epw = entries_per_wg<FMT>(stream);
   const dim3 fgrid = stream ? dim3((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups)
