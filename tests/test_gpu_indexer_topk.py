@@ -143,3 +143,22 @@ def test_fused_matches_oracle():
             tau = np.sort(keys)[::-1][min(k, len(keys)) - 1]
             for j in set(got.tolist()) ^ set(want.tolist()):
                 assert j >= 0 and abs(keys[j] - tau) <= bf16_ulp(tau)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_fused_clustered_best_entries(fmt):
+    """A row whose best entries all lie in one filter workgroup's chunk: that
+    workgroup's own threshold sits above the row's k-th score, so the select
+    finds its k-th candidate below the row's largest threshold and redoes the
+    row exactly.  The other row clusters its best entries across a chunk
+    boundary."""
+    rng = np.random.default_rng(67)
+    m, k = 4, 512
+    ctx = [131071, 40003]
+    kv_counts = [(c + 1) // m for c in ctx]
+    qi, ki = _inputs(rng, len(ctx), sum(kv_counts), fmt)
+    ki[:1024] *= 4.0                                            # row 0: its first chunk
+    ki[kv_counts[0] + 7000: kv_counts[0] + 8100] *= 4.0         # row 1: straddles chunks
+    batch = Batch.make([1] * len(ctx), ctx, kv_counts=kv_counts)
+    f, u = _both(qi, ki, fmt, batch, m, k, "bf16")
+    assert np.array_equal(f, u)
