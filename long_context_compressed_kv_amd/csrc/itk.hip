@@ -413,10 +413,40 @@ __device__ void emit_bitmap(const uint32_t* bm, int nwords, uint32_t* wsum, int3
   }
 }
 
+// Index of the nth (1-based) set bit of the LDS bitmap (nwords words; n at
+// most the number of set bits), the same in every thread.
+template <int NT>
+__device__ uint32_t bitmap_nth(const uint32_t* bm, int nwords, uint32_t n, uint32_t* wsum,
+                               uint32_t* found) {
+  const int tid = threadIdx.x;
+  const int per = (nwords + NT - 1) / NT;
+  const int w0 = tid * per;
+  const int w1 = w0 + per < nwords ? w0 + per : nwords;
+  uint32_t c = 0;
+  for (int w = w0; w < w1; ++w) c += __builtin_popcount(bm[w]);
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<NT / 64>(c, wsum, total);
+  if (pos < n && n <= pos + c) {
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = bm[w];
+      const uint32_t pc = __builtin_popcount(bits);
+      if (pos + pc >= n) {
+        for (uint32_t i = pos + 1; i < n; ++i) bits &= bits - 1;   // drop the lower ones
+        *found = 32u * w + __builtin_ctz(bits);
+        break;
+      }
+      pos += pc;
+    }
+  }
+  __syncthreads();
+  return *found;
+}
+
 template <int NT>
 struct SelectLds {
   RadixLds<NT> rx;
   uint32_t wsum[NT / 64];
+  uint32_t found;
 };
 
 // The exact top-k of a row whose keys visit(f) produces (f(key, entry), each
@@ -437,18 +467,17 @@ __device__ bool select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, i
       &n_eq);
   if (tau < floor) return false;          // the same in every thread
   for (int w = tid; w < nwords; w += NT) bm[w] = 0;
-  // the need-th lowest tied index is the need-th largest of the complements
+  // of the entries tied at tau only the need lowest are kept: mark the tied
+  // ones, find the need-th set bit of the row, start the bitmap again
   uint32_t iota = 0xffffffffu;
   if (need < n_eq) {
-    uint32_t rem;
-    iota = ~radix_select_visit<32, NT>(
-        sh.rx, need,
-        [&](auto&& f) {
-          visit([&](uint32_t key, uint32_t e) {
-            if (key == tau) f(~e);
-          });
-        },
-        rem);
+    __syncthreads();
+    visit([&](uint32_t key, uint32_t e) {
+      if (key == tau) atomicOr(&bm[e >> 5], 1u << (e & 31));
+    });
+    __syncthreads();
+    iota = bitmap_nth<NT>(bm, nwords, need, sh.wsum, &sh.found);
+    for (int w = tid; w < nwords; w += NT) bm[w] = 0;
   }
   __syncthreads();
   visit([&](uint32_t key, uint32_t e) {
