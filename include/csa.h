@@ -250,9 +250,13 @@ csa_status csa_topk_select(const void* scores, int32_t score_fmt, int64_t ld,
  * ties to the lower index, ascending, -1 padded.  The score matrix is never
  * written: each query keeps a list of candidates in `workspace`, sized by
  * csa_indexer_topk_workspace_size(n_q, k) and owned by the caller (16-byte
- * aligned; its contents are scratch).  Rows whose candidate list misses (more
- * than the list holds, or fewer than k) are redone exactly from recomputed
- * scores, so the result never depends on the estimate.
+ * aligned; its contents are scratch, nothing needs clearing between calls).
+ * Candidates are the entries at or above an estimated threshold (sampled per
+ * query for a single request's query groups, chosen by each filter workgroup
+ * for its own entries when every request has one query); rows whose list
+ * misses (more than it holds, fewer than k, or a k-th key below a threshold)
+ * are redone exactly from recomputed scores, so the result never depends on
+ * the estimate.
  *   qi, ki, head_w, batch, m, relu, score_fmt   as csa_indexer_score
  *   idx    int32 [n_q][k];  1 <= k <= 4096;  rows of at most 2^20 entries
  * Errors: CSA_ERR_WORKSPACE if workspace is NULL or short; CSA_ERR_UNSUPPORTED

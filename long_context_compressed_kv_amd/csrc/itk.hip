@@ -40,6 +40,7 @@ namespace {
 constexpr int kWaves = 4;            // waves of the scoring kernels
 constexpr int kTilesPerWave = 8;     // tiles per wave, several queries per group
 constexpr int kBitmapMax = 1 << 20;  // longest row the select kernel takes
+constexpr int kMaxWg = kBitmapMax / 1024;   // filter workgroups of a streamed row, at most
 
 struct ItkArgs {
   const void* qi;
@@ -55,9 +56,10 @@ struct ItkArgs {
   int k;
   int cap;            // candidates kept per query
   int64_t max_n;      // rows are cut to this many entries (the batch's max_kv, at most 2^20)
-  uint32_t* tau;      // [n_q] threshold keys (decode: the largest of the workgroups')
+  uint32_t* tau;      // [n_q] threshold keys (query groups)
   uint32_t* cnt;      // [n_q] candidates found (may exceed cap)
   uint2* cand;        // [n_q][cap] (key, entry)
+  uint2* hdr;         // [n_q][kMaxWg] streaming: (count, threshold) of each filter workgroup
   int32_t* idx;       // [n_q][k] result
 };
 
@@ -225,6 +227,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
   __shared__ uint32_t wcnt[kWaves][QS];   // candidates per (wave, query)
   __shared__ uint32_t gbase[QS];          // the workgroup's first list slot per query
   __shared__ uint32_t stau[QS];           // the queries' thresholds
+  __shared__ uint32_t send[QS];           // end of the workgroup's slots per query
   __shared__ RadixLds<256> frx;           // the workgroup's own threshold (streaming)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
 
@@ -330,12 +333,17 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
     }
     if (lane == 0) wcnt[wave][0] = x;
     __syncthreads();
+    // the workgroup's region of the list: R = cap / (workgroups of the row)
+    // slots from be * R; its count and threshold go to its header
+    const int64_t nwg = (nvq + kWaves * EW - 1) / (kWaves * EW);
+    const uint32_t reg = (uint32_t)(a.cap / nwg);
     if (tid == 0 && qblock < a.n_q) {
       uint32_t tot = 0;
       for (int w = 0; w < kWaves; ++w) tot += wcnt[w][0];
-      gbase[0] = tot > 0 ? atomicAdd(&a.cnt[qblock], tot) : 0u;
+      a.hdr[qblock * kMaxWg + be] = make_uint2(tot, tw);
+      gbase[0] = be * reg;
+      send[0] = (be + 1) * reg;
       stau[0] = tw;
-      atomicMax(&a.tau[qblock], tw);
     }
     __syncthreads();
   } else {
@@ -354,14 +362,15 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       uint32_t tot = 0;
       for (int w = 0; w < kWaves; ++w) tot += wcnt[w][tid];
       gbase[tid] = tot > 0 ? atomicAdd(&a.cnt[qblock + tid], tot) : 0u;
+      send[tid] = (uint32_t)a.cap;
       stau[tid] = a.tau[qblock + tid];
     }
     __syncthreads();
   }
 
   // pass 2: each wave writes its entries' candidates, query by query (slots
-  // past cap are dropped; the count still records them, which sends the row
-  // to the exact redo)
+  // past the workgroup's end are dropped; the count still records them, which
+  // sends the row to the exact redo)
   for (int ql = 0; ql < QS; ++ql) {
     const int64_t q = qblock + ql;
     if (q >= a.n_q || wcnt[wave][ql] == 0) continue;   // uniform over the wave
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
     int64_t nvq = (gr.qm.t + ql + 1) / a.m;
     if (nvq > gr.qm.kv_len) nvq = gr.qm.kv_len;
     if (nvq > a.max_n) nvq = a.max_n;
-    const uint32_t tq = stau[ql];
+    const uint32_t tq = stau[ql], end = send[ql];
     uint32_t base = gbase[ql];
     for (int w = 0; w < wave; ++w) base += wcnt[w][ql];
     uint2* list = a.cand + q * (int64_t)a.cap;
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       const uint64_t m = __ballot(f);
       if (f) {
         const uint32_t slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
-        if (slot < (uint32_t)a.cap) list[slot] = make_uint2(key, (uint32_t)(e_wg + el));
+        if (slot < end) list[slot] = make_uint2(key, (uint32_t)(e_wg + el));
       }
       base += __builtin_popcountll(m);
     }
@@ -447,6 +456,8 @@ struct SelectLds {
   RadixLds<NT> rx;
   uint32_t wsum[NT / 64];
   uint32_t found;
+  uint32_t hcount[kMaxWg];         // streaming: the filter workgroups' counts
+  uint32_t hfloor, htot, hover;    // their largest threshold, total, overflow
 };
 
 // The exact top-k of a row whose keys visit(f) produces (f(key, entry), each
@@ -509,8 +520,51 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
     return;
   }
   const int nwords = (int)((n + 31) / 32);
-  const uint32_t c = a.cnt[q];
-  const uint32_t floor = a.tau[q];
+  const bool streamed = a.qpg == 1;
+  uint32_t c, floor, reg = 0;
+  int64_t nwg = 0;
+  if (streamed) {
+    // the filter workgroups' headers: counts (each within its region of
+    // reg = cap / nwg slots), the largest threshold
+    nwg = (n + entries_per_wg<FMT>(true) - 1) / entries_per_wg<FMT>(true);
+    reg = (uint32_t)(a.cap / nwg);
+    if (tid == 0) {
+      sh.hfloor = 0;
+      sh.htot = 0;
+      sh.hover = 0;
+    }
+    __syncthreads();
+    uint32_t fl = 0, tot = 0, ov = 0;
+    for (int64_t w = tid; w < nwg; w += NT) {
+      const uint2 h = a.hdr[q * kMaxWg + w];
+      sh.hcount[w] = h.x;
+      fl = h.y > fl ? h.y : fl;
+      tot += h.x;
+      ov |= h.x > reg ? 1u : 0u;
+    }
+    // reduced within each wave first: atomics of every thread on one LDS
+    // word serialise
+    if ((int64_t)(tid & ~63) < nwg) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t f2 = __shfl_xor(fl, o);
+        fl = f2 > fl ? f2 : fl;
+        tot += __shfl_xor(tot, o);
+        ov |= __shfl_xor(ov, o);
+      }
+      if ((tid & 63) == 0) {
+        atomicMax(&sh.hfloor, fl);
+        atomicAdd(&sh.htot, tot);
+        atomicOr(&sh.hover, ov);
+      }
+    }
+    __syncthreads();
+    c = sh.hover ? (uint32_t)a.cap + 1 : sh.htot;
+    floor = sh.hfloor;
+  } else {
+    c = a.cnt[q];
+    floor = a.tau[q];
+  }
   auto redo = [&]() {
     // the exact redo over the whole row
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, rl = lane & 31;
@@ -539,34 +593,40 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
     return;
   }
   const uint2* list = a.cand + q * (int64_t)a.cap;
-  if (c <= (uint32_t)(CPT * NT)) {
+  // slot i holds a candidate: below c (query groups), or within the count of
+  // its workgroup's region (streaming)
+  const uint32_t span = streamed ? (uint32_t)(nwg * reg) : c;
+  auto live = [&](uint32_t i) {
+    if (!streamed) return i < c;
+    if (i >= span) return false;
+    const uint32_t w = i / reg;
+    return i - w * reg < sh.hcount[w];
+  };
+  if (span <= (uint32_t)(CPT * NT)) {
     uint2 cr[CPT];
+    bool lv[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const uint32_t i = tid + j * NT;
-      cr[j] = i < c ? list[i] : make_uint2(0, 0);
+      lv[j] = live(i);
+      cr[j] = lv[j] ? list[i] : make_uint2(0, 0);
     }
     if (!select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
 #pragma unroll
           for (int j = 0; j < CPT; ++j)
-            if (tid + j * NT < c) f(cr[j].x, cr[j].y);
+            if (lv[j]) f(cr[j].x, cr[j].y);
         }, floor))
       redo();
   } else {
     if (!select_row<KBITS, NT>(sh, bm, nwords, a.k, out, [&](auto&& f) {
-          for (uint32_t i = tid; i < c; i += NT) {
+          for (uint32_t i = tid; i < span; i += NT) {
+            if (!live(i)) continue;
             const uint2 ce = list[i];
             f(ce.x, ce.y);
           }
         }, floor))
       redo();
   }
-}
-
-// the per-query threshold and count words, cleared before a streaming filter
-__global__ __launch_bounds__(256) void itk_clear_kernel(uint32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
 }
 
 template <int FMT, bool SBF16, int NT>
@@ -586,13 +646,13 @@ template <int FMT, bool SBF16>
 csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   const int64_t groups = (a.n_q + a.qpg - 1) / a.qpg;
   const bool stream = a.qpg == 1;
-  // tau and cnt are adjacent: 2 n_q words
-  if (stream)
-    hipLaunchKernelGGL(itk_clear_kernel, dim3((unsigned)((2 * a.n_q + 255) / 256)), dim3(256), 0, s, a.tau,
-                       2 * a.n_q);
-  else
+  // query groups: the sample sets the thresholds and clears the counts;
+  // streaming needs neither (each workgroup writes its own header)
+  csa_status st = CSA_OK;
+  if (!stream) {
     hipLaunchKernelGGL((itk_sample_kernel<FMT, SBF16>), dim3((unsigned)groups), dim3(kSampleThreads), 0, s, a);
-  csa_status st = csa_host::check_launch(stream ? "csa_indexer_topk (clear)" : "csa_indexer_topk (sample)");
+    st = csa_host::check_launch("csa_indexer_topk (sample)");
+  }
   if (st != CSA_OK) return st;
   const int64_t epw = entries_per_wg<FMT>(stream);
   const dim3 fgrid = stream ? dim3((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups)
@@ -611,10 +671,13 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   return launch_select<FMT, SBF16, 256>(a, bm_bytes, s);
 }
 
-// candidates kept per query: the threshold aims at about 3k
+// candidates kept per query: the thresholds aim at about 3k.  A multiple of
+// the largest filter chunk (2048 entries), so that a row of at most cap
+// entries gives every filter workgroup a region of a whole chunk.
 int64_t cap_for(int32_t k) {
-  const int64_t c = 6 * (int64_t)k;
-  return c > 4096 ? c : 4096;
+  int64_t c = 6 * (int64_t)k;
+  c = c > 4096 ? c : 4096;
+  return (c + 2047) / 2048 * 2048;
 }
 
 }  // namespace
@@ -623,9 +686,10 @@ using namespace csa_host;
 
 extern "C" size_t csa_indexer_topk_workspace_size(int64_t n_q, int32_t k) {
   if (n_q <= 0 || k < 1) return 0;
-  // tau and cnt per query, then the candidate lists (16-byte aligned)
+  // tau and cnt per query, then the candidate lists (16-byte aligned), then
+  // the streaming filter's workgroup headers
   const size_t head = ((size_t)n_q * 2 * 4 + 15) / 16 * 16;
-  return head + (size_t)n_q * (size_t)cap_for(k) * 8;
+  return head + (size_t)n_q * (size_t)cap_for(k) * 8 + (size_t)n_q * kMaxWg * 8;
 }
 
 extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* head_w,
@@ -677,6 +741,7 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
   a.tau = reinterpret_cast<uint32_t*>(ws);
   a.cnt = a.tau + batch->n_q;
   a.cand = reinterpret_cast<uint2*>(ws + ((size_t)batch->n_q * 2 * 4 + 15) / 16 * 16);
+  a.hdr = a.cand + (size_t)batch->n_q * a.cap;
   a.idx = idx;
   const int64_t groups = (batch->n_q + a.qpg - 1) / a.qpg;
   const int64_t max_kv = batch->max_kv < ki->rows ? batch->max_kv : ki->rows;
