@@ -529,6 +529,40 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   } else {
     q_first = (int64_t)(wg / (unsigned)a.ngroups) * a.tok;
   }
+  // ---- this lane's query row.  It follows from the group alone (its last
+  // query is min(q_first + tok - 1, n_q - 1), as the geometry has it), so the
+  // query loads are issued before the geometry's chain of metadata loads and
+  // overlap it; a dead row loads row 0 and is zeroed by a select, so no load
+  // waits behind a branch.
+  const int64_t q_last = q_first + a.tok - 1 < a.n_q ? q_first + a.tok - 1 : a.n_q - 1;
+  const int row_in_wg = rb * 32 + ql;
+  const int g_row = row_in_wg / a.hg;
+  const int h_row = hgrp * a.hg + (row_in_wg - g_row * a.hg);
+  const int64_t q_row = q_first + g_row;
+  const bool row_live = q_row <= q_last;
+  const int64_t qrow_index = q_row * a.H + h_row;    // row of the q / out tensors
+  const int64_t qrow_load = row_live ? qrow_index : 0;
+
+  // queries (B operand), pre-loaded for the whole key loop
+  constexpr int QC = F32C ? DW / 2 : DW / 16;
+  using qreg_t = typename std::conditional<F32C, float, bf16x8_t>::type;
+  qreg_t qreg[QC];
+  if constexpr (F32C) {
+    const float* qp = static_cast<const float*>(a.q) + qrow_load * D + d0 + half;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      const float v = qp[2 * c];
+      qreg[c] = row_live ? v : 0.0f;
+    }
+  } else {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow_load * D + d0 + half * 8;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * c);
+      qreg[c] = __builtin_bit_cast(bf16x8_t, row_live ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+
   Geo g = splitk && !fixed ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
   if (splitk) {
     const int chunk = fixed ? a.static_chunk : *a.ws_chunk;
@@ -536,31 +570,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
     if (g.key_hi < g.key_lo) g.key_hi = g.key_lo;   // past this query's keys: an empty part
     lds_barrier();                 // LDS of the previous item fully consumed
-  }
-
-  // ---- this lane's query row
-  const int row_in_wg = rb * 32 + ql;
-  const int g_row = row_in_wg / a.hg;
-  const int h_row = hgrp * a.hg + (row_in_wg - g_row * a.hg);
-  const int64_t q_row = g.q_first + g_row;
-  const bool row_live = q_row <= g.q_last;
-  const int64_t qrow_index = q_row * a.H + h_row;    // row of the q / out tensors
-
-  // queries (B operand), pre-loaded for the whole key loop
-  constexpr int QC = F32C ? DW / 2 : DW / 16;
-  using qreg_t = typename std::conditional<F32C, float, bf16x8_t>::type;
-  qreg_t qreg[QC];
-  if constexpr (F32C) {
-    const float* qp = static_cast<const float*>(a.q) + qrow_index * D + d0 + half;
-#pragma unroll
-    for (int c = 0; c < QC; ++c) qreg[c] = row_live ? qp[2 * c] : 0.0f;
-  } else {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow_index * D + d0 + half * 8;
-#pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      uint4 v = row_live ? *reinterpret_cast<const uint4*>(qp + 16 * c) : make_uint4(0, 0, 0, 0);
-      qreg[c] = __builtin_bit_cast(bf16x8_t, v);
-    }
   }
 
   constexpr int NDB = DW / 32;
