@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -122,6 +122,21 @@ typedef struct csa_tensor {
  *                               (as csa_kv_compress_append writes them); C
  *                               must be at least the window plus the
  *                               request's queries minus one
+ *   kv_block_table            : NULL, or the paged compressed cache (page
+ *                               "DeepSeek V4 深度解析", section 4, KV-cache
+ *                               management: compressed entries kept in blocks
+ *                               that each cover LCM of the compression ratios
+ *                               raw tokens, i.e. 128 raw tokens = 32 CSA
+ *                               entries or 1 HCA entry).  int32 DEVICE array
+ *                               [n_req][kv_block_stride] of block ids; entry j
+ *                               of r is row table[r*stride + j/P]*P + j%P of
+ *                               the entry and indexer-key tensors, with P =
+ *                               kv_block_rows (a power of two, 1 .. 2^20).
+ *                               kv_off[r+1]-kv_off[r] still counts r's entries
+ *                               (at most stride*P are used).  A block id whose
+ *                               rows fall outside a tensor reads row 0 there
+ *                               (reads stay in bounds; that entry's value is
+ *                               unspecified).
  * n_q = q_off[n_req] and max_kv >= every kv_off[r+1]-kv_off[r] are host-side
  * copies used to size launch grids. */
 typedef struct csa_batch {
@@ -134,6 +149,10 @@ typedef struct csa_batch {
   const int64_t* kv_off;
   const int64_t* raw_off;
   const int64_t* raw_pos;
+  const int32_t* kv_block_table;
+  int64_t kv_block_stride;
+  int32_t kv_block_rows;
+  int32_t reserved;
 } csa_batch;
 
 /* ---------------------------------------------------------------------------
@@ -183,7 +202,14 @@ csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_p
  *              replaying such a tail re-emits the entries it completes
  *   entry_off  device int64 [n_req]: entry i of request r goes to row
  *              entry_off[r] + i of `cache` when position (i+1)m-1 is appended
- *              (rows outside the cache are skipped)
+ *              (rows outside the cache are skipped); ignored (may be NULL)
+ *              when block_table is given
+ *   block_table  NULL, or the paged compressed cache (as csa_batch's
+ *              kv_block_table): device int32 [n_req][block_stride] block ids,
+ *              entry i of request r goes to row table[r*block_stride + i/P]*P
+ *              + i%P with P = block_rows (a power of two, 1 .. 2^20); an entry
+ *              past the request's slots, a negative block id or a row outside
+ *              the cache is not written
  *   cache      F32, BF16 or FP8_MIXED (dim 512) entries of dim = x->dim, dim in
  *              {64, 128, 256, 512}
  *   window     NULL, or F32 / BF16 rows of dim: the raw row also goes to row
@@ -197,9 +223,10 @@ size_t csa_kv_append_state_size(int64_t n_req, int32_t dim);
 csa_status csa_kv_compress_append(const csa_tensor* x, const float* logits,
                                   const float* slot_bias, int32_t m, int32_t w,
                                   const int64_t* pos, float* state, const int64_t* entry_off,
-                                  const csa_tensor* cache, const csa_tensor* window,
-                                  const int64_t* window_off, int32_t window_rows,
-                                  hipStream_t stream);
+                                  const int32_t* block_table, int64_t block_stride,
+                                  int32_t block_rows, const csa_tensor* cache,
+                                  const csa_tensor* window, const int64_t* window_off,
+                                  int32_t window_rows, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * csa_indexer_score - CSA step 2, the lightning indexer.

@@ -21,12 +21,18 @@ class CsaTensor(ctypes.Structure):
                 ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("rope", ctypes.c_void_p)]
 
 
+# csa_abi_version() of the library these bindings describe (include/csa.h)
+ABI_VERSION = 2
+
+
 class CsaBatch(ctypes.Structure):
     _fields_ = [("n_req", ctypes.c_int32), ("window_ring", ctypes.c_int32),
                 ("n_q", ctypes.c_int64), ("max_kv", ctypes.c_int64),
                 ("q_off", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
                 ("kv_off", ctypes.c_void_p), ("raw_off", ctypes.c_void_p),
-                ("raw_pos", ctypes.c_void_p)]
+                ("raw_pos", ctypes.c_void_p), ("kv_block_table", ctypes.c_void_p),
+                ("kv_block_stride", ctypes.c_int64), ("kv_block_rows", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class CsaError(RuntimeError):
@@ -50,7 +56,7 @@ def load():
     B = ctypes.POINTER(CsaBatch)
     sig = {
         "csa_kv_compress": [T, P, I64, P, I32, I32, I64, I64, T, P],
-        "csa_kv_compress_append": [T, P, P, I32, I32, P, P, P, T, T, P, I32, P],
+        "csa_kv_compress_append": [T, P, P, I32, I32, P, P, P, P, I64, I32, T, T, P, I32, P],
         "csa_indexer_score": [T, I32, P, T, B, I32, I32, P, I32, I64, P],
         "csa_topk_select": [P, I32, I64, B, I32, I32, P, P],
         "csa_indexer_topk": [T, I32, P, T, B, I32, I32, I32, I32, P, P, ctypes.c_size_t, P],
@@ -73,6 +79,9 @@ def load():
     lib.csa_attn_workspace_size.argtypes = [I64, I32, I32, I64, I32]
     lib.csa_abi_version.restype = ctypes.c_int
     lib.csa_abi_version.argtypes = []
+    if lib.csa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.csa_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     lib.csa_status_string.restype = ctypes.c_char_p
     lib.csa_status_string.argtypes = [ctypes.c_int]
     lib.csa_last_error.restype = ctypes.c_char_p

@@ -371,12 +371,12 @@ __device__ __forceinline__ void key_meta(const AttnArgs& a, const Geo& g, int kk
       const int slot = kk - owner * a.k;
       const int j = a.idx[(g.q_first + owner) * (int64_t)a.k + slot];
       if (j >= 0 && j < g.kv_len) {
-        row = (int)(g.kv_base + j);
+        row = (int)entry_row(a.b, g.kv_base, j);
         lo = owner;
         hi = owner + 1;
       }
     } else {
-      row = (int)(g.kv_base + kk);
+      row = (int)entry_row(a.b, g.kv_base, kk);
       lo = (int64_t)(kk + 1) * a.m - 1 - g.t_first;
       hi = INT64_MAX;
     }
@@ -1306,6 +1306,7 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   a.b = BatchDev{batch->n_req, batch->q_off, batch->q_pos, has_kv ? batch->kv_off : nullptr,
                  has_raw ? batch->raw_off : nullptr, has_raw ? batch->raw_pos : nullptr,
                  has_kv ? kv->rows : 0, has_raw ? raw->rows : 0, batch->window_ring};
+  if (const csa_status st = batch_pages(batch, a.b, "csa_sparse_mqa_attn"); st != CSA_OK) return st;
   a.m = m;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;

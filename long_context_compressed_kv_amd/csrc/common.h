@@ -169,7 +169,7 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
 // clamped to the extents of the tensors involved.
 struct QueryMeta {
   int64_t t;        // absolute position of the query
-  int64_t kv_base;  // first entry row of the request
+  int64_t kv_base;  // first entry row of the request (paged: its first block-table slot)
   int64_t n_vis;    // visible entries
   int64_t kv_len;   // entry rows of the request
   int64_t raw_base; // first raw row of the request
@@ -187,7 +187,28 @@ struct BatchDev {
   int64_t kv_rows;   // rows of the entry tensor (0 if none)
   int64_t raw_rows;  // rows of the raw tensor (0 if none)
   int ring;          // raw rows of a request are a ring (position p at row p mod rows)
+  // paged entries (null: contiguous): entry j of request r at row
+  // pages[r * page_stride + j / 2^page_shift] * 2^page_shift + j mod 2^page_shift
+  const int32_t* pages = nullptr;
+  int64_t page_stride = 0;
+  int page_shift = 0;
 };
+
+// Row of entry j of a request whose QueryMeta::kv_base is kv_base.  A block
+// id that points outside the entry tensor gives row 0 (every read stays in
+// bounds; such an entry's value is unspecified).
+__device__ __forceinline__ int64_t entry_row(const BatchDev& b, int64_t kv_base, int64_t j) {
+  if (b.pages == nullptr) return kv_base + j;
+  const int64_t blk = b.pages[kv_base + (j >> b.page_shift)];
+  const int64_t row = (blk << b.page_shift) + (j & ((1ll << b.page_shift) - 1));
+  return blk >= 0 && row < b.kv_rows ? row : 0;
+}
+
+// The same for an entry that may lie past the request's entries (ok false):
+// such an entry takes row 0 and reads no block table.
+__device__ __forceinline__ int64_t entry_row_if(const BatchDev& b, int64_t kv_base, int64_t j, bool ok) {
+  return ok ? entry_row(b, kv_base, j) : 0;
+}
 
 __device__ __forceinline__ QueryMeta query_meta(const BatchDev& b, int64_t q, int m) {
   QueryMeta r;
@@ -201,7 +222,15 @@ __device__ __forceinline__ QueryMeta query_meta(const BatchDev& b, int64_t q, in
   const int64_t rpos = has_raw ? b.raw_pos[req] : 0;
   r.t = qpos + (q - qoff);
   if (r.t < 0) r.t = 0;
-  if (has_kv) {
+  if (has_kv && b.pages != nullptr) {
+    // paged: kv_off counts the entries, rows come from the block table
+    r.kv_base = (int64_t)req * b.page_stride;
+    r.kv_len = kv1 > kv0 ? kv1 - kv0 : 0;
+    const int64_t cap = b.page_stride << b.page_shift;   // the request's slots in the table
+    if (r.kv_len > cap) r.kv_len = cap;
+    const int64_t nc = (r.t + 1) / m;
+    r.n_vis = nc < r.kv_len ? nc : r.kv_len;
+  } else if (has_kv) {
     const int64_t lo = clamp64(kv0, 0, b.kv_rows);
     const int64_t hi = clamp64(kv1, lo, b.kv_rows);
     r.kv_base = lo;
@@ -239,5 +268,8 @@ void clear_error();
 csa_status check_launch(const char* what);
 bool fmt_valid_tensor(const csa_tensor* t, bool need_data = true);
 int64_t rows_of(const csa_tensor* t);
+// Copies the paged-cache fields of `b` (kv_block_table ...) into `d` after
+// checking them; `who` names the entry point in the error.
+csa_status batch_pages(const csa_batch* b, csa::BatchDev& d, const char* who);
 
 }  // namespace csa_host

@@ -44,6 +44,22 @@ bool fmt_valid_tensor(const csa_tensor* t, bool need_data) {
 
 int64_t rows_of(const csa_tensor* t) { return t == nullptr ? 0 : t->rows; }
 
+csa_status batch_pages(const csa_batch* b, csa::BatchDev& d, const char* who) {
+  d.pages = nullptr;
+  d.page_stride = 0;
+  d.page_shift = 0;
+  if (b->kv_block_table == nullptr) return CSA_OK;
+  const int32_t p = b->kv_block_rows;
+  if (b->kv_block_stride < 1 || p < 1 || p > (1 << 20) || (p & (p - 1)) != 0)
+    return fail(CSA_ERR_INVALID_ARGUMENT,
+                "%s: kv_block_table needs kv_block_stride >= 1 and kv_block_rows a power of two in [1, 2^20]",
+                who);
+  d.pages = b->kv_block_table;
+  d.page_stride = b->kv_block_stride;
+  d.page_shift = __builtin_ctz((unsigned)p);
+  return CSA_OK;
+}
+
 }  // namespace csa_host
 
 extern "C" {

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t e = e_wg + e_wave + (b * TB + tb) * 32 + rl;
-        load_key<FMT>(a.ki, a.ki_scale, kv_base + e, e < n_scan, half, k[tb]);
+        load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, kv_base, e, e < n_scan), e < n_scan, half, k[tb]);
       }
     };
     auto score_batch = [&](int b, const KeyOp<FMT>* k) {
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IdxArgs a) {
     if (e_wg + e_wave + t * 32 >= n_scan) break;
     KeyOp<FMT> kt;
     const int64_t e = e_wg + e_wave + t * 32 + rl;
-    load_key<FMT>(a.ki, a.ki_scale, kv_base + e, e < n_scan, half, kt);
+    load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, kv_base, e, e < n_scan), e < n_scan, half, kt);
     score_tile(t, kt, stage, staged);
   }
   if constexpr (!STREAM) {
@@ -249,6 +249,7 @@ extern "C" csa_status csa_indexer_score(const csa_tensor* qi, int32_t n_heads,
   a.ki_scale = static_cast<const uint8_t*>(ki->scale);
   a.b = BatchDev{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, nullptr, nullptr,
                  ki->rows, 0};
+  if (const csa_status st = batch_pages(batch, a.b, "csa_indexer_score"); st != CSA_OK) return st;
   a.m = m;
   a.relu = relu ? 1 : 0;
   a.qpg = batch->n_req == 1 ? 8 : 1;

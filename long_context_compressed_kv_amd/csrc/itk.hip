@@ -168,7 +168,9 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
       KeyOp<FMT> kt[STB];
 #pragma unroll
       for (int tb = 0; tb < STB; ++tb)
-        load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + run_start(r0 + tb) + rl, r0 + tb < nrun, half, kt[tb]);
+        load_key<FMT>(a.ki, a.ki_scale,
+                      entry_row_if(a.b, gr.qm.kv_base, run_start(r0 + tb) + rl, r0 + tb < nrun),
+                      r0 + tb < nrun, half, kt[tb]);
 #pragma unroll
       for (int tb = 0; tb < STB; ++tb) {
         const int r = r0 + tb;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t e = e_wg + e_wave + (b * TB + tb) * 32 + rl;
-        load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n_scan, half, k[tb]);
+        load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, gr.qm.kv_base, e, e < n_scan), e < n_scan, half, k[tb]);
       }
     };
     auto score_batch = [&](int b, const KeyOp<FMT>* k) {
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       if (!tile_live(t)) break;
       KeyOp<FMT> kt;
       const int64_t e = e_wg + e_wave + t * 32 + rl;
-      load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n_scan, half, kt);
+      load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, gr.qm.kv_base, e, e < n_scan), e < n_scan, half, kt);
       score_tile(t, kt);
     }
   }
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
       for (int64_t t0 = (int64_t)wave * 32; t0 < n; t0 += NW * 32) {
         const int64_t e = t0 + rl;
         KeyOp<FMT> kt;
-        load_key<FMT>(a.ki, a.ki_scale, gr.qm.kv_base + e, e < n, half, kt);
+        load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, gr.qm.kv_base, e, e < n), e < n, half, kt);
         const f32x16_t acc = tile_dots<FMT>(gr.aq, kt);
         float s = 0.0f;
 #pragma unroll
@@ -731,6 +733,7 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
   a.ki = ki->data;
   a.ki_scale = static_cast<const uint8_t*>(ki->scale);
   a.b = BatchDev{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, nullptr, nullptr, ki->rows, 0};
+  if (const csa_status st = batch_pages(batch, a.b, "csa_indexer_topk"); st != CSA_OK) return st;
   a.m = m;
   a.relu = relu ? 1 : 0;
   a.qpg = batch->n_req == 1 ? 8 : 1;

@@ -33,6 +33,9 @@ struct AppendArgs {
   const int64_t* pos;     // [n_req]
   float* state;           // [n_req][2][dim + kHead]
   const int64_t* entry_off;
+  const int32_t* pages;   // or a block table: entry i of r at row pages[r*page_stride + i/P]*P + i%P
+  int64_t page_stride;
+  int page_shift;         // P = 2^page_shift
   void* cache;            // entry rows (F32 / BF16 / mixed nope codes)
   uint8_t* cache_scale;
   uint16_t* cache_rope;
@@ -107,8 +110,14 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
       float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = acc[e][j] * inv;
-      const int64_t row = a.entry_off[r] + i;
-      if (row < 0 || row >= a.cache_rows) continue;   // metadata outside the cache
+      int64_t row = -1;
+      if (a.pages == nullptr) {
+        row = a.entry_off[r] + i;
+      } else if ((i >> a.page_shift) < a.page_stride) {
+        const int64_t blk = a.pages[(int64_t)r * a.page_stride + (i >> a.page_shift)];
+        row = blk < 0 ? -1 : (blk << a.page_shift) + (i & ((1ll << a.page_shift) - 1));
+      }
+      if (row < 0 || row >= a.cache_rows) continue;   // metadata outside the cache: not written
       if constexpr (OUTF == CSA_F32) {
         float* dst = static_cast<float*>(a.cache) + row * a.dim + d0;
         for (int j = 0; j < vpl; ++j) dst[j] = v[j];
@@ -172,9 +181,11 @@ extern "C" size_t csa_kv_append_state_size(int64_t n_req, int32_t dim) {
 extern "C" csa_status csa_kv_compress_append(const csa_tensor* x, const float* logits,
                                              const float* slot_bias, int32_t m, int32_t w,
                                              const int64_t* pos, float* state,
-                                             const int64_t* entry_off, const csa_tensor* cache,
-                                             const csa_tensor* window, const int64_t* window_off,
-                                             int32_t window_rows, hipStream_t stream) {
+                                             const int64_t* entry_off, const int32_t* block_table,
+                                             int64_t block_stride, int32_t block_rows,
+                                             const csa_tensor* cache, const csa_tensor* window,
+                                             const int64_t* window_off, int32_t window_rows,
+                                             hipStream_t stream) {
   clear_error();
   if (!fmt_valid_tensor(x) || !fmt_valid_tensor(cache))
     return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress_append: bad tensor descriptor");
@@ -198,9 +209,13 @@ extern "C" csa_status csa_kv_compress_append(const csa_tensor* x, const float* l
     if (window_off == nullptr || window_rows < 1)
       return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress_append: window needs window_off and window_rows >= 1");
   }
+  if (block_table != nullptr &&
+      (block_stride < 1 || block_rows < 1 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0))
+    return fail(CSA_ERR_INVALID_ARGUMENT,
+                "csa_kv_compress_append: block_table needs block_stride >= 1 and block_rows a power of two in [1, 2^20]");
   if (n_req == 0) return CSA_OK;
   if (logits == nullptr || slot_bias == nullptr || pos == nullptr || state == nullptr ||
-      entry_off == nullptr)
+      (entry_off == nullptr && block_table == nullptr))
     return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress_append: null pointer");
   AppendArgs a{};
   a.x = x->data;
@@ -213,6 +228,9 @@ extern "C" csa_status csa_kv_compress_append(const csa_tensor* x, const float* l
   a.pos = pos;
   a.state = state;
   a.entry_off = entry_off;
+  a.pages = block_table;
+  a.page_stride = block_table != nullptr ? block_stride : 0;
+  a.page_shift = block_table != nullptr ? __builtin_ctz((unsigned)block_rows) : 0;
   a.cache = cache->data;
   a.cache_scale = static_cast<uint8_t*>(cache->scale);
   a.cache_rope = static_cast<uint16_t*>(cache->rope);

@@ -99,6 +99,9 @@ class Batch:
     n_q: int
     max_kv: int
     window_ring: bool = False   # raw rows of a request form a ring (see csa_batch)
+    # paged entries (see csa_batch): int32 [n_req, stride] block ids, P entries a block
+    kv_block_table: Optional[torch.Tensor] = None
+    kv_block_rows: int = 0
 
     @property
     def n_req(self):
@@ -109,9 +112,16 @@ class Batch:
             if t is not None:
                 _need_cuda(t)
                 assert t.dtype == torch.int64
+        stride = 0
+        if self.kv_block_table is not None:
+            _need_cuda(self.kv_block_table)
+            assert self.kv_block_table.dtype == torch.int32 and self.kv_block_table.dim() == 2
+            assert self.kv_block_table.is_contiguous()
+            stride = self.kv_block_table.shape[1]
         return CsaBatch(self.n_req, int(bool(self.window_ring)), self.n_q, self.max_kv,
                         _ptr(self.q_off), _ptr(self.q_pos),
-                        _ptr(self.kv_off), _ptr(self.raw_off), _ptr(self.raw_pos))
+                        _ptr(self.kv_off), _ptr(self.raw_off), _ptr(self.raw_pos),
+                        _ptr(self.kv_block_table), stride, int(self.kv_block_rows), 0)
 
     @staticmethod
     def make(q_counts, q_pos, kv_counts=None, raw_counts=None, raw_pos=None, device="cuda"):
@@ -150,16 +160,25 @@ def kv_append_state_size(n_req, dim):
 
 
 def kv_compress_append(x: KV, logits, slot_bias, m, w, pos, state, entry_off, cache: KV,
-                       window: Optional[KV] = None, window_off=None, window_rows=0):
+                       window: Optional[KV] = None, window_off=None, window_rows=0,
+                       block_table=None, block_rows=0):
     """Decode-time compression: appends row r of x (at position pos[r]) to
-    request r's state; finished entries go to cache row entry_off[r] + i, and
-    with a window the raw row to window_off[r] + pos[r] % window_rows."""
-    _need_cuda(logits, slot_bias, pos, state, entry_off, window_off)
+    request r's state; finished entries go to cache row entry_off[r] + i (or,
+    with an int32 [n_req, stride] block table, to row
+    block_table[r, i // block_rows] * block_rows + i % block_rows), and with a
+    window the raw row to window_off[r] + pos[r] % window_rows."""
+    _need_cuda(logits, slot_bias, pos, state, entry_off, window_off, block_table)
+    stride = 0
+    if block_table is not None:
+        assert block_table.dtype == torch.int32 and block_table.dim() == 2
+        assert block_table.is_contiguous()
+        stride = block_table.shape[1]
     lib = _lib.load()
     xc, cc = x.c(), cache.c()
     wc = window.c() if window is not None else None
     check(lib.csa_kv_compress_append(ctypes.byref(xc), _ptr(logits), _ptr(slot_bias), int(m),
                                      int(w), _ptr(pos), _ptr(state), _ptr(entry_off),
+                                     _ptr(block_table), stride, int(block_rows),
                                      ctypes.byref(cc), ctypes.byref(wc) if wc is not None else None,
                                      _ptr(window_off), int(window_rows), _stream()),
           "csa_kv_compress_append")

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
     assert lib.csa_status_string(0) == b"ok"
     assert lib.csa_status_string(3) == b"workspace too small"
 
@@ -77,9 +77,10 @@ def _batch(n_q=4, n_req=1, max_kv=16):
 def test_kv_append_validation(lib):
     """Arguments the host refuses before any launch (no device needed)."""
     x, cache = _t(1, 128, 4), _t(1, 128, 64)
-    f = lambda xx, cc, m=4, w=8, win=None, woff=FAKE, wrows=0, pos=FAKE, st=FAKE: \
-        lib.csa_kv_compress_append(ctypes.byref(xx), FAKE, FAKE, m, w, pos, st, FAKE,
-                                   ctypes.byref(cc), ctypes.byref(win) if win is not None else None,
+    f = lambda xx, cc, m=4, w=8, win=None, woff=FAKE, wrows=0, pos=FAKE, st=FAKE, eoff=FAKE, \
+        table=None, stride=0, brows=0: \
+        lib.csa_kv_compress_append(ctypes.byref(xx), FAKE, FAKE, m, w, pos, st, eoff, table, stride,
+                                   brows, ctypes.byref(cc), ctypes.byref(win) if win is not None else None,
                                    woff, wrows, None)
     assert f(x, cache, w=9) == BAD_ARG                            # w > 2m
     assert f(x, cache, w=3) == BAD_ARG                            # w < m
@@ -91,6 +92,12 @@ def test_kv_append_validation(lib):
     assert f(x, cache, win=_t(1, 128, 256), woff=None, wrows=128) == BAD_ARG
     assert f(x, cache, pos=None) == BAD_ARG
     assert f(_t(1, 128, 0), cache, pos=None) == 0                 # no requests: nothing to do
+    # a paged cache: block rows a power of two, a stride of at least one block
+    assert f(x, cache, table=FAKE, stride=0, brows=32) == BAD_ARG
+    assert f(x, cache, table=FAKE, stride=4, brows=24) == BAD_ARG
+    assert f(x, cache, table=FAKE, stride=4, brows=0) == BAD_ARG
+    assert f(x, cache, eoff=None) == BAD_ARG                       # neither rows nor blocks
+    assert f(_t(1, 128, 0), cache, eoff=None, table=FAKE, stride=4, brows=32) == 0
     assert lib.csa_kv_append_state_size(3, 128) == 3 * 2 * 132 * 4
 
 
@@ -115,6 +122,24 @@ def test_indexer_validation(lib):
     assert f(_t(1, 64, 12), 4, ki, bt, 16) == BAD_ARG        # rows != n_q * heads
     assert f(qi, 4, ki, bt, 16, sf=2) == UNSUPPORTED         # score format
     assert f(_t(3, 64, 16, scale=None), 4, _t(3, 64, 32), bt, 16) == BAD_ARG  # MXFP4 without scales
+
+
+def test_block_table_validation(lib):
+    """A paged batch (kv_block_table) needs a stride of at least one block and
+    a power-of-two block size; every call that reads entries checks it."""
+    for stride, rows in ((0, 32), (4, 24), (4, 0), (4, 1 << 21)):
+        bt = _batch(n_q=2)
+        bt.kv_block_table, bt.kv_block_stride, bt.kv_block_rows = FAKE, stride, rows
+        q, kv = _t(1, 128, 2 * 64), _t(1, 128, 100)
+        assert lib.csa_sparse_mqa_attn(ctypes.byref(q), 64, ctypes.byref(kv), None, 0, None, 0,
+                                       ctypes.byref(bt), 4, 0.1, FAKE, 1, None, 0, None, 0,
+                                       None) == BAD_ARG
+        qi, ki = _t(1, 64, 8), _t(1, 64, 32)
+        assert lib.csa_indexer_score(ctypes.byref(qi), 4, None, ctypes.byref(ki), ctypes.byref(bt),
+                                     4, 1, FAKE, 1, 16, None) == BAD_ARG
+        assert lib.csa_indexer_topk(ctypes.byref(qi), 4, None, ctypes.byref(ki), ctypes.byref(bt),
+                                    4, 1, 1, 8, FAKE, FAKE, 1 << 30, None) == BAD_ARG
+        assert b"kv_block" in lib.csa_last_error()
 
 
 def test_topk_validation(lib):

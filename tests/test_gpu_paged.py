@@ -1,0 +1,185 @@
+"""The paged compressed cache (csa_batch.kv_block_table, and the block table
+of csa_kv_compress_append): every call that reads or writes compressed
+entries gives bit for bit the result of the same call on the entries stored
+contiguously.  Blocks are handed out in a shuffled order with spare blocks
+between them, and rows no request owns hold large garbage values, so a row
+read or written through a wrong block shows up."""
+import dataclasses
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_compressed_kv_amd import ops
+from long_context_compressed_kv_amd.ops import BF16, F32, KV, Batch
+
+from gpu_inputs import dev_f32, dev_kv
+
+pytestmark = pytest.mark.gpu
+
+
+def _paged(rng, per_req, P, spare=5):
+    """per_req: [n_r, dim] float arrays.  Returns (rows [blocks*P, dim], table
+    int32 [n_req, stride]) with request r's entry j at row
+    table[r, j // P] * P + j % P."""
+    dim = per_req[0].shape[1]
+    nb = [(len(e) + P - 1) // P for e in per_req]
+    stride = max(max(nb), 1)
+    total = sum(nb) + spare
+    ids = rng.permutation(total)
+    rows = (rng.standard_normal((total * P, dim)) * 40).astype(np.float32)
+    table = np.full((len(per_req), stride), -1, np.int32)
+    nxt = 0
+    for r, e in enumerate(per_req):
+        for b in range(nb[r]):
+            blk = int(ids[nxt])
+            nxt += 1
+            table[r, b] = blk
+            part = e[b * P:(b + 1) * P]
+            rows[blk * P: blk * P + len(part)] = part
+    return rows, table
+
+
+def _paged_batch(batch, table, P):
+    return dataclasses.replace(batch, kv_block_table=torch.from_numpy(table).cuda(), kv_block_rows=P)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_case(name):
+    """(H, D, kv_fmt, m, P, q_counts, q_pos, sparse k, window, split_keys)."""
+    return {
+        "hca_prefill_d128": (64, 128, "bf16", 128, 1, [200], [5000], 0, 128, 0),
+        "csa_prefill_d128_multi": (128, 128, "bf16", 4, 32, [40, 1, 25], [900, 77, 3000], 0, 128, 0),
+        "csa_decode_sparse_d512": (64, 512, "fp8_mixed", 4, 32, [1] * 6,
+                                   [4000, 131, 9000, 40, 2047, 700], 64, 128, 128),
+        "hca_decode_dense_d512": (64, 512, "fp8_mixed", 128, 1, [1] * 5,
+                                  [70000, 300, 128, 40000, 9999], 0, 128, 128),
+    }[name]
+
+
+@pytest.mark.parametrize("name", ["hca_prefill_d128", "csa_prefill_d128_multi",
+                                  "csa_decode_sparse_d512", "hca_decode_dense_d512"])
+def test_attention_paged_equals_contiguous(name):
+    H, D, kv_fmt, m, P, q_counts, q_pos, k, window, split = _attn_case(name)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    n_req = len(q_counts)
+    n_ent = [(p + c) // m for p, c in zip(q_pos, q_counts)]        # entries up to the last query
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    raw_pos = [max(0, p - window) for p in q_pos]
+    raws = [rng.standard_normal((p + c - rp, D)).astype(np.float32)
+            for p, c, rp in zip(q_pos, q_counts, raw_pos)]
+    n_q = sum(q_counts)
+    q = rng.standard_normal((n_q * H, D)).astype(np.float32)
+    idx_d = None
+    if k:
+        idx = np.full((n_q, k), -1, np.int32)
+        i = 0
+        for r in range(n_req):
+            for t in range(q_counts[r]):
+                nv = min((q_pos[r] + t + 1) // m, n_ent[r])
+                c = min(k, nv) - (t % 2)
+                if c > 0:
+                    idx[i, :c] = np.sort(rng.choice(nv, c, replace=False))
+                i += 1
+        idx_d = torch.from_numpy(idx).cuda()
+    batch = Batch.make(q_counts, q_pos, kv_counts=n_ent, raw_counts=[len(x) for x in raws],
+                       raw_pos=raw_pos)
+    rows, table = _paged(rng, ents, P)
+    qd, rd = dev_kv(q, "bf16"), dev_kv(np.concatenate(raws), "bf16")
+    outs = []
+    for kvd, bt in ((dev_kv(np.concatenate(ents), kv_fmt), batch),
+                    (dev_kv(rows, kv_fmt), _paged_batch(batch, table, P))):
+        out = torch.empty(n_q * H, D, device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty(n_q * H, device="cuda")
+        ops.sparse_mqa_attn(qd, H, kvd, idx_d, k, rd, window, bt, m, out, BF16, lse, split_keys=split)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0][0].float()).all()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------------- indexer and top-k
+
+@pytest.mark.parametrize("fmt,score_fmt,ctx,q_counts", [
+    ("bf16", "bf16", [20003, 803, 70001, 4, 16387], [1] * 5),   # decode (streamed filter)
+    ("mxfp4", "f32", [20003, 803, 70001, 4, 16387], [1] * 5),
+    ("bf16", "bf16", [60000], [48]),                             # prefill, sampled threshold
+])
+def test_indexer_and_topk_paged_equal_contiguous(fmt, score_fmt, ctx, q_counts):
+    rng = np.random.default_rng(91 + len(ctx))
+    m, k, P = 4, 64, 32
+    n_ent = [(p + c) // m for p, c in zip(ctx, q_counts)]
+    keys = [(rng.standard_normal((n, 64)) * 0.125).astype(np.float32) for n in n_ent]
+    n_q = sum(q_counts)
+    qi = (rng.standard_normal((n_q * 4, 64)) * 0.125).astype(np.float32)
+    batch = Batch.make(q_counts, ctx, kv_counts=n_ent)
+    rows, table = _paged(rng, keys, P)
+    qd = dev_kv(qi, fmt)
+    sf = F32 if score_fmt == "f32" else BF16
+    dt = torch.float32 if score_fmt == "f32" else torch.bfloat16
+    res = []
+    for kd, bt in ((dev_kv(np.concatenate(keys), fmt), batch),
+                   (dev_kv(rows, fmt), _paged_batch(batch, table, P))):
+        scores = torch.zeros(n_q, max(n_ent), device="cuda", dtype=dt)
+        ops.indexer_score(qd, 4, kd, bt, m, scores, sf)
+        idx = ops.indexer_topk(qd, 4, kd, bt, m, sf, k)
+        res.append((scores, idx))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0])
+    assert torch.equal(res[0][1], res[1][1])
+
+
+# ------------------------------------------------------------------- append
+
+@pytest.mark.parametrize("m,w,P,out_fmt,D", [(4, 8, 32, "bf16", 128), (128, 256, 1, "bf16", 128),
+                                             (4, 8, 32, "fp8_mixed", 512)])
+def test_append_paged_equals_contiguous(m, w, P, out_fmt, D):
+    """Decode-time compression writing finished entries through a block table
+    gives the rows the contiguous layout gets, at the remapped places; rows
+    of no block stay untouched."""
+    rng = np.random.default_rng(m + P + D)
+    lens = [300, 37, 0, 140] if m == 4 else [600, 130, 0, 260]
+    n_req, T = len(lens), max(lens)
+    n_ent = [L // m for L in lens]
+    x = rng.standard_normal((T, n_req, D)).astype(np.float32)
+    z = rng.standard_normal((T, n_req)).astype(np.float32)
+    pos = np.full((T, n_req), -1, np.int64)
+    for r, L in enumerate(lens):
+        pos[:L, r] = np.arange(L)
+    b = dev_f32(rng.standard_normal(w).astype(np.float32))
+    xd, zd, pd = dev_kv(x.reshape(-1, D), "bf16"), dev_f32(z), torch.from_numpy(pos).cuda()
+    # contiguous
+    off = np.concatenate([[0], np.cumsum(n_ent)]).astype(np.int64)
+    fmt_code = {"bf16": BF16, "fp8_mixed": ops.FP8_MIXED}[out_fmt]
+    cont = KV.empty(fmt_code, max(int(off[-1]), 1), D)
+    # paged: shuffled blocks; every row starts as encoded garbage, and the
+    # rows no entry owns must still hold it afterwards
+    _, table = _paged(rng, [np.zeros((n, 1), np.float32) for n in n_ent], P)
+    n_rows = (int(table.max()) + 1 + 2) * P
+    garbage = (rng.standard_normal((n_rows, D)) * 40).astype(np.float32)
+    paged = dev_kv(garbage, "bf16" if out_fmt == "bf16" else "fp8_mixed")
+    before = [t.clone() for t in (paged.data, paged.scale, paged.rope) if t is not None]
+    e_off = torch.from_numpy(off[:-1].copy()).cuda()
+    tab = torch.from_numpy(table).cuda()
+    for layout in ("cont", "paged"):
+        state = torch.full((ops.kv_append_state_size(n_req, D) // 4,), float("nan"), device="cuda")
+        for t in range(T):
+            if layout == "cont":
+                ops.kv_compress_append(xd.narrow(t * n_req, n_req), zd[t], b, m, w, pd[t], state, e_off, cont)
+            else:
+                ops.kv_compress_append(xd.narrow(t * n_req, n_req), zd[t], b, m, w, pd[t], state, None,
+                                       paged, block_table=tab, block_rows=P)
+    torch.cuda.synchronize()
+    owned = np.zeros(n_rows, bool)
+    for r, n in enumerate(n_ent):
+        for j in range(n):
+            row = int(table[r, j // P]) * P + j % P
+            owned[row] = True
+            for a, c in zip((paged.data, paged.scale, paged.rope), (cont.data, cont.scale, cont.rope)):
+                if a is not None:
+                    assert torch.equal(a[row], c[int(off[r]) + j]), (r, j)
+    free = torch.from_numpy(~owned).cuda()
+    for a, b0 in zip([t for t in (paged.data, paged.scale, paged.rope) if t is not None], before):
+        assert torch.equal(a[free], b0[free])
