@@ -142,9 +142,10 @@ class Decode:
     """One decode step over one or more layers; `copies` input sets rotated so
     successive steps do not find their data in the last-level cache."""
 
-    def __init__(self, wid, copies=3):
+    def __init__(self, wid, copies=3, paged=False):
         self.wl = wl = synth.WORKLOADS[wid]
         gen = Gen(2000 + wid)
+        perm_gen = torch.Generator().manual_seed(3000 + wid)
         ctxs = [int(c) for c in synth.decode_contexts(wl)]
         B, D, H = len(ctxs), wl.dim, wl.heads
         specs = wl.layers if wl.kind == "mixed_decode" else [("csa", wl.m, wl.k)]
@@ -157,15 +158,29 @@ class Decode:
                 csa = kind == "csa"
                 n_ent = [(t + 1) // m for t in ctxs]
                 swa_len = [min(wl.window, t + 1) for t in ctxs]
-                cache = gen.kv(sum(n_ent), D, wl.kv_fmt)
+                rows, table, P = sum(n_ent), None, 0
+                if paged:
+                    # blocks of 128 raw tokens (128 / m entries), handed out in a
+                    # shuffled order
+                    P = 128 // m
+                    nb = [(n + P - 1) // P for n in n_ent]
+                    ids = torch.randperm(sum(nb), generator=perm_gen).to(torch.int32)
+                    table = torch.full((B, max(nb)), -1, dtype=torch.int32)
+                    s0 = 0
+                    for r, n in enumerate(nb):
+                        table[r, :n] = ids[s0:s0 + n]
+                        s0 += n
+                    table, rows = table.cuda(), sum(nb) * P
+                cache = gen.kv(rows, D, wl.kv_fmt)
                 swa = gen.kv(sum(swa_len), D, "bf16")
                 q = gen.kv(B * H, D, "bf16")
                 qi = gen.kv(B * 4, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
-                ki = gen.kv(sum(n_ent), 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
+                ki = gen.kv(rows, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
                 layers.append(DecodeLayer(csa=csa, H=H, m=m, k=k, window=wl.window, ctx=ctxs,
                                           n_entries=n_ent, swa_len=swa_len, cache=cache,
                                           swa=swa, q=q, qi=qi, ki=ki,
-                                          score_fmt=FMT[wl.score_fmt], out_fmt=FMT[wl.out_fmt]))
+                                          score_fmt=FMT[wl.score_fmt], out_fmt=FMT[wl.out_fmt],
+                                          kv_block_table=table, kv_block_rows=P))
                 if c == 0:
                     nsum = sum(n_ent)
                     kb = IDX_KEY_BYTES[wl.idx_fmt]
@@ -473,6 +488,9 @@ def main():
                          "bf16 / MXFP4 indexer precision against fp32")
     ap.add_argument("--kv-append", action="store_true",
                     help="instead of the benchmark: time decode-time compression per call")
+    ap.add_argument("--paged", action="store_true",
+                    help="decode workloads: compressed entries and indexer keys in a paged "
+                         "cache (blocks of 128 raw tokens in a shuffled order)")
     args = ap.parse_args()
     if args.kv_append:
         torch.cuda.init()
@@ -500,7 +518,10 @@ def main():
     torch.cuda.init()
     t0 = time.time()
     decode = wl.kind in ("csa_decode", "mixed_decode")
-    w = Decode(wid) if decode else Prefill(wid)
+    if args.paged and not decode:
+        print("--paged applies to the decode workloads", file=sys.stderr)
+        sys.exit(2)
+    w = Decode(wid, paged=args.paged) if decode else Prefill(wid)
     torch.cuda.synchronize()
     log(f"workload {wl.name}: inputs ready in {time.time() - t0:.1f}s")
 
@@ -574,6 +595,8 @@ def main():
         line["config"]["step_bytes_algorithmic"] = int(w.bytes_step)
         line["config"]["step_hbm_frac"] = round(w.bytes_step / (ms * 1e-3) / 8e12, 4)
         line["config"]["graph_replay"] = True
+        if args.paged:
+            line["config"]["kv_layout"] = "paged: blocks of 128 raw tokens, shuffled"
     print(json.dumps(line), flush=True)
 
 

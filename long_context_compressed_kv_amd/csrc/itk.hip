@@ -266,13 +266,28 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
     }
   };
   auto tile_live = [&](int t) { return e_wg + e_wave + t * 32 < n_scan; };
+  // Paged keys with blocks of at least 32 entries: each of this wave's tiles
+  // (32 entries from a multiple of 32) lies in one block, whose id lane t
+  // loads up front for tile t, so the key loads wait on no block-table read.
+  const bool pre = a.b.pages != nullptr && a.b.page_shift >= 5;
+  int my_blk = -1;
+  if (pre && lane < TPW && tile_live(lane))
+    my_blk = a.b.pages[gr.qm.kv_base + ((e_wg + e_wave + lane * 32) >> a.b.page_shift)];
+  auto key_row = [&](int t, int64_t e, bool ok) -> int64_t {
+    if (pre) {
+      const int64_t blk = __builtin_amdgcn_readlane(my_blk, t);
+      const int64_t row = (blk << a.b.page_shift) + (e & ((1ll << a.b.page_shift) - 1));
+      return ok && blk >= 0 && row < a.b.kv_rows ? row : 0;
+    }
+    return entry_row_if(a.b, gr.qm.kv_base, e, ok);
+  };
   if constexpr (STREAM) {
     constexpr int NB = TPW / TB;
     auto load_batch = [&](int b, KeyOp<FMT>* k) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t e = e_wg + e_wave + (b * TB + tb) * 32 + rl;
-        load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, gr.qm.kv_base, e, e < n_scan), e < n_scan, half, k[tb]);
+        load_key<FMT>(a.ki, a.ki_scale, key_row(b * TB + tb, e, e < n_scan), e < n_scan, half, k[tb]);
       }
     };
     auto score_batch = [&](int b, const KeyOp<FMT>* k) {
@@ -301,7 +316,7 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
       if (!tile_live(t)) break;
       KeyOp<FMT> kt;
       const int64_t e = e_wg + e_wave + t * 32 + rl;
-      load_key<FMT>(a.ki, a.ki_scale, entry_row_if(a.b, gr.qm.kv_base, e, e < n_scan), e < n_scan, half, kt);
+      load_key<FMT>(a.ki, a.ki_scale, key_row(t, e, e < n_scan), e < n_scan, half, kt);
       score_tile(t, kt);
     }
   }

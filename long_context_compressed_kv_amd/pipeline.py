@@ -11,6 +11,7 @@ Decode (a batch of requests, one query each):
   HCA: sparse_mqa_attn(visible entries and window, split the same way)
 (page "DeepSeek V4 深度解析", section 2: the three CSA steps and HCA).
 """
+import dataclasses
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -154,6 +155,9 @@ class DecodeLayer:
     out_fmt: int = BF16
     split_keys: int = 128
     fused: bool = True
+    # paged compressed cache: int32 [B, stride] block ids, block_rows entries a block
+    kv_block_table: Optional[torch.Tensor] = None
+    kv_block_rows: int = 0
     buf: Buffers = field(default_factory=Buffers)
 
     def __post_init__(self):
@@ -163,6 +167,9 @@ class DecodeLayer:
         swa_pos = [int(c) - int(s) + 1 for c, s in zip(self.ctx, self.swa_len)]
         self.batch = Batch.make([1] * B, self.ctx, kv_counts=self.n_entries,
                                 raw_counts=self.swa_len, raw_pos=swa_pos, device=dev)
+        if self.kv_block_table is not None:
+            self.batch = dataclasses.replace(self.batch, kv_block_table=self.kv_block_table,
+                                             kv_block_rows=self.kv_block_rows)
         self.ld = max(int(x) for x in self.n_entries)
 
     def select(self):
