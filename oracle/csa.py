@@ -24,7 +24,8 @@ Readings where the pages are silent (each is a named constant or argument):
   (w = 2m: its own block and the previous one); slots before position 0 are
   left out of the softmax, not zero-padded;
 * weights: softmax over the valid slots s of z[p] + b[s], one scalar logit
-  per raw token and one bias per window slot;
+  per raw token and one bias per window slot (compress_entries_channel is the
+  variant with a logit and a bias per channel, one softmax per channel);
 * visibility: entry i is usable by the query at t once its block is complete,
   (i+1)m - 1 <= t, so n_c(t) = floor((t+1)/m) entries are visible;
 * indexer: one shared d_I-dim key per entry; S = sum_h w_h ReLU(q_h . k)
@@ -80,6 +81,35 @@ def compress_entries(x, z, x_pos0, b, m, w, i_begin, i_end):
         wgt = np.exp(logit - logit.max())
         wgt /= wgt.sum()
         out[i - i_begin] = wgt @ x[p - x_pos0]
+    return out
+
+
+def compress_entries_channel(x, z, x_pos0, b, m, w, i_begin, i_end):
+    """Compressed entries with one compression logit per raw token and
+    channel (page "DeepSeek V4 深度解析", section 2, CSA step 1, read with a
+    learned weight per token and channel instead of one per token).
+
+    x  : raw KV rows [n, D] for absolute positions x_pos0 .. x_pos0+n-1
+    z  : compression logits [n, D]
+    b  : position biases [w, D], one per window slot and channel
+    Entry i covers the slots of compress_entries; for every channel d the
+    weights are softmax_s(z[p][d] + b[s][d]) over the valid slots and the
+    entry's channel d is sum_s weight_s,d * x[p][d].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert z.shape == x.shape and b.shape == (w, x.shape[1]) and w >= m >= 1
+    out = np.empty((i_end - i_begin, x.shape[1]), dtype=np.float64)
+    for i in range(i_begin, i_end):
+        p = (i + 1) * m - w + np.arange(w)
+        valid = p >= 0
+        p, s = p[valid], np.arange(w)[valid]
+        assert p[0] >= x_pos0 and p[-1] < x_pos0 + x.shape[0], "raw rows missing"
+        logit = z[p - x_pos0] + b[s]                        # [slots, D]
+        wgt = np.exp(logit - logit.max(axis=0))
+        wgt /= wgt.sum(axis=0)
+        out[i - i_begin] = (wgt * x[p - x_pos0]).sum(axis=0)
     return out
 
 

@@ -103,6 +103,56 @@ def test_chunked_compression_equals_one_shot(m, w):
     assert np.allclose(part, full[first:], atol=0, rtol=0)
 
 
+# per-channel compression logits (the variant reading of the learned weight)
+
+def test_channel_compression_reduces_to_scalar():
+    """A logit and a bias shared by every channel give the scalar compression."""
+    rng = _rng(16)
+    for m, w in ((4, 8), (128, 256), (3, 5)):
+        n, D = 5 * m + 3, 6
+        x, z, b = rng.standard_normal((n, D)), rng.standard_normal(n), rng.standard_normal(w)
+        c = ref.compress_entries_channel(x, np.repeat(z[:, None], D, 1), 0,
+                                         np.repeat(b[:, None], D, 1), m, w, 0, n // m)
+        assert np.allclose(c, ref.compress_entries(x, z, 0, b, m, w, 0, n // m), rtol=0, atol=1e-13)
+
+
+def test_channel_compression_is_one_scalar_compression_per_channel():
+    """Channel d of every entry is the scalar compression of the one-channel
+    sequence x[:, d] with logits z[:, d] and biases b[:, d]."""
+    rng = _rng(17)
+    m, w, n, D = 4, 8, 70, 5
+    x, z, b = rng.standard_normal((n, D)), rng.standard_normal((n, D)) * 2, rng.standard_normal((w, D))
+    c = ref.compress_entries_channel(x, z, 0, b, m, w, 0, n // m)
+    for d in range(D):
+        cd = ref.compress_entries(x[:, d:d + 1], z[:, d], 0, b[:, d], m, w, 0, n // m)
+        assert np.allclose(c[:, d], cd[:, 0], rtol=0, atol=1e-13)
+    # and a shift of one channel's logits moves nothing
+    z2 = z.copy()
+    z2[:, 2] += 7.5
+    assert np.allclose(ref.compress_entries_channel(x, z2, 0, b, m, w, 0, n // m), c, rtol=0, atol=1e-13)
+
+
+def test_channel_compression_worked_example():
+    """m = 2, w = 3, two channels, by hand: entry 1 covers positions 1, 2, 3
+    (slots 0, 1, 2); entry 0 only positions 0, 1 (slot 0 would be -1)."""
+    x = np.array([[1.0, 10.0], [2.0, 20.0], [3.0, 30.0], [4.0, 40.0]])
+    z = np.array([[0.0, 1.0], [1.0, 0.0], [0.0, 0.0], [2.0, -1.0]])
+    b = np.array([[0.0, 0.0], [0.0, 1.0], [-1.0, 0.0]])
+    c = ref.compress_entries_channel(x, z, 0, b, 2, 3, 0, 2)
+    e = math.exp
+    # entry 0, slots 1, 2 = positions 0, 1
+    w0 = [e(0 + 0), e(1 - 1)], [e(1 + 1), e(0 + 0)]
+    ch0 = (w0[0][0] * 1 + w0[0][1] * 2) / sum(w0[0])
+    ch1 = (w0[1][0] * 10 + w0[1][1] * 20) / sum(w0[1])
+    assert np.allclose(c[0], [ch0, ch1], rtol=0, atol=1e-14)
+    # entry 1, slots 0, 1, 2 = positions 1, 2, 3
+    l0 = [1 + 0, 0 + 0, 2 - 1]
+    l1 = [0 + 0, 0 + 1, -1 + 0]
+    ch0 = sum(e(v) * xv for v, xv in zip(l0, [2, 3, 4])) / sum(e(v) for v in l0)
+    ch1 = sum(e(v) * xv for v, xv in zip(l1, [20, 30, 40])) / sum(e(v) for v in l1)
+    assert np.allclose(c[1], [ch0, ch1], rtol=0, atol=1e-13)
+
+
 def test_visibility_and_lcm_block():
     """n_c(t) = floor((t+1)/m): entry i is usable once (i+1)m - 1 <= t.  One
     block of lcm(4, 128) = 128 raw tokens holds 32 CSA and 1 HCA entries."""
