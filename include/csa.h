@@ -179,6 +179,24 @@ csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_p
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_kv_compress_channel - CSA step 1 with a learned weight per raw token and
+ * channel.  Page "DeepSeek V4 深度解析", section 2, CSA step 1, read with one
+ * compression logit per token and channel (and a position bias per slot and
+ * channel) instead of one per token: each channel has its own softmax.
+ *
+ * As csa_kv_compress, except:
+ *   logits     float [x->rows][dim], aligned with x
+ *   slot_bias  float [w][dim]
+ * Entry i, channel d: weights = softmax over the valid slots s of
+ * logits[p - x_pos0][d] + slot_bias[s][d]; channel d of the entry = sum of
+ * weight * x[p - x_pos0][d], fp32, stored as F32, BF16 or FP8_MIXED (dim 512).
+ * ------------------------------------------------------------------------- */
+csa_status csa_kv_compress_channel(const csa_tensor* x, const float* logits, int64_t x_pos0,
+                                   const float* slot_bias, int32_t m, int32_t w,
+                                   int64_t entry_begin, int64_t n_entries,
+                                   const csa_tensor* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * csa_kv_compress_append - decode-time compression through a state cache.
  * Page "DeepSeek V4 深度解析", section 4, the paragraph on KV-cache management
  * for the hybrid attention: a fixed per-request state holds the window and the

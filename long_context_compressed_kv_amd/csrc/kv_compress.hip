@@ -130,6 +130,97 @@ __global__ __launch_bounds__(kThreads) void kv_compress_kernel(
   }
 }
 
+// The variant with a logit and a bias per channel: z [x_rows][dim], bias
+// [w][dim], one softmax per channel.  Threads hold two channels of one entry
+// (512/dim entries a workgroup) and run an online softmax over the entry's
+// slots in order (running maximum, sum of exponentials and weighted sum,
+// fp32), so every channel is reduced in a fixed order.
+template <typename TIn, int OUTF>
+__global__ __launch_bounds__(kThreads) void kv_compress_channel_kernel(
+    const TIn* __restrict__ x, const float* __restrict__ z, int64_t x_pos0, int64_t x_rows,
+    const float* __restrict__ bias, int m, int w, int64_t entry_begin, int64_t n_entries, int dim,
+    OutPtrs out) {
+  __shared__ float acc_lds[2 * kThreads];
+  const int tid = threadIdx.x;
+  const int tpr = dim >> 1;                 // threads per entry
+  const int per_wg = kThreads / tpr;
+  const int g = tid / tpr;
+  const int d = (tid - g * tpr) * 2;
+  const int64_t e_local = (int64_t)blockIdx.x * per_wg + g;
+  const bool live = e_local < n_entries;
+  const int64_t i = entry_begin + e_local;
+  const int64_t p0 = (i + 1) * m - w;
+  float mx0 = -INFINITY, mx1 = -INFINITY, l0 = 0.0f, l1 = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  for (int s = 0; live && s < w; ++s) {
+    const int64_t p = p0 + s;
+    const int64_t r = p - x_pos0;
+    if (p < 0 || r < 0 || r >= x_rows) continue;
+    const float2 zz = *reinterpret_cast<const float2*>(z + r * dim + d);
+    const float2 bb = *reinterpret_cast<const float2*>(bias + (int64_t)s * dim + d);
+    const float2 v = load2(x + r * dim + d);
+    const float g0 = zz.x + bb.x, g1 = zz.y + bb.y;
+    if (g0 > mx0) {
+      const float sc = expf(mx0 - g0);      // 0 while the channel is empty
+      l0 *= sc;
+      a0 *= sc;
+      mx0 = g0;
+    }
+    if (g1 > mx1) {
+      const float sc = expf(mx1 - g1);
+      l1 *= sc;
+      a1 *= sc;
+      mx1 = g1;
+    }
+    const float e0 = expf(g0 - mx0), e1 = expf(g1 - mx1);
+    l0 += e0;
+    l1 += e1;
+    a0 = fmaf(e0, v.x, a0);
+    a1 = fmaf(e1, v.y, a1);
+  }
+  a0 = l0 > 0.0f ? a0 / l0 : 0.0f;
+  a1 = l1 > 0.0f ? a1 / l1 : 0.0f;
+  if (OUTF == CSA_F32) {
+    if (live)
+      *reinterpret_cast<float2*>(static_cast<float*>(out.data) + e_local * dim + d) = make_float2(a0, a1);
+  } else if (OUTF == CSA_BF16) {
+    if (live)
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out.data) + e_local * dim + d) = pack_bf16x2(a0, a1);
+  } else {  // CSA_FP8_MIXED, dim == 512: one entry a workgroup
+    acc_lds[d] = a0;
+    acc_lds[d + 1] = a1;
+    __syncthreads();
+    if (live && tid < 64) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = acc_lds[8 * tid + k];
+      encode_kv_mixed_row_wave(v, static_cast<uint8_t*>(out.data) + e_local * 448,
+                               out.scale + e_local * 4, out.rope + e_local * 64);
+    }
+  }
+}
+
+template <typename TIn>
+void launch_channel(const csa_tensor* x, const float* z, int64_t x_pos0, const float* bias, int m,
+                    int w, int64_t entry_begin, int64_t n, const csa_tensor* out, hipStream_t stream) {
+  OutPtrs o{out->data, static_cast<uint8_t*>(out->scale), static_cast<uint16_t*>(out->rope)};
+  const TIn* xp = static_cast<const TIn*>(x->data);
+  const int per_wg = kThreads / (x->dim >> 1);
+  dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(kThreads);
+  switch (out->fmt) {
+    case CSA_F32:
+      hipLaunchKernelGGL((kv_compress_channel_kernel<TIn, CSA_F32>), grid, block, 0, stream, xp, z,
+                         x_pos0, x->rows, bias, m, w, entry_begin, n, x->dim, o);
+      break;
+    case CSA_BF16:
+      hipLaunchKernelGGL((kv_compress_channel_kernel<TIn, CSA_BF16>), grid, block, 0, stream, xp, z,
+                         x_pos0, x->rows, bias, m, w, entry_begin, n, x->dim, o);
+      break;
+    default:
+      hipLaunchKernelGGL((kv_compress_channel_kernel<TIn, CSA_FP8_MIXED>), grid, block, 0, stream,
+                         xp, z, x_pos0, x->rows, bias, m, w, entry_begin, n, x->dim, o);
+  }
+}
+
 template <typename TIn>
 void launch(const csa_tensor* x, const float* z, int64_t x_pos0, const float* bias, int m, int w,
             int64_t entry_begin, int64_t n, const csa_tensor* out, hipStream_t stream) {
@@ -155,41 +246,70 @@ void launch(const csa_tensor* x, const float* z, int64_t x_pos0, const float* bi
 
 using namespace csa_host;
 
-extern "C" csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_pos0,
-                                      const float* slot_bias, int32_t m, int32_t w,
-                                      int64_t entry_begin, int64_t n_entries,
-                                      const csa_tensor* out, hipStream_t stream) {
-  clear_error();
+namespace {
+
+// Checks shared by both compression calls; CSA_OK with n_entries == 0 means
+// there is nothing to launch.
+csa_status check_compress(const char* who, const csa_tensor* x, const float* logits, int64_t x_pos0,
+                          const float* slot_bias, int32_t m, int32_t w, int64_t entry_begin,
+                          int64_t n_entries, const csa_tensor* out) {
   if (!fmt_valid_tensor(x) || !fmt_valid_tensor(out))
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress: bad tensor descriptor");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad tensor descriptor", who);
   if (x->fmt != CSA_F32 && x->fmt != CSA_BF16)
-    return fail(CSA_ERR_UNSUPPORTED, "csa_kv_compress: raw rows must be F32 or BF16");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: raw rows must be F32 or BF16", who);
   if (out->fmt != CSA_F32 && out->fmt != CSA_BF16 && out->fmt != CSA_FP8_MIXED)
-    return fail(CSA_ERR_UNSUPPORTED, "csa_kv_compress: output must be F32, BF16 or FP8_MIXED");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: output must be F32, BF16 or FP8_MIXED", who);
   const int d = x->dim;
-  if (out->dim != d) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress: dim mismatch");
+  if (out->dim != d) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: dim mismatch", who);
   if (d < 16 || d > 512 || (d & (d - 1)) != 0)
-    return fail(CSA_ERR_UNSUPPORTED, "csa_kv_compress: dim must be a power of two in [16, 512]");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: dim must be a power of two in [16, 512]", who);
   if (m < 1 || w < m || w > kMaxW)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress: need 1 <= m <= w <= %d", kMaxW);
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: need 1 <= m <= w <= %d", who, kMaxW);
   if (n_entries < 0 || entry_begin < 0 || n_entries > out->rows)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress: bad entry range / output rows");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad entry range / output rows", who);
   if (n_entries == 0) return CSA_OK;
   if (n_entries > 0x7fffffff)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress: too many entries for one launch");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: too many entries for one launch", who);
   if (logits == nullptr || slot_bias == nullptr)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress: null logits or biases");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: null logits or biases", who);
   // every valid slot of every requested entry must be inside the raw rows
   const int64_t first = (entry_begin + 1) * m - w;
   const int64_t lo = first < 0 ? 0 : first;
   const int64_t hi = (entry_begin + n_entries) * (int64_t)m - 1;
   if (lo < x_pos0 || hi >= x_pos0 + x->rows)
-    return fail(CSA_ERR_INVALID_ARGUMENT,
-                "csa_kv_compress: raw rows cover positions [%lld, %lld) but entries need [%lld, %lld]",
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: raw rows cover positions [%lld, %lld) but entries need [%lld, %lld]", who,
                 (long long)x_pos0, (long long)(x_pos0 + x->rows), (long long)lo, (long long)hi);
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_pos0,
+                                      const float* slot_bias, int32_t m, int32_t w,
+                                      int64_t entry_begin, int64_t n_entries,
+                                      const csa_tensor* out, hipStream_t stream) {
+  clear_error();
+  const csa_status st = check_compress("csa_kv_compress", x, logits, x_pos0, slot_bias, m, w,
+                                       entry_begin, n_entries, out);
+  if (st != CSA_OK || n_entries == 0) return st;
   if (x->fmt == CSA_F32)
     launch<float>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream);
   else
     launch<uint16_t>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream);
   return check_launch("csa_kv_compress");
+}
+
+extern "C" csa_status csa_kv_compress_channel(const csa_tensor* x, const float* logits,
+                                              int64_t x_pos0, const float* slot_bias, int32_t m,
+                                              int32_t w, int64_t entry_begin, int64_t n_entries,
+                                              const csa_tensor* out, hipStream_t stream) {
+  clear_error();
+  const csa_status st = check_compress("csa_kv_compress_channel", x, logits, x_pos0, slot_bias, m,
+                                       w, entry_begin, n_entries, out);
+  if (st != CSA_OK || n_entries == 0) return st;
+  if (x->fmt == CSA_F32)
+    launch_channel<float>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream);
+  else
+    launch_channel<uint16_t>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream);
+  return check_launch("csa_kv_compress_channel");
 }

@@ -154,6 +154,21 @@ def kv_compress(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, 
     return out
 
 
+def kv_compress_channel(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out: KV):
+    """CSA step 1 with a logit per raw token and channel: logits float
+    [x.rows, dim], slot_bias float [w, dim]; one softmax per channel."""
+    _need_cuda(logits, slot_bias)
+    assert logits.dtype == torch.float32 and logits.is_contiguous()
+    assert slot_bias.dtype == torch.float32 and slot_bias.is_contiguous()
+    assert tuple(logits.shape) == (x.rows, x.dim) and tuple(slot_bias.shape) == (int(w), x.dim)
+    lib = _lib.load()
+    xc, oc = x.c(), out.c()
+    check(lib.csa_kv_compress_channel(ctypes.byref(xc), _ptr(logits), int(x_pos0), _ptr(slot_bias),
+                                      int(m), int(w), int(entry_begin), int(n_entries),
+                                      ctypes.byref(oc), _stream()), "csa_kv_compress_channel")
+    return out
+
+
 def kv_append_state_size(n_req, dim):
     """Bytes of the per-request compression state csa_kv_compress_append keeps."""
     return int(_lib.load().csa_kv_append_state_size(int(n_req), int(dim)))

@@ -68,6 +68,14 @@ def test_kv_compress_validation(lib):
     assert call(_t(0, 96, 64), _t(0, 96, 16), 4, 8, 0, 4) == UNSUPPORTED  # not a power of two
     assert call(x, out, 4, 8, 0, 0) == 0                    # nothing to do, nothing launched
     assert b"raw rows" in lib.csa_last_error() or lib.csa_last_error() == b""
+    # the per-channel variant makes the same checks
+    chan = lambda xx, oo, m, w, e0, n, pos0=0: lib.csa_kv_compress_channel(
+        ctypes.byref(xx), z, pos0, b, m, w, e0, n, ctypes.byref(oo), None)
+    assert chan(x, out, 4, 2, 0, 4) == BAD_ARG
+    assert chan(x, out, 4, 8, 0, 16, pos0=1) == BAD_ARG
+    assert b"csa_kv_compress_channel" in lib.csa_last_error()
+    assert chan(_t(0, 96, 64), _t(0, 96, 16), 4, 8, 0, 4) == UNSUPPORTED
+    assert chan(x, out, 4, 8, 0, 0) == 0
 
 
 def _batch(n_q=4, n_req=1, max_kv=16):

@@ -98,3 +98,47 @@ def test_compress_deterministic():
     a = _run(x, z, b, 128, 256, 0, 0, 8, "bf16", "bf16")
     c = _run(x, z, b, 128, 256, 0, 0, 8, "bf16", "bf16")
     assert torch.equal(a.data, c.data)
+
+
+# ------------------------------------------------- per-channel logits variant
+
+@pytest.mark.parametrize("in_fmt,out_fmt,m,w,D,T,x_pos0,e0", [
+    ("f32", "f32", 4, 8, 128, 2048, 0, 0),         # CSA ratio, four entries a workgroup
+    ("bf16", "bf16", 128, 256, 128, 8192, 0, 0),   # HCA ratio and window
+    ("f32", "f32", 4, 8, 16, 37, 0, 0),            # 32 entries a workgroup, ragged tail
+    ("bf16", "f32", 3, 7, 64, 100, 0, 0),          # odd ratio and window
+    ("f32", "bf16", 4, 8, 256, 300, 96, 26),       # a chunk: history rows, later first entry
+])
+def test_compress_channel_against_oracle(in_fmt, out_fmt, m, w, D, T, x_pos0, e0):
+    rng = np.random.default_rng(T + D + m)
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    z = (rng.standard_normal((T, D)) * 2).astype(np.float32)
+    b = rng.standard_normal((w, D)).astype(np.float32)
+    n = (x_pos0 + T) // m - e0
+    out = KV.empty(FMT[out_fmt], n, D)
+    ops.kv_compress_channel(dev_kv(x, in_fmt), dev_f32(z), x_pos0, dev_f32(b), m, w, e0, n, out)
+    torch.cuda.synchronize()
+    c = ref.compress_entries_channel(ref_vals(x, in_fmt), z, x_pos0, b, m, w, e0, e0 + n)
+    g = to_np(out.data).astype(np.float64)
+    if out_fmt == "f32":
+        assert np.max(np.abs(g - c)) <= 1e-5
+    else:
+        assert np.all(np.abs(g - c) <= bf16_ulp(c) * 1.0001)
+
+
+def test_compress_channel_mixed_format():
+    """512-dim entries stored in the mixed format (e4m3 + e8m0 + bf16 RoPE)."""
+    rng = np.random.default_rng(77)
+    m, w, T, D = 4, 8, 600, 512
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    z = rng.standard_normal((T, D)).astype(np.float32)
+    b = rng.standard_normal((w, D)).astype(np.float32)
+    n = T // m
+    out = KV.empty(FMT["fp8_mixed"], n, D)
+    ops.kv_compress_channel(dev_kv(x, "bf16"), dev_f32(z), 0, dev_f32(b), m, w, 0, n, out)
+    torch.cuda.synchronize()
+    xv = ref_vals(x, "bf16")
+    c = ref.compress_entries_channel(xv, z, 0, b, m, w, 0, n)
+    cabs = ref.compress_entries_channel(np.abs(xv), z, 0, b, m, w, 0, n)
+    nd = check_mixed(out, c, cabs)
+    assert nd <= n * 448 * 2e-3
