@@ -142,3 +142,39 @@ def test_compress_channel_mixed_format():
     cabs = ref.compress_entries_channel(np.abs(xv), z, 0, b, m, w, 0, n)
     nd = check_mixed(out, c, cabs)
     assert nd <= n * 448 * 2e-3
+
+
+def test_indexer_keys_compressed_with_the_same_weights():
+    """The reading where an entry's indexer key is the compression of the raw
+    tokens' indexer keys with the entry's own softmax weights: the same call
+    on the 64-dim key rows with the same logits and biases, checked against
+    the oracle's compression of those rows, and the result used as indexer
+    keys gives the oracle's top-k."""
+    rng = np.random.default_rng(78)
+    m, w, T, D, DI = 4, 8, 2048, 512, 64
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    xi = (rng.standard_normal((T, DI)) * 0.125).astype(np.float32)
+    z = rng.standard_normal(T).astype(np.float32)
+    b = rng.standard_normal(w).astype(np.float32)
+    n = T // m
+    kv = KV.empty(FMT["bf16"], n, D)
+    ki = KV.empty(FMT["f32"], n, DI)
+    zd, bd = dev_f32(z), dev_f32(b)
+    ops.kv_compress(dev_kv(x, "bf16"), zd, 0, bd, m, w, 0, n, kv)
+    ops.kv_compress(dev_kv(xi, "f32"), zd, 0, bd, m, w, 0, n, ki)
+    torch.cuda.synchronize()
+    ki_ref = ref.compress_entries(xi, z, 0, b, m, w, 0, n)
+    assert np.max(np.abs(to_np(ki.data) - ki_ref)) <= 1e-6
+    # the compressed keys drive the selection of a query at the last position
+    qi = (rng.standard_normal((1, 4, DI)) * 0.125).astype(np.float32)
+    batch = ops.Batch.make([1], [T - 1], kv_counts=[n])
+    k = 32
+    idx = ops.indexer_topk(dev_kv(qi.reshape(-1, DI), "f32"), 4, ki, batch, m, ops.F32, k)
+    torch.cuda.synchronize()
+    s = ref.indexer_scores(qi[0].astype(np.float64), to_np(ki.data).astype(np.float64), np.ones(4))
+    want = set(ref.topk_indices(ref.score_keys(s, "f32"), k).tolist())
+    got = set(idx.cpu().numpy()[0].tolist())
+    # the selections agree except, at most, between entries tied at the k-th
+    # score within the fp32 accumulation's rounding
+    kth = np.sort(s)[-k]
+    assert all(abs(s[j] - kth) <= 1e-5 * abs(kth) + 1e-7 for j in got ^ want)
