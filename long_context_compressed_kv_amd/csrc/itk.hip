@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 // own threshold is selected from that row); one atomic per query reserves the
 // workgroup's span of the list; pass 2 rescans the LDS rows and writes the
 // candidates (each wave its own entries, so the reserved spans line up).
-template <int FMT, bool SBF16, bool STREAM>
+template <int FMT, bool SBF16, bool STREAM, bool PAGED>
 __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
   constexpr int TB = STREAM ? Tiling<FMT>::TB : 1;
   constexpr int TPW = STREAM ? Tiling<FMT>::TPW : kTilesPerWave;
@@ -266,20 +266,25 @@ __global__ __launch_bounds__(256) void itk_filter_kernel(ItkArgs a) {
     }
   };
   auto tile_live = [&](int t) { return e_wg + e_wave + t * 32 < n_scan; };
-  // Paged keys with blocks of at least 32 entries: each of this wave's tiles
+  // Paged keys (a separate instantiation, so the contiguous one keeps its
+  // registers): with blocks of at least 32 entries each of this wave's tiles
   // (32 entries from a multiple of 32) lies in one block, whose id lane t
   // loads up front for tile t, so the key loads wait on no block-table read.
-  const bool pre = a.b.pages != nullptr && a.b.page_shift >= 5;
+  const bool pre = PAGED && a.b.page_shift >= 5;
   int my_blk = -1;
   if (pre && lane < TPW && tile_live(lane))
     my_blk = a.b.pages[gr.qm.kv_base + ((e_wg + e_wave + lane * 32) >> a.b.page_shift)];
   auto key_row = [&](int t, int64_t e, bool ok) -> int64_t {
-    if (pre) {
-      const int64_t blk = __builtin_amdgcn_readlane(my_blk, t);
-      const int64_t row = (blk << a.b.page_shift) + (e & ((1ll << a.b.page_shift) - 1));
-      return ok && blk >= 0 && row < a.b.kv_rows ? row : 0;
+    if constexpr (!PAGED) {
+      return gr.qm.kv_base + e;
+    } else {
+      if (pre) {
+        const int64_t blk = __builtin_amdgcn_readlane(my_blk, t);
+        const int64_t row = (blk << a.b.page_shift) + (e & ((1ll << a.b.page_shift) - 1));
+        return ok && blk >= 0 && row < a.b.kv_rows ? row : 0;
+      }
+      return entry_row_if(a.b, gr.qm.kv_base, e, ok);
     }
-    return entry_row_if(a.b, gr.qm.kv_base, e, ok);
   };
   if constexpr (STREAM) {
     constexpr int NB = TPW / TB;
@@ -674,8 +679,11 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   const int64_t epw = entries_per_wg<FMT>(stream);
   const dim3 fgrid = stream ? dim3((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups)
                             : dim3((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
-  if (stream) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true>), fgrid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false>), fgrid, dim3(256), 0, s, a);
+  const bool paged = a.b.pages != nullptr;
+  if (stream && paged) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, true>), fgrid, dim3(256), 0, s, a);
+  else if (stream) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, false>), fgrid, dim3(256), 0, s, a);
+  else if (paged) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false, true>), fgrid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false, false>), fgrid, dim3(256), 0, s, a);
   st = csa_host::check_launch("csa_indexer_topk (filter)");
   if (st != CSA_OK) return st;
   const size_t bm_bytes = (size_t)((max_kv < kBitmapMax ? max_kv : kBitmapMax) + 31) / 32 * 4;
