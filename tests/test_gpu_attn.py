@@ -264,3 +264,36 @@ def test_attn_deterministic_and_batch_invariant():
     c = run([1])
     assert torch.equal(a[0], b[1]) and torch.equal(a[2], b[0]) and torch.equal(a[1], c[0])
     assert torch.equal(a, run([0, 1, 2]))
+
+
+def test_attn_decode_largest_selection_and_heads():
+    """The largest sizes the call takes at decode: k = 4096 selected entries,
+    128 heads (two head groups when split over keys), D = 512 mixed entries
+    with the 128-token window; one union call, split-K, against the oracle."""
+    rng = np.random.default_rng(12)
+    H, D, m, k, window = 128, 512, 4, 4096, 128
+    ctxs = [40000, 20000, 9000]
+    n_ent = [(c + 1) // m for c in ctxs]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    swas = [rng.standard_normal((window, D)).astype(np.float32) for _ in ctxs]
+    q = rng.standard_normal((len(ctxs), H, D)).astype(np.float32)
+    idx = np.full((len(ctxs), k), -1, np.int32)
+    for r, n in enumerate(n_ent):
+        c = min(k, n) - 7 * r                      # one full row, two shorter ones
+        idx[r, :c] = np.sort(rng.choice(n, c, replace=False))
+    batch = Batch.make([1] * len(ctxs), ctxs, kv_counts=n_ent, raw_counts=[window] * len(ctxs),
+                       raw_pos=[c - window + 1 for c in ctxs])
+    out = torch.empty(len(ctxs) * H, D, device="cuda")
+    lse = torch.empty(len(ctxs) * H, device="cuda")
+    ops.sparse_mqa_attn(dev_kv(q.reshape(-1, D), "bf16"), H, dev_kv(np.concatenate(ents), "fp8_mixed"),
+                        torch.from_numpy(idx).cuda(), k, dev_kv(np.concatenate(swas), "bf16"), window,
+                        batch, m, out, F32, lse, split_keys=128)
+    torch.cuda.synchronize()
+    qv, sc = ref_vals(q, "bf16"), 1 / math.sqrt(D)
+    for r in range(len(ctxs)):
+        keys = np.concatenate([ref_vals(ents[r], "fp8_mixed")[idx[r][idx[r] >= 0]],
+                               ref_vals(swas[r], "bf16")])
+        o, l = ref.attend(qv[r], keys, sc)
+        sl = slice(r * H, (r + 1) * H)
+        assert np.max(np.abs(to_np(out[sl]) - o)) <= 2e-2
+        assert np.max(np.abs(to_np(lse[sl]) - l)) <= 2e-2

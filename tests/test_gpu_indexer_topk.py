@@ -162,3 +162,21 @@ def test_fused_clustered_best_entries(fmt):
     batch = Batch.make([1] * len(ctx), ctx, kv_counts=kv_counts)
     f, u = _both(qi, ki, fmt, batch, m, k, "bf16")
     assert np.array_equal(f, u)
+
+
+@pytest.mark.parametrize("fmt,score_fmt", [("bf16", "bf16"), ("mxfp4", "f32")])
+def test_fused_largest_k(fmt, score_fmt):
+    """k = 4096, the largest the call takes: decode rows shorter than k, inside
+    the candidate list (cap = 6k) and far beyond it, and a prefill group of
+    queries straddling the list size; the same indices as score + select."""
+    rng = np.random.default_rng(66)
+    m, k = 4, 4096
+    ctx = [9000, 60000, 400000, 100]
+    n_ent = [(c + 1) // m for c in ctx]
+    qi, ki = _inputs(rng, len(ctx), sum(n_ent), fmt)
+    f, u = _both(qi, ki, fmt, Batch.make([1] * len(ctx), ctx, kv_counts=n_ent), m, k, score_fmt)
+    assert np.array_equal(f, u)
+    T, pos0 = 24, 98000
+    qi, ki = _inputs(rng, T, (pos0 + T) // m, fmt)
+    f, u = _both(qi, ki, fmt, Batch.make([T], [pos0], kv_counts=[(pos0 + T) // m]), m, k, score_fmt)
+    assert np.array_equal(f, u)
