@@ -179,6 +179,26 @@ csa_status csa_kv_compress(const csa_tensor* x, const float* logits, int64_t x_p
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_kv_compress_paged - csa_kv_compress into a paged compressed cache (page
+ * "DeepSeek V4 深度解析", section 4, KV-cache management: entries kept in
+ * blocks of LCM(compression ratios) raw tokens; see csa_batch.kv_block_table).
+ *
+ * As csa_kv_compress, except that entry j (entry_begin <= j < entry_begin +
+ * n_entries, counted from the request's first entry) goes to row
+ * blocks[j / block_rows] * block_rows + j % block_rows of `out`, the cache's
+ * block pool:
+ *   blocks      device int32, the request's block ids in order (at least
+ *               (entry_begin + n_entries + block_rows - 1) / block_rows of them)
+ *   block_rows  entries per block, a power of two in [1, 2^20]
+ * An entry whose block id is negative or whose row falls outside `out` is not
+ * written.  out->rows is the pool's size (no relation to n_entries).
+ * ------------------------------------------------------------------------- */
+csa_status csa_kv_compress_paged(const csa_tensor* x, const float* logits, int64_t x_pos0,
+                                 const float* slot_bias, int32_t m, int32_t w,
+                                 int64_t entry_begin, int64_t n_entries, const int32_t* blocks,
+                                 int32_t block_rows, const csa_tensor* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * csa_kv_compress_channel - CSA step 1 with a learned weight per raw token and
  * channel.  Page "DeepSeek V4 深度解析", section 2, CSA step 1, read with one
  * compression logit per token and channel (and a position bias per slot and

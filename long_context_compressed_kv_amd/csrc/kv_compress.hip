@@ -44,7 +44,22 @@ struct OutPtrs {
   void* data;
   uint8_t* scale;
   uint16_t* rope;
+  // rows: entry e_local goes to row e_local, or with a block list (a paged
+  // cache) entry j = entry_begin + e_local to row blocks[j / P] * P + j % P,
+  // P = 2^shift; rows outside the cache (or a negative block) are not written
+  const int32_t* blocks;
+  int shift;
+  int64_t rows;
+  int64_t entry_begin;
 };
+
+__device__ __forceinline__ int64_t out_row(const OutPtrs& o, int64_t e_local) {
+  if (o.blocks == nullptr) return e_local;
+  const int64_t j = o.entry_begin + e_local;
+  const int64_t blk = o.blocks[j >> o.shift];
+  const int64_t row = (blk << o.shift) + (j & ((1ll << o.shift) - 1));
+  return blk >= 0 && row < o.rows ? row : -1;
+}
 
 template <typename TIn, int OUTF>
 __global__ __launch_bounds__(kThreads) void kv_compress_kernel(
@@ -107,25 +122,26 @@ __global__ __launch_bounds__(kThreads) void kv_compress_kernel(
     }
   }
 
+  const int64_t row = out_row(out, e_local);
   if (OUTF == CSA_F32) {
-    if (g == 0)
-      *reinterpret_cast<float2*>(static_cast<float*>(out.data) + e_local * dim + d) =
+    if (g == 0 && row >= 0)
+      *reinterpret_cast<float2*>(static_cast<float*>(out.data) + row * dim + d) =
           make_float2(a0, a1);
   } else if (OUTF == CSA_BF16) {
-    if (g == 0)
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out.data) + e_local * dim + d) =
+    if (g == 0 && row >= 0)
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out.data) + row * dim + d) =
           pack_bf16x2(a0, a1);
   } else {  // CSA_FP8_MIXED, dim == 512, groups == 1
     __syncthreads();
     acc_lds[d] = a0;
     acc_lds[d + 1] = a1;
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 64 && row >= 0) {
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = acc_lds[8 * tid + k];
-      encode_kv_mixed_row_wave(v, static_cast<uint8_t*>(out.data) + e_local * 448,
-                               out.scale + e_local * 4, out.rope + e_local * 64);
+      encode_kv_mixed_row_wave(v, static_cast<uint8_t*>(out.data) + row * 448,
+                               out.scale + row * 4, out.rope + row * 64);
     }
   }
 }
@@ -179,30 +195,33 @@ __global__ __launch_bounds__(kThreads) void kv_compress_channel_kernel(
   }
   a0 = l0 > 0.0f ? a0 / l0 : 0.0f;
   a1 = l1 > 0.0f ? a1 / l1 : 0.0f;
+  const int64_t row = live ? out_row(out, e_local) : -1;
   if (OUTF == CSA_F32) {
-    if (live)
-      *reinterpret_cast<float2*>(static_cast<float*>(out.data) + e_local * dim + d) = make_float2(a0, a1);
+    if (row >= 0)
+      *reinterpret_cast<float2*>(static_cast<float*>(out.data) + row * dim + d) = make_float2(a0, a1);
   } else if (OUTF == CSA_BF16) {
-    if (live)
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out.data) + e_local * dim + d) = pack_bf16x2(a0, a1);
+    if (row >= 0)
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out.data) + row * dim + d) = pack_bf16x2(a0, a1);
   } else {  // CSA_FP8_MIXED, dim == 512: one entry a workgroup
     acc_lds[d] = a0;
     acc_lds[d + 1] = a1;
     __syncthreads();
-    if (live && tid < 64) {
+    if (row >= 0 && tid < 64) {
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = acc_lds[8 * tid + k];
-      encode_kv_mixed_row_wave(v, static_cast<uint8_t*>(out.data) + e_local * 448,
-                               out.scale + e_local * 4, out.rope + e_local * 64);
+      encode_kv_mixed_row_wave(v, static_cast<uint8_t*>(out.data) + row * 448,
+                               out.scale + row * 4, out.rope + row * 64);
     }
   }
 }
 
 template <typename TIn>
 void launch_channel(const csa_tensor* x, const float* z, int64_t x_pos0, const float* bias, int m,
-                    int w, int64_t entry_begin, int64_t n, const csa_tensor* out, hipStream_t stream) {
-  OutPtrs o{out->data, static_cast<uint8_t*>(out->scale), static_cast<uint16_t*>(out->rope)};
+                    int w, int64_t entry_begin, int64_t n, const csa_tensor* out, hipStream_t stream,
+                    const int32_t* blocks = nullptr, int shift = 0) {
+  OutPtrs o{out->data, static_cast<uint8_t*>(out->scale), static_cast<uint16_t*>(out->rope), blocks,
+            shift, out->rows, entry_begin};
   const TIn* xp = static_cast<const TIn*>(x->data);
   const int per_wg = kThreads / (x->dim >> 1);
   dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(kThreads);
@@ -223,8 +242,10 @@ void launch_channel(const csa_tensor* x, const float* z, int64_t x_pos0, const f
 
 template <typename TIn>
 void launch(const csa_tensor* x, const float* z, int64_t x_pos0, const float* bias, int m, int w,
-            int64_t entry_begin, int64_t n, const csa_tensor* out, hipStream_t stream) {
-  OutPtrs o{out->data, static_cast<uint8_t*>(out->scale), static_cast<uint16_t*>(out->rope)};
+            int64_t entry_begin, int64_t n, const csa_tensor* out, hipStream_t stream,
+            const int32_t* blocks = nullptr, int shift = 0) {
+  OutPtrs o{out->data, static_cast<uint8_t*>(out->scale), static_cast<uint16_t*>(out->rope), blocks,
+            shift, out->rows, entry_begin};
   const TIn* xp = static_cast<const TIn*>(x->data);
   dim3 grid((unsigned)n), block(kThreads);
   switch (out->fmt) {
@@ -252,7 +273,7 @@ namespace {
 // there is nothing to launch.
 csa_status check_compress(const char* who, const csa_tensor* x, const float* logits, int64_t x_pos0,
                           const float* slot_bias, int32_t m, int32_t w, int64_t entry_begin,
-                          int64_t n_entries, const csa_tensor* out) {
+                          int64_t n_entries, const csa_tensor* out, bool paged = false) {
   if (!fmt_valid_tensor(x) || !fmt_valid_tensor(out))
     return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad tensor descriptor", who);
   if (x->fmt != CSA_F32 && x->fmt != CSA_BF16)
@@ -265,7 +286,7 @@ csa_status check_compress(const char* who, const csa_tensor* x, const float* log
     return fail(CSA_ERR_UNSUPPORTED, "%s: dim must be a power of two in [16, 512]", who);
   if (m < 1 || w < m || w > kMaxW)
     return fail(CSA_ERR_INVALID_ARGUMENT, "%s: need 1 <= m <= w <= %d", who, kMaxW);
-  if (n_entries < 0 || entry_begin < 0 || n_entries > out->rows)
+  if (n_entries < 0 || entry_begin < 0 || (!paged && n_entries > out->rows))
     return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad entry range / output rows", who);
   if (n_entries == 0) return CSA_OK;
   if (n_entries > 0x7fffffff)
@@ -297,6 +318,27 @@ extern "C" csa_status csa_kv_compress(const csa_tensor* x, const float* logits, 
   else
     launch<uint16_t>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream);
   return check_launch("csa_kv_compress");
+}
+
+extern "C" csa_status csa_kv_compress_paged(const csa_tensor* x, const float* logits, int64_t x_pos0,
+                                            const float* slot_bias, int32_t m, int32_t w,
+                                            int64_t entry_begin, int64_t n_entries,
+                                            const int32_t* blocks, int32_t block_rows,
+                                            const csa_tensor* out, hipStream_t stream) {
+  clear_error();
+  const csa_status st = check_compress("csa_kv_compress_paged", x, logits, x_pos0, slot_bias, m, w,
+                                       entry_begin, n_entries, out, true);
+  if (st != CSA_OK) return st;
+  if (block_rows < 1 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress_paged: block_rows must be a power of two in [1, 2^20]");
+  if (n_entries == 0) return CSA_OK;
+  if (blocks == nullptr) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_kv_compress_paged: null blocks");
+  const int shift = __builtin_ctz((unsigned)block_rows);
+  if (x->fmt == CSA_F32)
+    launch<float>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream, blocks, shift);
+  else
+    launch<uint16_t>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream, blocks, shift);
+  return check_launch("csa_kv_compress_paged");
 }
 
 extern "C" csa_status csa_kv_compress_channel(const csa_tensor* x, const float* logits,

@@ -143,11 +143,22 @@ class Batch:
 # ----------------------------------------------------------------------------- calls
 
 
-def kv_compress(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out: KV):
-    """CSA step 1: entries entry_begin .. +n_entries of one sequence into out[0:n]."""
-    _need_cuda(logits, slot_bias)
+def kv_compress(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out: KV,
+                blocks=None, block_rows=0):
+    """CSA step 1: entries entry_begin .. +n_entries of one sequence into
+    out[0:n], or with `blocks` (int32, the request's block ids) into the
+    paged cache `out`: entry j at row blocks[j // block_rows] * block_rows +
+    j % block_rows."""
+    _need_cuda(logits, slot_bias, blocks)
     lib = _lib.load()
     xc, oc = x.c(), out.c()
+    if blocks is not None:
+        assert blocks.dtype == torch.int32 and blocks.is_contiguous()
+        check(lib.csa_kv_compress_paged(ctypes.byref(xc), _ptr(logits), int(x_pos0), _ptr(slot_bias),
+                                        int(m), int(w), int(entry_begin), int(n_entries),
+                                        _ptr(blocks), int(block_rows), ctypes.byref(oc), _stream()),
+              "csa_kv_compress_paged")
+        return out
     check(lib.csa_kv_compress(ctypes.byref(xc), _ptr(logits), int(x_pos0), _ptr(slot_bias),
                               int(m), int(w), int(entry_begin), int(n_entries),
                               ctypes.byref(oc), _stream()), "csa_kv_compress")

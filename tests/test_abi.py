@@ -76,6 +76,15 @@ def test_kv_compress_validation(lib):
     assert b"csa_kv_compress_channel" in lib.csa_last_error()
     assert chan(_t(0, 96, 64), _t(0, 96, 16), 4, 8, 0, 4) == UNSUPPORTED
     assert chan(x, out, 4, 8, 0, 0) == 0
+    # into a paged cache: block rows a power of two, a block list; the pool's
+    # size does not bound the entry count
+    paged = lambda xx, oo, m, w, e0, n, blk=FAKE, brows=32: lib.csa_kv_compress_paged(
+        ctypes.byref(xx), z, 0, b, m, w, e0, n, blk, brows, ctypes.byref(oo), None)
+    assert paged(x, out, 4, 8, 0, 4, brows=24) == BAD_ARG
+    assert paged(x, out, 4, 8, 0, 4, brows=0) == BAD_ARG
+    assert paged(x, out, 4, 8, 0, 4, blk=None) == BAD_ARG
+    assert paged(x, out, 4, 2, 0, 4) == BAD_ARG
+    assert paged(x, out, 4, 8, 0, 0) == 0
 
 
 def _batch(n_q=4, n_req=1, max_kv=16):

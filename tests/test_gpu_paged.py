@@ -183,3 +183,81 @@ def test_append_paged_equals_contiguous(m, w, P, out_fmt, D):
     free = torch.from_numpy(~owned).cuda()
     for a, b0 in zip([t for t in (paged.data, paged.scale, paged.rope) if t is not None], before):
         assert torch.equal(a[free], b0[free])
+
+
+# ------------------------------------------------------ prefill compression
+
+@pytest.mark.parametrize("m,w,P,out_fmt,D,e0", [(4, 8, 32, "bf16", 128, 0), (4, 8, 32, "fp8_mixed", 512, 40),
+                                                (128, 256, 1, "f32", 128, 3)])
+def test_compress_paged_equals_contiguous(m, w, P, out_fmt, D, e0):
+    """Prefill compression through a request's block list writes the rows the
+    contiguous call writes, at the remapped places (the first entry inside a
+    block when e0 is not a multiple of P); unowned rows stay untouched."""
+    rng = np.random.default_rng(m + P + D + e0)
+    T = 700 if m == 4 else 1300
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    z = rng.standard_normal(T).astype(np.float32)
+    b = rng.standard_normal(w).astype(np.float32)
+    n = T // m - e0
+    fmt_code = {"bf16": BF16, "f32": F32, "fp8_mixed": ops.FP8_MIXED}[out_fmt]
+    xd, zd, bd = dev_kv(x, "bf16"), dev_f32(z), dev_f32(b)
+    cont = KV.empty(fmt_code, n, D)
+    ops.kv_compress(xd, zd, 0, bd, m, w, e0, n, cont)
+    nb = (e0 + n + P - 1) // P
+    pool_blocks = nb + 4
+    blocks = rng.permutation(pool_blocks)[:nb].astype(np.int32)
+    enc = {"bf16": "bf16", "f32": "f32", "fp8_mixed": "fp8_mixed"}[out_fmt]
+    pool = dev_kv((rng.standard_normal((pool_blocks * P, D)) * 40).astype(np.float32), enc)
+    before = [t.clone() for t in (pool.data, pool.scale, pool.rope) if t is not None]
+    ops.kv_compress(xd, zd, 0, bd, m, w, e0, n, pool, blocks=torch.from_numpy(blocks).cuda(),
+                    block_rows=P)
+    torch.cuda.synchronize()
+    owned = np.zeros(pool_blocks * P, bool)
+    for jl in range(n):
+        j = e0 + jl
+        row = int(blocks[j // P]) * P + j % P
+        owned[row] = True
+        for a, c in zip((pool.data, pool.scale, pool.rope), (cont.data, cont.scale, cont.rope)):
+            if a is not None:
+                assert torch.equal(a[row], c[jl]), jl
+    free = torch.from_numpy(~owned).cuda()
+    for a, b0 in zip([t for t in (pool.data, pool.scale, pool.rope) if t is not None], before):
+        assert torch.equal(a[free], b0[free])
+
+
+def test_attention_paged_with_ring_window():
+    """Decode as a serving loop leaves it: entries in a paged cache and each
+    request's window rows in a ring (both as the decode-time append writes
+    them) give bitwise the output of contiguous entries and in-order rows."""
+    rng = np.random.default_rng(95)
+    H, D, m, k, window, C, P = 64, 512, 4, 64, 128, 160, 32
+    ts = [5000, 131, 900, 20000]
+    n_ent = [(t + 1) // m for t in ts]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    q = rng.standard_normal((len(ts) * H, D)).astype(np.float32)
+    lin, ring, p0s = [], np.zeros((len(ts) * C, D), np.float32), []
+    for r, t in enumerate(ts):
+        p0 = max(0, t - C + 1)
+        rows = rng.standard_normal((t - p0 + 1, D)).astype(np.float32)
+        lin.append(rows)
+        p0s.append(p0)
+        for i, p in enumerate(range(p0, t + 1)):
+            ring[r * C + p % C] = rows[i]
+    idx = np.full((len(ts), k), -1, np.int32)
+    for r, n in enumerate(n_ent):
+        idx[r, :min(k, n)] = np.sort(rng.choice(n, min(k, n), replace=False))
+    rows_p, table = _paged(rng, ents, P)
+    b_lin = Batch.make([1] * len(ts), ts, kv_counts=n_ent, raw_counts=[len(x) for x in lin], raw_pos=p0s)
+    b_pr = dataclasses.replace(_paged_batch(Batch.make([1] * len(ts), ts, kv_counts=n_ent,
+                                                       raw_counts=[C] * len(ts), raw_pos=[0] * len(ts)),
+                                            table, P), window_ring=True)
+    qd, idx_d = dev_kv(q, "bf16"), torch.from_numpy(idx).cuda()
+    outs = []
+    for kvd, rd, bt in ((dev_kv(np.concatenate(ents), "fp8_mixed"), dev_kv(np.concatenate(lin), "bf16"), b_lin),
+                        (dev_kv(rows_p, "fp8_mixed"), dev_kv(ring, "bf16"), b_pr)):
+        out = torch.empty(len(ts) * H, D, device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty(len(ts) * H, device="cuda")
+        ops.sparse_mqa_attn(qd, H, kvd, idx_d, k, rd, window, bt, m, out, BF16, lse, split_keys=128)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
