@@ -651,7 +651,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     if constexpr (F32C) {
       const int key = u / UPR;
       const int d = (u - key * UPR) * 4;
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(kb) + key * KSTR + d) = v[0];
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(kb + kofs) + key * KSTR + d) = v[0];
     } else {
       store_slot(dst, kofs, fp8, v[0], v[1]);
     }
@@ -803,10 +803,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     return make_uint4(x0.x, x0.y, x1.x, x1.y);
   };
 
-  auto tile_logits_with = [&](auto&& kget) -> f32x16_t {
+  auto tile_logits_with = [&](auto&& kget, int kofs) -> f32x16_t {
     f32x16_t acc_s = f32x16_t{};
     if constexpr (F32C) {
-      const float* kp = reinterpret_cast<const float*>(kb) + ql * KSTR + d0 + half;
+      const float* kp = reinterpret_cast<const float*>(kb + kofs) + ql * KSTR + d0 + half;
 #pragma unroll
       for (int c = 0; c < QC; ++c)
         acc_s = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[2 * c], qreg[c], acc_s, 0, 0, 0);
@@ -841,14 +841,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   };
   auto tile_logits = [&](int kofs) -> f32x16_t {
     launder_qk();
-    return tile_logits_with([&](int c) { return read_k(c, kofs); });
+    return tile_logits_with([&](int c) { return read_k(c, kofs); }, kofs);
   };
 
   // ---- mask, online softmax and O^T += V^T P^T for one tile whose logits are
   // acc_s; full = every key valid for every row, else mw holds this lane's
   // key bits.
   // vget(db, c) gives the V^T operand of value instruction c of dim block db.
-  auto tile_softmax_pv_with = [&](const f32x16_t& acc_s, int full, uint32_t mw, auto&& vget) {
+  auto tile_softmax_pv_with = [&](const f32x16_t& acc_s, int full, uint32_t mw, auto&& vget, int kofs) {
     // mask (skipped when every key of the tile is valid for every row).  The
     // logits are copied out of the matrix-core result before any lane is
     // masked: masking the result vector in place miscompiled (rows kept keys
@@ -897,7 +897,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       l_run += psum;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const float* vp = reinterpret_cast<const float*>(kb) + d0 + db * 32 + ql;
+        const float* vp = reinterpret_cast<const float*>(kb + kofs) + d0 + db * 32 + ql;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 8 * (i >> 2) + 4 * half + (i & 3);
@@ -954,7 +954,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   };
   auto tile_softmax_pv = [&](const f32x16_t& acc_s, int full, uint32_t mw, int kofs) {
     launder_tr();
-    tile_softmax_pv_with(acc_s, full, mw, [&](int db, int c) { return read_v(db, c, kofs); });
+    tile_softmax_pv_with(acc_s, full, mw, [&](int db, int c) { return read_v(db, c, kofs); }, kofs);
   };
 
   // this lane's key bits of the tile in ring slot `slot`
@@ -991,12 +991,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       tile_rows((t + 2) & (kMetaSlots - 1), rows);
       // the first key operands of this tile are in flight during the staging
       // (two: more cost the third wave per SIMD its registers)
-      constexpr int KPRE = 2;
-      uint4 kr[KPRE];
+      constexpr int KPRE = F32C ? 0 : 2;
+      uint4 kr[KPRE > 0 ? KPRE : 1];
       __builtin_amdgcn_sched_barrier(0);
       launder_qk();
+      if constexpr (!F32C) {
 #pragma unroll
-      for (int c = 0; c < KPRE; ++c) kr[c] = read_k(c, KO);
+        for (int c = 0; c < KPRE; ++c) kr[c] = read_k(c, KO);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 < ntiles) store_tile(KS);
       if (t + 2 < ntiles) load_tile_rows(rows);
@@ -1004,7 +1006,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
         const int tt = t + 4 + wave;
         if (tt < ntiles) meta_tile_by(g.key_lo + tt * KT, tt & (kMetaSlots - 1), wave);
       }
-      const f32x16_t sc = tile_logits_with([&](int c) { return c < KPRE ? kr[c] : read_k(c, KO); });
+      const f32x16_t sc = tile_logits_with([&](int c) { return c < KPRE ? kr[c] : read_k(c, KO); }, KO);
       tile_softmax_pv(sc, full, mw, KO);
       lds_barrier();
     };
@@ -1177,14 +1179,16 @@ csa_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int threads = a.nrb * DSPLIT * 64;
   if ((a.n_q + a.tok - 1) / a.tok * a.ngroups > 0x7fffffff)
     return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "attn: too many queries");
-  // register prefetch of the next tile (bf16 compute with registers to spare,
-  // enough threads to share it); with one wave per row block, double-buffered
-  constexpr bool kPref = !F32C && (D == 128 || DSPLIT == 4);
+  // register prefetch of the next tile (D = 128, bf16, or fp32 without
+  // split-K, which would spill; D = 512 bf16 over four waves per row block),
+  // with enough threads to share it; with one wave per row block,
+  // double-buffered
+  constexpr bool kPref = (D == 128 && (!F32C || OUTM != 2)) || (!F32C && DSPLIT == 4);
   if (kPref && threads < (D == 512 ? 512 : 256))
     return launch_attn_np<D, F32C, KVF, SPARSE, DSPLIT, OUTM>(a, stream);
   const size_t smem = attn_smem<D, F32C, DSPLIT>(a.nrb, kPref);
   auto kern = [] {
-    if constexpr (D == 128 && kPref && OUTM != 2) return attn_kernel_d128<KVF, SPARSE, OUTM>;
+    if constexpr (D == 128 && !F32C && kPref && OUTM != 2) return attn_kernel_d128<KVF, SPARSE, OUTM>;
     else return attn_kernel<D, F32C, KVF, SPARSE, DSPLIT, OUTM, kPref>;
   }();
   // the kernel's LDS ceiling is raised once per instantiation, to the most any
