@@ -651,9 +651,9 @@ __global__ __launch_bounds__(NT) void itk_select_kernel(ItkArgs a) {
   }
 }
 
-template <int FMT, bool SBF16, int NT>
+// (by default the list of k <= 1024 fits the registers: 6k slots)
+template <int FMT, bool SBF16, int NT, int CPT = 6144 / NT>
 csa_status launch_select(const ItkArgs& a, size_t bm_bytes, hipStream_t s) {
-  constexpr int CPT = 6144 / NT;         // the list of k <= 1024 fits the registers
   auto kern = itk_select_kernel<FMT, SBF16, NT, CPT>;
   const size_t lds = sizeof(SelectLds<NT>) + bm_bytes;
   static const hipError_t attr =
@@ -693,6 +693,10 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   if (a.n_q < 2 * (int64_t)cus) return launch_select<FMT, SBF16, 1024>(a, bm_bytes, s);
+  // many short rows (at most 1024 entries, so every entry is a candidate and
+  // the list fits one wave's registers): one wave a row, whose barriers cost
+  // next to nothing, and four times the rows resident
+  if (max_kv <= 1024) return launch_select<FMT, SBF16, 64, 16>(a, bm_bytes, s);
   return launch_select<FMT, SBF16, 256>(a, bm_bytes, s);
 }
 

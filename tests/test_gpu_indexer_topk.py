@@ -180,3 +180,16 @@ def test_fused_largest_k(fmt, score_fmt):
     qi, ki = _inputs(rng, T, (pos0 + T) // m, fmt)
     f, u = _both(qi, ki, fmt, Batch.make([T], [pos0], kv_counts=[(pos0 + T) // m]), m, k, score_fmt)
     assert np.array_equal(f, u)
+
+
+@pytest.mark.parametrize("fmt,score_fmt,T,pos0", [("f32", "f32", 4096, 0), ("bf16", "bf16", 600, 3400),
+                                                  ("mxfp4", "bf16", 300, 0)])
+def test_fused_short_rows_many_queries(fmt, score_fmt, T, pos0):
+    """Prefill rows of at most 1024 entries (every entry a candidate), as in
+    the fp32 CSA prefill at 4K: the same indices as score + select."""
+    rng = np.random.default_rng(67 + T)
+    m, k = 4, 64
+    n_keys = (pos0 + T) // m
+    qi, ki = _inputs(rng, T, n_keys, fmt)
+    f, u = _both(qi, ki, fmt, Batch.make([T], [pos0], kv_counts=[n_keys]), m, k, score_fmt)
+    assert np.array_equal(f, u)
