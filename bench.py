@@ -515,12 +515,12 @@ def main():
         sys.exit(2)
     wid = args.config
     wl = synth.WORKLOADS[wid]
-    torch.cuda.init()
-    t0 = time.time()
     decode = wl.kind in ("csa_decode", "mixed_decode")
     if args.paged and not decode:
         print("--paged applies to the decode workloads", file=sys.stderr)
         sys.exit(2)
+    torch.cuda.init()
+    t0 = time.time()
     w = Decode(wid, paged=args.paged) if decode else Prefill(wid)
     torch.cuda.synchronize()
     log(f"workload {wl.name}: inputs ready in {time.time() - t0:.1f}s")
