@@ -6,13 +6,16 @@
 A step is one pass of a layer's whole path over one batch of synthetic
 inputs already resident in HBM:
   1  CSA prefill, fp32, 4096 tokens:   compress -> indexer -> top-k -> attention
-  2  HCA prefill, bf16, 65536 tokens:  compress -> dense attention (default)
-  3  CSA decode, 32 x 128K context:    indexer -> top-k -> attention x2 -> merge
-  4  CSA chunked prefill, 8192 tokens at 1M: compress -> MXFP4 indexer -> top-k
-                                       -> attention
+  2  HCA prefill, bf16, 65536 tokens:  compress -> dense attention
+  3  CSA decode, 32 x 128K context:    indexer -> top-k -> attention -> merge
+  4  CSA chunked prefill, 8192 tokens at 1M context (default): compress ->
+                                       MXFP4 indexer + top-k -> attention
   5  4-layer C/H/C/H decode, 64 requests, 4K-1M contexts
-Prints one JSON line (throughput, roofline of the dominant kernel, and the CPU
-oracle timed on a bounded sample of the same workload).
+Prints one JSON line: throughput, the roofline (for a CSA prefill the
+indexer and the attention together: the sum over both of their algorithmic
+flops over the peak of their own dtype, divided by their measured time), and
+the CPU oracle timed on a bounded sample of the same workload on the host's
+cores.
 """
 import argparse
 import hashlib
@@ -116,26 +119,36 @@ class Prefill:
         self.attn_flops = 4.0 * D * H * pairs
         self.idx_flops = 2.0 * 4 * 64 * nv_sum if csa else 0.0
         cdt = "f32" if wl.act_fmt == "f32" else "bf16"
-        self.dominant = {"name": "attention", "bound": "mfma", "unit": "TFLOP/s",
-                         "work": self.attn_flops, "peak": PEAK[cdt],
-                         "per_unit": f"4*D*H = {4 * D * H} flop per (query, key) pair; "
-                                     f"{pairs} pairs per launch",
-                         "sha": src_sha("attn.hip", "common.h")}
+        idt = {"mxfp4": "fp4", "bf16": "bf16", "f32": "f32"}[wl.idx_fmt]
+        attn = {"name": "attention", "work": self.attn_flops, "peak": PEAK[cdt], "dtype": cdt,
+                "per_unit": f"4*D*H = {4 * D * H} flop per (query, key) pair; {pairs} pairs "
+                            f"per launch",
+                "sha": src_sha("attn.hip", "common.h")}
+        idx = {"name": "indexer_topk", "work": self.idx_flops, "peak": PEAK[idt], "dtype": idt,
+               "per_unit": f"2*4*64 = 512 flop per (query, visible entry) pair; {nv_sum} pairs "
+                           f"per launch",
+               "sha": src_sha("itk.hip", "indexer_core.h", "select_core.h", "common.h")}
+        # the roofline covers the indexer (with its top-k) and the attention of a
+        # CSA layer, the attention alone for HCA
+        self.parts = [idx, attn] if csa else [attn]
+        self.dominant = {"name": "+".join(p["name"] for p in self.parts), "bound": "mfma",
+                         "unit": "TFLOP/s"}
 
     def step(self, ev=None):
+        """ev: None, or three events recorded before the selection, between
+        selection and attention, and after the attention."""
         L = self.layer
         L.compress()
         idx = None
+        if ev is not None:
+            ev[0].record()
         if self.csa:
             _, idx = L.select()
         if ev is not None:
-            ev[0].record()
+            ev[1].record()
         L.attend(idx)
         if ev is not None:
-            ev[1].record()
-
-    def dominant_launch(self):
-        self.layer.attend(self.layer.buf.store.get("idx") if self.csa else None)
+            ev[2].record()
 
 
 class Decode:
@@ -239,68 +252,81 @@ class Decode:
 # ------------------------------------------------------------------ CPU baseline
 
 
-def cpu_baseline(wid, budget_s=15.0):
-    """The oracle as it stands, single-threaded BLAS, on a bounded sample of the
-    workload: the full compression it needs plus as many queries (prefill) or
-    requests (decode) as fit in about `budget_s` seconds."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_CPU = {}       # inputs shared with the forked workers
+
+
+def _cpu_prefill_worker(args):
+    """Queries i0, i0 + stride, ... of the prefill sample until the deadline;
+    returns how many were done."""
     from threadpoolctl import threadpool_limits
     from oracle import codecs
     from oracle import csa as ref
-    wl = synth.WORKLOADS[wid]
+    i0, stride, deadline = args
+    c = _CPU
+    wl, inp, vals, newv, e0, n_ent = c["wl"], c["inp"], c["vals"], c["newv"], c["e0"], c["n_ent"]
+    rawv, ki = c["rawv"], c.get("ki")
+    done = 0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        done = 0
-        if wl.kind in ("csa_prefill", "hca_prefill"):
-            # a chunk far into the sequence: its first 256 tokens are the sample
-            seq = wl.seq if wl.pos0 == 0 else min(wl.seq, 256)
-            inp = synth.prefill_inputs(wl, seq=seq)
-            t_gen = time.perf_counter() - t0
-            t0 = time.perf_counter()
-            vals = {"f32": lambda a: a.astype(np.float64),
-                    "bf16": lambda a: codecs.bf16_round(a).astype(np.float64),
-                    "mxfp4": lambda a: codecs.dequantize_mxfp4(*codecs.quantize_mxfp4(a))}
-            rawv = vals[wl.act_fmt](inp["raw"])
-            e0, n_ent = inp["first_new_entry"], inp["n_entries"]
-            new = ref.compress_entries(rawv, inp["z"], inp["raw_pos0"], inp["bias"], wl.m,
-                                       wl.w, e0, n_ent)
-            newv = ref.load_entries(ref.store_entries(new, wl.kv_fmt), wl.kv_fmt)
-            if e0 > 0:
-                ki = vals[wl.idx_fmt](inp["ki"])
-            rng = np.random.default_rng(0)
-            for i in rng.permutation(inp["seq"]):
-                t = inp["pos0"] + int(i)
-                q = vals[wl.act_fmt](inp["q"][i])
-                if wl.kind == "hca_prefill":
-                    ref.hca_query(t, q, newv, wl.m, rawv, inp["raw_pos0"], wl.window)
-                elif e0 == 0:
-                    ref.csa_query(t, q, newv, vals[wl.idx_fmt](inp["qi"][i]),
-                                  vals[wl.idx_fmt](inp["ki"]), wl.k, wl.m, rawv,
-                                  inp["raw_pos0"], wl.window, score_fmt=wl.score_fmt)
-                else:
-                    # selection first, then only the selected cached rows are decoded
-                    nv = min((t + 1) // wl.m, n_ent)
-                    keys = ref.score_keys(ref.indexer_scores(vals[wl.idx_fmt](inp["qi"][i]),
-                                                             ki[:nv]), wl.score_fmt)
-                    idx = ref.topk_indices(keys, wl.k)
-                    sel = idx[idx >= 0]
-                    old = sel[sel < e0]
-                    ent = np.concatenate([
-                        ref.load_entries(ref.store_entries(inp["cache"][old], wl.kv_fmt), wl.kv_fmt),
-                        newv[sel[sel >= e0] - e0]])
-                    pos = ref.window_positions(t, wl.window)
-                    ref.attend(q, np.concatenate([ent, rawv[pos - inp["raw_pos0"]]]),
-                               1.0 / math.sqrt(wl.dim))
-                done += 1
-                if time.perf_counter() - t0 > budget_s:
-                    break
-            sample = f"{done} of {wl.seq} query tokens (all heads) plus the compression of " \
-                     f"{n_ent - e0} entries; input draws excluded ({t_gen:.1f}s)"
-        else:
-            ctxs = synth.decode_contexts(wl)
-            specs = wl.layers if wl.kind == "mixed_decode" else [("csa", wl.m, wl.k)]
-            for r in range(len(ctxs)):
-                for li, (kind, m, k) in enumerate(specs):
-                    d = synth.decode_request(wl, r, int(ctxs[r]), m, kind == "csa", layer=li)
+        for i in range(i0, inp["seq"], stride):
+            if time.time() > deadline:
+                break
+            t = inp["pos0"] + i
+            q = vals[wl.act_fmt](inp["q"][i])
+            if wl.kind == "hca_prefill":
+                ref.hca_query(t, q, newv, wl.m, rawv, inp["raw_pos0"], wl.window)
+            elif e0 == 0:
+                ref.csa_query(t, q, newv, vals[wl.idx_fmt](inp["qi"][i]), ki, wl.k, wl.m, rawv,
+                              inp["raw_pos0"], wl.window, score_fmt=wl.score_fmt)
+            else:
+                # selection first, then only the selected cached rows are decoded
+                nv = min((t + 1) // wl.m, n_ent)
+                keys = ref.score_keys(ref.indexer_scores(vals[wl.idx_fmt](inp["qi"][i]),
+                                                         ki[:nv]), wl.score_fmt)
+                idx = ref.topk_indices(keys, wl.k)
+                sel = idx[idx >= 0]
+                old = sel[sel < e0]
+                ent = np.concatenate([
+                    ref.load_entries(ref.store_entries(inp["cache"][old], wl.kv_fmt), wl.kv_fmt),
+                    newv[sel[sel >= e0] - e0]])
+                pos = ref.window_positions(t, wl.window)
+                ref.attend(q, np.concatenate([ent, rawv[pos - inp["raw_pos0"]]]),
+                           1.0 / math.sqrt(wl.dim))
+            done += 1
+    return done
+
+
+def _cpu_decode_worker(args):
+    """Requests r0, r0 + stride, ...: each request's inputs are drawn (not
+    timed), then the oracle runs it through every layer `runs` times (each
+    timed); stops once the worker's compute time of one run passes the budget
+    or its wall time passes the cap.  Returns (requests done, [compute seconds
+    of run j])."""
+    from threadpoolctl import threadpool_limits
+    from oracle import codecs
+    from oracle import csa as ref
+    r0, stride, budget, cap, runs = args
+    wl, ctxs, specs = _CPU["wl"], _CPU["ctxs"], _CPU["specs"]
+    start = time.time()
+    done, secs = 0, [0.0] * runs
+    with threadpool_limits(limits=1):
+        for r in range(r0, len(ctxs), stride):
+            if secs[0] > budget or time.time() - start > cap:
+                break
+            layers = [synth.decode_request(wl, r, int(ctxs[r]), m, kind == "csa", layer=li)
+                      for li, (kind, m, k) in enumerate(specs)]
+            for j in range(runs):
+                t0 = time.perf_counter()
+                for (kind, m, k), d in zip(specs, layers):
                     cv = codecs.dequantize_kv_mixed(*codecs.quantize_kv_mixed(d["cache"]))
                     q = codecs.bf16_round(d["q"]).astype(np.float64)
                     sw = codecs.bf16_round(d["swa"]).astype(np.float64)
@@ -312,14 +338,87 @@ def cpu_baseline(wid, budget_s=15.0):
                                       d["swa_pos0"], wl.window, score_fmt=wl.score_fmt)
                     else:
                         ref.hca_query(d["t"], q, cv, m, sw, d["swa_pos0"], wl.window)
-                done += 1
-                if time.perf_counter() - t0 > budget_s:
-                    break
-            sample = f"{done} of {len(ctxs)} requests through all {len(specs)} layers " \
-                     f"(input draws and cache quantisation included)"
-        el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s" if "prefill" in wl.kind else "requests/s",
-            "cores": 1, "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
+                secs[j] += time.perf_counter() - t0
+            done += 1
+    return done, secs
+
+
+def cpu_baseline(wid, budget_s=8.0, runs=3, max_workers=16):
+    """The oracle as it stands on a bounded sample of the workload, on the
+    host's cores: one forked worker per core (at most max_workers, the CPU
+    share of one GPU), each with a single BLAS thread, takes an interleaved
+    share of the sample's queries (prefill) or requests (decode) until a
+    deadline of budget_s seconds.  Three such runs; the median rate is
+    reported.  Input draws and the compression of the chunk's new entries are
+    done once, before the timed runs, and are not counted."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import codecs
+    from oracle import csa as ref
+    wl = synth.WORKLOADS[wid]
+    ncpu = os.cpu_count() or 1
+    workers = max(1, min(ncpu, max_workers))
+    t0 = time.perf_counter()
+    prefill = wl.kind in ("csa_prefill", "hca_prefill")
+    _CPU.clear()
+    _CPU["wl"] = wl
+    if prefill:
+        # the whole chunk's queries; as many as the deadline allows are the sample
+        seq = wl.seq
+        inp = synth.prefill_inputs(wl, seq=seq)
+        vals = {"f32": lambda a: a.astype(np.float64),
+                "bf16": lambda a: codecs.bf16_round(a).astype(np.float64),
+                "mxfp4": lambda a: codecs.dequantize_mxfp4(*codecs.quantize_mxfp4(a))}
+        rawv = vals[wl.act_fmt](inp["raw"])
+        e0, n_ent = inp["first_new_entry"], inp["n_entries"]
+        with threadpool_limits(limits=workers):
+            new = ref.compress_entries(rawv, inp["z"], inp["raw_pos0"], inp["bias"], wl.m,
+                                       wl.w, e0, n_ent)
+            newv = ref.load_entries(ref.store_entries(new, wl.kv_fmt), wl.kv_fmt)
+        _CPU.update(inp=inp, vals=vals, rawv=rawv, e0=e0, n_ent=n_ent, newv=newv)
+        if wl.kind == "csa_prefill":
+            _CPU["ki"] = vals[wl.idx_fmt](inp["ki"])
+        fn, total = _cpu_prefill_worker, inp["seq"]
+        what = "query tokens (all heads)"
+    else:
+        _CPU["ctxs"] = synth.decode_contexts(wl)
+        _CPU["specs"] = wl.layers if wl.kind == "mixed_decode" else [("csa", wl.m, wl.k)]
+        fn, total = _cpu_decode_worker, len(_CPU["ctxs"])
+        what = f"requests through all {len(_CPU['specs'])} layers (the cache " \
+               f"quantisation included, the input draws not)"
+    t_prep = time.perf_counter() - t0
+    rates, dones = [], []
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        if prefill:
+            for _ in range(runs):
+                start = time.time()
+                counts = pool.map(fn, [(i, workers, start + budget_s) for i in range(workers)])
+                el = time.time() - start
+                rates.append(sum(counts) / el)
+                dones.append(sum(counts))
+        else:
+            # every request run `runs` times back to back after its draws; run j's
+            # rate is the requests done over the longest worker's compute time
+            res = pool.map(fn, [(i, workers, budget_s, 4 * budget_s, runs)
+                                for i in range(workers)])
+            n = sum(d for d, _ in res)
+            for j in range(runs):
+                rates.append(n / max(max(sec[j] for _, sec in res), 1e-9))
+                dones.append(n)
+    _CPU.clear()
+    med = sorted(rates)[len(rates) // 2]
+    blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")}
+            for i in threadpool_info()]
+    sample = f"up to {dones} of the first {total} {what}, in {runs} runs of about " \
+             f"{budget_s:.0f} s on {workers} worker processes (one BLAS thread each)"
+    if prefill and wl.pos0 > 0:
+        sample += f"; the chunk's first {total} of {wl.seq} tokens"
+    return {"value": round(med, 3), "unit": "tokens/s" if prefill else "requests/s",
+            "cores": workers, "kind": "oracle", "sample": sample,
+            "runs": [round(r, 3) for r in rates], "host_cpus": ncpu, "cpu_model": _cpu_model(),
+            "blas_threads_per_worker": 1, "blas_libraries": blas,
+            "prep_seconds": round(t_prep, 1)}
 
 
 # ------------------------------------------------------------------ main
@@ -335,6 +434,8 @@ def traffic_for(dom, wid):
         rec = json.load(open(path)).get(str(wid))
     except (ValueError, OSError):
         return None
+    if isinstance(rec, dict) and dom["name"] in rec:
+        rec = rec[dom["name"]]
     if not rec or rec.get("sha") != dom["sha"]:
         return None
     return rec.get("bytes_per_launch")
@@ -478,7 +579,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (three "
@@ -554,7 +655,8 @@ def main():
         for _ in range(args.warmup):
             w.step()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        # events on the stream the library launches on (torch's current one)
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
                for _ in range(args.steps)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -563,19 +665,43 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
-        work = dom["work"]
+        sel_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
+        att_ms = sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
+        part_ms = {"indexer_topk": sel_ms, "attention": att_ms}
+        dom_ms = sum(part_ms[p["name"]] for p in w.parts)
     log(f"step {ms:.4f} ms, dominant kernel ({dom['name']}) {dom_ms:.4f} ms per launch")
 
-    if dom["unit"] == "GB/s":
-        achieved = work / (dom_ms * 1e-3) / 1e9
-    else:
-        achieved = work / (dom_ms * 1e-3) / 1e12
     value = w.tokens / (ms * 1e-3)
-    roof = {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": dom["peak"],
-            "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4),
-            "traffic": traffic_for(dom, wid), "kernel": dom["name"],
-            "work_per_launch": dom["per_unit"], "launch_ms": round(dom_ms, 5)}
+    if decode:
+        achieved = work / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": dom["peak"],
+                "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4),
+                "traffic": traffic_for(dom, wid), "kernel": dom["name"],
+                "work_per_launch": dom["per_unit"], "launch_ms": round(dom_ms, 5)}
+    else:
+        # sum over the parts of (work / own peak) = ideal time; frac = ideal / measured;
+        # achieved and peak are the total work over the measured and the ideal time
+        ideal_s = sum(p["work"] / (p["peak"] * 1e12) for p in w.parts)
+        work = sum(p["work"] for p in w.parts)
+        t_s = dom_ms * 1e-3
+        kernels = []
+        traffic = 0
+        for p in w.parts:
+            pm = part_ms[p["name"]]
+            tb = traffic_for(p, wid)
+            traffic = None if traffic is None or tb is None else traffic + tb
+            kernels.append({"name": p["name"], "dtype": p["dtype"], "ms": round(pm, 5),
+                            "achieved": round(p["work"] / (pm * 1e-3) / 1e12, 2),
+                            "peak": p["peak"], "frac": round(p["work"] / (p["peak"] * 1e12) /
+                                                             (pm * 1e-3), 4),
+                            "work_per_launch": p["per_unit"], "traffic": tb})
+        roof = {"bound": "mfma", "achieved": round(work / t_s / 1e12, 2),
+                "peak": round(work / ideal_s / 1e12, 2), "unit": "TFLOP/s",
+                "frac": round(ideal_s / t_s, 4), "traffic": traffic,
+                "kernel": dom["name"], "launch_ms": round(dom_ms, 5),
+                "peak_is": "the work-weighted mix of the parts' dtype peaks "
+                           "(sum of work / sum of work over own peak)",
+                "kernels": kernels}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

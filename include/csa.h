@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -360,10 +360,14 @@ csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* 
  *   n_heads   8, 16 or a multiple of 32 up to 128 (8 and 16 need a single
  *             request and no split)
  *   split_keys 0: each query's keys are processed by one workgroup.  > 0
- *             (decode): a query's key list is cut into chunks of about
- *             split_keys keys (at most 64 chunks) processed in parallel and
- *             merged by log-sum-exp; needs `workspace` (device memory,
- *             caller-owned, contents not preserved) of at least
+ *             (decode): a query's key list (its entries, then its window
+ *             rows) is cut into chunks of split_keys keys rounded up to a
+ *             multiple of 32, processed in parallel and merged in order by
+ *             log-sum-exp.  The chunk depends on split_keys alone, so a
+ *             request's result does not depend on the other requests.  No
+ *             query may need more than 256 chunks (CSA_ERR_UNSUPPORTED
+ *             otherwise).  Needs `workspace` (device memory, caller-owned,
+ *             contents not preserved) of at least
  *             csa_attn_workspace_size(n_q, n_heads, D, max_keys, split_keys)
  *             bytes, where max_keys = (k if idx else batch->max_kv) + window.
  *             Calls sharing one workspace must not overlap.
@@ -374,7 +378,8 @@ csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads, const csa_t
                                void* out, int32_t out_fmt, float* lse, int32_t split_keys,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes csa_sparse_mqa_attn needs for split_keys > 0 (0 otherwise). */
+/* Workspace bytes csa_sparse_mqa_attn needs for split_keys > 0 (0 otherwise,
+ * and 0 when a query of max_keys keys would need more than 256 chunks). */
 size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t dim, int64_t max_keys,
                                int32_t split_keys);
 

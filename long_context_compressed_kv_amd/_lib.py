@@ -22,7 +22,7 @@ class CsaTensor(ctypes.Structure):
 
 
 # csa_abi_version() of the library these bindings describe (include/csa.h)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class CsaBatch(ctypes.Structure):

@@ -19,12 +19,15 @@
 // buffers in LDS (one barrier per tile), D = 512 decode one.
 //
 // Split-K (decode).  With split_keys > 0 a query's key list is cut into
-// chunks handled by a persistent grid of workgroups; each writes a normalised
-// partial output and its log-sum-exp to the workspace, and a combine pass
-// merges them (the same merge as csa_swa_merge).  Selected keys number at
-// most k + window per query, so the host fixes the chunk and the work items
-// are (query, split) pairs; all visible entries vary per request, so a plan
-// kernel reads the key counts, picks the chunk and lists the items.
+// chunks of split_keys keys (rounded up to whole tiles) handled by a
+// persistent grid of workgroups; each writes a normalised partial output and
+// its log-sum-exp to the workspace, and a combine pass merges a query's parts
+// in order (the same merge as csa_swa_merge).  The chunk depends on the call's
+// split_keys alone, so a request's parts, and the bits of its result, do not
+// depend on the other requests of the batch.  Selected keys number at most
+// k + window per query, so the work items are (query, split) pairs indexed
+// statically; all visible entries vary per request, so a plan kernel reads
+// the key counts and lists the items.
 //
 // Per tile and wave (bf16):
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, keys on M, queries on N;
@@ -52,7 +55,7 @@ constexpr int kTokMax = 16;      // query tokens per workgroup (128 rows / 8 hea
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kStale = 8.0f;   // log2 headroom before the running max moves
 constexpr int kMetaSlots = 8;    // ring of per-tile source rows and key masks
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 256;
 
 struct AttnArgs {
   const void* q;
@@ -78,7 +81,6 @@ struct AttnArgs {
   int nrb;           // 32-row blocks per workgroup
   int split_keys;    // 0: one workgroup per token group; else keys per split
   int max_splits;
-  int target_items;  // split-K: work items that keep the persistent grid busy
   float* ws_o;       // [max_splits][n_q*H][D]
   float* ws_lse;     // [max_splits][n_q*H]
   int* ws_cnt;       // [n_q] splits used per query
@@ -189,145 +191,30 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Sum of v over the 64 lanes of a wave (every lane active): an inclusive scan
-// by row shifts within each row of 16 lanes, then row broadcasts across rows,
-// whose last lane holds the total.
-__device__ __forceinline__ int wave_sum_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);    // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);    // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);    // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);    // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
-// Items a query of n keys makes at chunk c (rc about 1/c, within an ulp or
-// two): ceil(n / c) from a float estimate, corrected by one either way (n, c <
-// 2^24 keep the estimate within one), and one item for a query with no keys.
-__device__ __forceinline__ int plan_splits(int n, float fn, int c, float rc) {
-  int d = (int)ceilf(fn * rc);
-  const int lo = d * c;
-  d += (int)(lo < n) - ((int)(d > 0) & (int)(lo - c >= n));
-  return n > 0 ? d : 1;
-}
-
-// Split-K work list.  One chunk size (a multiple of the key tile) for the
-// whole batch, at least the caller's split_keys and enough that no query
-// needs more than max_splits.  With the key counts of at most kPlanQ queries
-// at hand, the chunk is the one that minimises the longest workgroup's work,
-// ceil(items / workgroups) * (chunk + kItemCost), where a query of n keys
-// makes ceil(n / chunk) items (fewer items on a tie: less to merge), and
-// kItemCost keys stand for an item's fixed costs; the candidates are every
-// tile multiple from the smallest chunk to the longest query, thinned to a
-// coarser step when candidates times queries would pass kPlanEvals.
-// Otherwise the chunk is raised so the batch's keys form about target_items
-// items.  Then the splits of every query, their prefix sums and the query of
-// every item, so the attention grid visits only real items.
-constexpr int kPlanQ = 4096;
-constexpr int kItemCost = 96;
-constexpr int kPlanEvals = 1 << 16;
+// Split-K work list.  The chunk is split_keys rounded up to whole tiles (the
+// host has checked that no query needs more than max_splits of them).  The
+// splits of every query, their prefix sums and the query of every item, so
+// the attention grid visits only real items; the geometry of every query is
+// recorded once for the items to load.
 template <bool SPARSE>
 __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
   __shared__ int wsum[16];
-  __shared__ int64_t ksum[16];
   __shared__ int carry;
-  __shared__ int chunk_s;
-  __shared__ int nks[kPlanQ];
-  __shared__ unsigned long long best[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool keep = a.n_q <= kPlanQ;   // key counts kept in LDS
-  // pass 1: geometry records, total and longest key counts
-  int64_t tot = 0;
-  int kmax = 0;
-  for (int64_t q = tid; q < a.n_q; q += 1024) {
-    const Geo g = make_geo<SPARSE>(a, q);
-    store_geo(a.ws_geo + q * 4, g);
-    if (keep) nks[q] = g.nkeys;
-    tot += g.nkeys;
-    kmax = g.nkeys > kmax ? g.nkeys : kmax;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    tot += __shfl_xor(tot, o);
-    const int m = __shfl_xor(kmax, o);
-    kmax = m > kmax ? m : kmax;
-  }
-  if (lane == 0) {
-    ksum[wave] = tot;
-    wsum[wave] = kmax;
-  }
-  __syncthreads();
-  int64_t t = 0;
-  int km = 0;
-  for (int w = 0; w < 16; ++w) {
-    t += ksum[w];
-    km = wsum[w] > km ? wsum[w] : km;
-  }
-  int64_t c_min = a.split_keys;
-  const int64_t need = (km + a.max_splits - 1) / a.max_splits;
-  if (need > c_min) c_min = need;
-  c_min = (c_min + KT - 1) / KT * KT;
-  const int64_t c_max = ((int64_t)km + KT - 1) / KT * KT;   // one item per query
-  if (keep && a.target_items > 0 && c_max > c_min) {
-    const int nq = (int)a.n_q;
-    int64_t ncand = (c_max - c_min) / KT + 1;
-    int64_t stride = 1;
-    if (ncand * nq > kPlanEvals) {
-      stride = (ncand * nq + kPlanEvals - 1) / kPlanEvals;
-      ncand = (c_max - c_min) / (KT * stride) + 1;
-    }
-    const int step = (int)(KT * stride), c0 = (int)c_min, nc = (int)ncand;
-    // wave w takes candidates w, w + 16, ..., its lanes the queries (the
-    // key count in a register when there are at most 64); a compact loop,
-    // since the plan runs once and every new instruction is a cache miss
-    const int nreg = lane < nq ? nks[lane] : 0;
-    unsigned long long mine = ~0ull;
-    for (int j = wave; j < nc; j += 16) {
-      const int c = c0 + step * j;
-      const float rc = __builtin_amdgcn_rcpf((float)c);
-      int cnt = 0;
-      if (nq <= 64) {
-        if (lane < nq) cnt = plan_splits(nreg, (float)nreg, c, rc);
-      } else {
-        for (int q = lane; q < nq; q += 64) cnt += plan_splits(nks[q], (float)nks[q], c, rc);
-      }
-      const int items = wave_sum_dpp(cnt);
-      // a workgroup's cost: its items' keys plus a fixed cost per item (the
-      // queries, the partial output and its share of the merge), in keys
-      const int rounds = items > 0 ? (items + a.target_items - 1) / a.target_items : 1;
-      const unsigned long long span = (unsigned long long)rounds * (unsigned)(c + kItemCost);
-      const unsigned long long key = (span << 32) | (unsigned)items;
-      mine = key < mine ? key : mine;
-    }
-    if (lane == 0) best[wave] = mine;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned long long b = best[0];
-      for (int w = 1; w < 16; ++w) b = best[w] < b ? best[w] : b;
-      // recover the chunk from the span and the item count
-      const int64_t span = (int64_t)(b >> 32), items = (int64_t)(b & 0xffffffffull);
-      const int64_t rounds = items > 0 ? (items + a.target_items - 1) / a.target_items : 1;
-      chunk_s = (int)(span / rounds - kItemCost);
-      carry = 0;
-    }
-  } else if (tid == 0) {
-    int64_t chunk = c_min;
-    const int64_t fill = a.target_items > 0 ? (t + a.target_items - 1) / a.target_items : 0;
-    if (fill > chunk) chunk = fill;
-    chunk_s = (int)((chunk + KT - 1) / KT * KT);
+  const int chunk = (a.split_keys + KT - 1) / KT * KT;
+  if (tid == 0) {
+    *a.ws_chunk = chunk;
     carry = 0;
   }
   __syncthreads();
-  const int chunk = chunk_s;
-  if (tid == 0) *a.ws_chunk = chunk;
-  // pass 2: splits, prefix sums, item -> query
   for (int64_t q0 = 0; q0 < a.n_q; q0 += 1024) {
     const int64_t q = q0 + tid;
     int ns = 0;
     if (q < a.n_q) {
-      const int nk = keep ? nks[q] : load_geo(a.ws_geo + q * 4, q).nkeys;
-      ns = nk > 0 ? (nk + chunk - 1) / chunk : 1;
+      const Geo g = make_geo<SPARSE>(a, q);
+      store_geo(a.ws_geo + q * 4, g);
+      ns = g.nkeys > 0 ? (g.nkeys + chunk - 1) / chunk : 1;
+      if (ns > a.max_splits) ns = a.max_splits;   // (excluded by the host's check)
       a.ws_cnt[q] = ns;
     }
     int x = ns;
@@ -1119,31 +1006,17 @@ csa_status launch_kernel(const AttnArgs& a0, K kern, int threads, size_t smem, h
   AttnArgs a = a0;
   dim3 grid = attn_grid(a, kern, threads, smem);
   if (a.split_keys > 0 && SPARSE && a.static_keys > 0) {
-    // selected keys: at most static_keys per query, so the host picks the
-    // chunk with the plan's cost (rounds of items over the grid times chunk
-    // plus the per-item cost) and the items are indexed statically
-    const int64_t nk = a.static_keys, T = grid.x;
-    int64_t c_min = a.split_keys;
-    const int64_t need = (nk + a.max_splits - 1) / a.max_splits;
-    if (need > c_min) c_min = need;
-    c_min = (c_min + KT - 1) / KT * KT;
-    const int64_t c_max = c_min > (nk + KT - 1) / KT * KT ? c_min : (nk + KT - 1) / KT * KT;
-    int64_t best_c = c_min, best_cost = -1, best_items = 0;
-    for (int64_t c = c_min; c <= c_max; c += KT) {
-      const int64_t items = a.n_q * ((nk + c - 1) / c);
-      const int64_t cost = (items + T - 1) / T * (c + kItemCost);
-      if (best_cost < 0 || cost < best_cost || (cost == best_cost && items < best_items)) {
-        best_cost = cost;
-        best_items = items;
-        best_c = c;
-      }
-    }
-    a.static_chunk = (int)best_c;
-    a.static_splits = (int)((nk + best_c - 1) / best_c);
+    // selected keys: at most static_keys (k + window) per query, so every
+    // query has the same splits of the fixed chunk and the items are indexed
+    // statically
+    const int64_t c = ((int64_t)a.split_keys + KT - 1) / KT * KT;
+    a.static_chunk = (int)c;
+    a.static_splits = (int)((a.static_keys + c - 1) / c);
+    if (a.static_splits < 1) a.static_splits = 1;
     if (a.host_splits != nullptr) *a.host_splits = a.static_splits;
-    if ((int64_t)grid.x > best_items) grid.x = (unsigned)best_items;
+    const int64_t items = a.n_q * a.static_splits;
+    if ((int64_t)grid.x > items) grid.x = (unsigned)items;
   } else if (a.split_keys > 0) {
-    a.target_items = (int)grid.x;
     const csa_status st = launch_plan(a, SPARSE, stream);
     if (st != CSA_OK) return st;
   }
@@ -1218,12 +1091,13 @@ csa_status launch_mode(const AttnArgs& a, bool sparse, int outm, hipStream_t s) 
   return launch_attn<D, F32C, KVF, false, DSPLIT, 1>(a, s);
 }
 
+// Parts a query of max_keys keys is cut into (0: more than kMaxSplits).
 int max_splits_for(int64_t max_keys, int split_keys) {
   if (split_keys <= 0) return 1;
   const int64_t chunk = ((int64_t)split_keys + KT - 1) / KT * KT;
   int64_t n = (max_keys + chunk - 1) / chunk;
   if (n < 1) n = 1;
-  return n > kMaxSplits ? kMaxSplits : (int)n;
+  return n > kMaxSplits ? 0 : (int)n;
 }
 
 }  // namespace
@@ -1234,6 +1108,7 @@ extern "C" size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t 
                                           int64_t max_keys, int32_t split_keys) {
   if (split_keys <= 0 || n_q <= 0 || n_heads <= 0 || dim <= 0 || max_keys < 0) return 0;
   const int ns = max_splits_for(max_keys, split_keys);
+  if (ns == 0) return 0;
   const size_t rows = (size_t)n_q * n_heads;
   // partial outputs and lse, then per query: split count, first item (+1),
   // the query of every item, and a 64-byte geometry record
@@ -1357,6 +1232,10 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
         (has_kv ? (sparse ? (int64_t)k : batch->max_kv) : 0) + (has_raw ? window : 0);
     a.split_keys = split_keys;
     a.max_splits = max_splits_for(max_keys, split_keys);
+    if (a.max_splits == 0)
+      return fail(CSA_ERR_UNSUPPORTED,
+                  "csa_sparse_mqa_attn: split_keys %d cuts %lld keys into more than %d parts",
+                  split_keys, (long long)max_keys, kMaxSplits);
     const size_t need = csa_attn_workspace_size(batch->n_q, H, D, max_keys, split_keys);
     if (workspace == nullptr || workspace_bytes < need)
       return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa_attn: split-K needs %zu workspace bytes", need);

@@ -696,7 +696,7 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   // many short rows (at most 1024 entries, so every entry is a candidate and
   // the list fits one wave's registers): one wave a row, whose barriers cost
   // next to nothing, and four times the rows resident
-  if (max_kv <= 1024) return launch_select<FMT, SBF16, 64, 16>(a, bm_bytes, s);
+  if (max_kv <= 1024 && a.qpg > 1) return launch_select<FMT, SBF16, 64, 16>(a, bm_bytes, s);
   return launch_select<FMT, SBF16, 256>(a, bm_bytes, s);
 }
 
@@ -721,38 +721,42 @@ extern "C" size_t csa_indexer_topk_workspace_size(int64_t n_q, int32_t k) {
   return head + (size_t)n_q * (size_t)cap_for(k) * 8 + (size_t)n_q * kMaxWg * 8;
 }
 
-extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* head_w,
-                                       const csa_tensor* ki, const csa_batch* batch, int32_t m,
-                                       int32_t relu, int32_t score_fmt, int32_t k, int32_t* idx,
-                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
+namespace {
+
+// Checks the arguments of csa_indexer_topk (all but the workspace) on the
+// host; `who` names the entry point in the error.
+csa_status itk_check(const csa_tensor* qi, int32_t n_heads, const csa_tensor* ki,
+                     const csa_batch* batch, int32_t m, int32_t score_fmt, int32_t k,
+                     const int32_t* idx, const char* who) {
   if (batch == nullptr || !fmt_valid_tensor(qi) || !fmt_valid_tensor(ki, false))
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: bad tensor or batch");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad tensor or batch", who);
   if (batch->n_req < 1 || batch->n_q < 0 || batch->q_off == nullptr || batch->q_pos == nullptr ||
       batch->kv_off == nullptr)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: bad batch descriptor");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad batch descriptor", who);
   if (n_heads != kHI || qi->dim != kDI || ki->dim != kDI)
-    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: implemented for 4 heads of dim 64");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: implemented for 4 heads of dim 64", who);
   if (qi->fmt != ki->fmt || (qi->fmt != CSA_F32 && qi->fmt != CSA_BF16 && qi->fmt != CSA_MXFP4))
-    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: qi and ki must both be F32, BF16 or MXFP4");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: qi and ki must both be F32, BF16 or MXFP4", who);
   if (score_fmt != CSA_F32 && score_fmt != CSA_BF16)
-    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: scores must be F32 or BF16");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: scores must be F32 or BF16", who);
   if (qi->rows != batch->n_q * n_heads)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: qi rows must be n_q * n_heads");
-  if (m < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: m must be >= 1");
-  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: need 1 <= k <= 4096");
-  if (batch->max_kv < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: max_kv < 0");
-  if (batch->max_kv > kBitmapMax)
-    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: rows above 2^20 entries");
-  if (batch->n_q == 0) return CSA_OK;
-  if (batch->n_q > 0x7fffffff) return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: too many queries");
-  if (idx == nullptr) return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: null idx");
-  const size_t need = csa_indexer_topk_workspace_size(batch->n_q, k);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "csa_indexer_topk: needs %zu workspace bytes", need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: workspace must be 16-byte aligned");
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: qi rows must be n_q * n_heads", who);
+  if (m < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: m must be >= 1", who);
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: need 1 <= k <= 4096", who);
+  if (batch->max_kv < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: max_kv < 0", who);
+  if (batch->max_kv > kBitmapMax) return fail(CSA_ERR_UNSUPPORTED, "%s: rows above 2^20 entries", who);
+  if (batch->n_q > 0x7fffffff) return fail(CSA_ERR_UNSUPPORTED, "%s: too many queries", who);
+  if (batch->n_q > 0 && idx == nullptr) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: null idx", who);
+  return CSA_OK;
+}
 
+// Launches the three kernels of csa_indexer_topk with the candidate lists in
+// `ws` (already checked: large enough and 16-byte aligned).
+csa_status itk_launch(const csa_tensor* qi, int32_t n_heads, const float* head_w,
+                      const csa_tensor* ki, const csa_batch* batch, int32_t m, int32_t relu,
+                      int32_t score_fmt, int32_t k, int32_t* idx, char* ws, const char* who,
+                      hipStream_t stream) {
+  (void)n_heads;
   ItkArgs a{};
   a.qi = qi->data;
   a.qi_scale = static_cast<const uint8_t*>(qi->scale);
@@ -760,14 +764,13 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
   a.ki = ki->data;
   a.ki_scale = static_cast<const uint8_t*>(ki->scale);
   a.b = BatchDev{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, nullptr, nullptr, ki->rows, 0};
-  if (const csa_status st = batch_pages(batch, a.b, "csa_indexer_topk"); st != CSA_OK) return st;
+  if (const csa_status st = batch_pages(batch, a.b, who); st != CSA_OK) return st;
   a.m = m;
   a.relu = relu ? 1 : 0;
   a.qpg = batch->n_req == 1 ? 8 : 1;
   a.n_q = batch->n_q;
   a.k = k;
   a.cap = (int)cap_for(k);
-  char* ws = static_cast<char*>(workspace);
   a.tau = reinterpret_cast<uint32_t*>(ws);
   a.cnt = a.tau + batch->n_q;
   a.cand = reinterpret_cast<uint2*>(ws + ((size_t)batch->n_q * 2 * 4 + 15) / 16 * 16);
@@ -778,9 +781,29 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
   a.max_n = max_kv;
   // (grid y: the queries when streaming; else the entry chunks, at most 1024)
   if (groups > 0x7fffffff || (a.qpg == 1 && groups > 65535))
-    return fail(CSA_ERR_UNSUPPORTED, "csa_indexer_topk: problem too large for one launch");
+    return fail(CSA_ERR_UNSUPPORTED, "%s: problem too large for one launch", who);
   const bool sb = score_fmt == CSA_BF16;
   if (qi->fmt == CSA_F32) return sb ? launch_all<CSA_F32, true>(a, max_kv, stream) : launch_all<CSA_F32, false>(a, max_kv, stream);
   if (qi->fmt == CSA_BF16) return sb ? launch_all<CSA_BF16, true>(a, max_kv, stream) : launch_all<CSA_BF16, false>(a, max_kv, stream);
   return sb ? launch_all<CSA_MXFP4, true>(a, max_kv, stream) : launch_all<CSA_MXFP4, false>(a, max_kv, stream);
+}
+
+}  // namespace
+
+extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* head_w,
+                                       const csa_tensor* ki, const csa_batch* batch, int32_t m,
+                                       int32_t relu, int32_t score_fmt, int32_t k, int32_t* idx,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (const csa_status st = itk_check(qi, n_heads, ki, batch, m, score_fmt, k, idx, "csa_indexer_topk");
+      st != CSA_OK)
+    return st;
+  if (batch->n_q == 0) return CSA_OK;
+  const size_t need = csa_indexer_topk_workspace_size(batch->n_q, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "csa_indexer_topk: needs %zu workspace bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: workspace must be 16-byte aligned");
+  return itk_launch(qi, n_heads, head_w, ki, batch, m, relu, score_fmt, k, idx,
+                    static_cast<char*>(workspace), "csa_indexer_topk", stream);
 }

@@ -31,17 +31,26 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   auto part_o = [&](int p) {
     return reinterpret_cast<const float*>(reinterpret_cast<const char*>(o0) + p * stride_o) + row * dim;
   };
-  const float lv = lane < n
-      ? *(reinterpret_cast<const float*>(reinterpret_cast<const char*>(l0) + lane * stride_l) + row)
-      : -INFINITY;
-  const float mx = wave_max(lv);
-  const float w = (mx == -INFINITY || lv == -INFINITY) ? 0.0f : expf(lv - mx);
-  const float den = wave_sum(w);
+  // part p's log-sum-exp and weight are held by lane p % 64, slot p / 64
+  float lv[4], w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = lane + 64 * j;
+    lv[j] = p < n ? *(reinterpret_cast<const float*>(reinterpret_cast<const char*>(l0) + p * stride_l) + row)
+                  : -INFINITY;
+  }
+  const float mx = wave_max(fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3])));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (mx == -INFINITY || lv[j] == -INFINITY) ? 0.0f : expf(lv[j] - mx);
+  // (with at most 64 parts the slots past the first hold 0 and add nothing)
+  const float den = wave_sum(((w[0] + w[1]) + w[2]) + w[3]);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   if (lse_out != nullptr && lane == 0) lse_out[row] = den > 0.0f ? mx + logf(den) : -INFINITY;
-  // part p's weight, read from lane p into a scalar register
+  // part p's weight, read from its lane into a scalar register
   auto weight = [&](int p) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), p));
+    const int j = p >> 6;
+    const float v = j == 0 ? w[0] : (j == 1 ? w[1] : (j == 2 ? w[2] : w[3]));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), p & 63));
   };
   // a part of weight 0 (lse = -inf) is skipped by a select, so its values
   // never reach the sum
@@ -91,7 +100,7 @@ csa_status launch_lse_merge_bytes(const float* o0, const float* l0, int64_t stri
                                   int rows_per_q, int64_t rows, int dim, void* out, int out_fmt,
                                   float* lse_out, hipStream_t stream) {
   const int64_t blocks = (rows + 3) / 4;
-  if (blocks > 0x7fffffff || nparts < 1 || nparts > 64)
+  if (blocks > 0x7fffffff || nparts < 1 || nparts > 256)
     return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "merge: bad row or part count");
   if (out_fmt == CSA_BF16)
     hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, o0,

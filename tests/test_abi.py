@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     assert lib.csa_status_string(0) == b"ok"
     assert lib.csa_status_string(3) == b"workspace too small"
 

@@ -3,9 +3,9 @@ pipeline the benchmark times.  The oracle evaluates sampled queries (prefill)
 or requests (decode) one by one from the same seeded float32 draws.
 
 Checks per workload:
-  - top-k: equal index sets, except entries whose key lies within one key ulp
-    of the oracle's k-th key (fp32 accumulation order can move a score
-    across a bf16 rounding boundary);
+  - top-k: equal index sets, except entries whose exact score lies within
+    the fp32 accumulation bound of the point where its rounding decides its
+    side of the oracle's k-th key (or whose key ties with it), in few rows;
   - attention, stage-wise: the GPU attention re-run on the oracle's index sets
     matches the oracle within 1e-4 (fp32 compute) or 2e-2 (bf16 compute);
   - attention, end to end: rows whose index sets agree match within the same
@@ -38,16 +38,48 @@ def log(*a):
     sys.stdout.flush()
 
 
-def topk_ok(got, want, keys, score_fmt):
+# fp32 accumulation bound of one score: four 64-term dot products summed
+# (each product exact), relative to the sum of the products' magnitudes
+ACC_BOUND = 70 * 2.0 ** -24
+
+
+def topk_ok(got, want, keys, score_fmt, s, qiv, kiv):
+    """The GPU's index set equals the oracle's, or every entry in which they
+    differ is explained by the fp32 accumulation order: its exact (fp64)
+    score s lies within the accumulation bound of the point where the score's
+    rounding decides its side of the k-th key tau (for bf16 keys the midpoints
+    between tau and its bf16 neighbours; for fp32 keys tau itself), or its key
+    equals tau (then the lowest-index rule among tied entries moves with the
+    others).  qiv [4, 64], kiv [n, 64]: the oracle's operand values."""
     got = set(int(x) for x in got if x >= 0)
     want_s = set(int(x) for x in want if x >= 0)
     if got == want_s:
         return True
     if len(got) != len(want_s):
         return False
-    tau = np.sort(keys)[::-1][len(want_s) - 1]
-    eps = abs(tau) * 1e-6 if score_fmt == "f32" else bf16_ulp(tau)
-    return all(abs(keys[j] - tau) <= eps for j in got ^ want_s)
+    tau = float(np.sort(keys)[::-1][len(want_s) - 1])
+    aq = np.abs(np.asarray(qiv, np.float64)).sum(axis=0)
+    if score_fmt == "bf16":
+        one = lambda a: float(np.asarray(a, np.float64).reshape(-1)[0])
+        up = one(codecs.bf16_round(np.array([np.nextafter(np.float32(tau), np.float32(np.inf)) +
+                                             np.float32(one(bf16_ulp(tau)) / 2)], np.float32)))
+        below = np.nextafter(np.float32(tau), np.float32(-np.inf)) if tau != 0 else 0.0
+        points = [(tau + up) / 2, tau - one(bf16_ulp(below)) / 2]
+    else:
+        points = [tau]
+    for j in got ^ want_s:
+        if float(keys[j]) == tau:
+            continue
+        eps = ACC_BOUND * float(np.abs(np.asarray(kiv[j], np.float64)) @ aq) + abs(tau) * 2.0 ** -23
+        if not any(abs(float(s[j]) - p) <= eps for p in points):
+            return False
+    return True
+
+
+def max_mismatched_rows(n_rows):
+    """Rows whose index set may differ from the oracle's (each difference also
+    explained entry by entry by topk_ok)."""
+    return max(2, math.ceil(0.1 * n_rows))
 
 
 # ------------------------------------------------------------------ prefill
@@ -127,7 +159,8 @@ def run_prefill(wid, seq=None, n_sample=48):
             keys = ref.score_keys(s, wl.score_fmt)
             want = ref.topk_indices(keys, wl.k)
             oracle_idx[int(i)] = want
-            assert topk_ok(idx_g[i], want, keys, wl.score_fmt), f"top-k of query {i}"
+            assert topk_ok(idx_g[i], want, keys, wl.score_fmt, s, qiv[si], kiv[:nv]), \
+                f"top-k of query {i}"
             sel = want[want >= 0]
             same = set(idx_g[i][idx_g[i] >= 0].tolist()) == set(sel.tolist())
             n_mismatch += 0 if same else 1
@@ -143,6 +176,7 @@ def run_prefill(wid, seq=None, n_sample=48):
     log(f"workload {wid}: end-to-end max err {worst_e2e:.3g}, top-k set mismatches "
         f"{n_mismatch}/{len(sample)}")
     assert worst_e2e <= tol
+    assert n_mismatch <= max_mismatched_rows(len(sample))
     if csa:
         # stage-wise: GPU attention over the oracle's selections, sampled queries only
         idx_o = np.stack([oracle_idx[int(i)] for i in sample]).astype(np.int32)
@@ -244,10 +278,12 @@ def run_decode(wid, batch=None, layers=None, sample_req=None):
             qv = ref_vals(d["q"], "bf16")
             swv = ref_vals(d["swa"], "bf16")
             if csa:
-                s = ref.indexer_scores(ref_vals(d["qi"], wl.idx_fmt), ref_vals(d["ki"], wl.idx_fmt))
+                qiv, kiv = ref_vals(d["qi"], wl.idx_fmt), ref_vals(d["ki"], wl.idx_fmt)
+                s = ref.indexer_scores(qiv, kiv)
                 keys = ref.score_keys(s, wl.score_fmt)
                 want = ref.topk_indices(keys, k)
-                assert topk_ok(idx_g[r], want, keys, wl.score_fmt), f"top-k of request {r}"
+                assert topk_ok(idx_g[r], want, keys, wl.score_fmt, s, qiv, kiv), \
+                    f"top-k of request {r}"
                 sel = want[want >= 0]
                 same = set(idx_g[r][idx_g[r] >= 0].tolist()) == set(sel.tolist())
                 mism += 0 if same else 1
@@ -270,6 +306,7 @@ def run_decode(wid, batch=None, layers=None, sample_req=None):
         log(f"workload {wid} layer {li}: end-to-end max err {worst:.3g}, stage-wise "
             f"{worst_sw:.3g}, top-k set mismatches {mism}/{len(reqs)}")
         assert worst <= TOL["bf16"] and worst_sw <= TOL["bf16"]
+        assert mism <= max_mismatched_rows(len(reqs))
         del layer, cache, swa, q, qi, ki, res
         torch.cuda.empty_cache()
 

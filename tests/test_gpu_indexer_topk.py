@@ -183,7 +183,8 @@ def test_fused_largest_k(fmt, score_fmt):
 
 
 @pytest.mark.parametrize("fmt,score_fmt,T,pos0", [("f32", "f32", 4096, 0), ("bf16", "bf16", 600, 3400),
-                                                  ("mxfp4", "bf16", 300, 0)])
+                                                  ("mxfp4", "bf16", 300, 0),
+                                                  ("mxfp4", "bf16", 1024, 3000)])
 def test_fused_short_rows_many_queries(fmt, score_fmt, T, pos0):
     """Prefill rows of at most 1024 entries (every entry a candidate), as in
     the fp32 CSA prefill at 4K: the same indices as score + select."""
@@ -192,4 +193,20 @@ def test_fused_short_rows_many_queries(fmt, score_fmt, T, pos0):
     n_keys = (pos0 + T) // m
     qi, ki = _inputs(rng, T, n_keys, fmt)
     f, u = _both(qi, ki, fmt, Batch.make([T], [pos0], kv_counts=[n_keys]), m, k, score_fmt)
+    assert np.array_equal(f, u)
+
+
+@pytest.mark.parametrize("fmt,score_fmt", [("bf16", "bf16"), ("mxfp4", "bf16"), ("f32", "f32")])
+def test_fused_many_short_single_query_requests(fmt, score_fmt):
+    """600 decode requests (one query each) of at most 1024 visible entries,
+    more rows than the device holds select workgroups at once: the streamed
+    filter's per-workgroup regions and the select over them give the same
+    indices as score + select."""
+    rng = np.random.default_rng(71)
+    m, k, n_req = 4, 64, 600
+    ctx = [int(c) for c in rng.integers(3, 4096, n_req)]
+    kv_counts = [(c + 1) // m for c in ctx]
+    qi, ki = _inputs(rng, n_req, sum(kv_counts), fmt)
+    batch = Batch.make([1] * n_req, ctx, kv_counts=kv_counts)
+    f, u = _both(qi, ki, fmt, batch, m, k, score_fmt)
     assert np.array_equal(f, u)
