@@ -334,6 +334,30 @@ csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, const float* 
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_indexer_topk_noalloc - csa_indexer_topk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same result, bit for bit, with the
+ * candidate lists in a static device array of the library instead of a
+ * caller workspace.  Nothing is allocated by the call.
+ *   arguments   as csa_indexer_topk, without workspace / workspace_bytes
+ *   limit       csa_indexer_topk_workspace_size(n_q, k) must not exceed
+ *               csa_indexer_topk_noalloc_max_bytes() (16 MiB: e.g. 256 decode
+ *               queries at k = 1024); larger calls return CSA_ERR_WORKSPACE
+ *               before anything is launched
+ *   sharing     each GPU holds one such array for the life of the process,
+ *               shared by every call on that GPU: calls on one GPU that may
+ *               overlap in time (different streams, threads) race and must
+ *               be ordered by the caller; calls on one stream are ordered
+ *   first call  on a device resolves the array's device address once
+ *               (hipGetSymbolAddress); a failure there is CSA_ERR_HIP
+ * ------------------------------------------------------------------------- */
+size_t csa_indexer_topk_noalloc_max_bytes(void);
+csa_status csa_indexer_topk_noalloc(const csa_tensor* qi, int32_t n_heads, const float* head_w,
+                                    const csa_tensor* ki, const csa_batch* batch, int32_t m,
+                                    int32_t relu, int32_t score_fmt, int32_t k, int32_t* idx,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * csa_sparse_mqa_attn - CSA step 3 / HCA dense attention.
  * Page "DeepSeek V4 深度解析", section 2: CSA step 3 (a sliding-window branch
  * of the latest 128 uncompressed tokens, attended together with the selected

@@ -10,7 +10,8 @@ CSA_F32, CSA_BF16, CSA_FP8_MIXED, CSA_MXFP4 = 0, 1, 2, 3
 
 EXPORTED = (
     "csa_kv_compress", "csa_kv_compress_paged", "csa_kv_compress_channel", "csa_kv_compress_append", "csa_kv_append_state_size", "csa_indexer_score", "csa_topk_select", "csa_indexer_topk",
-    "csa_indexer_topk_workspace_size", "csa_sparse_mqa_attn",
+    "csa_indexer_topk_workspace_size", "csa_indexer_topk_noalloc",
+    "csa_indexer_topk_noalloc_max_bytes", "csa_sparse_mqa_attn",
     "csa_swa_merge", "csa_quantize", "csa_dequantize", "csa_mxfp4_to_fp8",
     "csa_attn_workspace_size", "csa_abi_version", "csa_status_string", "csa_last_error",
 )
@@ -62,6 +63,7 @@ def load():
         "csa_indexer_score": [T, I32, P, T, B, I32, I32, P, I32, I64, P],
         "csa_topk_select": [P, I32, I64, B, I32, I32, P, P],
         "csa_indexer_topk": [T, I32, P, T, B, I32, I32, I32, I32, P, P, ctypes.c_size_t, P],
+        "csa_indexer_topk_noalloc": [T, I32, P, T, B, I32, I32, I32, I32, P, P],
         "csa_sparse_mqa_attn": [T, I32, T, P, I32, T, I32, B, I32, F32, P, I32, P, I32, P,
                                 ctypes.c_size_t, P],
         "csa_swa_merge": [P, P, P, P, I64, I32, P, I32, P, P],
@@ -77,6 +79,8 @@ def load():
     lib.csa_kv_append_state_size.argtypes = [I64, I32]
     lib.csa_indexer_topk_workspace_size.restype = ctypes.c_size_t
     lib.csa_indexer_topk_workspace_size.argtypes = [I64, I32]
+    lib.csa_indexer_topk_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.csa_indexer_topk_noalloc_max_bytes.argtypes = []
     lib.csa_attn_workspace_size.restype = ctypes.c_size_t
     lib.csa_attn_workspace_size.argtypes = [I64, I32, I32, I64, I32]
     lib.csa_abi_version.restype = ctypes.c_int

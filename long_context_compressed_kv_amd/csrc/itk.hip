@@ -28,6 +28,7 @@
 //      scores.
 // The candidates arrive in no fixed order, but every step after the filter
 // depends only on the candidate set, so the output is deterministic.
+#include <mutex>
 #include <type_traits>
 
 #include "indexer_core.h"
@@ -806,4 +807,67 @@ extern "C" csa_status csa_indexer_topk(const csa_tensor* qi, int32_t n_heads, co
     return fail(CSA_ERR_INVALID_ARGUMENT, "csa_indexer_topk: workspace must be 16-byte aligned");
   return itk_launch(qi, n_heads, head_w, ki, batch, m, relu, score_fmt, k, idx,
                     static_cast<char*>(workspace), "csa_indexer_topk", stream);
+}
+
+
+// ------------------------------------------------------------------ no allocation
+
+// csa_indexer_topk_noalloc keeps the candidate lists in this file-scope
+// device array instead of a caller workspace: one copy per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a handle); it uses the device address that
+// hipGetSymbolAddress returns for the current GPU.
+namespace {
+
+constexpr size_t kNoAllocScratch = 16u << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current GPU, resolved once per device.
+csa_status scratch_ptr(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(CSA_ERR_HIP, "csa_indexer_topk_noalloc: no current device (or more than %d)",
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CSA_ERR_HIP, "csa_indexer_topk_noalloc: hipGetSymbolAddress failed (%s)",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t csa_indexer_topk_noalloc_max_bytes(void) { return kNoAllocScratch; }
+
+extern "C" csa_status csa_indexer_topk_noalloc(const csa_tensor* qi, int32_t n_heads,
+                                               const float* head_w, const csa_tensor* ki,
+                                               const csa_batch* batch, int32_t m, int32_t relu,
+                                               int32_t score_fmt, int32_t k, int32_t* idx,
+                                               hipStream_t stream) {
+  clear_error();
+  if (const csa_status st = itk_check(qi, n_heads, ki, batch, m, score_fmt, k, idx,
+                                      "csa_indexer_topk_noalloc");
+      st != CSA_OK)
+    return st;
+  if (batch->n_q == 0) return CSA_OK;
+  const size_t need = csa_indexer_topk_workspace_size(batch->n_q, k);
+  if (need > kNoAllocScratch)
+    return fail(CSA_ERR_WORKSPACE,
+                "csa_indexer_topk_noalloc: %lld queries at k = %d need %zu bytes of candidate "
+                "lists, above the %zu-byte static scratch (use csa_indexer_topk)",
+                (long long)batch->n_q, k, need, kNoAllocScratch);
+  char* ws = nullptr;
+  if (const csa_status st = scratch_ptr(&ws); st != CSA_OK) return st;
+  return itk_launch(qi, n_heads, head_w, ki, batch, m, relu, score_fmt, k, idx, ws,
+                    "csa_indexer_topk_noalloc", stream);
 }

@@ -264,6 +264,26 @@ def indexer_topk(qi: KV, n_heads, ki: KV, batch: Batch, m, score_fmt, k, head_w=
     return idx
 
 
+def indexer_topk_noalloc_max_bytes():
+    return int(_lib.load().csa_indexer_topk_noalloc_max_bytes())
+
+
+def indexer_topk_noalloc(qi: KV, n_heads, ki: KV, batch: Batch, m, score_fmt, k, idx,
+                         head_w=None, relu=True):
+    """indexer_topk without a workspace: the candidate lists live in the
+    library's static device scratch (see csa_indexer_topk_noalloc); `idx`
+    int32 [n_q, k] is written in place."""
+    _need_cuda(head_w, idx)
+    lib = _lib.load()
+    qc, kc, bc = qi.c(), ki.c(), batch.c()
+    check(lib.csa_indexer_topk_noalloc(ctypes.byref(qc), int(n_heads), _ptr(head_w),
+                                       ctypes.byref(kc), ctypes.byref(bc), int(m),
+                                       1 if relu else 0, int(score_fmt), int(k), _ptr(idx),
+                                       _stream()),
+          "csa_indexer_topk_noalloc")
+    return idx
+
+
 def attn_workspace_size(n_q, n_heads, dim, max_keys, split_keys):
     return int(_lib.load().csa_attn_workspace_size(int(n_q), int(n_heads), int(dim),
                                                    int(max_keys), int(split_keys)))

@@ -222,3 +222,25 @@ def test_indexer_topk_validation(lib):
     assert f(qi_=_t(1, 64, 15)) == BAD_ARG               # rows != n_q * heads
     assert f(b_=_batch(max_kv=(1 << 20) + 1)) == UNSUPPORTED
     assert f(ws=ctypes.c_void_p(0x1008)) == BAD_ARG      # workspace not 16-byte aligned
+
+
+def test_indexer_topk_noalloc_limit_checked_on_the_host(lib):
+    """The entry point without a workspace refuses, before any HIP call, a call
+    whose candidate lists exceed its static scratch; its other checks are
+    those of csa_indexer_topk."""
+    cap = lib.csa_indexer_topk_noalloc_max_bytes()
+    assert cap == 16 << 20
+    n_q = 4096                                    # 4096 queries at k = 1024: far above
+    assert lib.csa_indexer_topk_workspace_size(n_q, 1024) > cap
+    qi = CsaTensor(3, 64, n_q * 4, FAKE, FAKE, None)
+    ki = CsaTensor(3, 64, 1000, FAKE, FAKE, None)
+    bt = CsaBatch(n_q, 0, n_q, 1000, FAKE, FAKE, FAKE, None, None, None, 0, 0, 0)
+    WORKSPACE = 3
+    st = lib.csa_indexer_topk_noalloc(ctypes.byref(qi), 4, None, ctypes.byref(ki), ctypes.byref(bt),
+                                      4, 1, 1, 1024, FAKE, None)
+    assert st == WORKSPACE
+    assert b"static scratch" in lib.csa_last_error()
+    # the shared checks: wrong head count
+    st = lib.csa_indexer_topk_noalloc(ctypes.byref(qi), 8, None, ctypes.byref(ki), ctypes.byref(bt),
+                                      4, 1, 1, 1024, FAKE, None)
+    assert st == UNSUPPORTED
