@@ -29,9 +29,18 @@ COMMON = [
 ]
 
 
+# Kernels whose matrix-core results feed vector arithmetic right away keep
+# them in ordinary VGPRs (otherwise every result is first copied out of the
+# accumulation registers).
+PER_FILE = {
+    "itk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "unknown target feature" not in l

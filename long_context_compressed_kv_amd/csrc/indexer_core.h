@@ -98,15 +98,35 @@ __device__ __forceinline__ f32x16_t tile_dots(const QueryOp<FMT>& q, const KeyOp
 
 // Score of the query in register block g of a tile result: ReLU (if relu)
 // of each head's dot product, weighted by hw[h] and summed over the heads.
+// The ReLU is an integer max on the bit pattern: a negative float (-0
+// included) is a negative int32 and becomes +0; without ReLU the floor is
+// INT_MIN, which keeps every value.
 __device__ __forceinline__ float head_score(const f32x16_t& acc, int g, const float* hw, int relu) {
+  int lo = relu ? 0 : (int)0x80000000u;
+  asm volatile("" : "+s"(lo));   // a value in a register, not a select per head
   float s = 0.0f;
 #pragma unroll
   for (int h = 0; h < kHI; ++h) {
-    float v = acc[4 * g + h];
-    if (relu) v = fmaxf(v, 0.0f);
+    const int b = __float_as_int(acc[4 * g + h]);
+    const float v = __int_as_float(b > lo ? b : lo);
     s = fmaf(hw[h], v, s);
   }
   return s;
+}
+
+// The same with every head weight 1 (no weights given): fma(1, v, s) is
+// v + s, and fma(1, v, 0) is v but for -0 (the sums can differ from
+// head_score's only in the sign of a zero, which the score's key folds).
+__device__ __forceinline__ float head_score_unit(const f32x16_t& acc, int g, int relu) {
+  int lo = relu ? 0 : (int)0x80000000u;
+  asm volatile("" : "+s"(lo));
+  float v[kHI];
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) {
+    const int b = __float_as_int(acc[4 * g + h]);
+    v[h] = __int_as_float(b > lo ? b : lo);
+  }
+  return ((v[0] + v[1]) + v[2]) + v[3];
 }
 
 }  // namespace csa

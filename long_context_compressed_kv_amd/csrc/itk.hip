@@ -210,6 +210,231 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ 2a. filter, query groups
+
+// The query groups of one request (prefill): the sample gave each query a
+// threshold key tau.  A workgroup scores its group against kGroupTiles tiles
+// of 32 entries per wave.  Per lane and register block a score is the ReLU'd
+// head sum (as the score kernel forms it) compared with a float floor below
+// which no score can reach tau; the few that pass are staged per (wave,
+// query) in LDS with their exact keys, then one atomic per query reserves
+// the workgroup's span of the list and the waves copy their candidates out.
+// A query whose row fits the list whole (at most cap entries, tau = 0) takes
+// every visible entry at list slot = entry index instead.
+constexpr int kGroupTiles = 32;     // tiles per wave: 4096 entries per workgroup
+constexpr int kStageSlots = 64;     // staged candidates per (wave, query)
+
+// A float below which a score's key cannot reach tau (taken a little low:
+// a score at or above it may still fall short, and is then only an extra
+// candidate).  fp32 keys: key(s) >= tau exactly when s >= the value of tau
+// (-0 and +0 compare equal).  bf16 keys: a score rounds to the value v of tau
+// or above only from above the midpoint below v, which lies above
+// v - |v| 2^-7; 2^-120 more keeps zero and tiny values on the safe side.
+template <bool SBF16>
+__device__ __forceinline__ float score_floor(uint32_t tau) {
+  const float v = key_value<SBF16>(tau);
+  if constexpr (!SBF16) return v;
+  return fmaf(-__builtin_fabsf(v), 0x1p-7f, v) - 0x1p-120f;
+}
+
+template <int FMT> struct GroupTiling { static constexpr int TB = 2; };
+template <> struct GroupTiling<CSA_MXFP4> { static constexpr int TB = 4; };
+
+// Bytes of one entry key row and of its block scales.
+template <int FMT> struct KeyRow;
+template <> struct KeyRow<CSA_F32> { static constexpr int B = kDI * 4, S = 0; };
+template <> struct KeyRow<CSA_BF16> { static constexpr int B = kDI * 2, S = 0; };
+template <> struct KeyRow<CSA_MXFP4> { static constexpr int B = kDI / 2, S = kDI / 32; };
+
+// The key operand of a lane whose row starts at `row` (bytes; the lane's
+// half of the dims as load_key reads it) and whose scales start at `srow`.
+template <int FMT>
+__device__ __forceinline__ void load_key_row(const uint8_t* row, const uint8_t* srow, int half,
+                                             KeyOp<FMT>& k) {
+  if constexpr (FMT == CSA_F32) {
+    const float* p = reinterpret_cast<const float*>(row) + half;
+#pragma unroll
+    for (int c = 0; c < kDI / 2; ++c) k.v[c] = p[2 * c];
+  } else if constexpr (FMT == CSA_BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + half * 8;
+#pragma unroll
+    for (int c = 0; c < kDI / 16; ++c) k.v[c] = *reinterpret_cast<const uint4*>(p + 16 * c);
+  } else {
+    k.v = *reinterpret_cast<const uint4*>(row + half * 16);
+    k.scale = srow[half];
+  }
+}
+
+template <int FMT, bool SBF16, bool PAGED>
+__global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
+  constexpr int QS = 8;                      // query slots of a group
+  constexpr int EW = kGroupTiles * 32;       // entries per wave
+  constexpr int TB = GroupTiling<FMT>::TB;   // tiles loaded together
+  constexpr int NB = kGroupTiles / TB;
+  // staged candidates: (score bits, entry); the key is formed when copied out
+  __shared__ uint2 stage[kWaves][QS][kStageSlots];
+  __shared__ uint32_t wcnt[kWaves][QS];
+  __shared__ uint32_t gbase[QS];
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, rl = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform over the wave
+
+  const int64_t qblock = (int64_t)blockIdx.x * a.qpg;
+  Group<FMT, 4> gr;
+  load_group<FMT, 4>(a, qblock, gr);
+  int64_t q_hi = qblock + a.qpg - 1;
+  if (q_hi >= a.n_q) q_hi = a.n_q - 1;
+  // the group's longest and shortest rows (at most 2^20 entries; uniform)
+  const int n_scan = __builtin_amdgcn_readfirstlane((int)visible(a, q_hi));
+  const int n_lo = __builtin_amdgcn_readfirstlane((int)visible(a, qblock));
+  const int e_wg = (int)blockIdx.y * (kWaves * EW);
+  if (e_wg >= n_scan) return;                // the whole workgroup: no barrier reached
+  const int e_wave = e_wg + wave * EW;
+  const int64_t kv_base = gr.qm.kv_base;
+
+  // the lane's queries (2g + half): their floors, and whether their rows are
+  // taken whole (at most cap entries)
+  float tf[4];
+  bool whole[4];
+  bool any_whole = false;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    whole[g] = gr.nv[g] > 0 && gr.nv[g] <= a.cap;
+    tf[g] = gr.nv[g] > 0 && !whole[g] ? score_floor<SBF16>(a.tau[qblock + 2 * g + half]) : INFINITY;
+    any_whole = any_whole || whole[g];
+  }
+  any_whole = __any(any_whole);
+  uint32_t cnt[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) cnt[q] = 0;
+
+  // key rows: a tile wholly inside the rows is addressed from a base shared by
+  // the wave plus this lane's row offset; a tile crossing the end (or a paged
+  // cache) per lane, rows past the end reading zeros
+  const uint8_t* kd = static_cast<const uint8_t*>(a.ki);
+  const uint32_t lrow = (uint32_t)rl * KeyRow<FMT>::B, lsrow = (uint32_t)rl * KeyRow<FMT>::S;
+  auto load_tile = [&](int t, KeyOp<FMT>& k) {
+    const int e0 = e_wave + t * 32;
+    if (!PAGED && e0 + 32 <= n_scan) {
+      const int64_t r0 = kv_base + e0;
+      load_key_row<FMT>(kd + r0 * KeyRow<FMT>::B + lrow, a.ki_scale + r0 * KeyRow<FMT>::S + lsrow,
+                        half, k);
+    } else {
+      const int e = e0 + rl;
+      const int64_t row = PAGED ? entry_row_if(a.b, kv_base, e, e < n_scan) : kv_base + e;
+      load_key<FMT>(a.ki, a.ki_scale, row, e < n_scan, half, k);
+    }
+  };
+  auto load_batch = [&](int b, KeyOp<FMT>* k) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) load_tile(b * TB + tb, k[tb]);
+  };
+  // one tile: scores of the lane's four queries against its entry.  WHOLE:
+  // some query of the group takes its row whole; HW: head weights given
+  auto score_tile = [&](int t, const KeyOp<FMT>& k, auto whole_c, auto hw_c) {
+    constexpr bool WHOLE = decltype(whole_c)::value;
+    constexpr bool HW = decltype(hw_c)::value;
+    const int e0 = e_wave + t * 32;          // the tile's first entry
+    const int el = e0 + rl;                  // this lane's entry
+    const f32x16_t acc = tile_dots<FMT>(gr.aq, k);
+    const bool tail = e0 + 32 > n_lo;        // some entry of the tile past a row's end
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float sc = HW ? head_score(acc, g, gr.hw[g], a.relu) : head_score_unit(acc, g, a.relu);
+      if constexpr (WHOLE) {
+        if (whole[g] && el < gr.nv[g])
+          a.cand[(qblock + 2 * g + half) * (int64_t)a.cap + el] =
+              make_uint2(score_key<SBF16>(sc), (uint32_t)el);
+      }
+      uint64_t m = __ballot(sc >= tf[g]);
+      if (tail) m &= __ballot(el < gr.nv[g]);
+      if (m != 0) {
+        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+        const uint32_t pclo = __builtin_popcount(mlo), pchi = __builtin_popcount(mhi);
+        // the lanes of each half count the passing lanes below them in their half
+        const uint32_t mb = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+        const uint32_t slot = (half ? cnt[2 * g + 1] - pclo : cnt[2 * g]) + mb;
+        if (((m >> lane) & 1ull) && slot < (uint32_t)kStageSlots)
+          stage[wave][2 * g + half][slot] = make_uint2(__float_as_uint(sc), (uint32_t)el);
+        cnt[2 * g] += pclo;
+        cnt[2 * g + 1] += pchi;
+      }
+    }
+  };
+  auto tile_live = [&](int t) { return e_wave + t * 32 < n_scan; };
+  auto run = [&](auto whole_c, auto hw_c) {
+    if (!tile_live(0)) return;
+    KeyOp<FMT> k0[TB], k1[TB];
+    load_batch(0, k0);
+    for (int b = 0; b < NB; b += 2) {
+      const bool l1 = b + 1 < NB && tile_live((b + 1) * TB);
+      if (l1) load_batch(b + 1, k1);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        if (tile_live(b * TB + tb)) score_tile(b * TB + tb, k0[tb], whole_c, hw_c);
+      if (!l1) break;
+      const bool l2 = b + 2 < NB && tile_live((b + 2) * TB);
+      if (l2) load_batch(b + 2, k0);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        if (tile_live((b + 1) * TB + tb)) score_tile((b + 1) * TB + tb, k1[tb], whole_c, hw_c);
+      if (!l2) break;
+    }
+  };
+  if (a.head_w != nullptr) {
+    if (any_whole) run(std::true_type{}, std::true_type{});
+    else run(std::false_type{}, std::true_type{});
+  } else {
+    if (any_whole) run(std::true_type{}, std::false_type{});
+    else run(std::false_type{}, std::false_type{});
+  }
+
+  // the workgroup's span of each query's list: its staged candidates (a
+  // (wave, query) that staged more than it holds sends the row to the exact
+  // redo by a count above cap), or for a row taken whole its visible entries
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < QS; ++q) wcnt[wave][q] = cnt[q];
+  }
+  __syncthreads();
+  if (tid < QS && qblock + tid < a.n_q) {
+    const int64_t nv = visible(a, qblock + tid);
+    uint32_t add = 0;
+    if (nv > 0 && nv <= a.cap) {
+      int64_t own = nv - e_wg;
+      own = own < 0 ? 0 : (own > kWaves * EW ? kWaves * EW : own);
+      add = (uint32_t)own;
+    } else {
+      bool over = false;
+      for (int w = 0; w < kWaves; ++w) {
+        const uint32_t c = wcnt[w][tid];
+        over = over || c > (uint32_t)kStageSlots;
+        add += c < (uint32_t)kStageSlots ? c : (uint32_t)kStageSlots;
+      }
+      if (over) add += (uint32_t)a.cap + 1u;
+    }
+    gbase[tid] = add > 0 ? atomicAdd(&a.cnt[qblock + tid], add) : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    if (qblock + q >= a.n_q) break;
+    const uint32_t c = wcnt[wave][q];
+    if (c == 0) continue;                    // (rows taken whole stage nothing)
+    const uint32_t n = c < (uint32_t)kStageSlots ? c : (uint32_t)kStageSlots;
+    uint32_t base = gbase[q];
+    for (int w = 0; w < wave; ++w) {
+      const uint32_t cw = wcnt[w][q];
+      base += cw < (uint32_t)kStageSlots ? cw : (uint32_t)kStageSlots;
+    }
+    uint2* list = a.cand + (qblock + q) * (int64_t)a.cap;
+    for (uint32_t i = lane; i < n; i += 64) {
+      const uint32_t slot = base + i;
+      const uint2 c = stage[wave][q][i];
+      if (slot < (uint32_t)a.cap) list[slot] = make_uint2(score_key<SBF16>(__uint_as_float(c.x)), c.y);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ 2. filter
 
 // Grid: entry chunks and query groups, as the score kernel.  Pass 1
@@ -677,14 +902,18 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
     st = csa_host::check_launch("csa_indexer_topk (sample)");
   }
   if (st != CSA_OK) return st;
-  const int64_t epw = entries_per_wg<FMT>(stream);
-  const dim3 fgrid = stream ? dim3((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups)
-                            : dim3((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
   const bool paged = a.b.pages != nullptr;
-  if (stream && paged) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, true>), fgrid, dim3(256), 0, s, a);
-  else if (stream) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, false>), fgrid, dim3(256), 0, s, a);
-  else if (paged) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false, true>), fgrid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, false, false>), fgrid, dim3(256), 0, s, a);
+  if (stream) {
+    const int64_t epw = entries_per_wg<FMT>(true);
+    const dim3 fgrid((unsigned)((max_kv + epw - 1) / epw), (unsigned)groups);
+    if (paged) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, true>), fgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, false>), fgrid, dim3(256), 0, s, a);
+  } else {
+    const int64_t epw = kWaves * kGroupTiles * 32;
+    const dim3 fgrid((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
+    if (paged) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true>), fgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false>), fgrid, dim3(256), 0, s, a);
+  }
   st = csa_host::check_launch("csa_indexer_topk (filter)");
   if (st != CSA_OK) return st;
   const size_t bm_bytes = (size_t)((max_kv < kBitmapMax ? max_kv : kBitmapMax) + 31) / 32 * 4;
