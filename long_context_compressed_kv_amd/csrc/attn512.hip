@@ -1,0 +1,445 @@
+// Shared-KV multi-query attention over 512-dim entries (page "DeepSeek V4
+// 深度解析", section 2: CSA step 3, the selected entries attended together with
+// the window of raw tokens; the HCA paragraph, all visible entries): one
+// softmax over the union, key = value, mixed-precision entries (RoPE dims
+// BF16, the rest FP8 with power-of-two block scales, dequantised exactly).
+//
+// Work split.  A workgroup owns one query token and all its heads; wave w
+// owns heads 16w .. 16w+15 over all 512 dims, so no wave needs another's
+// partial logits.  Keys are streamed in tiles of 32, staged once into LDS as
+// bf16 rows and read by every wave for both products:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, 16 keys on M, the wave's 16 heads
+//                 on N; lane (h = l%16, g = l/16) gets keys 4g .. 4g+3 of
+//                 each 16-key half for head h
+//   softmax       per head over the 4 lanes holding it (row swaps), base 2,
+//                 running maximum raised lazily
+//   O^T += V^T P^T  same instruction, 16 dims on M; contraction slot 8g + j
+//                 holds key 4g + j (j < 4) or 16 + 4g + j - 4, so P^T is the
+//                 lane's own probabilities; V^T comes from two transposing
+//                 LDS reads of 4 keys each
+// Pipeline: one barrier per tile.  The source rows of the token's keys are
+// resolved into LDS once.  Wave w owns keys of every tile (4 of 32 with eight
+// waves): it copies their raw bytes (fp8 codes, RoPE dims and block scales of
+// an entry, or a bf16 window row) from global memory straight into LDS two
+// tiles ahead (global_load_lds, no registers held), and one tile ahead turns
+// them into the bf16 key tile, so only the barrier after that conversion
+// joins the waves.
+#include <type_traits>
+
+#include "attn_common.h"
+#include "common.h"
+#include "merge.h"
+
+using namespace csa;
+using namespace csa_attn;
+
+namespace {
+
+constexpr int kD = 512;
+constexpr int kRowB = kD * 2;          // bytes of a bf16 key row
+constexpr int kTileB = KT * kRowB;     // 32 KB
+constexpr int kUPR = kD / 16;          // staging units (16 dims) per key row
+constexpr int kMaxKeys = 4096;        // keys of a token resolved at once
+
+// LDS layout: two bf16 key tiles, two raw tiles (1 KB per key), their block
+// scales (4 bytes per key), the token's source rows.
+constexpr int kOffRaw = 2 * kTileB;
+constexpr int kOffScale = kOffRaw + 2 * KT * 1024;
+constexpr int kOffRows = kOffScale + 2 * KT * 4;
+constexpr size_t kSmem512 = kOffRows + kMaxKeys * 4;
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
+
+// Position of logical 16-byte chunk j of key row r in a tile: rows are 1 KB,
+// chunks permuted by j ^ f(r), f(r) = 2 (r % 8) + (r / 8) % 2.  The logit
+// reads (one chunk of 16 consecutive rows per 16 lanes) and the transposed
+// value reads (32-byte runs of 8 consecutive rows per 32 lanes) then hit
+// every LDS bank once.
+__device__ __forceinline__ int chunk_swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+
+// Copies `bytes` (16 or 4) per active lane from global memory to LDS at
+// lds + lane * bytes, without registers (global_load_lds); completion is
+// counted in vmcnt like a load.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
+}
+// Wait until at most N of this wave's vector memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int KVF, bool SPARSE, int OUTM, int NW>
+__global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
+  constexpr int KPW = KT / NW;                    // keys of a tile per wave
+  constexpr bool FP8 = KVF == CSA_FP8_MIXED;
+  constexpr int NDMA = KPW + (FP8 ? 1 : 0);       // copies per wave and tile
+  constexpr int UPL = KPW * kUPR / 64;            // conversion units per lane
+  extern __shared__ __align__(16) unsigned char smem[];
+  lds_u8* kb = (lds_u8*)smem;                     // two key tiles
+  lds_u8* raw = (lds_u8*)(smem + kOffRaw);        // two raw tiles
+  lds_u8* rsc = (lds_u8*)(smem + kOffScale);      // their block scales
+  int* krow = reinterpret_cast<int*>(smem + kOffRows);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)kb;  // LDS address of the layout
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 15, lg = lane >> 4;
+
+  const int64_t q = blockIdx.x;                   // one token per workgroup
+  const int head = wave * 16 + hl;
+  const int64_t qrow = q * a.H + head;            // row of the q / out tensors
+
+  // queries: B operand of step s (dims 32s .. 32s+31): this lane's 8 dims
+  bf16x8_t qreg[16];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * kD + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
+  }
+  Geo g = make_geo<SPARSE>(a, q);
+  // the geometry is the same in every lane: kept in scalar registers
+  auto uni = [](int64_t v) -> int64_t {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  g.q_first = uni(g.q_first);
+  g.q_last = uni(g.q_last);
+  g.t_first = uni(g.t_first);
+  g.t_last = uni(g.t_last);
+  g.kv_base = uni(g.kv_base);
+  g.raw_base = uni(g.raw_base);
+  g.raw_pos = uni(g.raw_pos);
+  g.kv_len = uni(g.kv_len);
+  g.raw_cap = uni(g.raw_cap);
+  g.wlo = uni(g.wlo);
+  g.nE = __builtin_amdgcn_readfirstlane(g.nE);
+  g.nkeys = __builtin_amdgcn_readfirstlane(g.nkeys);
+  g.key_lo = __builtin_amdgcn_readfirstlane(g.key_lo);
+  g.key_hi = __builtin_amdgcn_readfirstlane(g.key_hi);
+  const int nk = g.key_hi - g.key_lo;             // at most kMaxKeys (host check)
+  const int ntiles = (nk + KT - 1) / KT;
+
+  // source rows of the token's keys (key_meta's encoding; a key without a
+  // source, or past the last, reads a row that exists and is masked)
+  const int dummy = a.kv != nullptr ? 0 : -2;
+  for (int i = tid; i < ntiles * KT; i += NW * 64) {
+    int row = -1;
+    int64_t lo, hi;
+    if (i < nk) key_meta<SPARSE>(a, g, g.key_lo + i, row, lo, hi);
+    krow[i] = row;
+  }
+  __syncthreads();
+
+  // copies of this wave's keys of tile t into raw tile t % 2
+  auto dma_tile = [&](int t) {
+    const int buf = t & 1;
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int key = wave * KPW + j;
+      int row = krow[t * KT + key];
+      row = row == -1 ? dummy : row;
+      const uint32_t dst = lds0 + kOffRaw + (buf * KT + key) * 1024;
+      if (row >= 0) {
+        if constexpr (FP8) {
+          if (lane < 28) dma16(dst, static_cast<const uint8_t*>(a.kv) + (int64_t)row * 448 + 16 * lane);
+          else if (lane < 36) dma16(dst, reinterpret_cast<const uint8_t*>(a.kv_rope) + (int64_t)row * 128 + 16 * (lane - 28));
+        } else {
+          dma16(dst, static_cast<const uint8_t*>(a.kv) + (int64_t)row * 1024 + 16 * lane);
+        }
+      } else {
+        dma16(dst, static_cast<const uint8_t*>(a.raw) + (int64_t)(-2 - row) * 1024 + 16 * lane);
+      }
+    }
+    if constexpr (FP8) {
+      if (lane < KPW) {
+        const int key = wave * KPW + lane;
+        const int row = krow[t * KT + key];
+        const int64_t r = row >= 0 ? row : 0;     // window keys copy a scale they never use
+        dma4(lds0 + kOffScale + (buf * KT + wave * KPW) * 4, a.kv_scale + r * 4);
+      }
+    }
+  };
+  // this wave's keys of tile t from raw tile t % 2 into key tile t % 2
+  auto convert_tile = [&](int t) {
+    const int buf = t & 1;
+    lds_u8* tile = kb + buf * kTileB;
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+      const int v = lane + 64 * i;
+      const int key = wave * KPW + (v >> 5), j = v & 31;
+      const lds_u8* src = raw + (buf * KT + key) * 1024;
+      int row = krow[t * KT + key];
+      row = row == -1 ? dummy : row;             // as dma_tile copied it
+      uint4 x0, x1;
+      if (FP8 && row >= 0) {
+        if (j < 28) {
+          const uint4 c = lds_read_b128(src + 16 * j);
+          const uint32_t sb = rsc[(buf * KT + key) * 4 + (j >> 3)];
+          fp8x16_to_bf16(c, e8m0_to_f32(sb), x0, x1);
+        } else {
+          x0 = lds_read_b128(src + 448 + 32 * (j - 28));
+          x1 = lds_read_b128(src + 448 + 32 * (j - 28) + 16);
+        }
+      } else {
+        x0 = lds_read_b128(src + 32 * j);
+        x1 = lds_read_b128(src + 32 * j + 16);
+      }
+      const int f = chunk_swz(key);
+      *(__attribute__((address_space(3))) u32x4_t*)(tile + key * kRowB + 16 * ((2 * j) ^ f)) =
+          u32x4_t{x0.x, x0.y, x0.z, x0.w};
+      *(__attribute__((address_space(3))) u32x4_t*)(tile + key * kRowB + 16 * ((2 * j + 1) ^ f)) =
+          u32x4_t{x1.x, x1.y, x1.z, x1.w};
+    }
+  };
+
+  // LDS read addresses (tile 0's buffer; the other buffer is kTileB above).
+  // K operand of half hk, step s = 4 sh + sl: row 16 hk + hl, logical chunk
+  // 4 s + lg.  V^T operand of dim block db = 8 dh + dl, read rho: rows
+  // 16 rho + 4 lg + hl / 4, dims 16 db + 4 (hl % 4) .. +3.
+  lds_u8* kptr[4];
+  lds_u8* vptr[8];
+  {
+    const int fk = chunk_swz(hl);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) kptr[sl] = kb + hl * kRowB + 16 * ((4 * sl + lg) ^ fk);
+    const int rv = 4 * lg + (hl >> 2);
+    const int fv = chunk_swz(rv);
+#pragma unroll
+    for (int dl = 0; dl < 8; ++dl)
+      vptr[dl] = kb + rv * kRowB + 16 * ((2 * dl + ((hl & 3) >> 1)) ^ fv) + 8 * (hl & 1);
+  }
+  auto launder = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(kptr[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(vptr[i]));
+  };
+
+  f4_t acc_o[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc_o[i] = f4_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < 16; ++s) asm volatile("" :: "v"(qreg[s]));
+
+  // the read addresses point into the key buffer of the tile being computed
+  // (moved to the other buffer after each tile)
+  auto compute = [&](int t) {
+    constexpr int bofs = 0;
+    launder();
+    // S^T = K Q^T, two 16-key halves; the operands of step s + 2 are read
+    // while step s multiplies
+    f4_t s0 = f4_t{}, s1 = f4_t{};
+    auto kread = [&](int s, uint4& k0, uint4& k1) {
+      const int sl = s & 3, sh = s >> 2;
+      k0 = lds_read_b128(kptr[sl] + bofs + sh * 256);
+      k1 = lds_read_b128(kptr[sl] + bofs + sh * 256 + 16 * kRowB);
+    };
+    uint4 ka0, ka1, kb0, kb1;
+    kread(0, ka0, ka1);
+    kread(1, kb0, kb1);
+#pragma unroll
+    for (int s = 0; s < 16; s += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka0), qreg[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka1), qreg[s], s1, 0, 0, 0);
+      if (s + 2 < 16) kread(s + 2, ka0, ka1);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb0), qreg[s + 1], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb1), qreg[s + 1], s1, 0, 0, 0);
+      if (s + 3 < 16) kread(s + 3, kb0, kb1);
+    }
+    // keep two steps of operand reads in flight ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of steps 0, 1
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // mask: key 4 lg + i of half hk is bit 16 hk + 4 lg + i of the tile's word
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = s0[i];
+      sv[4 + i] = s1[i];
+    }
+    const uint32_t w = (uint32_t)__ballot(lane < KT && krow[t * KT + (lane & 31)] != -1);
+    if (w != 0xffffffffu) {
+      const uint32_t mine = w >> (4 * lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = ((mine >> i) & 1u) ? sv[i] : -INFINITY;
+        sv[4 + i] = ((mine >> (16 + i)) & 1u) ? sv[4 + i] : -INFINITY;
+      }
+    }
+    // online softmax over the 4 lanes of each head
+    float tmax = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
+    {
+      const uint32_t u = __float_as_uint(tmax);
+      const auto x32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      const float m1 = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      const uint32_t v = __float_as_uint(m1);
+      const auto x16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      tmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1])) * a.scale_log2;
+    }
+    const bool raise = tmax > m_run + kStale || (m_run == -INFINITY && tmax != -INFINITY);
+    if (__any(raise)) {
+      const float m_new = raise ? tmax : m_run;
+      const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == -INFINITY ? 0.0f : -m_run;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, nm));
+    uint4 pu;
+    pu.x = pack_bf16x2_fast(p[0], p[1]);
+    pu.y = pack_bf16x2_fast(p[2], p[3]);
+    pu.z = pack_bf16x2_fast(p[4], p[5]);
+    pu.w = pack_bf16x2_fast(p[6], p[7]);
+    // the row sum of the probabilities as rounded for the product
+    {
+      const uint32_t pw[4] = {pu.x, pu.y, pu.z, pu.w};
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pw[j]),
+                                             __builtin_bit_cast(bf16x2_v, 0x3f803f80u), ps, false);
+      l_run += ps;
+    }
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pu);
+    // O^T += V^T P^T over 32 dim blocks; the operands of block db + 2 are
+    // read while block db multiplies
+    auto vread = [&](int db) -> uint4 {
+      const int dl = db & 7, dh = db >> 3;
+      const uint2 v0 = lds_read_tr16(vptr[dl] + bofs + dh * 256);
+      const uint2 v1 = lds_read_tr16(vptr[dl] + bofs + dh * 256 + 16 * kRowB);
+      return make_uint4(v0.x, v0.y, v1.x, v1.y);
+    };
+    uint4 va = vread(0), vb = vread(1);
+#pragma unroll
+    for (int db = 0; db < 32; db += 2) {
+      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc_o[db], 0, 0, 0);
+      if (db + 2 < 32) va = vread(db + 2);
+      acc_o[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vb), pb, acc_o[db + 1], 0, 0, 0);
+      if (db + 3 < 32) vb = vread(db + 3);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);      // LDS reads of blocks 0, 1
+#pragma unroll
+    for (int i = 0; i < 30; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);    // LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+  };
+
+  // ---- prologue: tile 0 in LDS, tile 1 copying
+  if (ntiles > 0) {
+    dma_tile(0);
+    if (ntiles > 1) {
+      dma_tile(1);
+      wait_vm<NDMA>();
+    } else {
+      wait_vm<0>();
+    }
+    convert_tile(0);
+    lds_barrier();
+  }
+  // ---- key loop: one barrier per tile
+  int flip = kTileB;
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles) dma_tile(t + 2);           // raw tile t % 2 was converted last tile
+    compute(t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kptr[i] += flip;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vptr[i] += flip;
+    flip = -flip;
+    if (t + 1 < ntiles) {
+      if (t + 2 < ntiles) wait_vm<NDMA>();          // this wave's copies of tile t+1 landed
+      else wait_vm<0>();
+      convert_tile(t + 1);                          // key tile (t+1) % 2 was read last tile
+    }
+    lds_barrier();
+  }
+
+  // ---- epilogue: normaliser over the 4 lanes of each head
+  float l_tot;
+  {
+    const uint32_t u = __float_as_uint(l_run);
+    const auto x32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float s1 = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
+    const uint32_t v = __float_as_uint(s1);
+    const auto x16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    l_tot = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
+  }
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (head < a.H) {
+    const float lse_v = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse != nullptr && lg == 0) a.lse[qrow] = lse_v;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const int d = db * 16 + 4 * lg;
+      const float o0 = acc_o[db][0] * inv, o1 = acc_o[db][1] * inv;
+      const float o2 = acc_o[db][2] * inv, o3 = acc_o[db][3] * inv;
+      if constexpr (OUTM == 1) {
+        uint2 uo;
+        uo.x = pack_bf16x2_fast(o0, o1);
+        uo.y = pack_bf16x2_fast(o2, o3);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + qrow * kD + d) = uo;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + qrow * kD + d) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+}
+
+template <int KVF, bool SPARSE, int OUTM, int NW>
+csa_status launch512(const AttnArgs& a, hipStream_t s) {
+  auto kern = attn512_kernel<KVF, SPARSE, OUTM, NW>;
+  const size_t smem = kSmem512;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_q), dim3(NW * 64), smem, s, a);
+  return csa_host::check_launch("csa_sparse_mqa_attn (D = 512)");
+}
+
+template <int KVF, bool SPARSE, int OUTM>
+csa_status launch512_heads(const AttnArgs& a, hipStream_t s) {
+  switch (a.H / 16) {
+    case 4: return launch512<KVF, SPARSE, OUTM, 4>(a, s);
+    case 8: return launch512<KVF, SPARSE, OUTM, 8>(a, s);
+    default: return csa_host::fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: this D = 512 path takes 64 or 128 heads");
+  }
+}
+
+}  // namespace
+
+// D = 512, bf16 compute, one workgroup per query token (no split over keys).
+bool attn512_fits(int64_t max_keys) { return max_keys <= kMaxKeys; }
+
+csa_status launch_attn512(const AttnArgs& a, int kvf, bool sparse, int outm, hipStream_t s) {
+  if (a.n_q > 0x7fffffff) return csa_host::fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: too many queries");
+  if (kvf == CSA_FP8_MIXED) {
+    if (sparse) return outm ? launch512_heads<CSA_FP8_MIXED, true, 1>(a, s) : launch512_heads<CSA_FP8_MIXED, true, 0>(a, s);
+    return outm ? launch512_heads<CSA_FP8_MIXED, false, 1>(a, s) : launch512_heads<CSA_FP8_MIXED, false, 0>(a, s);
+  }
+  if (sparse) return outm ? launch512_heads<CSA_BF16, true, 1>(a, s) : launch512_heads<CSA_BF16, true, 0>(a, s);
+  return outm ? launch512_heads<CSA_BF16, false, 1>(a, s) : launch512_heads<CSA_BF16, false, 0>(a, s);
+}
