@@ -237,9 +237,6 @@ __device__ __forceinline__ float score_floor(uint32_t tau) {
   return fmaf(-__builtin_fabsf(v), 0x1p-7f, v) - 0x1p-120f;
 }
 
-template <int FMT> struct GroupTiling { static constexpr int TB = 2; };
-template <> struct GroupTiling<CSA_MXFP4> { static constexpr int TB = 4; };
-
 // Bytes of one entry key row and of its block scales.
 template <int FMT> struct KeyRow;
 template <> struct KeyRow<CSA_F32> { static constexpr int B = kDI * 4, S = 0; };
@@ -265,12 +262,13 @@ __device__ __forceinline__ void load_key_row(const uint8_t* row, const uint8_t* 
   }
 }
 
-template <int FMT, bool SBF16, bool PAGED>
+// Tiles are scored in pairs: both products are issued before either result
+// is read, so one pair's matrix-core latency overlaps the other's vector work.
+template <int FMT, bool SBF16, bool PAGED, bool HW>
 __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
   constexpr int QS = 8;                      // query slots of a group
   constexpr int EW = kGroupTiles * 32;       // entries per wave
-  constexpr int TB = GroupTiling<FMT>::TB;   // tiles loaded together
-  constexpr int NB = kGroupTiles / TB;
+  constexpr int NP = kGroupTiles / 2;        // tile pairs per wave
   // staged candidates: (score bits, entry); the key is formed when copied out
   __shared__ uint2 stage[kWaves][QS][kStageSlots];
   __shared__ uint32_t wcnt[kWaves][QS];
@@ -279,8 +277,6 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform over the wave
 
   const int64_t qblock = (int64_t)blockIdx.x * a.qpg;
-  Group<FMT, 4> gr;
-  load_group<FMT, 4>(a, qblock, gr);
   int64_t q_hi = qblock + a.qpg - 1;
   if (q_hi >= a.n_q) q_hi = a.n_q - 1;
   // the group's longest and shortest rows (at most 2^20 entries; uniform)
@@ -289,18 +285,41 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
   const int e_wg = (int)blockIdx.y * (kWaves * EW);
   if (e_wg >= n_scan) return;                // the whole workgroup: no barrier reached
   const int e_wave = e_wg + wave * EW;
-  const int64_t kv_base = gr.qm.kv_base;
+  const QueryMeta qm = query_meta(a.b, qblock, a.m);
+  const int64_t kv_base = qm.kv_base;
 
-  // the lane's queries (2g + half): their floors, and whether their rows are
-  // taken whole (at most cap entries)
+  // A operand: query rl / 4, head rl % 4 of the group
+  QueryOp<FMT> aq;
+  {
+    const int qa = rl >> 2, ha = rl & 3;
+    load_query<FMT>(a.qi, a.qi_scale, (qblock + qa) * kHI + ha, qa < a.qpg && qblock + qa < a.n_q,
+                    half, aq);
+  }
+  // the lane's queries (2g + half): visible entries, floors, head weights,
+  // and whether their rows are taken whole (at most cap entries)
+  int nv[4];
   float tf[4];
+  float hw[HW ? 4 : 1][kHI];
   bool whole[4];
   bool any_whole = false;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    whole[g] = gr.nv[g] > 0 && gr.nv[g] <= a.cap;
-    tf[g] = gr.nv[g] > 0 && !whole[g] ? score_floor<SBF16>(a.tau[qblock + 2 * g + half]) : INFINITY;
+    const int ql = 2 * g + half;
+    int v = 0;
+    if (ql < a.qpg && qblock + ql < a.n_q) {
+      int64_t n = (qm.t + ql + 1) / a.m;
+      if (n > qm.kv_len) n = qm.kv_len;
+      if (n > a.max_n) n = a.max_n;
+      v = (int)n;
+    }
+    nv[g] = v;
+    whole[g] = v > 0 && v <= a.cap;
+    tf[g] = v > 0 && !whole[g] ? score_floor<SBF16>(a.tau[qblock + ql]) : INFINITY;
     any_whole = any_whole || whole[g];
+    if constexpr (HW) {
+#pragma unroll
+      for (int h = 0; h < kHI; ++h) hw[g][h] = v > 0 ? a.head_w[(qblock + ql) * kHI + h] : 1.0f;
+    }
   }
   any_whole = __any(any_whole);
   uint32_t cnt[QS];
@@ -324,29 +343,25 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
       load_key<FMT>(a.ki, a.ki_scale, row, e < n_scan, half, k);
     }
   };
-  auto load_batch = [&](int b, KeyOp<FMT>* k) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) load_tile(b * TB + tb, k[tb]);
-  };
-  // one tile: scores of the lane's four queries against its entry.  WHOLE:
-  // some query of the group takes its row whole; HW: head weights given
-  auto score_tile = [&](int t, const KeyOp<FMT>& k, auto whole_c, auto hw_c) {
+  // the scores of one tile's product: the lane's four queries against its
+  // entry.  WHOLE: some query of the group takes its row whole
+  auto score_tile = [&](int t, const f32x16_t& acc, auto whole_c) {
     constexpr bool WHOLE = decltype(whole_c)::value;
-    constexpr bool HW = decltype(hw_c)::value;
     const int e0 = e_wave + t * 32;          // the tile's first entry
     const int el = e0 + rl;                  // this lane's entry
-    const f32x16_t acc = tile_dots<FMT>(gr.aq, k);
     const bool tail = e0 + 32 > n_lo;        // some entry of the tile past a row's end
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float sc = HW ? head_score(acc, g, gr.hw[g], a.relu) : head_score_unit(acc, g, a.relu);
+      float sc;
+      if constexpr (HW) sc = head_score(acc, g, hw[g], a.relu);
+      else sc = head_score_unit(acc, g, a.relu);
       if constexpr (WHOLE) {
-        if (whole[g] && el < gr.nv[g])
+        if (whole[g] && el < nv[g])
           a.cand[(qblock + 2 * g + half) * (int64_t)a.cap + el] =
               make_uint2(score_key<SBF16>(sc), (uint32_t)el);
       }
       uint64_t m = __ballot(sc >= tf[g]);
-      if (tail) m &= __ballot(el < gr.nv[g]);
+      if (tail) m &= __ballot(el < nv[g]);
       if (m != 0) {
         const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
         const uint32_t pclo = __builtin_popcount(mlo), pchi = __builtin_popcount(mhi);
@@ -361,32 +376,38 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
     }
   };
   auto tile_live = [&](int t) { return e_wave + t * 32 < n_scan; };
-  auto run = [&](auto whole_c, auto hw_c) {
+  auto do_pair = [&](int p, const KeyOp<FMT>* k, auto whole_c) {
+    const bool l1 = tile_live(2 * p + 1);
+    const f32x16_t acc0 = tile_dots<FMT>(aq, k[0]);
+    f32x16_t acc1 = f32x16_t{};
+    if (l1) acc1 = tile_dots<FMT>(aq, k[1]);
+    score_tile(2 * p, acc0, whole_c);
+    if (l1) score_tile(2 * p + 1, acc1, whole_c);
+  };
+  auto run = [&](auto whole_c) {
     if (!tile_live(0)) return;
-    KeyOp<FMT> k0[TB], k1[TB];
-    load_batch(0, k0);
-    for (int b = 0; b < NB; b += 2) {
-      const bool l1 = b + 1 < NB && tile_live((b + 1) * TB);
-      if (l1) load_batch(b + 1, k1);
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-        if (tile_live(b * TB + tb)) score_tile(b * TB + tb, k0[tb], whole_c, hw_c);
+    KeyOp<FMT> ka[2], kb[2];
+    load_tile(0, ka[0]);
+    load_tile(1, ka[1]);
+    for (int p = 0; p < NP; p += 2) {
+      const bool l1 = p + 1 < NP && tile_live(2 * p + 2);
+      if (l1) {
+        load_tile(2 * p + 2, kb[0]);
+        load_tile(2 * p + 3, kb[1]);
+      }
+      do_pair(p, ka, whole_c);
       if (!l1) break;
-      const bool l2 = b + 2 < NB && tile_live((b + 2) * TB);
-      if (l2) load_batch(b + 2, k0);
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-        if (tile_live((b + 1) * TB + tb)) score_tile((b + 1) * TB + tb, k1[tb], whole_c, hw_c);
+      const bool l2 = p + 2 < NP && tile_live(2 * p + 4);
+      if (l2) {
+        load_tile(2 * p + 4, ka[0]);
+        load_tile(2 * p + 5, ka[1]);
+      }
+      do_pair(p + 1, kb, whole_c);
       if (!l2) break;
     }
   };
-  if (a.head_w != nullptr) {
-    if (any_whole) run(std::true_type{}, std::true_type{});
-    else run(std::false_type{}, std::true_type{});
-  } else {
-    if (any_whole) run(std::true_type{}, std::false_type{});
-    else run(std::false_type{}, std::false_type{});
-  }
+  if (any_whole) run(std::true_type{});
+  else run(std::false_type{});
 
   // the workgroup's span of each query's list: its staged candidates (a
   // (wave, query) that staged more than it holds sends the row to the exact
@@ -911,8 +932,11 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   } else {
     const int64_t epw = kWaves * kGroupTiles * 32;
     const dim3 fgrid((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
-    if (paged) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true>), fgrid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false>), fgrid, dim3(256), 0, s, a);
+    const bool hw = a.head_w != nullptr;
+    if (paged && hw) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true, true>), fgrid, dim3(256), 0, s, a);
+    else if (paged) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true, false>), fgrid, dim3(256), 0, s, a);
+    else if (hw) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false, true>), fgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false, false>), fgrid, dim3(256), 0, s, a);
   }
   st = csa_host::check_launch("csa_indexer_topk (filter)");
   if (st != CSA_OK) return st;
