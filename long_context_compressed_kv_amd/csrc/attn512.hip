@@ -18,14 +18,13 @@
 //                 lane's own probabilities; V^T comes from two transposing
 //                 LDS reads of 4 keys each
 // Pipeline: one barrier per tile.  The source rows of the token's keys are
-// resolved into LDS once.  Wave w owns keys of every tile (4 of 32 with eight
-// waves): it copies their raw bytes (fp8 codes, RoPE dims and block scales of
-// an entry, or a bf16 window row) from global memory straight into LDS two
-// tiles ahead (global_load_lds, no registers held), and one tile ahead turns
-// them into the bf16 key tile, so only the barrier after that conversion
-// joins the waves.
-#include <type_traits>
-
+// resolved into LDS once; each iteration reads the few it needs next with one
+// LDS read per lane, an iteration ahead.  Wave w owns keys of every tile (4
+// of 32 with eight waves): it copies their raw bytes (fp8 codes, RoPE dims
+// and block scales of an entry, or a bf16 window row) from global memory
+// straight into LDS two tiles ahead (global_load_lds, one instruction per
+// key, no registers held), and one tile ahead turns them into the bf16 key
+// tile, so only the barrier after that conversion joins the waves.
 #include "attn_common.h"
 #include "common.h"
 #include "merge.h"
@@ -36,8 +35,8 @@ using namespace csa_attn;
 namespace {
 
 constexpr int kD = 512;
-constexpr int kRowB = kD * 2;          // bytes of a bf16 key row
-constexpr int kTileB = KT * kRowB;     // 32 KB
+constexpr int kRowS = kD * 2 + 32;     // LDS stride of a bf16 key row (1 KB + pad)
+constexpr int kTileB = KT * kRowS;     // 33 KB
 constexpr int kUPR = kD / 16;          // staging units (16 dims) per key row
 constexpr int kMaxKeys = 4096;        // keys of a token resolved at once
 
@@ -47,15 +46,15 @@ constexpr int kOffRaw = 2 * kTileB;
 constexpr int kOffScale = kOffRaw + 2 * KT * 1024;
 constexpr int kOffRows = kOffScale + 2 * KT * 4;
 constexpr size_t kSmem512 = kOffRows + kMaxKeys * 4;
+static_assert(kSmem512 <= 160 * 1024, "LDS of a workgroup");
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
 
-// Position of logical 16-byte chunk j of key row r in a tile: rows are 1 KB,
-// chunks permuted by j ^ f(r), f(r) = 2 (r % 8) + (r / 8) % 2.  The logit
-// reads (one chunk of 16 consecutive rows per 16 lanes) and the transposed
-// value reads (32-byte runs of 8 consecutive rows per 32 lanes) then hit
-// every LDS bank once.
-__device__ __forceinline__ int chunk_swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+// Key rows sit kRowS = 1056 bytes apart in a tile, dims in order: with the
+// 32-byte pad, the logit operand reads (16 bytes of 16 consecutive rows per
+// 16 lanes) and the transposed value reads (8-byte runs of 4 dims, 4 rows
+// per 16 lanes) fall on distinct LDS banks, which neither an unpadded 1 KB
+// stride nor a 16-byte pad achieves for the 16-byte reads.
 
 // Copies `bytes` (16 or 4) per active lane from global memory to LDS at
 // lds + lane * bytes, without registers (global_load_lds); completion is
@@ -66,11 +65,12 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* src) {
 __device__ __forceinline__ void dma4(uint32_t lds, const void* src) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
 }
-// Wait until at most N of this wave's vector memory operations are in flight.
+// Wait until at most N of this wave's vector memory operations are in flight
+// (LDS reads of copied data stay behind it: a compiler memory barrier too).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt %0" :: "n"((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8)) : "memory");
 }
 
 template <int KVF, bool SPARSE, int OUTM, int NW>
@@ -138,37 +138,61 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // copies of this wave's keys of tile t into raw tile t % 2
-  auto dma_tile = [&](int t) {
+  // Source rows an iteration needs, read one iteration ahead with one LDS
+  // read per lane: lanes 0..31 the keys of tile t (its mask), lanes 32 ..
+  // 32+KPW-1 this wave's keys of tile t+1 (what to convert), lanes 40 ..
+  // 40+KPW-1 those of tile t+2 (what to copy).  Tiles past the last read row 0.
+  auto meta_read = [&](int t) -> int {
+    int tile = t, key = lane;
+    if (lane >= 32) {
+      tile = lane < 40 ? t + 1 : t + 2;
+      key = wave * KPW + (lane & 7);
+    }
+    const bool ok = tile < ntiles && (lane < 32 || (lane & 7) < KPW) && lane < 48;
+    return krow[ok ? tile * KT + key : 0];
+  };
+  // per-lane parts of an fp8 entry's copy: codes (lanes 0..27), RoPE dims
+  // (lanes 28..35)
+  const uint8_t* f8_src = lane < 28 ? static_cast<const uint8_t*>(a.kv) + 16 * lane
+                                    : reinterpret_cast<const uint8_t*>(a.kv_rope) + 16 * (lane - 28);
+  const uint32_t f8_stride = lane < 28 ? 448u : 128u;
+  // copies of this wave's keys of tile t into raw tile t % 2, one
+  // instruction per key (and one for the block scales); rows(j) gives the
+  // source row of the wave's key j (uniform), lane l0 + j holds it in lrow
+  auto dma_rows = [&](int t, auto rows, int lrow, int l0) {
     const int buf = t & 1;
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
       const int key = wave * KPW + j;
-      int row = krow[t * KT + key];
+      int row = rows(j);
       row = row == -1 ? dummy : row;
       const uint32_t dst = lds0 + kOffRaw + (buf * KT + key) * 1024;
-      if (row >= 0) {
-        if constexpr (FP8) {
-          if (lane < 28) dma16(dst, static_cast<const uint8_t*>(a.kv) + (int64_t)row * 448 + 16 * lane);
-          else if (lane < 36) dma16(dst, reinterpret_cast<const uint8_t*>(a.kv_rope) + (int64_t)row * 128 + 16 * (lane - 28));
-        } else {
-          dma16(dst, static_cast<const uint8_t*>(a.kv) + (int64_t)row * 1024 + 16 * lane);
+      const uint8_t* rbase = row >= 0 ? static_cast<const uint8_t*>(a.kv) + (int64_t)row * 1024
+                                      : static_cast<const uint8_t*>(a.raw) + (int64_t)(-2 - row) * 1024;
+      const uint8_t* src = rbase + 16 * lane;
+      bool act = true;
+      if constexpr (FP8) {
+        if (row >= 0) {
+          src = f8_src + (uint32_t)row * f8_stride;       // < 2^32: rows * 448 bytes
+          act = lane < 36;
         }
-      } else {
-        dma16(dst, static_cast<const uint8_t*>(a.raw) + (int64_t)(-2 - row) * 1024 + 16 * lane);
       }
+      if (act) dma16(dst, src);
     }
     if constexpr (FP8) {
-      if (lane < KPW) {
-        const int key = wave * KPW + lane;
-        const int row = krow[t * KT + key];
-        const int64_t r = row >= 0 ? row : 0;     // window keys copy a scale they never use
-        dma4(lds0 + kOffScale + (buf * KT + wave * KPW) * 4, a.kv_scale + r * 4);
+      if (lane >= l0 && lane < l0 + KPW) {
+        const int64_t r = lrow >= 0 ? lrow : 0;   // window keys copy a scale they never use
+        dma4(lds0 + kOffScale + (buf * KT + wave * KPW) * 4 - 4 * l0, a.kv_scale + r * 4);
       }
     }
   };
+  auto dma_tile = [&](int t) {
+    const int lrow = lane < KPW ? krow[t * KT + wave * KPW + lane] : 0;
+    dma_rows(t, [&](int j) { return __builtin_amdgcn_readfirstlane(krow[t * KT + wave * KPW + j]); }, lrow, 0);
+  };
   // this wave's keys of tile t from raw tile t % 2 into key tile t % 2
-  auto convert_tile = [&](int t) {
+  // rowof(kw): source row of the wave's key kw of tile t (uniform)
+  auto convert_rows = [&](int t, auto rowof) {
     const int buf = t & 1;
     lds_u8* tile = kb + buf * kTileB;
 #pragma unroll
@@ -176,8 +200,8 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
       const int v = lane + 64 * i;
       const int key = wave * KPW + (v >> 5), j = v & 31;
       const lds_u8* src = raw + (buf * KT + key) * 1024;
-      int row = krow[t * KT + key];
-      row = row == -1 ? dummy : row;             // as dma_tile copied it
+      int row = (lane >> 5) ? rowof(2 * i + 1) : rowof(2 * i);
+      row = row == -1 ? dummy : row;             // as dma_rows copied it
       uint4 x0, x1;
       if (FP8 && row >= 0) {
         if (j < 28) {
@@ -192,12 +216,14 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
         x0 = lds_read_b128(src + 32 * j);
         x1 = lds_read_b128(src + 32 * j + 16);
       }
-      const int f = chunk_swz(key);
-      *(__attribute__((address_space(3))) u32x4_t*)(tile + key * kRowB + 16 * ((2 * j) ^ f)) =
+      *(__attribute__((address_space(3))) u32x4_t*)(tile + key * kRowS + 32 * j) =
           u32x4_t{x0.x, x0.y, x0.z, x0.w};
-      *(__attribute__((address_space(3))) u32x4_t*)(tile + key * kRowB + 16 * ((2 * j + 1) ^ f)) =
+      *(__attribute__((address_space(3))) u32x4_t*)(tile + key * kRowS + 32 * j + 16) =
           u32x4_t{x1.x, x1.y, x1.z, x1.w};
     }
+  };
+  auto convert_tile = [&](int t) {
+    convert_rows(t, [&](int kw) { return __builtin_amdgcn_readfirstlane(krow[t * KT + wave * KPW + kw]); });
   };
 
   // LDS read addresses (tile 0's buffer; the other buffer is kTileB above).
@@ -207,14 +233,11 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   lds_u8* kptr[4];
   lds_u8* vptr[8];
   {
-    const int fk = chunk_swz(hl);
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) kptr[sl] = kb + hl * kRowB + 16 * ((4 * sl + lg) ^ fk);
+    for (int sl = 0; sl < 4; ++sl) kptr[sl] = kb + hl * kRowS + 16 * (4 * sl + lg);
     const int rv = 4 * lg + (hl >> 2);
-    const int fv = chunk_swz(rv);
 #pragma unroll
-    for (int dl = 0; dl < 8; ++dl)
-      vptr[dl] = kb + rv * kRowB + 16 * ((2 * dl + ((hl & 3) >> 1)) ^ fv) + 8 * (hl & 1);
+    for (int dl = 0; dl < 8; ++dl) vptr[dl] = kb + rv * kRowS + 32 * dl + 8 * (hl & 3);
   }
   auto launder = [&]() {
 #pragma unroll
@@ -233,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
 
   // the read addresses point into the key buffer of the tile being computed
   // (moved to the other buffer after each tile)
-  auto compute = [&](int t) {
+  auto compute = [&](int t, int meta) {
     constexpr int bofs = 0;
     launder();
     // S^T = K Q^T, two 16-key halves; the operands of step s + 2 are read
@@ -242,7 +265,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
     auto kread = [&](int s, uint4& k0, uint4& k1) {
       const int sl = s & 3, sh = s >> 2;
       k0 = lds_read_b128(kptr[sl] + bofs + sh * 256);
-      k1 = lds_read_b128(kptr[sl] + bofs + sh * 256 + 16 * kRowB);
+      k1 = lds_read_b128(kptr[sl] + bofs + sh * 256 + 16 * kRowS);
     };
     uint4 ka0, ka1, kb0, kb1;
     kread(0, ka0, ka1);
@@ -271,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
       sv[i] = s0[i];
       sv[4 + i] = s1[i];
     }
-    const uint32_t w = (uint32_t)__ballot(lane < KT && krow[t * KT + (lane & 31)] != -1);
+    const uint32_t w = (uint32_t)__ballot(lane < KT && meta != -1);
     if (w != 0xffffffffu) {
       const uint32_t mine = w >> (4 * lg);
 #pragma unroll
@@ -328,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
     auto vread = [&](int db) -> uint4 {
       const int dl = db & 7, dh = db >> 3;
       const uint2 v0 = lds_read_tr16(vptr[dl] + bofs + dh * 256);
-      const uint2 v1 = lds_read_tr16(vptr[dl] + bofs + dh * 256 + 16 * kRowB);
+      const uint2 v1 = lds_read_tr16(vptr[dl] + bofs + dh * 256 + 16 * kRowS);
       return make_uint4(v0.x, v0.y, v1.x, v1.y);
     };
     uint4 va = vread(0), vb = vread(1);
@@ -362,9 +385,12 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   }
   // ---- key loop: one barrier per tile
   int flip = kTileB;
+  int meta = meta_read(0);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) dma_tile(t + 2);           // raw tile t % 2 was converted last tile
-    compute(t);
+    if (t + 2 < ntiles)                             // raw tile t % 2 was converted last tile
+      dma_rows(t + 2, [&](int j) { return __builtin_amdgcn_readlane(meta, 40 + j); }, meta, 40);
+    const int meta_next = meta_read(t + 1);
+    compute(t, meta);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kptr[i] += flip;
 #pragma unroll
@@ -373,9 +399,10 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
     if (t + 1 < ntiles) {
       if (t + 2 < ntiles) wait_vm<NDMA>();          // this wave's copies of tile t+1 landed
       else wait_vm<0>();
-      convert_tile(t + 1);                          // key tile (t+1) % 2 was read last tile
-    }
+      convert_rows(t + 1, [&](int kw) { return __builtin_amdgcn_readlane(meta, 32 + kw); });
+    }                                               // (key tile (t+1) % 2 was read last tile)
     lds_barrier();
+    meta = meta_next;
   }
 
   // ---- epilogue: normaliser over the 4 lanes of each head

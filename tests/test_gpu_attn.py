@@ -70,6 +70,8 @@ def _prefill_case(rng, T, H, D, n_ent, m, k, window, q_fmt, kv_fmt, out_fmt, spa
     (9, 128, 512, 277, 4, 200, 128, "bf16", "fp8_mixed", "bf16", True, 1100, 128),
     (40, 64, 512, 9, 4, 0, 16, "bf16", "fp8_mixed", "f32", False, 0, 0),
     (33, 32, 512, 20, 2, 12, 8, "bf16", "bf16", "bf16", True, 0, 0),
+    (37, 128, 512, 600, 4, 0, 64, "bf16", "bf16", "f32", False, 2000, 64),
+    (19, 128, 512, 700, 4, 300, 128, "bf16", "bf16", "bf16", True, 2400, 128),
 ])
 def test_attn_prefill(T, H, D, n_ent, m, k, window, qf, kvf, of, sparse, pos0, hist):
     rng = np.random.default_rng(T * 7 + H + D)
@@ -87,6 +89,8 @@ def test_attn_prefill(T, H, D, n_ent, m, k, window, qf, kvf, of, sparse, pos0, h
     (301, 64, 128, 18, 16, 0, 128, "bf16", "bf16", False, 0, 0),
     (45, 64, 128, 40, 4, 24, 32, "bf16", "bf16", True, 0, 0),
     (21, 64, 512, 130, 4, 100, 16, "bf16", "fp8_mixed", True, 500, 16),
+    (9, 128, 512, 277, 4, 200, 128, "bf16", "fp8_mixed", True, 1100, 128),
+    (23, 128, 512, 400, 4, 0, 32, "bf16", "fp8_mixed", False, 1500, 32),
 ])
 def test_attn_large_logits(T, H, D, n_ent, m, k, window, qf, kvf, sparse, pos0, hist):
     """Inputs scaled by 6: logits spread over hundreds of units, so a running
@@ -99,6 +103,16 @@ def test_attn_large_logits(T, H, D, n_ent, m, k, window, qf, kvf, sparse, pos0, 
     tol = TOL["bf16"] if qf == "bf16" else TOL["f32"]
     assert np.isfinite(err) and err <= tol * amp, err
     assert np.isfinite(lerr) and lerr <= (1e-4 if qf == "f32" else 2e-2) * amp * amp, lerr
+
+
+@pytest.mark.parametrize("k,window", [(2, 8), (40, 16), (70, 16), (100, 28), (150, 10)])
+def test_attn_128_heads_few_tiles(k, window):
+    """128 heads over 512 dims with 1 .. 5 key tiles of 32 (the pipelined
+    path's start-up and drain), the last tile ragged."""
+    rng = np.random.default_rng(k + window)
+    err, lerr = _prefill_case(rng, 6, 128, 512, 300, 4, k, window, "bf16", "fp8_mixed", "bf16",
+                              True, pos0=1000, raw_hist=window)
+    assert err <= 2e-2 and lerr <= 2e-2, (err, lerr)
 
 
 def test_attn_chunk_with_history():
