@@ -123,7 +123,7 @@ class Prefill:
         attn = {"name": "attention", "work": self.attn_flops, "peak": PEAK[cdt], "dtype": cdt,
                 "per_unit": f"4*D*H = {4 * D * H} flop per (query, key) pair; {pairs} pairs "
                             f"per launch",
-                "sha": src_sha("attn.hip", "common.h")}
+                "sha": src_sha("attn.hip", "attn512.hip", "attn_common.h", "common.h")}
         idx = {"name": "indexer_topk", "work": self.idx_flops, "peak": PEAK[idt], "dtype": idt,
                "per_unit": f"2*4*64 = 512 flop per (query, visible entry) pair; {nv_sum} pairs "
                            f"per launch",
