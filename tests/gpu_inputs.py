@@ -97,3 +97,22 @@ def check_mixed(out, c64, cabs, rel=2.0 ** -20):
         assert abs(int(nope_g[r, c] & 0x7F) - int(nope_r[r, c] & 0x7F)) == 1
         assert abs(c64[r, c] - (a + bb) / 2 * s) <= err[r, c]
     return int(diff.sum())
+
+
+def check_attention(out, lse, qv, H, ent_rows, win_rows, tol=2e-2):
+    """Attention outputs against the oracle, query by query.
+
+    qv [n_q, H, D]: the oracle's query values; ent_rows[i] / win_rows[i]: the
+    oracle's values of query i's compressed keys (selected or visible) and
+    window rows.  Outputs and log-sum-exps within tol (bf16 compute)."""
+    from oracle import csa as ref
+    g, gl = to_np(out).reshape(len(qv), H, -1), to_np(lse).reshape(len(qv), H)
+    sc = ref.default_scale(qv.shape[-1])
+    err = lerr = 0.0
+    for i in range(len(qv)):
+        keys = np.concatenate([ent_rows[i], win_rows[i]])
+        o, l = ref.attend(qv[i], keys, sc)
+        err = max(err, float(np.max(np.abs(g[i] - o))))
+        lerr = max(lerr, float(np.max(np.abs(gl[i] - l))))
+    assert err <= tol and lerr <= tol, (err, lerr)
+    return err, lerr

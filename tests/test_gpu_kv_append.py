@@ -1,6 +1,8 @@
 """csa_kv_compress_append (decode-time compression through a per-request
 state) against the oracle's compression of the whole sequence, and attention
-over a ring of window rows against the same rows stored in order."""
+over a ring of window rows against the same rows stored in order and against
+the oracle (page "DeepSeek V4 深度解析", section 4, KV-cache management: the
+raw tokens of the window kept in a state cache)."""
 import dataclasses
 
 import numpy as np
@@ -11,7 +13,7 @@ from long_context_compressed_kv_amd import ops
 from long_context_compressed_kv_amd.ops import BF16, F32, KV, Batch
 from oracle import csa as ref
 
-from gpu_inputs import FMT, bf16_ulp, check_mixed, dev_f32, dev_kv, ref_vals, to_np
+from gpu_inputs import FMT, bf16_ulp, check_attention, check_mixed, dev_f32, dev_kv, ref_vals, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -150,6 +152,17 @@ def _ring_case(rng, ts, H, D, kv_fmt, sparse, k, window, C, split):
                             lse, split_keys=split)
         outs.append((out, lse))
     torch.cuda.synchronize()
+    # the ring result against the oracle: each request's keys (selected or
+    # visible entries) and its window rows in position order
+    qv = ref_vals(q, "bf16")
+    ev = ref_vals(ent, kv_fmt)
+    off = np.concatenate([[0], np.cumsum(n_ent)])
+    ent_rows, win_rows = [], []
+    for r, t in enumerate(ts):
+        mine = ev[off[r]: off[r + 1]]
+        ent_rows.append(mine[idx[r][idx[r] >= 0]] if sparse else mine)
+        win_rows.append(ref_vals(lin_rows[r], "bf16")[ref.window_positions(t, window) - lin_pos[r]])
+    check_attention(outs[1][0], outs[1][1], qv, H, ent_rows, win_rows)
     return outs
 
 

@@ -1,9 +1,12 @@
 """The paged compressed cache (csa_batch.kv_block_table, and the block table
 of csa_kv_compress_append): every call that reads or writes compressed
 entries gives bit for bit the result of the same call on the entries stored
-contiguously.  Blocks are handed out in a shuffled order with spare blocks
-between them, and rows no request owns hold large garbage values, so a row
-read or written through a wrong block shows up."""
+contiguously, and the readers (attention, indexer scores, fused top-k) also
+match the oracle computed from each request's entries in logical order (page
+"DeepSeek V4 深度解析", section 4, KV-cache management: the compressed cache
+is kept in blocks).  Blocks are handed out in a shuffled order with spare
+blocks between them, and rows no request owns hold large garbage values, so
+a row read or written through a wrong block shows up."""
 import dataclasses
 import zlib
 
@@ -13,8 +16,10 @@ import torch
 
 from long_context_compressed_kv_amd import ops
 from long_context_compressed_kv_amd.ops import BF16, F32, KV, Batch
+from oracle import csa as ref
 
-from gpu_inputs import dev_f32, dev_kv
+from gpu_inputs import bf16_ulp, check_attention, dev_f32, dev_kv, ref_vals, to_np
+from test_gpu_configs import topk_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +103,22 @@ def test_attention_paged_equals_contiguous(name):
     torch.cuda.synchronize()
     assert torch.isfinite(outs[0][0].float()).all()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # the paged result against the oracle over each request's entries in order
+    qv = ref_vals(q, "bf16").reshape(n_q, H, D)
+    ent_rows, win_rows = [], []
+    i = 0
+    for r in range(n_req):
+        ev, rv = ref_vals(ents[r], kv_fmt), ref_vals(raws[r], "bf16")
+        for tt in range(q_counts[r]):
+            t = q_pos[r] + tt
+            if k:
+                sel = idx[i][idx[i] >= 0]
+            else:
+                sel = np.arange(min((t + 1) // m, n_ent[r]))
+            ent_rows.append(ev[sel])
+            win_rows.append(rv[ref.window_positions(t, window) - raw_pos[r]])
+            i += 1
+    check_attention(outs[1][0], outs[1][1], qv, H, ent_rows, win_rows)
 
 
 # ------------------------------------------------------- indexer and top-k
@@ -129,6 +150,23 @@ def test_indexer_and_topk_paged_equal_contiguous(fmt, score_fmt, ctx, q_counts):
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0])
     assert torch.equal(res[0][1], res[1][1])
+    # the paged scores and selection against the oracle
+    qv, kv = ref_vals(qi, fmt).reshape(n_q, 4, 64), [ref_vals(x, fmt) for x in keys]
+    g, got = to_np(res[1][0]), res[1][1].cpu().numpy()
+    i = 0
+    for r in range(len(ctx)):
+        for tt in range(q_counts[r]):
+            nv = min((ctx[r] + tt + 1) // m, n_ent[r])
+            sv = ref.indexer_scores(qv[i], kv[r][:nv])
+            key = ref.score_keys(sv, score_fmt).astype(np.float64)
+            gv = g[i, :nv].astype(np.float64)
+            if score_fmt == "f32":
+                assert np.all(np.abs(gv - sv) <= 1e-6 + 1e-5 * np.abs(sv))
+            else:
+                assert np.all(np.abs(gv - key) <= bf16_ulp(key) * 1.0001)
+            want = ref.topk_indices(key, k)
+            assert topk_ok(got[i], want, key, score_fmt, sv, qv[i], kv[r][:nv]), (r, tt)
+            i += 1
 
 
 # ------------------------------------------------------------------- append
@@ -261,3 +299,8 @@ def test_attention_paged_with_ring_window():
         outs.append((out, lse))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # and against the oracle: each request's selected entries and its window
+    qv = ref_vals(q, "bf16").reshape(len(ts), H, D)
+    ent_rows = [ref_vals(ents[r], "fp8_mixed")[idx[r][idx[r] >= 0]] for r in range(len(ts))]
+    win_rows = [ref_vals(lin[r], "bf16")[ref.window_positions(t, window) - p0s[r]] for r, t in enumerate(ts)]
+    check_attention(outs[1][0], outs[1][1], qv, H, ent_rows, win_rows)
