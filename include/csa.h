@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -197,6 +197,35 @@ csa_status csa_kv_compress_paged(const csa_tensor* x, const float* logits, int64
                                  const float* slot_bias, int32_t m, int32_t w,
                                  int64_t entry_begin, int64_t n_entries, const int32_t* blocks,
                                  int32_t block_rows, const csa_tensor* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_kv_compress_batch - csa_kv_compress for a batch of prefill chunks in one
+ * launch (page "DeepSeek V4 深度解析", section 2, CSA step 1, applied to every
+ * request of a ragged batch).
+ *
+ * For each request r of `batch`: its chunk covers positions q_pos[r] ..
+ * q_pos[r] + T_r - 1, T_r = q_off[r+1] - q_off[r], and completes entries
+ * floor(q_pos[r] / m) .. floor((q_pos[r] + T_r) / m) - 1 (an entry is
+ * complete once its last raw token, position (i+1)m - 1, is in).  Each is
+ * computed as csa_kv_compress computes entry i, from r's raw rows x[raw_off[r]
+ * .. raw_off[r+1]) at positions raw_pos[r] .. (logits aligned with x), and
+ * written to r's cache row kv_off[r] + i, or through batch->kv_block_table
+ * when it is set (row table[r*stride + i/P]*P + i%P).
+ *   x, logits  raw rows of all requests (F32 or BF16) and their logits
+ *   slot_bias  float [w]; 1 <= m <= w <= 1024
+ *   batch      q_off, q_pos, kv_off, raw_off, raw_pos (device); window_ring 0
+ *   out        the entry tensor (F32, BF16 or FP8_MIXED at dim 512)
+ * Each chunk's raw rows must start at position (floor(q_pos[r] / m) + 1) m - w
+ * (the first slot of its first new entry) or at 0: a slot at a position >= 0
+ * outside r's raw rows is left out of that entry's softmax, as a slot at a
+ * negative position is.
+ * An entry past r's cache rows (i >= kv_off[r+1] - kv_off[r]) or whose block
+ * id is negative or out of the tensor is not written.  Sizes and formats are
+ * checked on the host; offsets are read on the device.
+ * ------------------------------------------------------------------------- */
+csa_status csa_kv_compress_batch(const csa_tensor* x, const float* logits, const float* slot_bias,
+                                 int32_t m, int32_t w, const csa_batch* batch, const csa_tensor* out,
+                                 hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * csa_kv_compress_channel - CSA step 1 with a learned weight per raw token and

@@ -9,7 +9,7 @@ CSA_OK = 0
 CSA_F32, CSA_BF16, CSA_FP8_MIXED, CSA_MXFP4 = 0, 1, 2, 3
 
 EXPORTED = (
-    "csa_kv_compress", "csa_kv_compress_paged", "csa_kv_compress_channel", "csa_kv_compress_append", "csa_kv_append_state_size", "csa_indexer_score", "csa_topk_select", "csa_indexer_topk",
+    "csa_kv_compress", "csa_kv_compress_paged", "csa_kv_compress_batch", "csa_kv_compress_channel", "csa_kv_compress_append", "csa_kv_append_state_size", "csa_indexer_score", "csa_topk_select", "csa_indexer_topk",
     "csa_indexer_topk_workspace_size", "csa_indexer_topk_noalloc",
     "csa_indexer_topk_noalloc_max_bytes", "csa_sparse_mqa_attn",
     "csa_swa_merge", "csa_quantize", "csa_dequantize", "csa_mxfp4_to_fp8",
@@ -23,7 +23,7 @@ class CsaTensor(ctypes.Structure):
 
 
 # csa_abi_version() of the library these bindings describe (include/csa.h)
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class CsaBatch(ctypes.Structure):
@@ -59,6 +59,7 @@ def load():
         "csa_kv_compress": [T, P, I64, P, I32, I32, I64, I64, T, P],
         "csa_kv_compress_channel": [T, P, I64, P, I32, I32, I64, I64, T, P],
         "csa_kv_compress_paged": [T, P, I64, P, I32, I32, I64, I64, P, I32, T, P],
+        "csa_kv_compress_batch": [T, P, P, I32, I32, B, T, P],
         "csa_kv_compress_append": [T, P, P, I32, I32, P, P, P, P, I64, I32, T, T, P, I32, P],
         "csa_indexer_score": [T, I32, P, T, B, I32, I32, P, I32, I64, P],
         "csa_topk_select": [P, I32, I64, B, I32, I32, P, P],

@@ -61,16 +61,16 @@ __device__ __forceinline__ int64_t out_row(const OutPtrs& o, int64_t e_local) {
   return blk >= 0 && row < o.rows ? row : -1;
 }
 
+// Entry i from raw rows x (positions x_pos0 .. x_pos0 + x_rows - 1) into
+// row `row` of `out` (not written if row < 0); the whole workgroup calls it.
 template <typename TIn, int OUTF>
-__global__ __launch_bounds__(kThreads) void kv_compress_kernel(
-    const TIn* __restrict__ x, const float* __restrict__ z, int64_t x_pos0, int64_t x_rows,
-    const float* __restrict__ bias, int m, int w, int64_t entry_begin, int dim, OutPtrs out) {
+__device__ __forceinline__ void compress_entry(const TIn* __restrict__ x, const float* __restrict__ z,
+                                               int64_t x_pos0, int64_t x_rows, const float* __restrict__ bias,
+                                               int m, int w, int64_t i, int dim, const OutPtrs& out, int64_t row) {
   __shared__ float wgt[kMaxW];
   __shared__ float red[kThreads / 64];
   __shared__ float acc_lds[2 * kThreads];
 
-  const int64_t e_local = blockIdx.x;
-  const int64_t i = entry_begin + e_local;
   const int64_t p0 = (i + 1) * m - w;
   const int tid = threadIdx.x;
 
@@ -122,7 +122,6 @@ __global__ __launch_bounds__(kThreads) void kv_compress_kernel(
     }
   }
 
-  const int64_t row = out_row(out, e_local);
   if (OUTF == CSA_F32) {
     if (g == 0 && row >= 0)
       *reinterpret_cast<float2*>(static_cast<float*>(out.data) + row * dim + d) =
@@ -144,6 +143,87 @@ __global__ __launch_bounds__(kThreads) void kv_compress_kernel(
                                out.scale + row * 4, out.rope + row * 64);
     }
   }
+}
+
+template <typename TIn, int OUTF>
+__global__ __launch_bounds__(kThreads) void kv_compress_kernel(
+    const TIn* __restrict__ x, const float* __restrict__ z, int64_t x_pos0, int64_t x_rows,
+    const float* __restrict__ bias, int m, int w, int64_t entry_begin, int dim, OutPtrs out) {
+  const int64_t e_local = blockIdx.x;
+  compress_entry<TIn, OUTF>(x, z, x_pos0, x_rows, bias, m, w, entry_begin + e_local, dim, out,
+                            out_row(out, e_local));
+}
+
+// A batch of prefill chunks (csa_batch): request r's chunk covers positions
+// q_pos[r] .. q_pos[r] + T_r - 1 (T_r = q_off[r+1] - q_off[r]) and completes
+// entries floor(q_pos/m) .. floor((q_pos + T_r)/m) - 1, computed from r's raw
+// rows (raw_off / raw_pos) into r's cache rows (kv_off, or its blocks).
+// Workgroup g takes the g-th of those entries in request order; the ones past
+// the last exit.
+__device__ __forceinline__ int64_t chunk_entries(const BatchDev& b, int r, int m, int64_t& first) {
+  const int64_t pos = max(b.q_pos[r], (int64_t)0), T = max(b.q_off[r + 1] - b.q_off[r], (int64_t)0);
+  first = pos / m;
+  return (pos + T) / m - first;
+}
+
+template <typename TIn, int OUTF>
+__global__ __launch_bounds__(kThreads) void kv_compress_batch_kernel(
+    const TIn* __restrict__ x, const float* __restrict__ z, const float* __restrict__ bias, int m, int w,
+    int dim, BatchDev b, OutPtrs out) {
+  __shared__ int64_t scan[kThreads / 64];
+  __shared__ int found_req;
+  __shared__ int64_t found_e;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t g = blockIdx.x;
+  if (tid == 0) found_req = -1;
+  int64_t base = 0;
+  for (int r0 = 0; r0 < b.n_req; r0 += kThreads) {
+    const int r = r0 + tid;
+    int64_t first = 0;
+    const int64_t c = r < b.n_req ? chunk_entries(b, r, m, first) : 0;
+    // inclusive scan of c over the workgroup (wave scans, then the wave totals)
+    int64_t v = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t u = __shfl_up(v, d);
+      if (lane >= d) v += u;
+    }
+    __syncthreads();
+    if (lane == 63) scan[wv] = v;
+    __syncthreads();
+    int64_t before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) {
+      before += k < wv ? scan[k] : 0;
+      total += scan[k];
+    }
+    const int64_t incl = base + before + v;
+    if (r < b.n_req && g >= incl - c && g < incl) {
+      found_req = r;
+      found_e = first + (g - (incl - c));
+    }
+    base += total;
+    __syncthreads();
+    if (found_req >= 0 || base > g) break;
+  }
+  const int r = found_req;
+  if (r < 0) return;                               // past the batch's last entry
+  const int64_t i = found_e;
+  // offsets clamped to the tensors, so every access stays in bounds
+  const int64_t rw0 = min(max(b.raw_off[r], (int64_t)0), b.raw_rows);
+  const int64_t rw1 = min(max(b.raw_off[r + 1], rw0), b.raw_rows);
+  const int64_t kv0 = b.kv_off[r], kv1 = b.kv_off[r + 1];
+  int64_t row = -1;
+  if (i < kv1 - kv0) {                            // the request's cache has a row for it
+    if (b.pages == nullptr) {
+      row = kv0 >= 0 && kv0 + i < out.rows ? kv0 + i : -1;
+    } else {
+      const int64_t blk = b.pages[(int64_t)r * b.page_stride + (i >> b.page_shift)];
+      const int64_t pr = (blk << b.page_shift) + (i & ((1ll << b.page_shift) - 1));
+      row = blk >= 0 && pr < out.rows ? pr : -1;
+    }
+  }
+  compress_entry<TIn, OUTF>(x + rw0 * dim, z + rw0, b.raw_pos[r], rw1 - rw0, bias, m, w, i, dim, out, row);
 }
 
 // The variant with a logit and a bias per channel: z [x_rows][dim], bias
@@ -263,6 +343,28 @@ void launch(const csa_tensor* x, const float* z, int64_t x_pos0, const float* bi
   }
 }
 
+template <typename TIn>
+void launch_batch(const csa_tensor* x, const float* z, const float* bias, int m, int w,
+                  const BatchDev& b, int64_t grid_n, const csa_tensor* out, hipStream_t stream) {
+  OutPtrs o{out->data, static_cast<uint8_t*>(out->scale), static_cast<uint16_t*>(out->rope), nullptr,
+            0, out->rows, 0};
+  const TIn* xp = static_cast<const TIn*>(x->data);
+  dim3 grid((unsigned)grid_n), block(kThreads);
+  switch (out->fmt) {
+    case CSA_F32:
+      hipLaunchKernelGGL((kv_compress_batch_kernel<TIn, CSA_F32>), grid, block, 0, stream, xp, z, bias, m, w,
+                         x->dim, b, o);
+      break;
+    case CSA_BF16:
+      hipLaunchKernelGGL((kv_compress_batch_kernel<TIn, CSA_BF16>), grid, block, 0, stream, xp, z, bias, m, w,
+                         x->dim, b, o);
+      break;
+    default:
+      hipLaunchKernelGGL((kv_compress_batch_kernel<TIn, CSA_FP8_MIXED>), grid, block, 0, stream, xp, z, bias,
+                         m, w, x->dim, b, o);
+  }
+}
+
 }  // namespace
 
 using namespace csa_host;
@@ -354,4 +456,36 @@ extern "C" csa_status csa_kv_compress_channel(const csa_tensor* x, const float* 
   else
     launch_channel<uint16_t>(x, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out, stream);
   return check_launch("csa_kv_compress_channel");
+}
+
+extern "C" csa_status csa_kv_compress_batch(const csa_tensor* x, const float* logits, const float* slot_bias,
+                                            int32_t m, int32_t w, const csa_batch* batch, const csa_tensor* out,
+                                            hipStream_t stream) {
+  clear_error();
+  const char* who = "csa_kv_compress_batch";
+  if (batch == nullptr) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: null batch", who);
+  // the per-tensor and (m, w) checks of the single-sequence call (no entry range)
+  const csa_status st = check_compress(who, x, logits, 0, slot_bias, m, w, 0, 0, out, true);
+  if (st != CSA_OK) return st;
+  if (batch->n_req < 0 || batch->n_q < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: bad batch sizes", who);
+  if (batch->n_req == 0 || batch->n_q == 0) return CSA_OK;
+  if (logits == nullptr || slot_bias == nullptr)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: null logits or biases", who);
+  if (batch->q_off == nullptr || batch->q_pos == nullptr || batch->kv_off == nullptr ||
+      batch->raw_off == nullptr || batch->raw_pos == nullptr)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "%s: the batch needs q_off, q_pos, kv_off, raw_off and raw_pos", who);
+  if (batch->window_ring != 0)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: raw rows must be stored in position order (no window ring)", who);
+  BatchDev b{batch->n_req, batch->q_off, batch->q_pos, batch->kv_off, batch->raw_off, batch->raw_pos,
+             out->rows, x->rows, 0};
+  const csa_status pst = batch_pages(batch, b, who);
+  if (pst != CSA_OK) return pst;
+  // every request completes at most floor(T_r / m) + 1 entries
+  const int64_t grid_n = batch->n_q / m + batch->n_req;
+  if (grid_n > 0x7fffffff) return fail(CSA_ERR_INVALID_ARGUMENT, "%s: too many entries for one launch", who);
+  if (x->fmt == CSA_F32)
+    launch_batch<float>(x, logits, slot_bias, m, w, b, grid_n, out, stream);
+  else
+    launch_batch<uint16_t>(x, logits, slot_bias, m, w, b, grid_n, out, stream);
+  return check_launch(who);
 }

@@ -165,6 +165,19 @@ def kv_compress(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, 
     return out
 
 
+def kv_compress_batch(x: KV, logits, slot_bias, m, w, batch, out: KV):
+    """CSA step 1 for a batch of prefill chunks in one launch: for each
+    request r, the entries its chunk completes (floor(q_pos/m) ..
+    floor((q_pos+T_r)/m) - 1) from its raw rows (raw_off / raw_pos) into its
+    cache rows (kv_off, or its blocks when the batch is paged)."""
+    _need_cuda(logits, slot_bias)
+    lib = _lib.load()
+    xc, oc, bc = x.c(), out.c(), batch.c()
+    check(lib.csa_kv_compress_batch(ctypes.byref(xc), _ptr(logits), _ptr(slot_bias), int(m), int(w),
+                                    ctypes.byref(bc), ctypes.byref(oc), _stream()), "csa_kv_compress_batch")
+    return out
+
+
 def kv_compress_channel(x: KV, logits, x_pos0, slot_bias, m, w, entry_begin, n_entries, out: KV):
     """CSA step 1 with a logit per raw token and channel: logits float
     [x.rows, dim], slot_bias float [w, dim]; one softmax per channel."""

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     assert lib.csa_status_string(0) == b"ok"
     assert lib.csa_status_string(3) == b"workspace too small"
 
@@ -89,6 +89,25 @@ def test_kv_compress_validation(lib):
 
 def _batch(n_q=4, n_req=1, max_kv=16):
     return CsaBatch(n_req, 0, n_q, max_kv, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_kv_compress_batch_validation(lib):
+    """The ragged compression call's host checks (no device needed)."""
+    x, out = _t(0, 128, 64), _t(0, 128, 64)
+    z = b = FAKE
+    call = lambda bt, m=4, w=8, xx=x, oo=out: lib.csa_kv_compress_batch(
+        ctypes.byref(xx), z, b, m, w, None if bt is None else ctypes.byref(bt), ctypes.byref(oo), None)
+    assert call(None) == BAD_ARG                             # no batch
+    assert call(_batch(), m=4, w=2) == BAD_ARG               # w < m
+    assert call(_batch(), xx=_t(0, 64, 64)) == BAD_ARG       # dim mismatch
+    ring = CsaBatch(1, 1, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(ring) == UNSUPPORTED                         # raw rows must be in order
+    assert b"csa_kv_compress_batch" in lib.csa_last_error()
+    no_raw = CsaBatch(1, 0, 4, 16, FAKE, FAKE, FAKE, None, None)
+    assert call(no_raw) == BAD_ARG                           # raw offsets needed
+    paged = CsaBatch(1, 0, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 24, 0)
+    assert call(paged) == BAD_ARG                            # block rows not a power of two
+    assert call(CsaBatch(0, 0, 0, 0, None, None, None, None, None)) == 0   # empty batch, nothing launched
 
 
 def test_kv_append_validation(lib):

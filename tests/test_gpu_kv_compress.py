@@ -178,3 +178,129 @@ def test_indexer_keys_compressed_with_the_same_weights():
     # score within the fp32 accumulation's rounding
     kth = np.sort(s)[-k]
     assert all(abs(s[j] - kth) <= 1e-5 * abs(kth) + 1e-7 for j in got ^ want)
+
+
+# ------------------------------------------------------------ ragged batch
+
+def _batch_case(rng, chunks, m, w, D, in_fmt, out_fmt, paged=0):
+    """chunks: [(q_pos, T)]; each request's raw rows start at the first slot
+    of its first new entry (or at 0).  Returns (device out, per-request oracle
+    entries, first entry index, cache rows of each entry, owned-row mask)."""
+    from gpu_inputs import dev_kv as _dev
+    raws, zs, rpos, kv_counts = [], [], [], []
+    for pos, T in chunks:
+        p0 = max(0, (pos // m + 1) * m - w)      # the first new entry's first slot
+        raws.append(rng.standard_normal((pos + T - p0, D)).astype(np.float32))
+        zs.append(rng.standard_normal(pos + T - p0).astype(np.float32))
+        rpos.append(p0)
+        kv_counts.append((pos + T) // m + 3)        # the cache holds every entry up to the chunk
+    b = rng.standard_normal(w).astype(np.float32)
+    batch = ops.Batch.make([T for _, T in chunks], [p for p, _ in chunks], kv_counts=kv_counts,
+                           raw_counts=[len(x) for x in raws], raw_pos=rpos)
+    n_rows = sum(kv_counts)
+    rows_of = []
+    if paged:
+        nb = [(c + paged - 1) // paged for c in kv_counts]
+        ids = rng.permutation(sum(nb) + 3)
+        table = np.full((len(chunks), max(nb)), -1, np.int32)
+        k = 0
+        for r, n in enumerate(nb):
+            table[r, :n] = ids[k:k + n]
+            k += n
+        n_rows = (sum(nb) + 3) * paged
+        import dataclasses
+        batch = dataclasses.replace(batch, kv_block_table=torch.from_numpy(table).cuda(), kv_block_rows=paged)
+        rows_of = lambda r, i: int(table[r, i // paged]) * paged + i % paged
+    else:
+        off = np.concatenate([[0], np.cumsum(kv_counts)])
+        rows_of = lambda r, i: int(off[r]) + i
+    sentinel = (rng.standard_normal((n_rows, D)) * 40).astype(np.float32)
+    out = _dev(sentinel, out_fmt if out_fmt != "f32" else "f32")
+    before = [t.clone() for t in (out.data, out.scale, out.rope) if t is not None]
+    ops.kv_compress_batch(_dev(np.concatenate(raws), in_fmt), dev_f32(np.concatenate(zs)), dev_f32(b), m, w,
+                          batch, out)
+    torch.cuda.synchronize()
+    want, places = [], []
+    for r, (pos, T) in enumerate(chunks):
+        e0, e1 = pos // m, (pos + T) // m
+        c = ref.compress_entries(ref_vals(raws[r], in_fmt), zs[r].astype(np.float64), rpos[r], b, m, w, e0, e1)
+        ca = ref.compress_entries(np.abs(ref_vals(raws[r], in_fmt)), zs[r].astype(np.float64), rpos[r], b, m, w,
+                                  e0, e1)
+        want.append((c, ca))
+        places.append([rows_of(r, i) for i in range(e0, e1)])
+    owned = np.zeros(n_rows, bool)
+    for pl in places:
+        owned[pl] = True
+    return out, want, places, owned, before
+
+
+@pytest.mark.parametrize("out_fmt,in_fmt,m,w,D,paged", [
+    ("f32", "f32", 4, 8, 128, 0),
+    ("bf16", "bf16", 128, 256, 128, 0),
+    ("fp8_mixed", "bf16", 4, 8, 512, 0),
+    ("bf16", "f32", 4, 8, 256, 32),      # a paged cache
+])
+def test_compress_batch_against_oracle(out_fmt, in_fmt, m, w, D, paged):
+    """One launch for a ragged batch of prefill chunks: every request's new
+    entries match the oracle's compression of its own rows; a chunk that
+    completes no entry, an empty chunk and a chunk at position 0 are in the
+    batch; rows that no new entry owns keep their contents."""
+    rng = np.random.default_rng(D + m + paged)
+    if m == 4:
+        chunks = [(0, 300), (1001, 2), (5000, 777), (64, 0), (90, 45), (1 << 20, 129)]
+    else:
+        chunks = [(0, 1000), (70000, 300), (130, 10), (4096, 2048)]
+    out, want, places, owned, before = _batch_case(rng, chunks, m, w, D, in_fmt, out_fmt, paged)
+    for (c, ca), pl in zip(want, places):
+        if not pl:
+            continue
+        if out_fmt == "fp8_mixed":
+            view = KV(out.fmt, out.dim, out.data[pl], out.scale[pl], out.rope[pl])
+            assert check_mixed(view, c, ca) <= len(pl) * 448 * 1e-3
+        else:
+            g = to_np(out.data[pl]).astype(np.float64)
+            if out_fmt == "f32":
+                assert np.max(np.abs(g - c)) <= 1e-5
+            else:
+                assert np.all(np.abs(g - c) <= bf16_ulp(c) * 1.0001)
+    free = torch.from_numpy(~owned).cuda()
+    for a, b0 in zip([t for t in (out.data, out.scale, out.rope) if t is not None], before):
+        assert torch.equal(a[free], b0[free])
+
+
+def test_compress_batch_equals_per_request_calls():
+    """The batch call gives bit for bit what one csa_kv_compress call per
+    request gives (the same arithmetic per entry), whatever the order of the
+    requests in the batch."""
+    rng = np.random.default_rng(11)
+    m, w, D = 4, 8, 512
+    chunks = [(2000, 513), (0, 64), (777, 1000), (10, 1)]
+    raws, zs, rpos = [], [], []
+    for pos, T in chunks:
+        p0 = max(0, (pos // m + 1) * m - w)      # the first new entry's first slot
+        raws.append(rng.standard_normal((pos + T - p0, D)).astype(np.float32))
+        zs.append(rng.standard_normal(pos + T - p0).astype(np.float32))
+        rpos.append(p0)
+    b = dev_f32(rng.standard_normal(w).astype(np.float32))
+    singles = []
+    for r, (pos, T) in enumerate(chunks):
+        e0, n = pos // m, (pos + T) // m - pos // m
+        one = KV.empty(FMT["fp8_mixed"], max(n, 1), D)
+        if n:
+            ops.kv_compress(dev_kv(raws[r], "bf16"), dev_f32(zs[r]), rpos[r], b, m, w, e0, n, one)
+        singles.append((one, n))
+    for order in ([0, 1, 2, 3], [3, 2, 0, 1]):
+        kv_counts = [(chunks[r][0] + chunks[r][1]) // m for r in order]
+        batch = ops.Batch.make([chunks[r][1] for r in order], [chunks[r][0] for r in order], kv_counts=kv_counts,
+                               raw_counts=[len(raws[r]) for r in order], raw_pos=[rpos[r] for r in order])
+        out = KV.empty(FMT["fp8_mixed"], sum(kv_counts), D)
+        ops.kv_compress_batch(dev_kv(np.concatenate([raws[r] for r in order]), "bf16"),
+                              dev_f32(np.concatenate([zs[r] for r in order])), b, m, w, batch, out)
+        torch.cuda.synchronize()
+        off = np.concatenate([[0], np.cumsum(kv_counts)])
+        for j, r in enumerate(order):
+            one, n = singles[r]
+            e0 = chunks[r][0] // m
+            rows = slice(int(off[j]) + e0, int(off[j]) + e0 + n)
+            assert torch.equal(out.data[rows], one.data[:n]), r
+            assert torch.equal(out.scale[rows], one.scale[:n]) and torch.equal(out.rope[rows], one.rope[:n])
