@@ -413,14 +413,16 @@ csa_status csa_indexer_topk_noalloc(const csa_tensor* qi, int32_t n_heads, const
  *   n_heads   8, 16 or a multiple of 32 up to 128 (8 and 16 need a single
  *             request and no split)
  *   split_keys 0: each query's keys are processed by one workgroup.  > 0
- *             (decode): a query's key list (its entries, then its window
- *             rows) is cut into chunks of split_keys keys rounded up to a
- *             multiple of 32, processed in parallel and merged in order by
- *             log-sum-exp.  The chunk depends on split_keys alone, so a
- *             request's result does not depend on the other requests.  No
- *             query may need more than 256 chunks (CSA_ERR_UNSUPPORTED
- *             otherwise).  Needs `workspace` (device memory, caller-owned,
- *             contents not preserved) of at least
+ *             (decode): a query's key list of n keys (its entries, then its
+ *             window rows) is cut into p = min(32, ceil(n/split_keys))
+ *             parts of ceil(n/p) keys rounded up to a multiple of 32 (the
+ *             last takes the rest), processed in parallel and merged in
+ *             order by log-sum-exp.  The
+ *             parts depend on n and split_keys alone, so a request's result
+ *             does not depend on the other requests.  With D = 512 a part
+ *             holds at most 2048 keys with 64 heads and 4096 with 128
+ *             (CSA_ERR_UNSUPPORTED otherwise).  Needs `workspace` (device
+ *             memory, caller-owned, contents not preserved) of at least
  *             csa_attn_workspace_size(n_q, n_heads, D, max_keys, split_keys)
  *             bytes, where max_keys = (k if idx else batch->max_kv) + window.
  *             Calls sharing one workspace must not overlap.
@@ -431,8 +433,7 @@ csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads, const csa_t
                                void* out, int32_t out_fmt, float* lse, int32_t split_keys,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes csa_sparse_mqa_attn needs for split_keys > 0 (0 otherwise,
- * and 0 when a query of max_keys keys would need more than 256 chunks). */
+/* Workspace bytes csa_sparse_mqa_attn needs for split_keys > 0 (0 otherwise). */
 size_t csa_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t dim, int64_t max_keys,
                                int32_t split_keys);
 

@@ -19,15 +19,16 @@
 // buffers in LDS (one barrier per tile), D = 512 decode one.
 //
 // Split-K (decode).  With split_keys > 0 a query's key list is cut into
-// chunks of split_keys keys (rounded up to whole tiles) handled by a
-// persistent grid of workgroups; each writes a normalised partial output and
+// parts of about split_keys keys (split_chunk) handled by a persistent grid
+// of workgroups; each writes a normalised partial output and
 // its log-sum-exp to the workspace, and a combine pass merges a query's parts
-// in order (the same merge as csa_swa_merge).  The chunk depends on the call's
-// split_keys alone, so a request's parts, and the bits of its result, do not
-// depend on the other requests of the batch.  Selected keys number at most
-// k + window per query, so the work items are (query, split) pairs indexed
-// statically; all visible entries vary per request, so a plan kernel reads
-// the key counts and lists the items.
+// in order (the same merge as csa_swa_merge).  The parts follow from the
+// query's own key count and split_keys alone, so a request's parts, and the
+// bits of its result, do not depend on the other requests of the batch.
+// Selected keys number at most k + window per query, so the work items are
+// (query, split) pairs indexed statically (a query with fewer keys leaves its
+// last parts empty); all visible entries vary per request, so a plan kernel
+// reads the key counts and lists the items.
 //
 // Per tile and wave (bf16):
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, keys on M, queries on N;
@@ -52,21 +53,15 @@ using namespace csa_attn;
 
 namespace {
 
-// Split-K work list.  The chunk is split_keys rounded up to whole tiles (the
-// host has checked that no query needs more than max_splits of them).  The
-// splits of every query, their prefix sums and the query of every item, so
-// the attention grid visits only real items; the geometry of every query is
-// recorded once for the items to load.
+// Split-K work list.  The parts of every query (split_parts), their prefix
+// sums and the query of every item, so the attention grid visits only real
+// items; the geometry of every query is recorded once for the items to load.
 template <bool SPARSE>
 __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
   __shared__ int wsum[16];
   __shared__ int carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = (a.split_keys + KT - 1) / KT * KT;
-  if (tid == 0) {
-    *a.ws_chunk = chunk;
-    carry = 0;
-  }
+  if (tid == 0) carry = 0;
   __syncthreads();
   for (int64_t q0 = 0; q0 < a.n_q; q0 += 1024) {
     const int64_t q = q0 + tid;
@@ -74,8 +69,8 @@ __global__ __launch_bounds__(1024) void attn_split_plan(AttnArgs a) {
     if (q < a.n_q) {
       const Geo g = make_geo<SPARSE>(a, q);
       store_geo(a.ws_geo + q * 4, g);
-      ns = g.nkeys > 0 ? (g.nkeys + chunk - 1) / chunk : 1;
-      if (ns > a.max_splits) ns = a.max_splits;   // (excluded by the host's check)
+      ns = split_parts(g.nkeys, a.split_keys);
+      if (ns > a.max_splits) ns = a.max_splits;   // (excluded by the host's sizing)
       a.ws_cnt[q] = ns;
     }
     int x = ns;
@@ -195,7 +190,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 
   Geo g = splitk && !fixed ? load_geo(a.ws_geo + q_first * 4, q_first) : make_geo<SPARSE>(a, q_first);
   if (splitk) {
-    const int chunk = fixed ? a.static_chunk : *a.ws_chunk;
+    const int chunk = (int)split_chunk(g.nkeys, a.split_keys);
     g.key_lo = split * chunk;
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
     if (g.key_hi < g.key_lo) g.key_hi = g.key_lo;   // past this query's keys: an empty part
@@ -752,10 +747,9 @@ csa_status launch_kernel(const AttnArgs& a0, K kern, int threads, size_t smem, h
     // selected keys: at most static_keys (k + window) per query, so every
     // query has the same splits of the fixed chunk and the items are indexed
     // statically
-    const int64_t c = ((int64_t)a.split_keys + KT - 1) / KT * KT;
-    a.static_chunk = (int)c;
-    a.static_splits = (int)((a.static_keys + c - 1) / c);
-    if (a.static_splits < 1) a.static_splits = 1;
+    // (a query with fewer keys has at most as many parts)
+    a.static_chunk = (int)split_chunk(a.static_keys, a.split_keys);
+    a.static_splits = split_parts_max(a.static_keys, a.split_keys);
     if (a.host_splits != nullptr) *a.host_splits = a.static_splits;
     const int64_t items = a.n_q * a.static_splits;
     if ((int64_t)grid.x > items) grid.x = (unsigned)items;
@@ -834,13 +828,10 @@ csa_status launch_mode(const AttnArgs& a, bool sparse, int outm, hipStream_t s) 
   return launch_attn<D, F32C, KVF, false, DSPLIT, 1>(a, s);
 }
 
-// Parts a query of max_keys keys is cut into (0: more than kMaxSplits).
+// Most parts a query of at most max_keys keys is cut into.
 int max_splits_for(int64_t max_keys, int split_keys) {
   if (split_keys <= 0) return 1;
-  const int64_t chunk = ((int64_t)split_keys + KT - 1) / KT * KT;
-  int64_t n = (max_keys + chunk - 1) / chunk;
-  if (n < 1) n = 1;
-  return n > kMaxSplits ? 0 : (int)n;
+  return split_parts_max(max_keys, split_keys);
 }
 
 }  // namespace
@@ -975,10 +966,6 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
         (has_kv ? (sparse ? (int64_t)k : batch->max_kv) : 0) + (has_raw ? window : 0);
     a.split_keys = split_keys;
     a.max_splits = max_splits_for(max_keys, split_keys);
-    if (a.max_splits == 0)
-      return fail(CSA_ERR_UNSUPPORTED,
-                  "csa_sparse_mqa_attn: split_keys %d cuts %lld keys into more than %d parts",
-                  split_keys, (long long)max_keys, kMaxSplits);
     const size_t need = csa_attn_workspace_size(batch->n_q, H, D, max_keys, split_keys);
     if (workspace == nullptr || workspace_bytes < need)
       return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa_attn: split-K needs %zu workspace bytes", need);
@@ -996,13 +983,20 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
     outm = 2;
   }
   const int kvf = has_kv ? kv->fmt : (f32c ? CSA_F32 : CSA_BF16);
-  // D = 512 without a split over keys (prefill): one workgroup per token,
-  // 16 heads per wave (attn512.hip)
-  if (D == 512 && !f32c && !split && (H == 64 || H == 128) &&
-      attn512_fits((has_kv ? (sparse ? (int64_t)k : batch->max_kv) : 0) + (has_raw ? window : 0)))
-    return launch_attn512(a, kvf, sparse, outm, stream);
+  // D = 512 with 64 or 128 heads: one workgroup per token (or per part of its
+  // keys with split-K), 16 heads per wave (attn512.hip).  Without a split a
+  // token whose keys exceed its capacity takes the general kernel; with a
+  // split the choice must not depend on the batch, so a part longer than
+  // that capacity is refused instead.
+  const int64_t tok_keys = (has_kv ? (sparse ? (int64_t)k : batch->max_kv) : 0) + (has_raw ? window : 0);
+  const bool wide = D == 512 && !f32c && (H == 64 || H == 128);
+  if (wide && split && split_chunk_max(tok_keys, split_keys) > attn512_part_keys(H))
+    return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: split parts of up to %lld keys exceed %d with %d heads",
+                (long long)split_chunk_max(tok_keys, split_keys), attn512_part_keys(H), H);
+  const bool use512 = wide && (split || attn512_fits(tok_keys));
   csa_status st;
-  if (f32c && split) st = launch_split<128, true, CSA_F32, 1>(a, sparse, stream);
+  if (use512) st = launch_attn512(a, kvf, sparse, outm, stream);
+  else if (f32c && split) st = launch_split<128, true, CSA_F32, 1>(a, sparse, stream);
   else if (f32c) st = launch_mode<128, true, CSA_F32, 1>(a, sparse, outm, stream);
   else if (D == 128 && split) st = launch_split<128, false, CSA_BF16, 1>(a, sparse, stream);
   else if (D == 128) st = launch_mode<128, false, CSA_BF16, 1>(a, sparse, outm, stream);
@@ -1011,10 +1005,11 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   else if (split) st = launch_split<512, false, CSA_BF16, 4>(a, sparse, stream);
   else st = launch_mode<512, false, CSA_BF16, 2>(a, sparse, outm, stream);
   if (st != CSA_OK || !split) return st;
-  // combine the split partials of every query row (a fixed split: all of its
-  // parts, the empty ones with lse = -inf)
+  // combine the split partials of every query row: the parts each query
+  // used (ws_cnt), or with a fixed split all of its parts, the empty ones
+  // with lse = -inf
   const size_t rows_total = (size_t)batch->n_q * H;
-  const bool fixed = a.static_keys > 0;
+  const bool fixed = !use512 && a.static_keys > 0;
   return launch_lse_merge(a.ws_o, a.ws_lse, (int64_t)rows_total * D, (int64_t)rows_total,
                           fixed ? static_splits : a.max_splits, fixed ? nullptr : a.ws_cnt, H,
                           (int64_t)rows_total, D, out, out_fmt, lse, stream);

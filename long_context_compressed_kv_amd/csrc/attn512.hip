@@ -4,7 +4,9 @@
 // softmax over the union, key = value, mixed-precision entries (RoPE dims
 // BF16, the rest FP8 with power-of-two block scales, dequantised exactly).
 //
-// Work split.  A workgroup owns one query token and all its heads; wave w
+// Work split.  A workgroup owns one query token and all its heads (with
+// split-K, decode: one part of the token's keys, cut by split_chunk, writing
+// a normalised partial output and its log-sum-exp for the merge); wave w
 // owns heads 16w .. 16w+15 over all 512 dims, so no wave needs another's
 // partial logits.  Keys are streamed in tiles of 32, staged once into LDS as
 // bf16 rows and read by every wave for both products:
@@ -25,6 +27,8 @@
 // straight into LDS two tiles ahead (global_load_lds, one instruction per
 // key, no registers held), and one tile ahead turns them into the bf16 key
 // tile, so only the barrier after that conversion joins the waves.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "common.h"
 #include "merge.h"
@@ -38,15 +42,23 @@ constexpr int kD = 512;
 constexpr int kRowS = kD * 2 + 32;     // LDS stride of a bf16 key row (1 KB + pad)
 constexpr int kTileB = KT * kRowS;     // 33 KB
 constexpr int kUPR = kD / 16;          // staging units (16 dims) per key row
-constexpr int kMaxKeys = 4096;        // keys of a token resolved at once
 
-// LDS layout: two bf16 key tiles, two raw tiles (1 KB per key), their block
-// scales (4 bytes per key), the token's source rows.
-constexpr int kOffRaw = 2 * kTileB;
-constexpr int kOffScale = kOffRaw + 2 * KT * 1024;
-constexpr int kOffRows = kOffScale + 2 * KT * 4;
-constexpr size_t kSmem512 = kOffRows + kMaxKeys * 4;
-static_assert(kSmem512 <= 160 * 1024, "LDS of a workgroup");
+// LDS layout: NB bf16 key tiles, NB raw tiles (1 KB per key), their block
+// scales (4 bytes per key), and the source rows of up to kMax keys of the
+// token.  The double-buffered layout (one barrier per tile) fills a CU; the
+// decode layout (split-K over 64 heads) holds one of each, so two workgroups
+// share a CU and one's waits are covered by the other's work.
+template <bool DEC>
+struct Lay {
+  static constexpr int NB = DEC ? 1 : 2;
+  static constexpr int kMax = DEC ? 2048 : 4096;
+  static constexpr int raw = NB * kTileB;
+  static constexpr int scale = raw + NB * KT * 1024;
+  static constexpr int rows = scale + NB * KT * 4;
+  static constexpr size_t smem = rows + (size_t)kMax * 4;
+};
+static_assert(Lay<false>::smem <= 160 * 1024, "LDS of a workgroup");
+static_assert(2 * Lay<true>::smem <= 160 * 1024, "two decode workgroups per CU");
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
 
@@ -73,17 +85,18 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt %0" :: "n"((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8)) : "memory");
 }
 
-template <int KVF, bool SPARSE, int OUTM, int NW>
-__global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
+template <int KVF, bool SPARSE, int OUTM, int NW, bool DEC>
+__device__ __forceinline__ void attn512_body(const AttnArgs& a) {
+  using L = Lay<DEC>;
   constexpr int KPW = KT / NW;                    // keys of a tile per wave
   constexpr bool FP8 = KVF == CSA_FP8_MIXED;
   constexpr int NDMA = KPW + (FP8 ? 1 : 0);       // copies per wave and tile
   constexpr int UPL = KPW * kUPR / 64;            // conversion units per lane
   extern __shared__ __align__(16) unsigned char smem[];
-  lds_u8* kb = (lds_u8*)smem;                     // two key tiles
-  lds_u8* raw = (lds_u8*)(smem + kOffRaw);        // two raw tiles
-  lds_u8* rsc = (lds_u8*)(smem + kOffScale);      // their block scales
-  int* krow = reinterpret_cast<int*>(smem + kOffRows);
+  lds_u8* kb = (lds_u8*)smem;                     // key tiles
+  lds_u8* raw = (lds_u8*)(smem + L::raw);         // raw tiles
+  lds_u8* rsc = (lds_u8*)(smem + L::scale);       // their block scales
+  int* krow = reinterpret_cast<int*>(smem + L::rows);
   const uint32_t lds0 = (uint32_t)(uintptr_t)kb;  // LDS address of the layout
 
   const int tid = threadIdx.x;
@@ -91,19 +104,37 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane & 15, lg = lane >> 4;
 
-  const int64_t q = blockIdx.x;                   // one token per workgroup
+  // one token per workgroup, or with split-K (partial outputs) one part of a
+  // token: workgroup x takes part x % max_splits of token x / max_splits
+  constexpr bool SPLIT = OUTM == 2;
+  const int64_t q = SPLIT ? (int64_t)(blockIdx.x / (unsigned)a.max_splits) : (int64_t)blockIdx.x;
+  const int split = SPLIT ? (int)(blockIdx.x - (unsigned)q * (unsigned)a.max_splits) : 0;
   const int head = wave * 16 + hl;
   const int64_t qrow = q * a.H + head;            // row of the q / out tensors
 
   // queries: B operand of step s (dims 32s .. 32s+31): this lane's 8 dims
   bf16x8_t qreg[16];
-  {
+  auto load_q = [&]() {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * kD + 8 * lg;
 #pragma unroll
     for (int s = 0; s < 16; ++s)
       qreg[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
-  }
+  };
+  // (without a split the loads overlap the geometry's chain of loads; a split
+  // workgroup first learns whether its part exists)
+  if constexpr (!SPLIT) load_q();
   Geo g = make_geo<SPARSE>(a, q);
+  if constexpr (SPLIT) {
+    // parts from the token's own key count (split_chunk): the same whatever
+    // the rest of the batch
+    const int parts = split_parts(g.nkeys, a.split_keys);
+    if (split >= parts) return;                   // (uniform: before any barrier)
+    const int chunk = (int)split_chunk(g.nkeys, a.split_keys);
+    g.key_lo = split * chunk;
+    g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
+    if (split == 0 && tid == 0) a.ws_cnt[q] = parts;
+    load_q();
+  }
   // the geometry is the same in every lane: kept in scalar registers
   auto uni = [](int64_t v) -> int64_t {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -124,7 +155,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   g.nkeys = __builtin_amdgcn_readfirstlane(g.nkeys);
   g.key_lo = __builtin_amdgcn_readfirstlane(g.key_lo);
   g.key_hi = __builtin_amdgcn_readfirstlane(g.key_hi);
-  const int nk = g.key_hi - g.key_lo;             // at most kMaxKeys (host check)
+  const int nk = g.key_hi - g.key_lo;             // at most L::kMax (host check)
   const int ntiles = (nk + KT - 1) / KT;
 
   // source rows of the token's keys (key_meta's encoding; a key without a
@@ -141,11 +172,13 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   // Source rows an iteration needs, read one iteration ahead with one LDS
   // read per lane: lanes 0..31 the keys of tile t (its mask), lanes 32 ..
   // 32+KPW-1 this wave's keys of tile t+1 (what to convert), lanes 40 ..
-  // 40+KPW-1 those of tile t+2 (what to copy).  Tiles past the last read row 0.
+  // 40+KPW-1 those of tile t+2 (what to copy); one tile earlier each in the
+  // decode layout (convert t, copy t+1).  Tiles past the last read row 0.
+  constexpr int AHEAD = DEC ? 0 : 1;
   auto meta_read = [&](int t) -> int {
     int tile = t, key = lane;
     if (lane >= 32) {
-      tile = lane < 40 ? t + 1 : t + 2;
+      tile = lane < 40 ? t + AHEAD : t + AHEAD + 1;
       key = wave * KPW + (lane & 7);
     }
     const bool ok = tile < ntiles && (lane < 32 || (lane & 7) < KPW) && lane < 48;
@@ -160,13 +193,13 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   // instruction per key (and one for the block scales); rows(j) gives the
   // source row of the wave's key j (uniform), lane l0 + j holds it in lrow
   auto dma_rows = [&](int t, auto rows, int lrow, int l0) {
-    const int buf = t & 1;
+    const int buf = DEC ? 0 : (t & 1);
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
       const int key = wave * KPW + j;
       int row = rows(j);
       row = row == -1 ? dummy : row;
-      const uint32_t dst = lds0 + kOffRaw + (buf * KT + key) * 1024;
+      const uint32_t dst = lds0 + L::raw + (buf * KT + key) * 1024;
       const uint8_t* rbase = row >= 0 ? static_cast<const uint8_t*>(a.kv) + (int64_t)row * 1024
                                       : static_cast<const uint8_t*>(a.raw) + (int64_t)(-2 - row) * 1024;
       const uint8_t* src = rbase + 16 * lane;
@@ -182,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
     if constexpr (FP8) {
       if (lane >= l0 && lane < l0 + KPW) {
         const int64_t r = lrow >= 0 ? lrow : 0;   // window keys copy a scale they never use
-        dma4(lds0 + kOffScale + (buf * KT + wave * KPW) * 4 - 4 * l0, a.kv_scale + r * 4);
+        dma4(lds0 + L::scale + (buf * KT + wave * KPW) * 4 - 4 * l0, a.kv_scale + r * 4);
       }
     }
   };
@@ -193,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   // this wave's keys of tile t from raw tile t % 2 into key tile t % 2
   // rowof(kw): source row of the wave's key kw of tile t (uniform)
   auto convert_rows = [&](int t, auto rowof) {
-    const int buf = t & 1;
+    const int buf = DEC ? 0 : (t & 1);
     lds_u8* tile = kb + buf * kTileB;
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
@@ -371,6 +404,26 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
   };
 
+  if constexpr (DEC) {
+    // ---- decode layout, two barriers per tile: convert tile t, copy tile
+    // t+1 while computing t
+    if (ntiles > 0) {
+      dma_tile(0);
+      wait_vm<0>();
+    }
+    int meta = meta_read(0);
+    for (int t = 0; t < ntiles; ++t) {
+      convert_rows(t, [&](int kw) { return __builtin_amdgcn_readlane(meta, 32 + kw); });
+      lds_barrier();                                // key tile complete, raw tile free
+      if (t + 1 < ntiles)
+        dma_rows(t + 1, [&](int j) { return __builtin_amdgcn_readlane(meta, 40 + j); }, meta, 40);
+      const int meta_next = meta_read(t + 1);
+      compute(t, meta);
+      wait_vm<0>();                                 // this wave's copies of tile t+1 landed
+      lds_barrier();                                // every wave done with the key tile
+      meta = meta_next;
+    }
+  } else {
   // ---- prologue: tile 0 in LDS, tile 1 copying
   if (ntiles > 0) {
     dma_tile(0);
@@ -404,6 +457,7 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
     lds_barrier();
     meta = meta_next;
   }
+  }
 
   // ---- epilogue: normaliser over the 4 lanes of each head
   float l_tot;
@@ -418,7 +472,10 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (head < a.H) {
     const float lse_v = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if (a.lse != nullptr && lg == 0) a.lse[qrow] = lse_v;
+    // split-K: normalised partial output and lse of this part, [split][row]
+    const int64_t prow = SPLIT ? (int64_t)split * (a.n_q * a.H) + qrow : qrow;
+    float* lse_dst = SPLIT ? a.ws_lse : a.lse;
+    if (lse_dst != nullptr && lg == 0) lse_dst[prow] = lse_v;
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
       const int d = db * 16 + 4 * lg;
@@ -430,20 +487,40 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
         uo.y = pack_bf16x2_fast(o2, o3);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + qrow * kD + d) = uo;
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + qrow * kD + d) = make_float4(o0, o1, o2, o3);
+        float* dst = SPLIT ? a.ws_o + prow * kD + d : static_cast<float*>(a.out) + qrow * kD + d;
+        *reinterpret_cast<float4*>(dst) = make_float4(o0, o1, o2, o3);
       }
     }
   }
 }
 
 template <int KVF, bool SPARSE, int OUTM, int NW>
+__global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
+  attn512_body<KVF, SPARSE, OUTM, NW, false>(a);
+}
+
+// decode layout (split-K, 64 heads): registers held to two waves per SIMD,
+// so two workgroups fit a CU
+template <int KVF, bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn512_dec_kernel(AttnArgs a) {
+  attn512_body<KVF, SPARSE, 2, 4, true>(a);
+}
+
+template <int KVF, bool SPARSE, int OUTM, int NW>
 csa_status launch512(const AttnArgs& a, hipStream_t s) {
-  auto kern = attn512_kernel<KVF, SPARSE, OUTM, NW>;
-  const size_t smem = kSmem512;
+  constexpr bool DEC = OUTM == 2 && NW == 4;
+  const void* kern = DEC ? (const void*)attn512_dec_kernel<KVF, SPARSE>
+                         : (const void*)attn512_kernel<KVF, SPARSE, OUTM, NW>;
+  const size_t smem = Lay<DEC>::smem;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay<DEC>::smem);
   if (attr != hipSuccess) return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
-  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_q), dim3(NW * 64), smem, s, a);
+  const int64_t blocks = OUTM == 2 ? a.n_q * a.max_splits : a.n_q;
+  if constexpr (DEC)
+    hipLaunchKernelGGL((attn512_dec_kernel<KVF, SPARSE>), dim3((unsigned)blocks), dim3(256), smem, s, a);
+  else
+    hipLaunchKernelGGL((attn512_kernel<KVF, SPARSE, OUTM, NW>), dim3((unsigned)blocks), dim3(NW * 64), smem, s, a);
   return csa_host::check_launch("csa_sparse_mqa_attn (D = 512)");
 }
 
@@ -458,15 +535,24 @@ csa_status launch512_heads(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// D = 512, bf16 compute, one workgroup per query token (no split over keys).
-bool attn512_fits(int64_t max_keys) { return max_keys <= kMaxKeys; }
+// D = 512, bf16 compute, one workgroup per query token, or per part of a
+// token's keys with split-K (outm 2: partial outputs to the workspace).
+bool attn512_fits(int64_t max_keys) { return max_keys <= Lay<false>::kMax; }
+int attn512_part_keys(int n_heads) { return n_heads == 64 ? Lay<true>::kMax : Lay<false>::kMax; }
 
 csa_status launch_attn512(const AttnArgs& a, int kvf, bool sparse, int outm, hipStream_t s) {
-  if (a.n_q > 0x7fffffff) return csa_host::fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: too many queries");
-  if (kvf == CSA_FP8_MIXED) {
-    if (sparse) return outm ? launch512_heads<CSA_FP8_MIXED, true, 1>(a, s) : launch512_heads<CSA_FP8_MIXED, true, 0>(a, s);
-    return outm ? launch512_heads<CSA_FP8_MIXED, false, 1>(a, s) : launch512_heads<CSA_FP8_MIXED, false, 0>(a, s);
-  }
-  if (sparse) return outm ? launch512_heads<CSA_BF16, true, 1>(a, s) : launch512_heads<CSA_BF16, true, 0>(a, s);
-  return outm ? launch512_heads<CSA_BF16, false, 1>(a, s) : launch512_heads<CSA_BF16, false, 0>(a, s);
+  const int64_t blocks = outm == 2 ? a.n_q * a.max_splits : a.n_q;
+  if (blocks > 0x7fffffff) return csa_host::fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: too many queries");
+  auto by_out = [&](auto kvf_c, auto sparse_c) -> csa_status {
+    constexpr int K = decltype(kvf_c)::value;
+    constexpr bool S = decltype(sparse_c)::value;
+    if (outm == 2) return launch512_heads<K, S, 2>(a, s);
+    return outm ? launch512_heads<K, S, 1>(a, s) : launch512_heads<K, S, 0>(a, s);
+  };
+  using fp8_t = std::integral_constant<int, CSA_FP8_MIXED>;
+  using bf16_t = std::integral_constant<int, CSA_BF16>;
+  using yes = std::true_type;
+  using no = std::false_type;
+  if (kvf == CSA_FP8_MIXED) return sparse ? by_out(fp8_t{}, yes{}) : by_out(fp8_t{}, no{});
+  return sparse ? by_out(bf16_t{}, yes{}) : by_out(bf16_t{}, no{});
 }

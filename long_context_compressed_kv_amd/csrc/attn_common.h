@@ -16,7 +16,40 @@ constexpr int kTokMax = 16;      // query tokens per workgroup (128 rows / 8 hea
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kStale = 8.0f;   // log2 headroom before the running max moves
 constexpr int kMetaSlots = 8;    // ring of per-tile source rows and key masks
-constexpr int kMaxSplits = 256;
+constexpr int kPartsMax = 32;    // split-K parts of one query (see split_chunk)
+
+// Split-K parts of a query with nkeys keys: ceil(nkeys / split_keys), at
+// most kPartsMax, of equal length rounded up to whole tiles (the last part
+// takes the rest).  They depend on the query's own key count alone, so a
+// request's parts (and the bits of its merged result) do not depend on the
+// rest of the batch.  (Each part writes an fp32 partial of every head row, D
+// floats: parts of a few hundred keys keep that below the keys' own bytes.)
+__host__ __device__ inline int64_t split_chunk(int64_t nkeys, int split_keys) {
+  if (nkeys <= 0) return KT;
+  int64_t p = (nkeys + split_keys - 1) / split_keys;
+  if (p > kPartsMax) p = kPartsMax;
+  const int64_t c = (nkeys + p - 1) / p;
+  return (c + KT - 1) / KT * KT;
+}
+__host__ __device__ inline int split_parts(int64_t nkeys, int split_keys) {
+  if (nkeys <= 0) return 1;
+  const int64_t c = split_chunk(nkeys, split_keys);
+  return (int)((nkeys + c - 1) / c);
+}
+// Longest part of any query of at most max_keys keys: split_keys rounded up
+// while ceil(n / split_keys) <= kPartsMax, else ceil(n / kPartsMax) rounded up.
+__host__ __device__ inline int64_t split_chunk_max(int64_t max_keys, int split_keys) {
+  const int64_t a = ((int64_t)split_keys + KT - 1) / KT * KT;
+  const int64_t b = ((max_keys + kPartsMax - 1) / kPartsMax + KT - 1) / KT * KT;
+  return a > b ? a : b;
+}
+// Most parts of any query of at most max_keys keys: a query of n keys has at
+// most min(kPartsMax, ceil(n / split_keys)), which grows with n.
+__host__ __device__ inline int split_parts_max(int64_t max_keys, int split_keys) {
+  int64_t p = (max_keys + split_keys - 1) / split_keys;
+  if (p > kPartsMax) p = kPartsMax;
+  return p < 1 ? 1 : (int)p;
+}
 
 struct AttnArgs {
   const void* q;
@@ -48,7 +81,7 @@ struct AttnArgs {
   int* ws_start;     // [n_q + 1] first work item of each query (split-K)
   int* ws_item_q;    // [n_q * max_splits] query of each work item (split-K)
   int4* ws_geo;      // [n_q][4] geometry record of each query (split-K)
-  int* ws_chunk;     // keys per split chosen by the plan (split-K)
+  int* ws_chunk;     // (unused word of the split-K workspace layout)
   // split-K without a plan (selected keys: every query has at most
   // static_keys): chunk and splits per query fixed by the host, work item
   // i = (query i / static_splits, split i % static_splits); 0 = planned
@@ -279,3 +312,5 @@ csa_status launch_attn512(const csa_attn::AttnArgs& a, int kvf, bool sparse, int
                           hipStream_t stream);
 // Whether a token of at most max_keys keys (entries and window rows) fits it.
 bool attn512_fits(int64_t max_keys);
+// Most keys of one split-K part it takes with n_heads (64 or 128) heads.
+int attn512_part_keys(int n_heads);

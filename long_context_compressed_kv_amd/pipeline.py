@@ -153,7 +153,7 @@ class DecodeLayer:
     ki: Optional[KV] = None
     score_fmt: int = BF16
     out_fmt: int = BF16
-    split_keys: int = 128
+    split_keys: int = 288
     fused: bool = True
     # paged compressed cache: int32 [B, stride] block ids, block_rows entries a block
     kv_block_table: Optional[torch.Tensor] = None

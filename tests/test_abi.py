@@ -209,6 +209,11 @@ def test_attn_validation(lib):
     assert f(q, 64, kv, split=64, ws=FAKE, wsb=need - 1) == 3
     assert f(_t(1, 128, 2 * 16), 16, kv, split=64, ws=FAKE, wsb=need) == UNSUPPORTED
     assert lib.csa_attn_workspace_size(2, 64, 128, 16, 0) == 0
+    # D = 512 with 64 heads split over keys: a part may hold at most 4096 keys
+    q5, kv5 = _t(1, 512, 2 * 64), _t(1, 512, 100)
+    need5 = lib.csa_attn_workspace_size(2, 64, 512, 16, 5000)
+    assert f(q5, 64, kv5, split=5000, ws=FAKE, wsb=need5) == UNSUPPORTED
+    assert b"exceed 2048" in lib.csa_last_error()
 
 
 def test_merge_and_codec_validation(lib):

@@ -212,6 +212,38 @@ def test_attn_decode_split_k(split_keys, kv_fmt, sparse, amp):
     assert np.isfinite(worst) and worst <= 2e-2, worst
 
 
+def test_attn_split_request_without_keys():
+    """Split-K at D = 512: a request with no keys at all (no entries, no
+    window rows) between two that have many: its rows are o = 0 and
+    lse = -inf, the others match the oracle (dense keys, parts of several
+    lengths, the short request's missing parts skipped)."""
+    rng = np.random.default_rng(77)
+    H, D, m, window = 64, 512, 4, 128
+    ctxs = [9000, 2, 700]
+    n_ent = [2250, 0, 175]
+    swa_len = [128, 0, 128]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent if n]
+    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len if s]
+    q = rng.standard_normal((3, H, D)).astype(np.float32)
+    batch = Batch.make([1] * 3, ctxs, kv_counts=n_ent, raw_counts=swa_len,
+                       raw_pos=[c - s + 1 for c, s in zip(ctxs, swa_len)])
+    out = torch.full((3 * H, D), 5.0, device="cuda")
+    lse = torch.zeros(3 * H, device="cuda")
+    print("[attn] split over keys, request without keys", flush=True)
+    ops.sparse_mqa_attn(dev_kv(q.reshape(-1, D), "bf16"), H, dev_kv(np.concatenate(ents), "fp8_mixed"),
+                        None, 0, dev_kv(np.concatenate(swas), "bf16"), window, batch, m, out, F32,
+                        lse, split_keys=96)
+    torch.cuda.synchronize()
+    qv, sc = ref_vals(q, "bf16"), 1 / math.sqrt(D)
+    assert torch.all(out[H:2 * H] == 0)
+    assert torch.all(torch.isneginf(lse[H:2 * H]))
+    for r, (e, s) in ((0, (ents[0], swas[0])), (2, (ents[1], swas[1]))):
+        o, l = ref.attend(qv[r], np.concatenate([ref_vals(e, "fp8_mixed"), ref_vals(s, "bf16")]), sc)
+        sl = slice(r * H, (r + 1) * H)
+        assert np.max(np.abs(to_np(out[sl]) - o)) <= 2e-2
+        assert np.max(np.abs(to_np(lse[sl]) - l)) <= 2e-2
+
+
 def test_attn_window_only_and_empty_rows():
     """No entries and window 0 for some rows: o = 0, lse = -inf."""
     H, D = 32, 128

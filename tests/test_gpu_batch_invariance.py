@@ -1,7 +1,8 @@
 """A request's decode result does not depend on the rest of the batch (page
 wmrh.cn/news/726125, "V4 改进二": the same token gives the same output
 wherever it sits in a batch), on the path the decode workloads run: attention
-split over keys (split_keys > 0) and merged, after the fused indexer + top-k.
+split over keys (the pipeline's split_keys) and merged, after the fused
+indexer + top-k.
 
 The 64 requests of the 4-layer decode workload (contexts log-uniform from 4K
 to 1M) run as one batch in order, as the same batch permuted, and alone; the
@@ -56,7 +57,7 @@ def _run(reqs, ctxs, order, m, k, csa):
                         q=KV(BF16, D, torch.cat([x["q"] for x in sel])),
                         qi=_cat([x["qi"] for x in sel]) if csa else None,
                         ki=_cat([x["ki"] for x in sel]) if csa else None,
-                        score_fmt=BF16, out_fmt=BF16, split_keys=128)
+                        score_fmt=BF16, out_fmt=BF16)
     res = layer.run()
     torch.cuda.synchronize()
     out = res["out"].view(len(order), H, D).clone()
