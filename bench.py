@@ -517,6 +517,74 @@ def score_study():
                       "data": "synthetic, N(0, 1/64) queries and keys", "cases": out}), flush=True)
 
 
+# ------------------------------------------------- projections around the path
+
+# Sizes of the projections (the pages give none): model width 7168, a
+# low-rank query side of rank 1536 into every head's 512-dim entry space, the
+# KV row (512) and the indexer's key (64) from the token, the indexer's
+# queries (4 x 64) from the query rank, and the grouped output projection:
+# 8 groups of heads, 1024 values each, then back to the model width.
+PROJ = {"d_model": 7168, "q_rank": 1536, "groups": 8, "d_group": 1024}
+
+
+def proj_bench(reps=10):
+    """csa_linear and csa_grouped_out_proj at the chunked prefill's shapes
+    (8192 tokens, 128 heads) and the 4-layer decode's (64 requests, 64
+    heads); flop = 2 M N K per product.  torch.matmul (hipBLASLt) on the same
+    bf16 operands is timed beside each plain product for reference."""
+    gen = Gen(20264)
+    dm, rq, G, dg = PROJ["d_model"], PROJ["q_rank"], PROJ["groups"], PROJ["d_group"]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    cases = []
+    for wl, M, H in (("csa_chunk_prefill_s8192_at_1M", 8192, 128), ("mixed_decode_4layer_b64_4K_1M", 64, 64)):
+        D = 512
+        prods = [("q_down", M, rq, dm), ("q_up", M, H * D, rq), ("kv", M, D, dm),
+                 ("indexer_q", M, 4 * 64, rq), ("indexer_k", M, 64, dm)]
+        tot_ms = tot_fl = 0.0
+        for name, m_, n_, k_ in prods:
+            x = gen.normal((m_, k_)).to(torch.bfloat16)
+            w = (0.02 * gen.normal((n_, k_))).to(torch.bfloat16)
+            y = torch.empty(m_, n_, dtype=torch.bfloat16, device="cuda")
+            ms = timed(lambda: ops.linear(x, w, y))
+            ref = timed(lambda: torch.matmul(x, w.t()))
+            fl = 2.0 * m_ * n_ * k_
+            tot_ms += ms
+            tot_fl += fl
+            cases.append({"workload": wl, "product": name, "M": m_, "N": n_, "K": k_, "us": round(ms * 1e3, 2),
+                          "tflops": round(fl / ms / 1e9, 1), "mfma_frac": round(fl / ms / 1e9 / PEAK["bf16"], 4),
+                          "weight_gbs": round(n_ * k_ * 2 / ms / 1e6, 1), "torch_matmul_us": round(ref * 1e3, 2)})
+            log(f"proj {wl} {name} {m_}x{n_}x{k_}: {ms * 1e3:.1f} us, {fl / ms / 1e9:.1f} TFLOP/s "
+                f"(torch.matmul {ref * 1e3:.1f} us)")
+            del x, w, y
+        o = gen.normal((M, H, D)).to(torch.bfloat16)
+        wg = (0.02 * gen.normal((G, dg, (H // G) * D))).to(torch.bfloat16)
+        wo = (0.02 * gen.normal((dm, G * dg))).to(torch.bfloat16)
+        y = torch.empty(M, dm, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(ops.grouped_out_proj_workspace_size(M, G, dg), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: ops.grouped_out_proj(o, H, wg, wo, y, ws))
+        fl = 2.0 * M * (H * D * dg + G * dg * dm)
+        tot_ms += ms
+        tot_fl += fl
+        cases.append({"workload": wl, "product": "grouped_out", "M": M, "heads": H, "us": round(ms * 1e3, 2),
+                      "tflops": round(fl / ms / 1e9, 1), "mfma_frac": round(fl / ms / 1e9 / PEAK["bf16"], 4)})
+        log(f"proj {wl} grouped output: {ms * 1e3:.1f} us, {fl / ms / 1e9:.1f} TFLOP/s")
+        cases.append({"workload": wl, "product": "all", "us": round(tot_ms * 1e3, 2),
+                      "tflops": round(tot_fl / tot_ms / 1e9, 1)})
+    print(json.dumps({"measure": "projections around the path (csa_linear, csa_grouped_out_proj)",
+                      "sizes": PROJ, "data": "synthetic, random weights", "cases": cases}), flush=True)
+
+
 # ------------------------------------------------- decode-time compression
 
 
@@ -587,12 +655,18 @@ def main():
     ap.add_argument("--score-study", action="store_true",
                     help="instead of the benchmark: top-k recall and selection time with "
                          "bf16 / MXFP4 indexer precision against fp32")
+    ap.add_argument("--proj", action="store_true",
+                    help="instead of the benchmark: time the projections around the path")
     ap.add_argument("--kv-append", action="store_true",
                     help="instead of the benchmark: time decode-time compression per call")
     ap.add_argument("--paged", action="store_true",
                     help="decode workloads: compressed entries and indexer keys in a paged "
                          "cache (blocks of 128 raw tokens in a shuffled order)")
     args = ap.parse_args()
+    if args.proj:
+        torch.cuda.init()
+        proj_bench()
+        return
     if args.kv_append:
         torch.cuda.init()
         append_bench()

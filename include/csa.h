@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -469,6 +469,50 @@ csa_status csa_quantize(const csa_tensor* src, const csa_tensor* dst, hipStream_
 csa_status csa_dequantize(const csa_tensor* src, float* dst, hipStream_t stream);
 csa_status csa_mxfp4_to_fp8(const csa_tensor* src, uint8_t* fp8, uint8_t* group_scale,
                             uint8_t* lossless, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Projections around the path.  Page "DeepSeek V4 深度解析", section 2, HCA
+ * paragraph (CSA and HCA both project their outputs in groups to cut
+ * compute); page "wmrh.cn/news/726125", "V4 改进一" (the output side projected
+ * in groups; before it, the MLA passage: a low-rank query side, the key/value
+ * up-projections absorbed into the query and output projections).  The pages
+ * give no sizes: these calls take any that meet the alignment rules below.
+ *
+ * csa_linear: y_b = x_b W_b^T for b < batch (the q, KV, indexer and output
+ *   projections), bf16 operands, fp32 accumulation, y F32 or BF16 (nearest
+ *   even).  Element strides:
+ *     x  bf16 [batch][M][K] at x + b*x_bstride + m*ldx + k
+ *     w  bf16 [batch][N][K] at w + b*w_bstride + n*ldw + k  (weights [out][in])
+ *     y  [batch][M][N]      at y + b*y_bstride + m*ldy + n
+ *   K a positive multiple of 64; ldx, ldw >= K and ldy >= N; x and w 16-byte
+ *   aligned with ldx, ldw, x_bstride, w_bstride multiples of 8; M, N >= 0
+ *   (0: nothing to do); 1 <= batch <= 65535.  Caller-owned device memory; y
+ *   must not overlap x or w.  Errors: CSA_ERR_INVALID_ARGUMENT (null pointer,
+ *   short leading dimension, misalignment), CSA_ERR_UNSUPPORTED (K not a
+ *   multiple of 64, a size beyond 2^31, y format).
+ *
+ * csa_grouped_out_proj: out[n] = W_out . concat_g(W_g . o[n, heads of g]):
+ *     o       bf16 [n_q][n_heads][dim] (the attention outputs)
+ *     w_group bf16 [groups][d_group][(n_heads/groups)*dim]: group g takes
+ *             heads g*n_heads/groups .. (g+1)*n_heads/groups - 1, flattened
+ *             in head order
+ *     w_out   bf16 [d_model][groups*d_group]
+ *     out     [n_q][d_model] F32 or BF16
+ *   The group results are rounded to bf16 (nearest even) into `workspace`
+ *   (caller-owned device memory of csa_grouped_out_proj_workspace_size bytes,
+ *   contents not preserved; calls sharing one must not overlap).  groups must
+ *   divide n_heads; (n_heads/groups)*dim and groups*d_group multiples of 64.
+ *   Errors as csa_linear, and CSA_ERR_WORKSPACE for a missing or short
+ *   workspace.
+ * ------------------------------------------------------------------------- */
+csa_status csa_linear(const void* x, int64_t ldx, int64_t x_bstride, const void* w, int64_t ldw,
+                      int64_t w_bstride, void* y, int32_t y_fmt, int64_t ldy, int64_t y_bstride,
+                      int64_t M, int64_t N, int64_t K, int32_t batch, hipStream_t stream);
+size_t csa_grouped_out_proj_workspace_size(int64_t n_q, int32_t groups, int32_t d_group);
+csa_status csa_grouped_out_proj(const void* o, int64_t n_q, int32_t n_heads, int32_t dim,
+                                int32_t groups, const void* w_group, int32_t d_group,
+                                const void* w_out, int32_t d_model, void* out, int32_t out_fmt,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Introspection (host only).

@@ -13,7 +13,8 @@ EXPORTED = (
     "csa_indexer_topk_workspace_size", "csa_indexer_topk_noalloc",
     "csa_indexer_topk_noalloc_max_bytes", "csa_sparse_mqa_attn",
     "csa_swa_merge", "csa_quantize", "csa_dequantize", "csa_mxfp4_to_fp8",
-    "csa_attn_workspace_size", "csa_abi_version", "csa_status_string", "csa_last_error",
+    "csa_attn_workspace_size", "csa_linear", "csa_grouped_out_proj",
+    "csa_grouped_out_proj_workspace_size", "csa_abi_version", "csa_status_string", "csa_last_error",
 )
 
 
@@ -23,7 +24,7 @@ class CsaTensor(ctypes.Structure):
 
 
 # csa_abi_version() of the library these bindings describe (include/csa.h)
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class CsaBatch(ctypes.Structure):
@@ -71,6 +72,8 @@ def load():
         "csa_quantize": [T, T, P],
         "csa_dequantize": [T, P, P],
         "csa_mxfp4_to_fp8": [T, P, P, P, P],
+        "csa_linear": [P, I64, I64, P, I64, I64, P, I32, I64, I64, I64, I64, I64, I32, P],
+        "csa_grouped_out_proj": [P, I64, I32, I32, I32, P, I32, P, I32, P, I32, P, ctypes.c_size_t, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -82,6 +85,8 @@ def load():
     lib.csa_indexer_topk_workspace_size.argtypes = [I64, I32]
     lib.csa_indexer_topk_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.csa_indexer_topk_noalloc_max_bytes.argtypes = []
+    lib.csa_grouped_out_proj_workspace_size.restype = ctypes.c_size_t
+    lib.csa_grouped_out_proj_workspace_size.argtypes = [I64, I32, I32]
     lib.csa_attn_workspace_size.restype = ctypes.c_size_t
     lib.csa_attn_workspace_size.argtypes = [I64, I32, I32, I64, I32]
     lib.csa_abi_version.restype = ctypes.c_int

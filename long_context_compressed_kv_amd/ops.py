@@ -24,6 +24,15 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _fmt_of(t):
+    """Output format code of a float32 or bfloat16 tensor."""
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError("output must be float32 or bfloat16")
+
+
 def _need_cuda(*ts):
     for t in ts:
         if t is not None:
@@ -341,6 +350,63 @@ def swa_merge(o_a, lse_a, o_b, lse_b, out, out_fmt, lse_out=None):
     check(lib.csa_swa_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), int(o_a.shape[0]),
                             int(o_a.shape[1]), _ptr(out), int(out_fmt), _ptr(lse_out), _stream()),
           "csa_swa_merge")
+    return out
+
+
+def linear(x, w, y):
+    """y = x W^T (the projections around the path): x bf16 [..., M, K],
+    w bf16 [..., N, K] (weights stored [out, in]), y F32 or BF16 [..., M, N];
+    a leading batch dimension (the same on all three, or absent) runs the
+    batch in one launch.  Row strides and batch strides are taken from the
+    tensors (the last dimension must be contiguous)."""
+    if not (x.is_cuda and w.is_cuda and y.is_cuda):
+        raise ValueError("tensors must live on the GPU")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("x and w must be bfloat16")
+    batched = x.dim() == 3
+    if batched != (w.dim() == 3) or batched != (y.dim() == 3):
+        raise ValueError("x, w and y must all be batched or none")
+    if x.stride(-1) != 1 or w.stride(-1) != 1 or y.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    M, K = x.shape[-2], x.shape[-1]
+    N = w.shape[-2]
+    if w.shape[-1] != K or y.shape[-2] != M or y.shape[-1] != N:
+        raise ValueError("shape mismatch")
+    batch = x.shape[0] if batched else 1
+    bs = lambda t: t.stride(0) if batched else 0
+    lib = _lib.load()
+    check(lib.csa_linear(_ptr(x), x.stride(-2), bs(x), _ptr(w), w.stride(-2), bs(w), _ptr(y),
+                         _fmt_of(y), y.stride(-2), bs(y), M, N, K, batch, _stream()), "csa_linear")
+    return y
+
+
+def grouped_out_proj_workspace_size(n_q, groups, d_group):
+    return int(_lib.load().csa_grouped_out_proj_workspace_size(int(n_q), int(groups), int(d_group)))
+
+
+def grouped_out_proj(o, n_heads, w_group, w_out, out, workspace=None):
+    """Grouped output projection of attention outputs o bf16 [n_q*n_heads, D]
+    (or [n_q, n_heads, D]): w_group bf16 [G, d_g, (n_heads/G)*D], w_out bf16
+    [d_model, G*d_g], out F32 or BF16 [n_q, d_model]; `workspace` a uint8
+    device tensor of grouped_out_proj_workspace_size(...) bytes (allocated
+    here when None)."""
+    _need_cuda(o, w_group, w_out, out, workspace)
+    if o.dtype != torch.bfloat16 or w_group.dtype != torch.bfloat16 or w_out.dtype != torch.bfloat16:
+        raise ValueError("o and the weights must be bfloat16")
+    for t in (o, w_group, w_out, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    D = o.shape[-1]
+    n_q = o.numel() // (n_heads * D)
+    G, d_g = w_group.shape[0], w_group.shape[1]
+    d_model = w_out.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(grouped_out_proj_workspace_size(n_q, G, d_g), 1),
+                                dtype=torch.uint8, device=o.device)
+    lib = _lib.load()
+    check(lib.csa_grouped_out_proj(_ptr(o), n_q, int(n_heads), D, G, _ptr(w_group), d_g, _ptr(w_out),
+                                   d_model, _ptr(out), _fmt_of(out), _ptr(workspace),
+                                   workspace.numel(), _stream()), "csa_grouped_out_proj")
     return out
 
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.csa_abi_version() == 4
+    assert lib.csa_abi_version() == 5
     assert lib.csa_status_string(0) == b"ok"
     assert lib.csa_status_string(3) == b"workspace too small"
 
@@ -214,6 +214,31 @@ def test_attn_validation(lib):
     need5 = lib.csa_attn_workspace_size(2, 64, 512, 16, 5000)
     assert f(q5, 64, kv5, split=5000, ws=FAKE, wsb=need5) == UNSUPPORTED
     assert b"exceed 2048" in lib.csa_last_error()
+
+
+def test_projection_validation(lib):
+    """Host checks of csa_linear and csa_grouped_out_proj (no device needed)."""
+    A = ctypes.c_void_p(1 << 20)       # 16-byte aligned stand-in pointers
+    f = lambda M=4, N=4, K=64, ldx=64, ldw=64, ldy=4, fmt=0, batch=1, x=A, sx=0: lib.csa_linear(
+        x, ldx, sx, A, ldw, 0, A, fmt, ldy, 0, M, N, K, batch, None)
+    assert f(K=0) == BAD_ARG
+    assert f(K=96, ldx=96, ldw=96) == UNSUPPORTED          # K not a multiple of 64
+    assert f(fmt=2) == UNSUPPORTED                          # y format
+    assert f(ldx=32) == BAD_ARG                             # short leading dimension
+    assert f(ldy=3) == BAD_ARG
+    assert f(x=ctypes.c_void_p((1 << 20) + 8)) == BAD_ARG   # misaligned x
+    assert f(ldx=68) == BAD_ARG                             # rows not 16-byte aligned
+    assert f(x=None) == BAD_ARG
+    assert f(batch=0) == BAD_ARG
+    assert f(M=0) == 0 and f(N=0, x=None) == 0              # nothing to do
+    g = lambda H=64, D=512, G=8, dg=256, ws=A, wsb=1 << 30: lib.csa_grouped_out_proj(
+        A, 4, H, D, G, A, dg, A, 384, A, 0, ws, wsb, None)
+    assert g(G=6) == BAD_ARG                                # groups must divide the heads
+    assert g(H=8, D=8, G=8) == UNSUPPORTED                  # group inputs not a multiple of 64
+    assert g(dg=36) == UNSUPPORTED                          # 8 * 36 not a multiple of 64
+    assert g(ws=None) == 3
+    assert g(wsb=lib.csa_grouped_out_proj_workspace_size(4, 8, 256) - 1) == 3
+    assert lib.csa_grouped_out_proj_workspace_size(4, 8, 256) >= 4 * 8 * 256 * 2
 
 
 def test_merge_and_codec_validation(lib):
