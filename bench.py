@@ -94,7 +94,7 @@ def attn_pairs_prefill(pos0, T, m, n_ent, window, k=None):
 
 
 class Prefill:
-    def __init__(self, wid, copies=1):
+    def __init__(self, wid, copies=1, fp8_q=False):
         self.wl = wl = synth.WORKLOADS[wid]
         gen = Gen(1000 + wid)
         D, H, T = wl.dim, wl.heads, wl.seq
@@ -105,7 +105,9 @@ class Prefill:
         cache = gen.kv(n_ent, D, wl.kv_fmt)          # rows before pos0/m act as the cached prefix
         raw = gen.kv(hist + T, D, wl.act_fmt)
         z, bias = gen.normal((hist + T,)), gen.normal((wl.w,))
-        q = gen.kv(T * H, D, wl.act_fmt)
+        # (fp8 queries: stored like KV entries, the variant's NoPE logits on
+        # the fp8 matrix cores)
+        q = gen.kv(T * H, D, "fp8_mixed" if fp8_q else wl.act_fmt)
         qi = gen.kv(T * 4, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
         ki = gen.kv(n_ent, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
         self.layer = PrefillLayer(csa=csa, H=H, m=wl.m, w=wl.w, k=wl.k, window=wl.window,
@@ -155,7 +157,7 @@ class Decode:
     """One decode step over one or more layers; `copies` input sets rotated so
     successive steps do not find their data in the last-level cache."""
 
-    def __init__(self, wid, copies=3, paged=False):
+    def __init__(self, wid, copies=3, paged=False, fp8_q=False):
         self.wl = wl = synth.WORKLOADS[wid]
         gen = Gen(2000 + wid)
         perm_gen = torch.Generator().manual_seed(3000 + wid)
@@ -186,7 +188,7 @@ class Decode:
                     table, rows = table.cuda(), sum(nb) * P
                 cache = gen.kv(rows, D, wl.kv_fmt)
                 swa = gen.kv(sum(swa_len), D, "bf16")
-                q = gen.kv(B * H, D, "bf16")
+                q = gen.kv(B * H, D, "fp8_mixed" if fp8_q else "bf16")
                 qi = gen.kv(B * 4, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
                 ki = gen.kv(rows, 64, wl.idx_fmt, synth.INDEXER_STD) if csa else None
                 layers.append(DecodeLayer(csa=csa, H=H, m=m, k=k, window=wl.window, ctx=ctxs,
@@ -655,6 +657,9 @@ def main():
     ap.add_argument("--score-study", action="store_true",
                     help="instead of the benchmark: top-k recall and selection time with "
                          "bf16 / MXFP4 indexer precision against fp32")
+    ap.add_argument("--fp8-q", action="store_true",
+                    help="workloads with 512-dim mixed entries: queries stored like KV entries "
+                         "(fp8 NoPE dims), the attention's NoPE logits on the fp8 matrix cores")
     ap.add_argument("--proj", action="store_true",
                     help="instead of the benchmark: time the projections around the path")
     ap.add_argument("--kv-append", action="store_true",
@@ -696,7 +701,10 @@ def main():
         sys.exit(2)
     torch.cuda.init()
     t0 = time.time()
-    w = Decode(wid, paged=args.paged) if decode else Prefill(wid)
+    if args.fp8_q and (wl.dim != 512 or wl.kv_fmt != "fp8_mixed"):
+        print("--fp8-q applies to the workloads with 512-dim mixed entries", file=sys.stderr)
+        sys.exit(2)
+    w = Decode(wid, paged=args.paged, fp8_q=args.fp8_q) if decode else Prefill(wid, fp8_q=args.fp8_q)
     torch.cuda.synchronize()
     log(f"workload {wl.name}: inputs ready in {time.time() - t0:.1f}s")
 
@@ -777,7 +785,7 @@ def main():
                            "(sum of work / sum of work over own peak)",
                 "kernels": kernels}
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8_q:   # (the oracle leg times the bf16-query path)
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(wid)
     metric = "CSA/HCA layer tokens/s (prefill + decode) at 128K-1M ctx; % HBM/MFMA peak"
@@ -797,6 +805,8 @@ def main():
         line["config"]["graph_replay"] = True
         if args.paged:
             line["config"]["kv_layout"] = "paged: blocks of 128 raw tokens, shuffled"
+    if args.fp8_q:
+        line["config"]["queries"] = "fp8: stored like KV entries, NoPE logits on the fp8 matrix cores"
     print(json.dumps(line), flush=True)
 
 

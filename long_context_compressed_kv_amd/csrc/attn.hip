@@ -886,7 +886,9 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: more than 2^31 entries");
   }
   if (has_raw) {
-    if (!fmt_valid_tensor(raw) || raw->dim != D || raw->fmt != q->fmt)
+    // (window rows are bf16 with fp8 queries)
+    const int raw_fmt = q->fmt == CSA_FP8_MIXED ? (int)CSA_BF16 : (int)q->fmt;
+    if (!fmt_valid_tensor(raw) || raw->dim != D || raw->fmt != raw_fmt)
       return fail(CSA_ERR_INVALID_ARGUMENT, "csa_sparse_mqa_attn: raw must match q's format and dim");
     if (batch->raw_off == nullptr || batch->raw_pos == nullptr)
       return fail(CSA_ERR_INVALID_ARGUMENT, "csa_sparse_mqa_attn: raw given without raw_off/raw_pos");
@@ -907,6 +909,8 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   int static_splits = 0;       // reported by a fixed split-K launch
   a.host_splits = &static_splits;
   a.q = q->data;
+  a.q_scale = static_cast<const uint8_t*>(q->scale);
+  a.q_rope = static_cast<const uint16_t*>(q->rope);
   a.H = H;
   a.n_q = batch->n_q;
   a.kv = has_kv ? kv->data : nullptr;
@@ -936,8 +940,14 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: D must be 128 or 512");
     if (has_kv && kv->fmt == CSA_FP8_MIXED && D != 512)
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: FP8_MIXED kv needs D = 512");
+  } else if (q->fmt == CSA_FP8_MIXED) {
+    // fp8 queries: the 512-dim kernel only, over mixed fp8 entries
+    if (has_kv && kv->fmt != CSA_FP8_MIXED)
+      return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fp8 queries need FP8_MIXED kv");
+    if (H != 64 && H != 128)
+      return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fp8 queries need 64 or 128 heads");
   } else {
-    return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: q must be F32 or BF16");
+    return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: q must be F32, BF16 or FP8_MIXED");
   }
 
   // rows per workgroup: D = 128 packs several tokens into 128 rows (when one
@@ -989,13 +999,17 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   // split the choice must not depend on the batch, so a part longer than
   // that capacity is refused instead.
   const int64_t tok_keys = (has_kv ? (sparse ? (int64_t)k : batch->max_kv) : 0) + (has_raw ? window : 0);
+  const bool q8 = q->fmt == CSA_FP8_MIXED;
   const bool wide = D == 512 && !f32c && (H == 64 || H == 128);
-  if (wide && split && split_chunk_max(tok_keys, split_keys) > attn512_part_keys(H))
+  const int part_cap = q8 ? attn512_part_keys(128) : attn512_part_keys(H);
+  if (wide && split && split_chunk_max(tok_keys, split_keys) > part_cap)
     return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: split parts of up to %lld keys exceed %d with %d heads",
-                (long long)split_chunk_max(tok_keys, split_keys), attn512_part_keys(H), H);
+                (long long)split_chunk_max(tok_keys, split_keys), part_cap, H);
+  if (q8 && !split && !attn512_fits(tok_keys))
+    return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fp8 queries see at most 4096 keys each");
   const bool use512 = wide && (split || attn512_fits(tok_keys));
   csa_status st;
-  if (use512) st = launch_attn512(a, kvf, sparse, outm, stream);
+  if (use512) st = launch_attn512(a, kvf, sparse, outm, q8, stream);
   else if (f32c && split) st = launch_split<128, true, CSA_F32, 1>(a, sparse, stream);
   else if (f32c) st = launch_mode<128, true, CSA_F32, 1>(a, sparse, outm, stream);
   else if (D == 128 && split) st = launch_split<128, false, CSA_BF16, 1>(a, sparse, stream);

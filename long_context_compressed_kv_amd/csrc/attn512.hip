@@ -43,22 +43,32 @@ constexpr int kRowS = kD * 2 + 32;     // LDS stride of a bf16 key row (1 KB + p
 constexpr int kTileB = KT * kRowS;     // 33 KB
 constexpr int kUPR = kD / 16;          // staging units (16 dims) per key row
 
-// LDS layout: NB bf16 key tiles, NB raw tiles (1 KB per key), their block
-// scales (4 bytes per key), and the source rows of up to kMax keys of the
-// token.  The double-buffered layout (one barrier per tile) fills a CU; the
-// decode layout (split-K over 64 heads) holds one of each, so two workgroups
-// share a CU and one's waits are covered by the other's work.
-template <bool DEC>
+// LDS layout: NK bf16 key tiles, NR raw tiles (RS bytes per key), their
+// block scales (4 bytes per key), and the source rows of up to kMax keys of
+// the token.  Three arrangements (MODE):
+//   0  prefill: two key and two raw tiles, one barrier per tile; fills a CU;
+//   1  decode (split-K over 64 heads): one of each, two barriers per tile, so
+//      two workgroups share a CU and one's waits are covered by the other's
+//      work;
+//   2  fp8 queries: the logits read the fp8 codes of a tile's entries from
+//      its raw tile while the key tile (bf16, for the values) is in use, so
+//      one key tile and three raw tiles (copies two tiles ahead), two
+//      barriers per tile; raw rows padded like key rows for the fp8 operand
+//      reads of 16 consecutive rows.
+template <int MODE>
 struct Lay {
-  static constexpr int NB = DEC ? 1 : 2;
-  static constexpr int kMax = DEC ? 2048 : 4096;
-  static constexpr int raw = NB * kTileB;
-  static constexpr int scale = raw + NB * KT * 1024;
-  static constexpr int rows = scale + NB * KT * 4;
+  static constexpr int NK = MODE == 0 ? 2 : 1;
+  static constexpr int NR = MODE == 0 ? 2 : (MODE == 1 ? 1 : 3);
+  static constexpr int RS = MODE == 2 ? kRowS : 1024;
+  static constexpr int kMax = MODE == 1 ? 2048 : 4096;
+  static constexpr int raw = NK * kTileB;
+  static constexpr int scale = raw + NR * KT * RS;
+  static constexpr int rows = scale + NR * KT * 4;
   static constexpr size_t smem = rows + (size_t)kMax * 4;
 };
-static_assert(Lay<false>::smem <= 160 * 1024, "LDS of a workgroup");
-static_assert(2 * Lay<true>::smem <= 160 * 1024, "two decode workgroups per CU");
+static_assert(Lay<0>::smem <= 160 * 1024, "LDS of a workgroup");
+static_assert(2 * Lay<1>::smem <= 160 * 1024, "two decode workgroups per CU");
+static_assert(Lay<2>::smem <= 160 * 1024, "LDS of a workgroup");
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
 
@@ -85,9 +95,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt %0" :: "n"((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8)) : "memory");
 }
 
-template <int KVF, bool SPARSE, int OUTM, int NW, bool DEC>
+template <int KVF, bool SPARSE, int OUTM, int NW, int MODE>
 __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
-  using L = Lay<DEC>;
+  using L = Lay<MODE>;
+  constexpr bool DEC = MODE == 1;
+  constexpr bool Q8 = MODE == 2;                  // fp8 queries (entries fp8 too)
+  static_assert(!Q8 || KVF == CSA_FP8_MIXED, "fp8 queries take fp8 entries");
   constexpr int KPW = KT / NW;                    // keys of a tile per wave
   constexpr bool FP8 = KVF == CSA_FP8_MIXED;
   constexpr int NDMA = KPW + (FP8 ? 1 : 0);       // copies per wave and tile
@@ -112,13 +125,37 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   const int head = wave * 16 + hl;
   const int64_t qrow = q * a.H + head;            // row of the q / out tensors
 
-  // queries: B operand of step s (dims 32s .. 32s+31): this lane's 8 dims
-  bf16x8_t qreg[16];
+  // queries: B operand of step s (dims 32s .. 32s+31): this lane's 8 dims.
+  // fp8 queries: the codes of block b (dims 128b + 32lg .. +31, zero past
+  // dim 447) as the B operand of the fp8 product of block b, the head's four
+  // block scales (byte b), and the RoPE dims 448 + 32s + 8lg .. +7 (s < 2) in
+  // bf16
+  bf16x8_t qreg[Q8 ? 1 : 16];
+  i32x8_t qc[Q8 ? 4 : 1];
+  bf16x8_t qrope[Q8 ? 2 : 1];
+  uint32_t qsc = 0;
   auto load_q = [&]() {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * kD + 8 * lg;
+    if constexpr (Q8) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * 448 + 32 * lg;
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      qreg[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
+      for (int b = 0; b < 4; ++b) {
+        qc[b] = i32x8_t{};
+        if (b < 3 || lg < 2) {
+          const uint4 v0 = *reinterpret_cast<const uint4*>(qp + 128 * b);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(qp + 128 * b + 16);
+          qc[b] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        }
+      }
+      qsc = *reinterpret_cast<const uint32_t*>(a.q_scale + qrow * 4);
+      const uint16_t* rp = a.q_rope + qrow * 64 + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) qrope[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rp + 32 * s));
+    } else {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * kD + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        qreg[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
+    }
   };
   // (without a split the loads overlap the geometry's chain of loads; a split
   // workgroup first learns whether its part exists)
@@ -171,14 +208,18 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
 
   // Source rows an iteration needs, read one iteration ahead with one LDS
   // read per lane: lanes 0..31 the keys of tile t (its mask), lanes 32 ..
-  // 32+KPW-1 this wave's keys of tile t+1 (what to convert), lanes 40 ..
-  // 40+KPW-1 those of tile t+2 (what to copy); one tile earlier each in the
-  // decode layout (convert t, copy t+1).  Tiles past the last read row 0.
-  constexpr int AHEAD = DEC ? 0 : 1;
+  // 32+KPW-1 this wave's keys of the tile it converts (t+1 in the prefill
+  // layout, t in the others), lanes 40 .. 40+KPW-1 those of the tile it
+  // copies (t+2, or t+1 in the decode layout).  Tiles past the last read row 0.
+  constexpr int CONV_AHEAD = MODE == 0 ? 1 : 0;
+  constexpr int COPY_AHEAD = MODE == 1 ? 1 : 2;
+  // key and raw buffers of tile t
+  auto kbuf = [](int t) { return MODE == 0 ? (t & 1) : 0; };
+  auto rbuf = [](int t) { return MODE == 0 ? (t & 1) : (MODE == 1 ? 0 : t % 3); };
   auto meta_read = [&](int t) -> int {
     int tile = t, key = lane;
     if (lane >= 32) {
-      tile = lane < 40 ? t + AHEAD : t + AHEAD + 1;
+      tile = lane < 40 ? t + CONV_AHEAD : t + COPY_AHEAD;
       key = wave * KPW + (lane & 7);
     }
     const bool ok = tile < ntiles && (lane < 32 || (lane & 7) < KPW) && lane < 48;
@@ -189,17 +230,17 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   const uint8_t* f8_src = lane < 28 ? static_cast<const uint8_t*>(a.kv) + 16 * lane
                                     : reinterpret_cast<const uint8_t*>(a.kv_rope) + 16 * (lane - 28);
   const uint32_t f8_stride = lane < 28 ? 448u : 128u;
-  // copies of this wave's keys of tile t into raw tile t % 2, one
+  // copies of this wave's keys of tile t into its raw tile, one
   // instruction per key (and one for the block scales); rows(j) gives the
   // source row of the wave's key j (uniform), lane l0 + j holds it in lrow
   auto dma_rows = [&](int t, auto rows, int lrow, int l0) {
-    const int buf = DEC ? 0 : (t & 1);
+    const int buf = rbuf(t);
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
       const int key = wave * KPW + j;
       int row = rows(j);
       row = row == -1 ? dummy : row;
-      const uint32_t dst = lds0 + L::raw + (buf * KT + key) * 1024;
+      const uint32_t dst = lds0 + L::raw + (buf * KT + key) * L::RS;
       const uint8_t* rbase = row >= 0 ? static_cast<const uint8_t*>(a.kv) + (int64_t)row * 1024
                                       : static_cast<const uint8_t*>(a.raw) + (int64_t)(-2 - row) * 1024;
       const uint8_t* src = rbase + 16 * lane;
@@ -223,16 +264,16 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     const int lrow = lane < KPW ? krow[t * KT + wave * KPW + lane] : 0;
     dma_rows(t, [&](int j) { return __builtin_amdgcn_readfirstlane(krow[t * KT + wave * KPW + j]); }, lrow, 0);
   };
-  // this wave's keys of tile t from raw tile t % 2 into key tile t % 2
+  // this wave's keys of tile t from its raw tile into its key tile
   // rowof(kw): source row of the wave's key kw of tile t (uniform)
   auto convert_rows = [&](int t, auto rowof) {
-    const int buf = DEC ? 0 : (t & 1);
-    lds_u8* tile = kb + buf * kTileB;
+    const int buf = rbuf(t);
+    lds_u8* tile = kb + kbuf(t) * kTileB;
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
       const int v = lane + 64 * i;
       const int key = wave * KPW + (v >> 5), j = v & 31;
-      const lds_u8* src = raw + (buf * KT + key) * 1024;
+      const lds_u8* src = raw + (buf * KT + key) * L::RS;
       int row = (lane >> 5) ? rowof(2 * i + 1) : rowof(2 * i);
       row = row == -1 ? dummy : row;             // as dma_rows copied it
       uint4 x0, x1;
@@ -284,8 +325,15 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   for (int i = 0; i < 32; ++i) acc_o[i] = f4_t{};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  if constexpr (Q8) {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" :: "v"(qreg[s]));
+    for (int b = 0; b < 4; ++b) asm volatile("" :: "v"(qc[b]));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) asm volatile("" :: "v"(qrope[s]));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) asm volatile("" :: "v"(qreg[s]));
+  }
 
   // the read addresses point into the key buffer of the tile being computed
   // (moved to the other buffer after each tile)
@@ -295,31 +343,101 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     // S^T = K Q^T, two 16-key halves; the operands of step s + 2 are read
     // while step s multiplies
     f4_t s0 = f4_t{}, s1 = f4_t{};
-    auto kread = [&](int s, uint4& k0, uint4& k1) {
-      const int sl = s & 3, sh = s >> 2;
-      k0 = lds_read_b128(kptr[sl] + bofs + sh * 256);
-      k1 = lds_read_b128(kptr[sl] + bofs + sh * 256 + 16 * kRowS);
-    };
-    uint4 ka0, ka1, kb0, kb1;
-    kread(0, ka0, ka1);
-    kread(1, kb0, kb1);
+    if constexpr (!Q8) {
+      auto kread = [&](int s, uint4& k0, uint4& k1) {
+        const int sl = s & 3, sh = s >> 2;
+        k0 = lds_read_b128(kptr[sl] + bofs + sh * 256);
+        k1 = lds_read_b128(kptr[sl] + bofs + sh * 256 + 16 * kRowS);
+      };
+      uint4 ka0, ka1, kb0, kb1;
+      kread(0, ka0, ka1);
+      kread(1, kb0, kb1);
+  #pragma unroll
+      for (int s = 0; s < 16; s += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka0), qreg[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka1), qreg[s], s1, 0, 0, 0);
+        if (s + 2 < 16) kread(s + 2, ka0, ka1);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb0), qreg[s + 1], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb1), qreg[s + 1], s1, 0, 0, 0);
+        if (s + 3 < 16) kread(s + 3, kb0, kb1);
+      }
+      // keep two steps of operand reads in flight ahead of the products
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of steps 0, 1
+  #pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS reads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    } else {
+      // fp8 queries.  A tile of entries only: the NoPE dims on the fp8
+      // matrix cores, the keys' codes (row 16 hk + hl, bytes 128 b + 32 lg
+      // .. +31 of block b, zero past byte 447) read from the tile's raw
+      // copy, each product scaled in the instruction by the key's and the
+      // head's power-of-two block scales (exact); the RoPE dims in bf16 from
+      // the key tile.
+      const int rb = rbuf(t);
+      const lds_u8* rt = raw + rb * KT * L::RS;
+      auto rope = [&](f4_t acc, int hk) {
 #pragma unroll
-    for (int s = 0; s < 16; s += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka0), qreg[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka1), qreg[s], s1, 0, 0, 0);
-      if (s + 2 < 16) kread(s + 2, ka0, ka1);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb0), qreg[s + 1], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb1), qreg[s + 1], s1, 0, 0, 0);
-      if (s + 3 < 16) kread(s + 3, kb0, kb1);
-    }
-    // keep two steps of operand reads in flight ahead of the products
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of steps 0, 1
+        for (int s = 0; s < 2; ++s) {
+          const uint4 k = lds_read_b128(kb + (16 * hk + hl) * kRowS + 2 * (448 + 32 * s + 8 * lg));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k), qrope[s], acc, 0, 0, 0);
+        }
+        return acc;
+      };
+      if (g.key_lo + (t + 1) * KT <= g.nE) {
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS reads
+        for (int hk = 0; hk < 2; ++hk) {
+          const lds_u8* rowp = rt + (16 * hk + hl) * L::RS + 32 * lg;
+          const uint32_t ksc =
+              *(const __attribute__((address_space(3))) uint32_t*)(rsc + (rb * KT + 16 * hk + hl) * 4);
+          f4_t acc = f4_t{};
+          auto block = [&](auto bc) {
+            constexpr int b = decltype(bc)::value;
+            i32x8_t ka = i32x8_t{};
+            if (b < 3 || lg < 2) {
+              const uint4 x0 = lds_read_b128(rowp + 128 * b), x1 = lds_read_b128(rowp + 128 * b + 16);
+              ka = i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            }
+            // both operands e4m3 (format 0); opsel picks block b's scale byte
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qc[b], acc, 0, 0, b, (int)ksc, b, (int)qsc);
+          };
+          block(std::integral_constant<int, 0>{});
+          block(std::integral_constant<int, 1>{});
+          block(std::integral_constant<int, 2>{});
+          block(std::integral_constant<int, 3>{});
+          acc = rope(acc, hk);
+          if (hk == 0) s0 = acc;
+          else s1 = acc;
+        }
+      } else {
+        // a window key in the tile (bf16 rows): the NoPE products in bf16,
+        // the query codes converted exactly; contraction slots of step j of
+        // block b hold dims 128 b + 32 lg + 8 j .. +7 in both operands
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float sc = e8m0_to_f32((qsc >> (8 * b)) & 255u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w0 = (uint32_t)qc[b][2 * j], w1 = (uint32_t)qc[b][2 * j + 1];
+            const uint32_t o[4] = {
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0 >> 16, sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1 >> 16, sc, false))};
+            const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+            const int dofs = 2 * (128 * b + 32 * lg + 8 * j);
+            const uint4 k0 = lds_read_b128(kb + hl * kRowS + dofs);
+            const uint4 k1 = lds_read_b128(kb + (16 + hl) * kRowS + dofs);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qb, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qb, s1, 0, 0, 0);
+          }
+        }
+        s0 = rope(s0, 0);
+        s1 = rope(s1, 1);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // mask: key 4 lg + i of half hk is bit 16 hk + 4 lg + i of the tile's word
     float sv[8];
 #pragma unroll
@@ -423,6 +541,31 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
       lds_barrier();                                // every wave done with the key tile
       meta = meta_next;
     }
+  } else if constexpr (Q8) {
+    // ---- fp8 queries, two barriers per tile: convert tile t, copy tile t+2
+    // while computing t (three raw tiles: t's codes are read by the logits)
+    if (ntiles > 0) {
+      dma_tile(0);
+      if (ntiles > 1) {
+        dma_tile(1);
+        wait_vm<NDMA>();
+      } else {
+        wait_vm<0>();
+      }
+    }
+    int meta = meta_read(0);
+    for (int t = 0; t < ntiles; ++t) {
+      convert_rows(t, [&](int kw) { return __builtin_amdgcn_readlane(meta, 32 + kw); });
+      lds_barrier();                                // key tile and every wave's raw tile t complete
+      if (t + 2 < ntiles)                           // (its raw tile held t-1, consumed last tile)
+        dma_rows(t + 2, [&](int j) { return __builtin_amdgcn_readlane(meta, 40 + j); }, meta, 40);
+      const int meta_next = meta_read(t + 1);
+      compute(t, meta);
+      if (t + 2 < ntiles) wait_vm<NDMA>();          // this wave's copies of tile t+1 landed
+      else wait_vm<0>();
+      lds_barrier();                                // every wave done with the key tile
+      meta = meta_next;
+    }
   } else {
   // ---- prologue: tile 0 in LDS, tile 1 copying
   if (ntiles > 0) {
@@ -494,9 +637,9 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   }
 }
 
-template <int KVF, bool SPARSE, int OUTM, int NW>
+template <int KVF, bool SPARSE, int OUTM, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
-  attn512_body<KVF, SPARSE, OUTM, NW, false>(a);
+  attn512_body<KVF, SPARSE, OUTM, NW, MODE>(a);
 }
 
 // decode layout (split-K, 64 heads): registers held to two waves per SIMD,
@@ -504,31 +647,31 @@ __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
 template <int KVF, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn512_dec_kernel(AttnArgs a) {
-  attn512_body<KVF, SPARSE, 2, 4, true>(a);
+  attn512_body<KVF, SPARSE, 2, 4, 1>(a);
 }
 
-template <int KVF, bool SPARSE, int OUTM, int NW>
+template <int KVF, bool SPARSE, int OUTM, int NW, bool Q8>
 csa_status launch512(const AttnArgs& a, hipStream_t s) {
-  constexpr bool DEC = OUTM == 2 && NW == 4;
-  const void* kern = DEC ? (const void*)attn512_dec_kernel<KVF, SPARSE>
-                         : (const void*)attn512_kernel<KVF, SPARSE, OUTM, NW>;
-  const size_t smem = Lay<DEC>::smem;
+  constexpr int MODE = Q8 ? 2 : (OUTM == 2 && NW == 4 ? 1 : 0);
+  const void* kern = MODE == 1 ? (const void*)attn512_dec_kernel<KVF, SPARSE>
+                               : (const void*)attn512_kernel<KVF, SPARSE, OUTM, NW, MODE>;
+  const size_t smem = Lay<MODE>::smem;
   static const hipError_t attr =
-      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay<DEC>::smem);
+      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay<MODE>::smem);
   if (attr != hipSuccess) return csa_host::fail(CSA_ERR_HIP, "csa_sparse_mqa_attn: cannot reserve %zu B of LDS", smem);
   const int64_t blocks = OUTM == 2 ? a.n_q * a.max_splits : a.n_q;
-  if constexpr (DEC)
+  if constexpr (MODE == 1)
     hipLaunchKernelGGL((attn512_dec_kernel<KVF, SPARSE>), dim3((unsigned)blocks), dim3(256), smem, s, a);
   else
-    hipLaunchKernelGGL((attn512_kernel<KVF, SPARSE, OUTM, NW>), dim3((unsigned)blocks), dim3(NW * 64), smem, s, a);
+    hipLaunchKernelGGL((attn512_kernel<KVF, SPARSE, OUTM, NW, MODE>), dim3((unsigned)blocks), dim3(NW * 64), smem, s, a);
   return csa_host::check_launch("csa_sparse_mqa_attn (D = 512)");
 }
 
-template <int KVF, bool SPARSE, int OUTM>
+template <int KVF, bool SPARSE, int OUTM, bool Q8>
 csa_status launch512_heads(const AttnArgs& a, hipStream_t s) {
   switch (a.H / 16) {
-    case 4: return launch512<KVF, SPARSE, OUTM, 4>(a, s);
-    case 8: return launch512<KVF, SPARSE, OUTM, 8>(a, s);
+    case 4: return launch512<KVF, SPARSE, OUTM, 4, Q8>(a, s);
+    case 8: return launch512<KVF, SPARSE, OUTM, 8, Q8>(a, s);
     default: return csa_host::fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: this D = 512 path takes 64 or 128 heads");
   }
 }
@@ -537,22 +680,24 @@ csa_status launch512_heads(const AttnArgs& a, hipStream_t s) {
 
 // D = 512, bf16 compute, one workgroup per query token, or per part of a
 // token's keys with split-K (outm 2: partial outputs to the workspace).
-bool attn512_fits(int64_t max_keys) { return max_keys <= Lay<false>::kMax; }
-int attn512_part_keys(int n_heads) { return n_heads == 64 ? Lay<true>::kMax : Lay<false>::kMax; }
+bool attn512_fits(int64_t max_keys) { return max_keys <= Lay<0>::kMax; }
+int attn512_part_keys(int n_heads) { return n_heads == 64 ? Lay<1>::kMax : Lay<0>::kMax; }
 
-csa_status launch_attn512(const AttnArgs& a, int kvf, bool sparse, int outm, hipStream_t s) {
+csa_status launch_attn512(const AttnArgs& a, int kvf, bool sparse, int outm, bool q8, hipStream_t s) {
   const int64_t blocks = outm == 2 ? a.n_q * a.max_splits : a.n_q;
   if (blocks > 0x7fffffff) return csa_host::fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: too many queries");
-  auto by_out = [&](auto kvf_c, auto sparse_c) -> csa_status {
+  auto by_out = [&](auto kvf_c, auto sparse_c, auto q8_c) -> csa_status {
     constexpr int K = decltype(kvf_c)::value;
     constexpr bool S = decltype(sparse_c)::value;
-    if (outm == 2) return launch512_heads<K, S, 2>(a, s);
-    return outm ? launch512_heads<K, S, 1>(a, s) : launch512_heads<K, S, 0>(a, s);
+    constexpr bool Q = decltype(q8_c)::value;
+    if (outm == 2) return launch512_heads<K, S, 2, Q>(a, s);
+    return outm ? launch512_heads<K, S, 1, Q>(a, s) : launch512_heads<K, S, 0, Q>(a, s);
   };
   using fp8_t = std::integral_constant<int, CSA_FP8_MIXED>;
   using bf16_t = std::integral_constant<int, CSA_BF16>;
   using yes = std::true_type;
   using no = std::false_type;
-  if (kvf == CSA_FP8_MIXED) return sparse ? by_out(fp8_t{}, yes{}) : by_out(fp8_t{}, no{});
-  return sparse ? by_out(bf16_t{}, yes{}) : by_out(bf16_t{}, no{});
+  if (q8) return sparse ? by_out(fp8_t{}, yes{}, yes{}) : by_out(fp8_t{}, no{}, yes{});
+  if (kvf == CSA_FP8_MIXED) return sparse ? by_out(fp8_t{}, yes{}, no{}) : by_out(fp8_t{}, no{}, no{});
+  return sparse ? by_out(bf16_t{}, yes{}, no{}) : by_out(bf16_t{}, no{}, no{});
 }

@@ -52,7 +52,9 @@ __host__ __device__ inline int split_parts_max(int64_t max_keys, int split_keys)
 }
 
 struct AttnArgs {
-  const void* q;
+  const void* q;             // bf16 or fp32 rows; with fp8 queries the e4m3 codes [rows][448]
+  const uint8_t* q_scale;    // fp8 queries: e8m0 block scales [rows][4]
+  const uint16_t* q_rope;    // fp8 queries: bf16 RoPE dims [rows][64]
   int H;
   int64_t n_q;
   // compressed entries
@@ -307,8 +309,10 @@ __device__ __forceinline__ void store_slot(lds_u8* const* lds, int ofs, bool fp8
 }  // namespace csa_attn
 
 // D = 512 attention with 16 heads per wave (attn512.hip): one workgroup per
-// query token; kvf F32 | BF16 | FP8_MIXED entries, outm 0 (fp32) or 1 (bf16).
-csa_status launch_attn512(const csa_attn::AttnArgs& a, int kvf, bool sparse, int outm,
+// query token (or per part of its keys); kvf BF16 | FP8_MIXED entries, outm 0
+// (fp32), 1 (bf16) or 2 (split-K partials); q8: fp8 queries (FP8_MIXED
+// entries), the NoPE logits on the fp8 matrix cores.
+csa_status launch_attn512(const csa_attn::AttnArgs& a, int kvf, bool sparse, int outm, bool q8,
                           hipStream_t stream);
 // Whether a token of at most max_keys keys (entries and window rows) fits it.
 bool attn512_fits(int64_t max_keys);

@@ -200,6 +200,18 @@ def _window_rows(t, window, raw, raw_pos0):
     return np.asarray(raw, np.float64)[pos - raw_pos0]
 
 
+def fp8_query(q):
+    """Query rows as the fp8-Q attention variant sees them (page "DeepSeek V4
+    深度解析", section 2, the mixed-precision paragraph: RoPE dims BF16, the rest
+    FP8; read here for the query side as well): each row is stored like a KV
+    entry, its 448 non-RoPE dims as e4m3 codes with a power-of-two scale per
+    128-dim block and its 64 RoPE dims in bf16, and the logits use the stored
+    values exactly.  q [..., 512] -> float64 values of the same shape."""
+    a = np.asarray(q, np.float32)
+    rows = a.reshape(-1, a.shape[-1])
+    return codecs.dequantize_kv_mixed(*codecs.quantize_kv_mixed(rows)).reshape(a.shape)
+
+
 def attend(q, keys, scale):
     """Shared-KV multi-query attention of one query token.
 

@@ -20,13 +20,16 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def _prefill_case(rng, T, H, D, n_ent, m, k, window, q_fmt, kv_fmt, out_fmt, sparse,
-                  pos0=0, raw_hist=0, amp=1.0):
+                  pos0=0, raw_hist=0, amp=1.0, raw_fmt=None):
+    raw_fmt = raw_fmt or q_fmt
     raw = (amp * rng.standard_normal((raw_hist + T, D))).astype(np.float32)
     ent = (amp * rng.standard_normal((n_ent, D))).astype(np.float32)
     q = (amp * rng.standard_normal((T, H, D))).astype(np.float32)
     raw_pos0 = pos0 - raw_hist
-    qd, kvd, rd = dev_kv(q.reshape(-1, D), q_fmt), dev_kv(ent, kv_fmt), dev_kv(raw, q_fmt)
-    qv, ev, rv = ref_vals(q, q_fmt), ref_vals(ent, kv_fmt), ref_vals(raw, q_fmt)
+    qd, kvd, rd = dev_kv(q.reshape(-1, D), q_fmt), dev_kv(ent, kv_fmt), dev_kv(raw, raw_fmt)
+    # (fp8 queries: the oracle's reading of the stored query, ref.fp8_query)
+    qv = ref.fp8_query(q) if q_fmt == "fp8_mixed" else ref_vals(q, q_fmt)
+    ev, rv = ref_vals(ent, kv_fmt), ref_vals(raw, raw_fmt)
     idx = None
     if sparse:
         idx = np.full((T, k), -1, np.int64)
@@ -121,6 +124,59 @@ def test_attn_chunk_with_history():
     err, lerr = _prefill_case(rng, 40, 128, 512, 260, 4, 64, 128, "bf16", "fp8_mixed", "bf16",
                               True, pos0=1000, raw_hist=128)
     assert err <= 2e-2 and lerr <= 2e-2
+
+
+@pytest.mark.parametrize("H,sparse,k,window,n_ent,T", [
+    (128, True, 100, 128, 400, 20), (64, True, 40, 16, 300, 9), (128, False, 0, 128, 200, 12),
+    (64, False, 0, 28, 90, 7), (128, True, 2, 8, 300, 6)])
+def test_attn_fp8_queries_prefill(H, sparse, k, window, n_ent, T):
+    """fp8 queries (stored like KV entries): the NoPE logits of entry tiles on
+    the fp8 matrix cores, tiles holding window rows in bf16; against the
+    oracle's attention of the stored query values (ref.fp8_query) over the
+    same keys.  Tiles of entries only, of entries and window rows, of window
+    rows only; selected and dense entries; 64 and 128 heads."""
+    rng = np.random.default_rng(H + k + window + n_ent)
+    print(f"[attn] fp8 queries prefill H={H} sparse={sparse} k={k} window={window}", flush=True)
+    err, lerr = _prefill_case(rng, T, H, 512, n_ent, 4, k, window, "fp8_mixed", "fp8_mixed", "bf16",
+                              sparse, pos0=1600, raw_hist=window, raw_fmt="bf16")
+    assert err <= 2e-2 and lerr <= 2e-2, (err, lerr)
+
+
+@pytest.mark.parametrize("H,sparse,split_keys", [(64, True, 288), (64, False, 96), (128, True, 128)])
+def test_attn_fp8_queries_decode_split(H, sparse, split_keys):
+    """fp8 queries at decode, split over keys and merged: ragged contexts,
+    rows shorter than k, against the oracle."""
+    rng = np.random.default_rng(H + split_keys)
+    D, m, k, window = 512, 4, 200, 128
+    ctxs = [3000, 50, 999, 12000, 400]
+    B = len(ctxs)
+    n_ent = [(c + 1) // m for c in ctxs]
+    swa_len = [min(window, c + 1) for c in ctxs]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len]
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    idx = np.full((B, k), -1, np.int64)
+    for r in range(B):
+        cnt = min(k, n_ent[r]) - (5 if r == 2 else 0)
+        idx[r, :cnt] = np.sort(rng.choice(n_ent[r], cnt, replace=False))
+    batch = Batch.make([1] * B, ctxs, kv_counts=n_ent, raw_counts=swa_len,
+                       raw_pos=[c - s + 1 for c, s in zip(ctxs, swa_len)])
+    out = torch.empty(B * H, D, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(B * H, device="cuda")
+    idx_d = torch.from_numpy(idx.astype(np.int32)).cuda() if sparse else None
+    print(f"[attn] fp8 queries decode H={H} sparse={sparse} split={split_keys}", flush=True)
+    ops.sparse_mqa_attn(dev_kv(q.reshape(-1, D), "fp8_mixed"), H, dev_kv(np.concatenate(ents), "fp8_mixed"),
+                        idx_d, k if sparse else 0, dev_kv(np.concatenate(swas), "bf16"), window, batch, m,
+                        out, BF16, lse, split_keys=split_keys)
+    torch.cuda.synchronize()
+    qv, sc = ref.fp8_query(q), 1 / math.sqrt(D)
+    for r in range(B):
+        ev, sv = ref_vals(ents[r], "fp8_mixed"), ref_vals(swas[r], "bf16")
+        ke = ev[idx[r][idx[r] >= 0]] if sparse else ev
+        o, l = ref.attend(qv[r], np.concatenate([ke, sv]), sc)
+        sl = slice(r * H, (r + 1) * H)
+        assert np.max(np.abs(to_np(out[sl]) - o)) <= 2e-2
+        assert np.max(np.abs(to_np(lse[sl]) - l)) <= 2e-2
 
 
 def _decode_case(rng, ctxs, H, D, m, k, window, kv_fmt, amp=1.0):

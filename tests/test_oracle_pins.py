@@ -366,3 +366,44 @@ def test_mixed_cache_store_load_is_exact_view():
     assert np.array_equal(v, codecs.dequantize_kv_mixed(*codecs.quantize_kv_mixed(c.astype(np.float32))))
     assert np.array_equal(ref.load_entries(ref.store_entries(c, "bf16"), "bf16"),
                           codecs.bf16_round(c).astype(np.float64))
+
+
+def test_fp8_query_keeps_representable_rows():
+    """A row whose non-RoPE blocks are e4m3 values times 2^e with each block's
+    maximum exactly 448 * 2^e, and whose RoPE dims are bf16 values, is stored
+    without change (the smallest power-of-two scale is 2^e)."""
+    rng = np.random.default_rng(31)
+    grid = np.array([0.0, 0.015625, 0.5, 1.0, 1.125, 1.5, 3.25, 13.0, 96.0, 240.0, 448.0])
+    q = np.zeros((3, 512))
+    for r in range(3):
+        for b, (lo, hi) in enumerate([(0, 128), (128, 256), (256, 384), (384, 448)]):
+            e = int(rng.integers(-8, 4))
+            v = rng.choice(grid, hi - lo) * rng.choice([-1.0, 1.0], hi - lo)
+            v[int(rng.integers(0, hi - lo))] = 448.0
+            q[r, lo:hi] = v * 2.0 ** e
+        q[r, 448:] = codecs.bf16_round(rng.standard_normal(64))
+    assert np.array_equal(ref.fp8_query(q), q)
+
+
+def test_fp8_query_error_bound_and_rope_in_bf16():
+    """Each non-RoPE value moves by at most half an e4m3 step at its block's
+    scale (2^-4 of the block's power-of-two scale times 2^floor(log2|x/s|),
+    at most 16 * 2^-4 s at the top binade), the RoPE dims are their bf16
+    rounding, and the attention over fp8 queries stays within the logit
+    perturbation the rounding allows."""
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((4, 512)) * 3
+    v = ref.fp8_query(q)
+    q32 = q.astype(np.float32).astype(np.float64)
+    for lo, hi in [(0, 128), (128, 256), (256, 384), (384, 448)]:
+        blk = q32[:, lo:hi]
+        s = 2.0 ** np.ceil(np.log2(np.max(np.abs(blk), axis=1, keepdims=True) / 448.0))
+        step = 2.0 ** np.floor(np.log2(np.maximum(np.abs(blk) / s, 2.0 ** -6))) * 2.0 ** -3
+        assert np.all(np.abs(v[:, lo:hi] - blk) <= step / 2 * s + 1e-300)
+    assert np.array_equal(v[:, 448:], codecs.bf16_round(q[:, 448:]).astype(np.float64))
+    keys = rng.standard_normal((40, 512))
+    sc = 1 / math.sqrt(512)
+    o_a, _ = ref.attend(v[:1], keys, sc)
+    o_b, _ = ref.attend(q32[:1], keys, sc)
+    dl = np.max(np.abs(keys @ (v[0] - q32[0]))) * sc
+    assert np.max(np.abs(o_a - o_b)) <= 2 * dl * np.max(np.abs(keys)) + 1e-12
