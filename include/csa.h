@@ -401,13 +401,22 @@ csa_status csa_indexer_topk_noalloc(const csa_tensor* qi, int32_t n_heads, const
  *   o[q][h] = sum_key softmax(scale * q_h . key) * key,
  *   lse[q][h] = natural log-sum-exp of the scaled logits (optional).
  * A row whose key set is empty gets o = 0 and lse = -inf.
- *   q         rows = n_q*n_heads, dim D (128 | 512), F32 or BF16
+ *   q         rows = n_q*n_heads, dim D (128 | 512), F32 or BF16; or
+ *             FP8_MIXED (fp8 queries, stored like KV entries: the same
+ *             section's mixed-precision paragraph read for the query side;
+ *             D 512, FP8_MIXED kv, BF16 raw, 64 or 128 heads, at most 4096
+ *             keys per query without a split)
  *   kv        entries: F32 (D 128), BF16, or FP8_MIXED (D 512); may be NULL
  *             for a window-only call
- *   raw       window rows, F32 or BF16 (q's format), dim D; may be NULL
+ *   raw       window rows, F32 or BF16 (q's format; BF16 for fp8 queries),
+ *             dim D; may be NULL
  *   compute   F32 q, kv and raw use fp32 matrix cores; otherwise all operands
  *             are bf16 (FP8_MIXED rows dequantised to bf16 exactly) with
- *             fp32 accumulation and bf16 probabilities
+ *             fp32 accumulation and bf16 probabilities.  With fp8 queries
+ *             the logits' non-RoPE products over entries run on the fp8
+ *             matrix cores with both block scales (exact products, fp32
+ *             sums); tiles holding window rows, the RoPE dims and the
+ *             values as above
  *   scale     > 0 (the pages fix none; 1/sqrt(D) is the usual choice)
  *   out       [n_q*n_heads][D] F32 or BF16;  lse float [n_q*n_heads] or NULL
  *   n_heads   8, 16 or a multiple of 32 up to 128 (8 and 16 need a single
