@@ -219,6 +219,18 @@ def test_attn_validation(lib):
     assert b"exceed 2048" in lib.csa_last_error()
 
 
+@pytest.mark.parametrize("max_keys,split_keys", [(1152, 288), (640, 288), (8320, 288), (100000, 128),
+                                                 (31, 32), (1, 1), (4224, 128), (1025, 32)])
+def test_attn_workspace_follows_the_split_rule(lib, max_keys, split_keys):
+    """The split-K workspace holds min(32, ceil(max_keys / split_keys)) parts of
+    fp32 partials and lse per row (the parts rule the header states), plus the
+    per-query bookkeeping."""
+    n_q, H, D = 7, 64, 512
+    parts = min(32, -(-max_keys // split_keys))
+    expect = parts * n_q * H * (D + 1) * 4 + (n_q * (2 + parts) + 2) * 4 + 16 + n_q * 64 + 256
+    assert lib.csa_attn_workspace_size(n_q, H, D, max_keys, split_keys) == expect
+
+
 def test_projection_validation(lib):
     """Host checks of csa_linear and csa_grouped_out_proj (no device needed)."""
     A = ctypes.c_void_p(1 << 20)       # 16-byte aligned stand-in pointers
