@@ -426,9 +426,10 @@ csa_status csa_indexer_topk_noalloc(const csa_tensor* qi, int32_t n_heads, const
  *             window rows) is cut into p = min(32, ceil(n/split_keys))
  *             parts of ceil(n/p) keys rounded up to a multiple of 32 (the
  *             last takes the rest), processed in parallel and merged in
- *             order by log-sum-exp.  The
- *             parts depend on n and split_keys alone, so a request's result
- *             does not depend on the other requests.  With D = 512 a part
+ *             order by log-sum-exp (with D = 512, 64 or 128 heads and a BF16
+ *             out, each part's normalised output is kept in bf16 before the
+ *             merge).  The parts depend on n and split_keys alone, so a
+ *             request's result does not depend on the other requests.  With D = 512 a part
  *             holds at most 2048 keys with 64 heads and 4096 with 128
  *             (CSA_ERR_UNSUPPORTED otherwise).  Needs `workspace` (device
  *             memory, caller-owned, contents not preserved) of at least

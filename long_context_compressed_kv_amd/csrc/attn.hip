@@ -1008,6 +1008,8 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   if (q8 && !split && !attn512_fits(tok_keys))
     return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fp8 queries see at most 4096 keys each");
   const bool use512 = wide && (split || attn512_fits(tok_keys));
+  // the 512-dim kernel keeps split partials in bf16 when the output is bf16
+  a.part_bf16 = use512 && split && out_fmt == CSA_BF16 ? 1 : 0;
   csa_status st;
   if (use512) st = launch_attn512(a, kvf, sparse, outm, q8, stream);
   else if (f32c && split) st = launch_split<128, true, CSA_F32, 1>(a, sparse, stream);
@@ -1026,5 +1028,5 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
   const bool fixed = !use512 && a.static_keys > 0;
   return launch_lse_merge(a.ws_o, a.ws_lse, (int64_t)rows_total * D, (int64_t)rows_total,
                           fixed ? static_splits : a.max_splits, fixed ? nullptr : a.ws_cnt, H,
-                          (int64_t)rows_total, D, out, out_fmt, lse, stream);
+                          (int64_t)rows_total, D, out, out_fmt, lse, a.part_bf16 != 0, stream);
 }

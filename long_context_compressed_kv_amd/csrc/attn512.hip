@@ -624,11 +624,15 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
       const int d = db * 16 + 4 * lg;
       const float o0 = acc_o[db][0] * inv, o1 = acc_o[db][1] * inv;
       const float o2 = acc_o[db][2] * inv, o3 = acc_o[db][3] * inv;
-      if constexpr (OUTM == 1) {
+      // (split-K partials in bf16 when the output is bf16: one more rounding
+      // of each part, half the partial bytes)
+      if (OUTM == 1 || (SPLIT && a.part_bf16 != 0)) {
         uint2 uo;
         uo.x = pack_bf16x2_fast(o0, o1);
         uo.y = pack_bf16x2_fast(o2, o3);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + qrow * kD + d) = uo;
+        uint16_t* dst = SPLIT ? reinterpret_cast<uint16_t*>(a.ws_o) + prow * kD + d
+                              : static_cast<uint16_t*>(a.out) + qrow * kD + d;
+        *reinterpret_cast<uint2*>(dst) = uo;
       } else {
         float* dst = SPLIT ? a.ws_o + prow * kD + d : static_cast<float*>(a.out) + qrow * kD + d;
         *reinterpret_cast<float4*>(dst) = make_float4(o0, o1, o2, o3);

@@ -77,9 +77,10 @@ struct AttnArgs {
   int nrb;           // 32-row blocks per workgroup
   int split_keys;    // 0: one workgroup per token group; else keys per split
   int max_splits;
-  float* ws_o;       // [max_splits][n_q*H][D]
+  float* ws_o;       // [max_splits][n_q*H][D] (bf16 values when part_bf16)
   float* ws_lse;     // [max_splits][n_q*H]
   int* ws_cnt;       // [n_q] splits used per query
+  int part_bf16;     // split-K partial outputs stored as bf16 (a bf16 output)
   int* ws_start;     // [n_q + 1] first work item of each query (split-K)
   int* ws_item_q;    // [n_q * max_splits] query of each work item (split-K)
   int4* ws_geo;      // [n_q][4] geometry record of each query (split-K)

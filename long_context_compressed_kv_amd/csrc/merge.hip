@@ -12,8 +12,8 @@ using namespace csa;
 
 namespace {
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ o0,
+template <bool OUT_BF16, bool PART_BF16>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const void* __restrict__ o0,
                                                         const float* __restrict__ l0,
                                                         int64_t stride_o, int64_t stride_l,
                                                         int nparts, const int* __restrict__ cnt,
@@ -28,8 +28,16 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
     n = cnt[row / rows_per_q];
     n = n < 1 ? 1 : (n > nparts ? nparts : n);
   }
-  auto part_o = [&](int p) {
-    return reinterpret_cast<const float*>(reinterpret_cast<const char*>(o0) + p * stride_o) + row * dim;
+  // part p's values d .. d+3 of this row
+  auto part_o = [&](int p, int d) -> float4 {
+    const char* base = reinterpret_cast<const char*>(o0) + p * stride_o;
+    if constexpr (PART_BF16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + row * dim + d);
+      return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    } else {
+      return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + row * dim + d);
+    }
   };
   // part p's log-sum-exp and weight are held by lane p % 64, slot p / 64
   float lv[4], w[4];
@@ -62,7 +70,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
     for (; p + 4 <= n; p += 4) {
       float4 x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4*>(part_o(p + i) + d);
+      for (int i = 0; i < 4; ++i) x[i] = part_o(p + i, d);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float wp = weight(p + i);
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
       }
     }
     for (; p < n; ++p) {
-      const float4 x = *reinterpret_cast<const float4*>(part_o(p) + d);
+      const float4 x = part_o(p, d);
       const float wp = weight(p);
       add(r0, wp, x.x);
       add(r1, wp, x.y);
@@ -95,30 +103,34 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
 
 }  // namespace
 
-csa_status launch_lse_merge_bytes(const float* o0, const float* l0, int64_t stride_o_bytes,
+csa_status launch_lse_merge_bytes(const void* o0, const float* l0, int64_t stride_o_bytes,
                                   int64_t stride_l_bytes, int nparts, const int* cnt,
                                   int rows_per_q, int64_t rows, int dim, void* out, int out_fmt,
-                                  float* lse_out, hipStream_t stream) {
+                                  float* lse_out, bool part_bf16, hipStream_t stream) {
   const int64_t blocks = (rows + 3) / 4;
   if (blocks > 0x7fffffff || nparts < 1 || nparts > 256)
     return csa_host::fail(CSA_ERR_INVALID_ARGUMENT, "merge: bad row or part count");
-  if (out_fmt == CSA_BF16)
-    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, o0,
-                       l0, stride_o_bytes, stride_l_bytes, nparts, cnt, rows_per_q, rows, dim,
-                       out, lse_out);
-  else
-    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, o0,
-                       l0, stride_o_bytes, stride_l_bytes, nparts, cnt, rows_per_q, rows, dim,
-                       out, lse_out);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, o0, l0, stride_o_bytes,
+                       stride_l_bytes, nparts, cnt, rows_per_q, rows, dim, out, lse_out);
+  };
+  if (out_fmt == CSA_BF16) {
+    if (part_bf16) go(lse_merge_kernel<true, true>);
+    else go(lse_merge_kernel<true, false>);
+  } else {
+    if (part_bf16) go(lse_merge_kernel<false, true>);
+    else go(lse_merge_kernel<false, false>);
+  }
   return csa_host::check_launch("lse merge");
 }
 
-csa_status launch_lse_merge(const float* o0, const float* l0, int64_t stride_o_elems,
+csa_status launch_lse_merge(const void* o0, const float* l0, int64_t stride_o_elems,
                             int64_t stride_l_elems, int nparts, const int* cnt, int rows_per_q,
                             int64_t rows, int dim, void* out, int out_fmt, float* lse_out,
-                            hipStream_t stream) {
-  return launch_lse_merge_bytes(o0, l0, stride_o_elems * 4, stride_l_elems * 4, nparts, cnt,
-                                rows_per_q, rows, dim, out, out_fmt, lse_out, stream);
+                            bool part_bf16, hipStream_t stream) {
+  const int64_t vb = part_bf16 ? 2 : 4;
+  return launch_lse_merge_bytes(o0, l0, stride_o_elems * vb, stride_l_elems * 4, nparts, cnt,
+                                rows_per_q, rows, dim, out, out_fmt, lse_out, part_bf16, stream);
 }
 
 using namespace csa_host;
@@ -138,5 +150,5 @@ extern "C" csa_status csa_swa_merge(const float* o_a, const float* lse_a, const 
   const int64_t so = (int64_t)((intptr_t)o_b - (intptr_t)o_a);
   const int64_t sl = (int64_t)((intptr_t)lse_b - (intptr_t)lse_a);
   return launch_lse_merge_bytes(o_a, lse_a, so, sl, 2, nullptr, 1, rows, dim, out, out_fmt,
-                                lse_out, stream);
+                                lse_out, false, stream);
 }
