@@ -268,6 +268,44 @@ def test_attn_decode_split_k(split_keys, kv_fmt, sparse, amp):
     assert np.isfinite(worst) and worst <= 2e-2, worst
 
 
+@pytest.mark.parametrize("H,sparse,split_keys", [(32, True, 128), (96, False, 160), (32, False, 1)])
+def test_attn_decode_split_other_head_counts(H, sparse, split_keys):
+    """D = 512 split over keys with head counts the 16-heads-per-wave kernel
+    does not take (32, 96: the general kernel with its plan of work items),
+    ragged contexts, against the oracle."""
+    rng = np.random.default_rng(H + split_keys + int(sparse))
+    D, m, k, window = 512, 4, 120, 128
+    ctxs = [2500, 40, 900, 6000]
+    B = len(ctxs)
+    n_ent = [(c + 1) // m for c in ctxs]
+    swa_len = [min(window, c + 1) for c in ctxs]
+    ents = [rng.standard_normal((n, D)).astype(np.float32) for n in n_ent]
+    swas = [rng.standard_normal((s, D)).astype(np.float32) for s in swa_len]
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    idx = np.full((B, k), -1, np.int64)
+    for r in range(B):
+        cnt = min(k, n_ent[r])
+        idx[r, :cnt] = np.sort(rng.choice(n_ent[r], cnt, replace=False))
+    batch = Batch.make([1] * B, ctxs, kv_counts=n_ent, raw_counts=swa_len,
+                       raw_pos=[c - s + 1 for c, s in zip(ctxs, swa_len)])
+    out = torch.empty(B * H, D, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(B * H, device="cuda")
+    idx_d = torch.from_numpy(idx.astype(np.int32)).cuda() if sparse else None
+    print(f"[attn] split, {H} heads, sparse={sparse}, split_keys={split_keys}", flush=True)
+    ops.sparse_mqa_attn(dev_kv(q.reshape(-1, D), "bf16"), H, dev_kv(np.concatenate(ents), "fp8_mixed"),
+                        idx_d, k if sparse else 0, dev_kv(np.concatenate(swas), "bf16"), window, batch, m,
+                        out, BF16, lse, split_keys=split_keys)
+    torch.cuda.synchronize()
+    qv, sc = ref_vals(q, "bf16"), 1 / math.sqrt(D)
+    for r in range(B):
+        ev, sv = ref_vals(ents[r], "fp8_mixed"), ref_vals(swas[r], "bf16")
+        ke = ev[idx[r][idx[r] >= 0]] if sparse else ev
+        o, l = ref.attend(qv[r], np.concatenate([ke, sv]), sc)
+        sl = slice(r * H, (r + 1) * H)
+        assert np.max(np.abs(to_np(out[sl]) - o)) <= 2e-2
+        assert np.max(np.abs(to_np(lse[sl]) - l)) <= 2e-2
+
+
 def test_attn_split_request_without_keys():
     """Split-K at D = 512: a request with no keys at all (no entries, no
     window rows) between two that have many: its rows are o = 0 and
