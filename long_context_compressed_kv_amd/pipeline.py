@@ -153,7 +153,10 @@ class DecodeLayer:
     ki: Optional[KV] = None
     score_fmt: int = BF16
     out_fmt: int = BF16
-    split_keys: int = 288
+    # keys per split-K part: None = a quarter of a CSA query's k + window
+    # (at least 128), 288 for HCA; a layer constant, so a request's parts
+    # depend on its own key count only
+    split_keys: Optional[int] = None
     fused: bool = True
     # paged compressed cache: int32 [B, stride] block ids, block_rows entries a block
     kv_block_table: Optional[torch.Tensor] = None
@@ -171,6 +174,8 @@ class DecodeLayer:
             self.batch = dataclasses.replace(self.batch, kv_block_table=self.kv_block_table,
                                              kv_block_rows=self.kv_block_rows)
         self.ld = max(int(x) for x in self.n_entries)
+        if self.split_keys is None:
+            self.split_keys = max(128, -(-(self.k + self.window) // 4)) if self.csa else 288
 
     def select(self):
         """(scores, or None when fused; idx [B, k])"""
