@@ -404,8 +404,8 @@ csa_status csa_indexer_topk_noalloc(const csa_tensor* qi, int32_t n_heads, const
  *   q         rows = n_q*n_heads, dim D (128 | 512), F32 or BF16; or
  *             FP8_MIXED (fp8 queries, stored like KV entries: the same
  *             section's mixed-precision paragraph read for the query side;
- *             D 512, FP8_MIXED kv, BF16 raw, 64 or 128 heads, at most 4096
- *             keys per query without a split)
+ *             D 512, FP8_MIXED kv (not NULL), BF16 raw, 64 or 128 heads, at
+ *             most 4096 keys per query without a split)
  *   kv        entries: F32 (D 128), BF16, or FP8_MIXED (D 512); may be NULL
  *             for a window-only call
  *   raw       window rows, F32 or BF16 (q's format; BF16 for fp8 queries),

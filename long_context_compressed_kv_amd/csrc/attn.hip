@@ -941,8 +941,9 @@ extern "C" csa_status csa_sparse_mqa_attn(const csa_tensor* q, int32_t n_heads,
     if (has_kv && kv->fmt == CSA_FP8_MIXED && D != 512)
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: FP8_MIXED kv needs D = 512");
   } else if (q->fmt == CSA_FP8_MIXED) {
-    // fp8 queries: the 512-dim kernel only, over mixed fp8 entries
-    if (has_kv && kv->fmt != CSA_FP8_MIXED)
+    // fp8 queries: the 512-dim kernel only, over mixed fp8 entries (their
+    // block scales are read with every tile, so the entries must be given)
+    if (!has_kv || kv->fmt != CSA_FP8_MIXED)
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fp8 queries need FP8_MIXED kv");
     if (H != 64 && H != 128)
       return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_attn: fp8 queries need 64 or 128 heads");

@@ -205,6 +205,7 @@ def test_attn_validation(lib):
     assert f(q, 64, kv, sc=0.0) == BAD_ARG             # scale must be positive
     q8 = _t(2, 512, 2 * 64, scale=FAKE, rope=FAKE)     # fp8 queries
     assert f(q8, 64, _t(1, 512, 100)) == UNSUPPORTED    # need FP8_MIXED entries
+    assert f(q8, 64, None) == UNSUPPORTED                # ... given
     assert f(_t(2, 512, 2 * 32, scale=FAKE, rope=FAKE), 32, _t(2, 512, 100, scale=FAKE, rope=FAKE)) == UNSUPPORTED
     assert f(q, 64, kv, split=64) == 3                 # split-K without workspace
     need = lib.csa_attn_workspace_size(2, 64, 128, 16, 64)
