@@ -306,11 +306,13 @@ def test_attn_decode_split_other_head_counts(H, sparse, split_keys):
         assert np.max(np.abs(to_np(lse[sl]) - l)) <= 2e-2
 
 
-def test_attn_split_request_without_keys():
+@pytest.mark.parametrize("q_fmt", ["bf16", "fp8_mixed"])
+def test_attn_split_request_without_keys(q_fmt):
     """Split-K at D = 512: a request with no keys at all (no entries, no
     window rows) between two that have many: its rows are o = 0 and
     lse = -inf, the others match the oracle (dense keys, parts of several
-    lengths, the short request's missing parts skipped)."""
+    lengths, the short request's missing parts skipped); bf16 and fp8
+    queries."""
     rng = np.random.default_rng(77)
     H, D, m, window = 64, 512, 4, 128
     ctxs = [9000, 2, 700]
@@ -323,12 +325,13 @@ def test_attn_split_request_without_keys():
                        raw_pos=[c - s + 1 for c, s in zip(ctxs, swa_len)])
     out = torch.full((3 * H, D), 5.0, device="cuda")
     lse = torch.zeros(3 * H, device="cuda")
-    print("[attn] split over keys, request without keys", flush=True)
-    ops.sparse_mqa_attn(dev_kv(q.reshape(-1, D), "bf16"), H, dev_kv(np.concatenate(ents), "fp8_mixed"),
+    print(f"[attn] split over keys, request without keys, {q_fmt} queries", flush=True)
+    ops.sparse_mqa_attn(dev_kv(q.reshape(-1, D), q_fmt), H, dev_kv(np.concatenate(ents), "fp8_mixed"),
                         None, 0, dev_kv(np.concatenate(swas), "bf16"), window, batch, m, out, F32,
                         lse, split_keys=96)
     torch.cuda.synchronize()
-    qv, sc = ref_vals(q, "bf16"), 1 / math.sqrt(D)
+    qv = ref.fp8_query(q) if q_fmt == "fp8_mixed" else ref_vals(q, "bf16")
+    sc = 1 / math.sqrt(D)
     assert torch.all(out[H:2 * H] == 0)
     assert torch.all(torch.isneginf(lse[H:2 * H]))
     for r, (e, s) in ((0, (ents[0], swas[0])), (2, (ents[1], swas[1]))):
