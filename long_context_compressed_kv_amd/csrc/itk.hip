@@ -221,8 +221,19 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 // the workgroup's span of the list and the waves copy their candidates out.
 // A query whose row fits the list whole (at most cap entries, tau = 0) takes
 // every visible entry at list slot = entry index instead.
+//
+// Staging: the two queries of a lane's register block g (lanes 0-31 query
+// 2g, lanes 32-63 query 2g + 1) share one area per (wave, g), in the order
+// of their lanes, the upper half's entries tagged in bit 31; a lane's slot is
+// the area's count plus the passing lanes below it, all counts uniform.  An
+// area takes a tile's passes while it holds fewer than kStageSlots, so 64
+// more slots hold any tile's; every lane writes, a lane that does not pass
+// into a slot of its own past the areas (no branch per lane).  Passes that
+// find the area full are counted, not staged, and send both rows to the
+// exact redo.
 constexpr int kGroupTiles = 32;     // tiles per wave: 4096 entries per workgroup
-constexpr int kStageSlots = 64;     // staged candidates per (wave, query)
+constexpr int kStageSlots = 64;     // staged candidates per (wave, register block)
+constexpr int kStageCap = kStageSlots + 64;
 
 // A float below which a score's key cannot reach tau (taken a little low:
 // a score at or above it may still fall short, and is then only an extra
@@ -268,10 +279,11 @@ template <int FMT, bool SBF16, bool PAGED, bool HW>
 __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
   constexpr int QS = 8;                      // query slots of a group
   constexpr int EW = kGroupTiles * 32;       // entries per wave
-  constexpr int NP = kGroupTiles / 2;        // tile pairs per wave
-  // staged candidates: (score bits, entry); the key is formed when copied out
-  __shared__ uint2 stage[kWaves][QS][kStageSlots];
+  // staged candidates: (score bits, entry | upper half << 31); the key is
+  // formed when copied out
+  __shared__ uint2 stage[kWaves][4 * kStageCap + 64];
   __shared__ uint32_t wcnt[kWaves][QS];
+  __shared__ uint32_t wover[kWaves][4];
   __shared__ uint32_t gbase[QS];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, rl = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform over the wave
@@ -322,9 +334,12 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
     }
   }
   any_whole = __any(any_whole);
-  uint32_t cnt[QS];
+  uint32_t cnt[QS];                          // candidates per query (uniform)
 #pragma unroll
   for (int q = 0; q < QS; ++q) cnt[q] = 0;
+  uint32_t ns[4] = {0u, 0u, 0u, 0u};         // passes per register block (uniform)
+  uint32_t st[4] = {0u, 0u, 0u, 0u};         // of them staged (uniform)
+  const uint32_t htag = (uint32_t)half << 31;
 
   // key rows: a tile wholly inside the rows is addressed from a base shared by
   // the wave plus this lane's row offset; a tile crossing the end (or a paged
@@ -344,12 +359,32 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
     }
   };
   // the scores of one tile's product: the lane's four queries against its
-  // entry.  WHOLE: some query of the group takes its row whole
-  auto score_tile = [&](int t, const f32x16_t& acc, auto whole_c) {
+  // entry.  WHOLE: some query of the group takes its row whole; TAIL: some
+  // entry of the tile lies past a row's end (separate code, so that the
+  // other tiles carry no test of it)
+  auto score_tile = [&](int t, const f32x16_t& acc, auto whole_c, auto tail_c) {
     constexpr bool WHOLE = decltype(whole_c)::value;
+    constexpr bool TAIL = decltype(tail_c)::value;
     const int e0 = e_wave + t * 32;          // the tile's first entry
     const int el = e0 + rl;                  // this lane's entry
-    const bool tail = e0 + 32 > n_lo;        // some entry of the tile past a row's end
+    const uint32_t elt = (uint32_t)el | htag;
+    auto stage_g = [&](int g, float sc, float thr) {
+      const bool pass = sc >= thr;
+      const uint64_t m = __ballot(pass);
+      if (m != 0) {                          // (uniform)
+        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+        const uint32_t pclo = __builtin_popcount(mlo), pchi = __builtin_popcount(mhi);
+        if (ns[g] < (uint32_t)kStageSlots) {    // (then every pass is staged so far)
+          const uint32_t slot = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, ns[g]));
+          stage[wave][pass ? g * kStageCap + slot : 4 * kStageCap + lane] =
+              make_uint2(__float_as_uint(sc), elt);
+          st[g] = ns[g] + pclo + pchi;
+        }
+        ns[g] += pclo + pchi;
+        cnt[2 * g] += pclo;
+        cnt[2 * g + 1] += pchi;
+      }
+    };
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float sc;
@@ -360,61 +395,75 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
           a.cand[(qblock + 2 * g + half) * (int64_t)a.cap + el] =
               make_uint2(score_key<SBF16>(sc), (uint32_t)el);
       }
-      uint64_t m = __ballot(sc >= tf[g]);
-      if (tail) m &= __ballot(el < nv[g]);
-      if (m != 0) {
-        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-        const uint32_t pclo = __builtin_popcount(mlo), pchi = __builtin_popcount(mhi);
-        // the lanes of each half count the passing lanes below them in their half
-        const uint32_t mb = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-        const uint32_t slot = (half ? cnt[2 * g + 1] - pclo : cnt[2 * g]) + mb;
-        if (((m >> lane) & 1ull) && slot < (uint32_t)kStageSlots)
-          stage[wave][2 * g + half][slot] = make_uint2(__float_as_uint(sc), (uint32_t)el);
-        cnt[2 * g] += pclo;
-        cnt[2 * g + 1] += pchi;
-      }
+      float thr = tf[g];
+      if constexpr (TAIL) thr = el < nv[g] ? thr : INFINITY;
+      stage_g(g, sc, thr);
     }
   };
   auto tile_live = [&](int t) { return e_wave + t * 32 < n_scan; };
+  // tiles [0, t_full) lie wholly below the group's shortest row, so they need
+  // no row-end test; they are scored in pairs, both products issued before
+  // either is read
+  int t_full = (n_lo - e_wave) / 32;
+  t_full = t_full < 0 ? 0 : (t_full > kGroupTiles ? kGroupTiles : t_full);
+  const int np_full = t_full / 2;
   auto do_pair = [&](int p, const KeyOp<FMT>* k, auto whole_c) {
-    const bool l1 = tile_live(2 * p + 1);
     const f32x16_t acc0 = tile_dots<FMT>(aq, k[0]);
-    f32x16_t acc1 = f32x16_t{};
-    if (l1) acc1 = tile_dots<FMT>(aq, k[1]);
-    score_tile(2 * p, acc0, whole_c);
-    if (l1) score_tile(2 * p + 1, acc1, whole_c);
+    const f32x16_t acc1 = tile_dots<FMT>(aq, k[1]);
+    score_tile(2 * p, acc0, whole_c, std::false_type{});
+    score_tile(2 * p + 1, acc1, whole_c, std::false_type{});
+  };
+  // a tile of those in contiguous rows: no test of the rows' end
+  auto load_full = [&](int t, KeyOp<FMT>& k) {
+    if constexpr (PAGED) {
+      load_tile(t, k);
+    } else {
+      const int64_t r0 = kv_base + e_wave + t * 32;
+      load_key_row<FMT>(kd + r0 * KeyRow<FMT>::B + lrow, a.ki_scale + r0 * KeyRow<FMT>::S + lsrow,
+                        half, k);
+    }
   };
   auto run = [&](auto whole_c) {
-    if (!tile_live(0)) return;
-    KeyOp<FMT> ka[2], kb[2];
-    load_tile(0, ka[0]);
-    load_tile(1, ka[1]);
-    for (int p = 0; p < NP; p += 2) {
-      const bool l1 = p + 1 < NP && tile_live(2 * p + 2);
-      if (l1) {
-        load_tile(2 * p + 2, kb[0]);
-        load_tile(2 * p + 3, kb[1]);
+    if (np_full > 0) {
+      KeyOp<FMT> ka[2], kb[2];
+      load_full(0, ka[0]);
+      load_full(1, ka[1]);
+      for (int p = 0; p < np_full; p += 2) {
+        const bool l1 = p + 1 < np_full;
+        if (l1) {
+          load_full(2 * p + 2, kb[0]);
+          load_full(2 * p + 3, kb[1]);
+        }
+        do_pair(p, ka, whole_c);
+        if (!l1) break;
+        const bool l2 = p + 2 < np_full;
+        if (l2) {
+          load_full(2 * p + 4, ka[0]);
+          load_full(2 * p + 5, ka[1]);
+        }
+        do_pair(p + 1, kb, whole_c);
+        if (!l2) break;
       }
-      do_pair(p, ka, whole_c);
-      if (!l1) break;
-      const bool l2 = p + 2 < NP && tile_live(2 * p + 4);
-      if (l2) {
-        load_tile(2 * p + 4, ka[0]);
-        load_tile(2 * p + 5, ka[1]);
-      }
-      do_pair(p + 1, kb, whole_c);
-      if (!l2) break;
+    }
+    // the wave's other live tiles (at the rows' ends), one at a time
+    for (int t = 2 * np_full; t < kGroupTiles && tile_live(t); ++t) {
+      KeyOp<FMT> kt;
+      load_tile(t, kt);
+      score_tile(t, tile_dots<FMT>(aq, kt), whole_c, std::true_type{});
     }
   };
   if (any_whole) run(std::true_type{});
   else run(std::false_type{});
 
   // the workgroup's span of each query's list: its staged candidates (a
-  // (wave, query) that staged more than it holds sends the row to the exact
-  // redo by a count above cap), or for a row taken whole its visible entries
+  // (wave, register block) that staged more than its area holds sends both
+  // rows to the exact redo by a count above cap), or for a row taken whole
+  // its visible entries
   if (lane == 0) {
 #pragma unroll
     for (int q = 0; q < QS; ++q) wcnt[wave][q] = cnt[q];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) wover[wave][g] = ns[g] != st[g] ? 1u : 0u;
   }
   __syncthreads();
   if (tid < QS && qblock + tid < a.n_q) {
@@ -427,31 +476,37 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
     } else {
       bool over = false;
       for (int w = 0; w < kWaves; ++w) {
-        const uint32_t c = wcnt[w][tid];
-        over = over || c > (uint32_t)kStageSlots;
-        add += c < (uint32_t)kStageSlots ? c : (uint32_t)kStageSlots;
+        over = over || wover[w][tid >> 1] != 0;
+        add += wcnt[w][tid];
       }
       if (over) add += (uint32_t)a.cap + 1u;
     }
     gbase[tid] = add > 0 ? atomicAdd(&a.cnt[qblock + tid], add) : 0u;
   }
   __syncthreads();
+  // each wave copies its areas out, query by query, in staging order
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
     if (qblock + q >= a.n_q) break;
-    const uint32_t c = wcnt[wave][q];
-    if (c == 0) continue;                    // (rows taken whole stage nothing)
-    const uint32_t n = c < (uint32_t)kStageSlots ? c : (uint32_t)kStageSlots;
+    if (cnt[q] == 0) continue;               // (rows taken whole stage nothing)
+    const int g = q >> 1;
+    const uint32_t tag = (uint32_t)(q & 1);
+    const uint32_t n = st[g];
     uint32_t base = gbase[q];
-    for (int w = 0; w < wave; ++w) {
-      const uint32_t cw = wcnt[w][q];
-      base += cw < (uint32_t)kStageSlots ? cw : (uint32_t)kStageSlots;
-    }
+    for (int w = 0; w < wave; ++w) base += wcnt[w][q];
     uint2* list = a.cand + (qblock + q) * (int64_t)a.cap;
-    for (uint32_t i = lane; i < n; i += 64) {
-      const uint32_t slot = base + i;
-      const uint2 c = stage[wave][q][i];
-      if (slot < (uint32_t)a.cap) list[slot] = make_uint2(score_key<SBF16>(__uint_as_float(c.x)), c.y);
+    for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+      const uint32_t i = i0 + lane;
+      const uint2 c = i < n ? stage[wave][g * kStageCap + i] : make_uint2(0u, 0u);
+      const bool mine = i < n && (c.y >> 31) == tag;
+      const uint64_t m = __ballot(mine);
+      if (mine) {
+        const uint32_t slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (slot < (uint32_t)a.cap)
+          list[slot] = make_uint2(score_key<SBF16>(__uint_as_float(c.x)), c.y & 0x7fffffffu);
+      }
+      base += (uint32_t)__builtin_popcountll(m);
     }
   }
 }
