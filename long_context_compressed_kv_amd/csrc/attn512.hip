@@ -157,9 +157,12 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
         qreg[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
     }
   };
-  // (without a split the loads overlap the geometry's chain of loads; a split
-  // workgroup first learns whether its part exists)
-  if constexpr (!SPLIT) load_q();
+  // The loads overlap the geometry's chain of loads.  With a split over
+  // selected keys every token has about k + window keys, so its parts exist
+  // and are loaded for early; with a split over all visible entries most of
+  // the grid's parts of short rows do not, and load nothing.
+  constexpr bool EARLY_Q = !SPLIT || SPARSE;
+  if constexpr (EARLY_Q) load_q();
   Geo g = make_geo<SPARSE>(a, q);
   if constexpr (SPLIT) {
     // parts from the token's own key count (split_chunk): the same whatever
@@ -170,7 +173,7 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     g.key_lo = split * chunk;
     g.key_hi = g.key_lo + chunk < g.nkeys ? g.key_lo + chunk : g.nkeys;
     if (split == 0 && tid == 0) a.ws_cnt[q] = parts;
-    load_q();
+    if constexpr (!EARLY_Q) load_q();
   }
   // the geometry is the same in every lane: kept in scalar registers
   auto uni = [](int64_t v) -> int64_t {
