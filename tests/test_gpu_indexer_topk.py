@@ -120,6 +120,35 @@ def test_fused_long_rows_k1024():
     assert np.array_equal(f, u)
 
 
+@pytest.mark.parametrize("score_fmt", ["bf16", "f32"])
+def test_fused_prefill_groups_many_ties(score_fmt):
+    """Query groups (prefill) over keys drawn from 8 rows: each query's scores
+    take 8 values, so thousands of entries tie at the threshold and pass;
+    the waves' staging areas fill and the rows are redone exactly."""
+    rng = np.random.default_rng(71)
+    m, k, T, pos0 = 4, 256, 40, 200000
+    n_keys = (pos0 + T) // m
+    qi, ki = _inputs(rng, T, n_keys, "bf16", ki_levels=8)
+    batch = Batch.make([T], [pos0], kv_counts=[n_keys])
+    f, u = _both(qi, ki, "bf16", batch, m, k, score_fmt)
+    assert np.array_equal(f, u)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_fused_prefill_groups_crowded_wave(fmt):
+    """Query groups (prefill) whose best entries form one run of 1100 keys:
+    for every query nearly all entries of the waves covering the run pass,
+    more than a staging area holds, so every row takes the exact redo."""
+    rng = np.random.default_rng(72)
+    m, k, T, pos0 = 4, 512, 72, 131072
+    n_keys = (pos0 + T) // m
+    qi, ki = _inputs(rng, T, n_keys, fmt)
+    ki[5000:6100] *= 4.0
+    batch = Batch.make([T], [pos0], kv_counts=[n_keys])
+    f, u = _both(qi, ki, fmt, batch, m, k, "bf16")
+    assert np.array_equal(f, u)
+
+
 def test_fused_matches_oracle():
     """Against the oracle's top-k of its own scores: equal except where a key
     lies within one rounding step of the k-th key."""
