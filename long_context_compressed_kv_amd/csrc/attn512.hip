@@ -582,24 +582,33 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     convert_tile(0);
     lds_barrier();
   }
-  // ---- key loop: one barrier per tile
+  // ---- key loop: one barrier per tile.  The upper half of the waves (one
+  // per SIMD) converts its keys of tile t+1 before computing tile t, the
+  // lower half after, so the two waves of a SIMD are out of phase: one
+  // multiplies while the other converts or runs its softmax.
+  const bool conv_first = wave >= NW / 2;           // (uniform)
   int flip = kTileB;
   int meta = meta_read(0);
   for (int t = 0; t < ntiles; ++t) {
     if (t + 2 < ntiles)                             // raw tile t % 2 was converted last tile
       dma_rows(t + 2, [&](int j) { return __builtin_amdgcn_readlane(meta, 40 + j); }, meta, 40);
     const int meta_next = meta_read(t + 1);
+    // (key tile (t+1) % 2 was last read in the tile before, behind the barrier)
+    auto convert_next = [&]() {
+      if (t + 1 < ntiles) {
+        if (t + 2 < ntiles) wait_vm<NDMA>();        // this wave's copies of tile t+1 landed
+        else wait_vm<0>();
+        convert_rows(t + 1, [&](int kw) { return __builtin_amdgcn_readlane(meta, 32 + kw); });
+      }
+    };
+    if (conv_first) convert_next();
     compute(t, meta);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kptr[i] += flip;
 #pragma unroll
     for (int i = 0; i < 8; ++i) vptr[i] += flip;
     flip = -flip;
-    if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) wait_vm<NDMA>();          // this wave's copies of tile t+1 landed
-      else wait_vm<0>();
-      convert_rows(t + 1, [&](int kw) { return __builtin_amdgcn_readlane(meta, 32 + kw); });
-    }                                               // (key tile (t+1) % 2 was read last tile)
+    if (!conv_first) convert_next();
     lds_barrier();
     meta = meta_next;
   }
