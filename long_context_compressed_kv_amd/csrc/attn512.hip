@@ -590,8 +590,14 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   int flip = kTileB;
   int meta = meta_read(0);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles)                             // raw tile t % 2 was converted last tile
-      dma_rows(t + 2, [&](int j) { return __builtin_amdgcn_readlane(meta, 40 + j); }, meta, 40);
+    // copies of tile t+2 (raw tile t % 2 was converted last tile): the waves
+    // that convert first issue them first, the others after their products
+    // (the wait before each conversion counts them either way)
+    auto dma_next = [&]() {
+      if (t + 2 < ntiles)
+        dma_rows(t + 2, [&](int j) { return __builtin_amdgcn_readlane(meta, 40 + j); }, meta, 40);
+    };
+    if (conv_first) dma_next();
     const int meta_next = meta_read(t + 1);
     // (key tile (t+1) % 2 was last read in the tile before, behind the barrier)
     auto convert_next = [&]() {
@@ -608,7 +614,10 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) vptr[i] += flip;
     flip = -flip;
-    if (!conv_first) convert_next();
+    if (!conv_first) {
+      dma_next();
+      convert_next();
+    }
     lds_barrier();
     meta = meta_next;
   }
