@@ -231,8 +231,8 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 // into a slot of its own past the areas (no branch per lane).  Passes that
 // find the area full are counted, not staged, and send both rows to the
 // exact redo.
-constexpr int kGroupTiles = 32;     // tiles per wave: 4096 entries per workgroup
-constexpr int kStageSlots = 64;     // staged candidates per (wave, register block)
+constexpr int kGroupTiles = 64;     // tiles per wave: 8192 entries per workgroup
+constexpr int kStageSlots = 128;    // staged candidates per (wave, register block)
 constexpr int kStageCap = kStageSlots + 64;
 
 // A float below which a score's key cannot reach tau (taken a little low:
