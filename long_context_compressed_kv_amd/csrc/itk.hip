@@ -996,7 +996,7 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   st = csa_host::check_launch("csa_indexer_topk (filter)");
   if (st != CSA_OK) return st;
   const size_t bm_bytes = (size_t)((max_kv < kBitmapMax ? max_kv : kBitmapMax) + 31) / 32 * 4;
-  // few rows (decode): 16 waves per row; many: 4, so several rows share a CU
+  // few rows (decode): 16 waves per row; many: 8, so several rows share a CU
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1006,7 +1006,7 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   // the list fits one wave's registers): one wave a row, whose barriers cost
   // next to nothing, and four times the rows resident
   if (max_kv <= 1024 && a.qpg > 1) return launch_select<FMT, SBF16, 64, 16>(a, bm_bytes, s);
-  return launch_select<FMT, SBF16, 256>(a, bm_bytes, s);
+  return launch_select<FMT, SBF16, 512>(a, bm_bytes, s);
 }
 
 // candidates kept per query: the thresholds aim at about 3k.  A multiple of

@@ -87,6 +87,9 @@ struct RadixLds {
 template <int KBITS, int NT, typename Visit>
 __device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit visit, uint32_t& remain,
                                        uint32_t* n_equal = nullptr) {
+  // one wave (its histogram is the total), or at least one thread per digit
+  // to sum the waves' histograms
+  static_assert(NT == 64 || (NT >= 256 && NT % 64 == 0), "radix select: 64 or at least 256 threads");
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
