@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
   constexpr int S = SBF16 ? 4096 : 2048;
   constexpr int NRUN = S / kSampleRun;
   constexpr int NW = kSampleThreads / 64;
+  static_assert(NW >= 8, "one wave per query of a group");
   constexpr int STB = SampleTiles<FMT>::STB;
   using skey_t = typename std::conditional<SBF16, uint16_t, uint32_t>::type;
   __shared__ skey_t sk[8][S];
@@ -186,7 +187,10 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
     }
   }
   __syncthreads();
-  for (int ql = 0; ql < nq; ++ql) {
+  // wave ql selects the threshold of query ql (a group holds at most one
+  // query per wave)
+  const int ql = wave;
+  if (ql < nq) {
     const int64_t q = qblock + ql;
     const int64_t n = visible(a, q);
     uint32_t tau = 0;
@@ -195,15 +199,9 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
       int64_t rank = (3 * (int64_t)a.k * ns + n - 1) / n;
       if (rank < 1) rank = 1;
       if (rank > ns) rank = ns;
-      uint32_t rem;
-      tau = radix_select_visit<SBF16 ? 16 : 32, kSampleThreads>(
-          rx, (uint32_t)rank,
-          [&](auto&& f) {
-            for (int i = tid; i < ns; i += kSampleThreads) f((uint32_t)sk[ql][i]);
-          },
-          rem);
+      tau = wave_radix_select<SBF16 ? 16 : 32>(&sk[ql][0], ns, (uint32_t)rank, &rx.hist[wave][0]);
     }
-    if (tid == 0) {
+    if (lane == 0) {
       a.tau[q] = tau;
       a.cnt[q] = 0;
     }

@@ -142,4 +142,56 @@ __device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit vi
   return prefix;
 }
 
+// The same select by one wave alone, over n keys it reads from src (LDS):
+// 8-bit digits, most significant first, over a 256-bin histogram of its own
+// (hist, 256 words of LDS); no barrier of the workgroup.  Returns the
+// rank-th largest key, 1 <= rank <= n.
+template <int KBITS, typename Key>
+__device__ uint32_t wave_radix_select(const Key* src, int n, uint32_t rank, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, remain = rank;
+  for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
+    for (int i = lane; i < n; i += 64) {
+      const uint32_t key = src[i];
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // lane l owns digits 4l..4l+3; suffix counts from the top digit down
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = hist[4 * lane + i];
+    const uint32_t s = c[0] + c[1] + c[2] + c[3];
+    uint32_t x = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_down(x, o);
+      if (lane + o < 64) x += y;
+    }
+    uint32_t acc = x - s, dig = 0, rem = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (acc < remain && remain <= acc + c[i]) {
+        dig = 4 * lane + i;
+        rem = remain - acc;
+        found = true;
+      }
+      acc += c[i];
+    }
+    const uint64_t m = __ballot(found);     // exactly one lane
+    const int fl = __builtin_ctzll(m);
+    prefix |= (uint32_t)__shfl((int)dig, fl) << shift;
+    remain = (uint32_t)__shfl((int)rem, fl);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();        // (the histogram is cleared again next)
+  }
+  return prefix;
+}
+
 }  // namespace csa
