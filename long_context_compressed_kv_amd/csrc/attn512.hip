@@ -307,20 +307,17 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   // K operand of half hk, step s = 4 sh + sl: row 16 hk + hl, logical chunk
   // 4 s + lg.  V^T operand of dim block db = 8 dh + dl, read rho: rows
   // 16 rho + 4 lg + hl / 4, dims 16 db + 4 (hl % 4) .. +3.
-  lds_u8* kptr[4];
-  lds_u8* vptr[8];
+  // (one base each; the reads of step s and block db add constants)
+  lds_u8* kptr0;
+  lds_u8* vptr0;
   {
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) kptr[sl] = kb + hl * kRowS + 16 * (4 * sl + lg);
+    kptr0 = kb + hl * kRowS + 16 * lg;
     const int rv = 4 * lg + (hl >> 2);
-#pragma unroll
-    for (int dl = 0; dl < 8; ++dl) vptr[dl] = kb + rv * kRowS + 32 * dl + 8 * (hl & 3);
+    vptr0 = kb + rv * kRowS + 8 * (hl & 3);
   }
   auto launder = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(kptr[i]));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(vptr[i]));
+    asm volatile("" : "+v"(kptr0));
+    asm volatile("" : "+v"(vptr0));
   };
 
   f4_t acc_o[32];
@@ -340,6 +337,7 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
 
   // the read addresses point into the key buffer of the tile being computed
   // (moved to the other buffer after each tile)
+  constexpr int KD = 3;                          // logit steps of operand reads in flight
   auto compute = [&](int t, int meta) {
     constexpr int bofs = 0;
     launder();
@@ -349,29 +347,26 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     if constexpr (!Q8) {
       auto kread = [&](int s, uint4& k0, uint4& k1) {
         const int sl = s & 3, sh = s >> 2;
-        k0 = lds_read_b128(kptr[sl] + bofs + sh * 256);
-        k1 = lds_read_b128(kptr[sl] + bofs + sh * 256 + 16 * kRowS);
+        k0 = lds_read_b128(kptr0 + 64 * sl + bofs + sh * 256);
+        k1 = lds_read_b128(kptr0 + 64 * sl + bofs + sh * 256 + 16 * kRowS);
       };
-      uint4 ka0, ka1, kb0, kb1;
-      kread(0, ka0, ka1);
-      kread(1, kb0, kb1);
+      // KD steps of operand reads in flight ahead of the products
+      uint4 kr[KD][2];
+#pragma unroll
+      for (int s = 0; s < KD; ++s) kread(s, kr[s][0], kr[s][1]);
   #pragma unroll
-      for (int s = 0; s < 16; s += 2) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka0), qreg[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka1), qreg[s], s1, 0, 0, 0);
-        if (s + 2 < 16) kread(s + 2, ka0, ka1);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb0), qreg[s + 1], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb1), qreg[s + 1], s1, 0, 0, 0);
-        if (s + 3 < 16) kread(s + 3, kb0, kb1);
+      for (int s = 0; s < 16; ++s) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s % KD][0]), qreg[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s % KD][1]), qreg[s], s1, 0, 0, 0);
+        if (s + KD < 16) kread(s + KD, kr[s % KD][0], kr[s % KD][1]);
       }
-      // keep two steps of operand reads in flight ahead of the products
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of steps 0, 1
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KD, 0);      // LDS reads of steps 0 .. KD-1
   #pragma unroll
-      for (int i = 0; i < 14; ++i) {
+      for (int i = 0; i < 16 - KD; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS reads
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KD, 0);
     } else {
       // fp8 queries.  A tile of entries only: the NoPE dims on the fp8
       // matrix cores, the keys' codes (row 16 hk + hl, bytes 128 b + 32 lg
@@ -504,8 +499,8 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     // read while block db multiplies
     auto vread = [&](int db) -> uint4 {
       const int dl = db & 7, dh = db >> 3;
-      const uint2 v0 = lds_read_tr16(vptr[dl] + bofs + dh * 256);
-      const uint2 v1 = lds_read_tr16(vptr[dl] + bofs + dh * 256 + 16 * kRowS);
+      const uint2 v0 = lds_read_tr16(vptr0 + 32 * dl + bofs + dh * 256);
+      const uint2 v1 = lds_read_tr16(vptr0 + 32 * dl + bofs + dh * 256 + 16 * kRowS);
       return make_uint4(v0.x, v0.y, v1.x, v1.y);
     };
     uint4 va = vread(0), vb = vread(1);
@@ -609,10 +604,8 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     };
     if (conv_first) convert_next();
     compute(t, meta);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kptr[i] += flip;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vptr[i] += flip;
+    kptr0 += flip;
+    vptr0 += flip;
     flip = -flip;
     if (!conv_first) {
       dma_next();
