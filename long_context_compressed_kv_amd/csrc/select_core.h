@@ -69,12 +69,11 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return before + x - v;
 }
 
-// LDS of a radix select: one 256-bin histogram per wave, the chosen digit and
-// the rank left inside it.
+// LDS of a radix select: one 256-bin histogram per wave and their sums.
 template <int NT>
 struct RadixLds {
   uint32_t hist[NT / 64][256];
-  uint32_t sel_digit, sel_remain;
+  uint32_t tot[256];
 };
 
 // Radix select (8-bit digits, most significant first) of the rank-th largest
@@ -84,6 +83,13 @@ struct RadixLds {
 // many keys equal to it are needed to reach rank (rank - remain keys are
 // strictly greater) and, if n_equal is given, *n_equal = how many keys equal
 // it.  1 <= rank <= the multiset's size.
+//
+// Per digit: each wave clears and fills its own histogram; after one barrier
+// the threads below 256 sum them into tot; after a second every wave finds
+// the digit from tot by itself (the same in every wave).  A wave's histogram
+// is only read between those two barriers, and tot only after the second and
+// before the next digit's first, so no other barrier is needed, also across
+// calls.
 template <int KBITS, int NT, typename Visit>
 __device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit visit, uint32_t& remain,
                                        uint32_t* n_equal = nullptr) {
@@ -92,52 +98,61 @@ __device__ uint32_t radix_select_visit(RadixLds<NT>& sh, uint32_t rank, Visit vi
   static_assert(NT == 64 || (NT >= 256 && NT % 64 == 0), "radix select: 64 or at least 256 threads");
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int wave = tid >> 6;
   uint32_t prefix = 0;
   remain = rank;
   for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kWaves * 256; i += NT) (&sh.hist[0][0])[i] = 0;
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh.hist[wave][lane + 64 * i] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
     visit([&](uint32_t key) {
       if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
     });
     __syncthreads();
-    if (tid < 256) {          // per-digit totals of the per-wave histograms
-      uint32_t s = 0;
+    if constexpr (kWaves > 1) {
+      if (tid < 256) {          // per-digit totals of the per-wave histograms
+        uint32_t s = 0;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += sh.hist[w][tid];
-      sh.hist[0][tid] = s;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 4l..4l+3; suffix counts from the top digit down
-      uint32_t c[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = sh.hist[0][4 * tid + i];
-      const uint32_t s = c[0] + c[1] + c[2] + c[3];
-      uint32_t x = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(x, o);
-        if (tid + o < 64) x += y;
+        for (int w = 0; w < kWaves; ++w) s += sh.hist[w][tid];
+        sh.tot[tid] = s;
       }
-      uint32_t acc = x - s;                  // keys with a digit above this lane's group
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (acc < remain && remain <= acc + c[i]) {
-          sh.sel_digit = 4 * tid + i;
-          sh.sel_remain = remain - acc;
-        }
-        acc += c[i];
-      }
+      __syncthreads();
     }
-    __syncthreads();
-    prefix |= sh.sel_digit << shift;
-    remain = sh.sel_remain;
+    const uint32_t* tot = kWaves > 1 ? sh.tot : sh.hist[0];
+    // lane l owns digits 4l..4l+3; suffix counts from the top digit down
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = tot[4 * lane + i];
+    const uint32_t s = c[0] + c[1] + c[2] + c[3];
+    uint32_t x = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_down(x, o);
+      if (lane + o < 64) x += y;
+    }
+    uint32_t acc = x - s, dig = 0, rem = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (acc < remain && remain <= acc + c[i]) {
+        dig = 4 * lane + i;
+        rem = remain - acc;
+        found = true;
+      }
+      acc += c[i];
+    }
+    const uint64_t m = __ballot(found);     // exactly one lane
+    const int fl = __builtin_ctzll(m);
+    const uint32_t digit = (uint32_t)__shfl((int)dig, fl);
+    remain = (uint32_t)__shfl((int)rem, fl);
+    prefix |= digit << shift;
     // after the last digit, its bin counts the keys equal to the result
-    if (shift == 0 && n_equal != nullptr) *n_equal = sh.hist[0][sh.sel_digit];
-    __syncthreads();
+    if (shift == 0 && n_equal != nullptr) *n_equal = tot[digit];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();        // (one wave: its histogram is cleared next)
   }
   return prefix;
 }
