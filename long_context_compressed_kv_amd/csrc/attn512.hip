@@ -95,7 +95,9 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt %0" :: "n"((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8)) : "memory");
 }
 
-template <int KVF, bool SPARSE, int OUTM, int NW, int MODE>
+// DS: waves per head group; each keeps the output of 512 / DS of the dims
+// (all of them compute the group's logits and softmax, the same in each)
+template <int KVF, bool SPARSE, int OUTM, int NW, int MODE, int DS = 1>
 __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   using L = Lay<MODE>;
   constexpr bool DEC = MODE == 1;
@@ -122,7 +124,11 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   constexpr bool SPLIT = OUTM == 2;
   const int64_t q = SPLIT ? (int64_t)(blockIdx.x / (unsigned)a.max_splits) : (int64_t)blockIdx.x;
   const int split = SPLIT ? (int)(blockIdx.x - (unsigned)q * (unsigned)a.max_splits) : 0;
-  const int head = wave * 16 + hl;
+  constexpr int NHG = NW / DS;                    // head groups of 16 heads
+  constexpr int DB = 32 / DS;                     // 16-dim output blocks per wave
+  static_assert(DS == 1 || (DS == 2 && MODE == 0), "dims split over the waves of a head group");
+  const int dpart = wave / NHG;                   // (uniform)
+  const int head = (wave - dpart * NHG) * 16 + hl;
   const int64_t qrow = q * a.H + head;            // row of the q / out tensors
 
   // queries: B operand of step s (dims 32s .. 32s+31): this lane's 8 dims.
@@ -313,16 +319,16 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   {
     kptr0 = kb + hl * kRowS + 16 * lg;
     const int rv = 4 * lg + (hl >> 2);
-    vptr0 = kb + rv * kRowS + 8 * (hl & 3);
+    vptr0 = kb + rv * kRowS + 8 * (hl & 3) + 32 * (dpart * DB);   // (this wave's dim blocks)
   }
   auto launder = [&]() {
     asm volatile("" : "+v"(kptr0));
     asm volatile("" : "+v"(vptr0));
   };
 
-  f4_t acc_o[32];
+  f4_t acc_o[DB];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc_o[i] = f4_t{};
+  for (int i = 0; i < DB; ++i) acc_o[i] = f4_t{};
   float m_run = -INFINITY, l_run = 0.0f;
 
   if constexpr (Q8) {
@@ -470,7 +476,7 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
       const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc_o[db][i] *= alpha;
       m_run = m_new;
@@ -505,15 +511,15 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     };
     uint4 va = vread(0), vb = vread(1);
 #pragma unroll
-    for (int db = 0; db < 32; db += 2) {
+    for (int db = 0; db < DB; db += 2) {
       acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc_o[db], 0, 0, 0);
-      if (db + 2 < 32) va = vread(db + 2);
+      if (db + 2 < DB) va = vread(db + 2);
       acc_o[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vb), pb, acc_o[db + 1], 0, 0, 0);
-      if (db + 3 < 32) vb = vread(db + 3);
+      if (db + 3 < DB) vb = vread(db + 3);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);      // LDS reads of blocks 0, 1
 #pragma unroll
-    for (int i = 0; i < 30; ++i) {
+    for (int i = 0; i < DB - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);    // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);    // LDS reads
     }
@@ -632,10 +638,10 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
     // split-K: normalised partial output and lse of this part, [split][row]
     const int64_t prow = SPLIT ? (int64_t)split * (a.n_q * a.H) + qrow : qrow;
     float* lse_dst = SPLIT ? a.ws_lse : a.lse;
-    if (lse_dst != nullptr && lg == 0) lse_dst[prow] = lse_v;
+    if (lse_dst != nullptr && lg == 0 && dpart == 0) lse_dst[prow] = lse_v;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const int d = db * 16 + 4 * lg;
+    for (int db = 0; db < DB; ++db) {
+      const int d = (dpart * DB + db) * 16 + 4 * lg;
       const float o0 = acc_o[db][0] * inv, o1 = acc_o[db][1] * inv;
       const float o2 = acc_o[db][2] * inv, o3 = acc_o[db][3] * inv;
       // (split-K partials in bf16 when the output is bf16: one more rounding
@@ -655,9 +661,9 @@ __device__ __forceinline__ void attn512_body(const AttnArgs& a) {
   }
 }
 
-template <int KVF, bool SPARSE, int OUTM, int NW, int MODE>
+template <int KVF, bool SPARSE, int OUTM, int NW, int MODE, int DS = 1>
 __global__ __launch_bounds__(NW * 64) void attn512_kernel(AttnArgs a) {
-  attn512_body<KVF, SPARSE, OUTM, NW, MODE>(a);
+  attn512_body<KVF, SPARSE, OUTM, NW, MODE, DS>(a);
 }
 
 // decode layout (split-K, 64 heads): registers held to two waves per SIMD,
@@ -670,9 +676,18 @@ void attn512_dec_kernel(AttnArgs a) {
 
 template <int KVF, bool SPARSE, int OUTM, int NW, bool Q8>
 csa_status launch512(const AttnArgs& a, hipStream_t s) {
-  constexpr int MODE = Q8 ? 2 : (OUTM == 2 && NW == 4 ? 1 : 0);
+  // 64 heads split over selected keys (a CSA decode: every token's parts
+  // exist): eight waves, two per head group each keeping half the dims, in
+  // the prefill layout (one workgroup per CU); over all visible entries (HCA)
+  // most of the grid's parts of short rows do not exist, and the decode
+  // layout (two workgroups per CU) keeps the parts that do in one wave of
+  // workgroups
+  constexpr bool DSPL = OUTM == 2 && NW == 4 && !Q8 && SPARSE;
+  constexpr int MODE = Q8 ? 2 : (OUTM == 2 && NW == 4 && !SPARSE ? 1 : 0);
+  constexpr int NWK = DSPL ? 8 : NW;
+  constexpr int DS = DSPL ? 2 : 1;
   const void* kern = MODE == 1 ? (const void*)attn512_dec_kernel<KVF, SPARSE>
-                               : (const void*)attn512_kernel<KVF, SPARSE, OUTM, NW, MODE>;
+                               : (const void*)attn512_kernel<KVF, SPARSE, OUTM, NWK, MODE, DS>;
   const size_t smem = Lay<MODE>::smem;
   static const hipError_t attr =
       hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay<MODE>::smem);
@@ -681,7 +696,7 @@ csa_status launch512(const AttnArgs& a, hipStream_t s) {
   if constexpr (MODE == 1)
     hipLaunchKernelGGL((attn512_dec_kernel<KVF, SPARSE>), dim3((unsigned)blocks), dim3(256), smem, s, a);
   else
-    hipLaunchKernelGGL((attn512_kernel<KVF, SPARSE, OUTM, NW, MODE>), dim3((unsigned)blocks), dim3(NW * 64), smem, s, a);
+    hipLaunchKernelGGL((attn512_kernel<KVF, SPARSE, OUTM, NWK, MODE, DS>), dim3((unsigned)blocks), dim3(NWK * 64), smem, s, a);
   return csa_host::check_launch("csa_sparse_mqa_attn (D = 512)");
 }
 
