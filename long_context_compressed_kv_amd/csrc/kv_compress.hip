@@ -102,8 +102,30 @@ __device__ __forceinline__ void compress_entry(const TIn* __restrict__ x, const 
   const int groups = kThreads / tpr;
   const int g = tid / tpr;
   const int d = (tid - g * tpr) * 2;
+  // (U slots' loads in flight before their sums; a slot of weight 0, whose
+  // row may not exist, reads row 0 and is skipped by a select, so the sums
+  // are those of the slots in order)
+  constexpr int U = 8;
   float a0 = 0.0f, a1 = 0.0f;
-  for (int s = g; s < w; s += groups) {
+  int s = g;
+  if (sum > 0.0f) {                     // (then some slot has a row: x_rows >= 1)
+    for (; s + (U - 1) * groups < w; s += U * groups) {
+      float wsv[U];
+      float2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        wsv[u] = wgt[s + u * groups];
+        const int64_t r = wsv[u] != 0.0f ? p0 + s + u * groups - x_pos0 : 0;
+        v[u] = load2(x + r * dim + d);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a0 = wsv[u] != 0.0f ? fmaf(wsv[u], v[u].x, a0) : a0;
+        a1 = wsv[u] != 0.0f ? fmaf(wsv[u], v[u].y, a1) : a1;
+      }
+    }
+  }
+  for (; s < w; s += groups) {
     const float ws = wgt[s];
     if (ws != 0.0f) {
       const int64_t r = p0 + s - x_pos0;
