@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 // ------------------------------------------------------------------ 2a. filter, query groups
 
 // The query groups of one request (prefill): the sample gave each query a
-// threshold key tau.  A workgroup scores its group against kGroupTiles tiles
-// of 32 entries per wave.  Per lane and register block a score is the ReLU'd
+// threshold key tau.  A workgroup scores its group against GT tiles of 32
+// entries per wave (kGroupTiles, or kGroupTilesShort for short rows).  Per lane and register block a score is the ReLU'd
 // head sum (as the score kernel forms it) compared with a float floor below
 // which no score can reach tau; the few that pass are staged per (wave,
 // query) in LDS with their exact keys, then one atomic per query reserves
@@ -230,6 +230,10 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 // find the area full are counted, not staged, and send both rows to the
 // exact redo.
 constexpr int kGroupTiles = 64;     // tiles per wave: 8192 entries per workgroup
+// rows of at most kShortRows entries: 8 tiles per wave, so that all four
+// waves of a workgroup have entries (1024 per workgroup)
+constexpr int kGroupTilesShort = 8;
+constexpr int64_t kShortRows = 8192;
 constexpr int kStageSlots = 128;    // staged candidates per (wave, register block)
 constexpr int kStageCap = kStageSlots + 64;
 
@@ -273,10 +277,10 @@ __device__ __forceinline__ void load_key_row(const uint8_t* row, const uint8_t* 
 
 // Tiles are scored in pairs: both products are issued before either result
 // is read, so one pair's matrix-core latency overlaps the other's vector work.
-template <int FMT, bool SBF16, bool PAGED, bool HW>
+template <int FMT, bool SBF16, bool PAGED, bool HW, int GT>
 __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
   constexpr int QS = 8;                      // query slots of a group
-  constexpr int EW = kGroupTiles * 32;       // entries per wave
+  constexpr int EW = GT * 32;                // entries per wave (GT tiles)
   // staged candidates: (score bits, entry | upper half << 31); the key is
   // formed when copied out
   __shared__ uint2 stage[kWaves][4 * kStageCap + 64];
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
   // no row-end test; they are scored in pairs, both products issued before
   // either is read
   int t_full = (n_lo - e_wave) / 32;
-  t_full = t_full < 0 ? 0 : (t_full > kGroupTiles ? kGroupTiles : t_full);
+  t_full = t_full < 0 ? 0 : (t_full > GT ? GT : t_full);
   const int np_full = t_full / 2;
   auto do_pair = [&](int p, const KeyOp<FMT>* k, auto whole_c) {
     const f32x16_t acc0 = tile_dots<FMT>(aq, k[0]);
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(256) void itk_group_filter_kernel(ItkArgs a) {
       }
     }
     // the wave's other live tiles (at the rows' ends), one at a time
-    for (int t = 2 * np_full; t < kGroupTiles && tile_live(t); ++t) {
+    for (int t = 2 * np_full; t < GT && tile_live(t); ++t) {
       KeyOp<FMT> kt;
       load_tile(t, kt);
       score_tile(t, tile_dots<FMT>(aq, kt), whole_c, std::true_type{});
@@ -983,13 +987,18 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
     if (paged) hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, true>), fgrid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((itk_filter_kernel<FMT, SBF16, true, false>), fgrid, dim3(256), 0, s, a);
   } else {
-    const int64_t epw = kWaves * kGroupTiles * 32;
-    const dim3 fgrid((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
     const bool hw = a.head_w != nullptr;
-    if (paged && hw) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true, true>), fgrid, dim3(256), 0, s, a);
-    else if (paged) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true, false>), fgrid, dim3(256), 0, s, a);
-    else if (hw) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false, true>), fgrid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false, false>), fgrid, dim3(256), 0, s, a);
+    auto go = [&](auto gt_c) {
+      constexpr int GT = decltype(gt_c)::value;
+      const int64_t epw = kWaves * GT * 32;
+      const dim3 fgrid((unsigned)groups, (unsigned)((max_kv + epw - 1) / epw));
+      if (paged && hw) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true, true, GT>), fgrid, dim3(256), 0, s, a);
+      else if (paged) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, true, false, GT>), fgrid, dim3(256), 0, s, a);
+      else if (hw) hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false, true, GT>), fgrid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((itk_group_filter_kernel<FMT, SBF16, false, false, GT>), fgrid, dim3(256), 0, s, a);
+    };
+    if (max_kv <= kShortRows) go(std::integral_constant<int, kGroupTilesShort>{});
+    else go(std::integral_constant<int, kGroupTiles>{});
   }
   st = csa_host::check_launch("csa_indexer_topk (filter)");
   if (st != CSA_OK) return st;
