@@ -212,11 +212,12 @@ __global__ __launch_bounds__(kSampleThreads) void itk_sample_kernel(ItkArgs a) {
 
 // The query groups of one request (prefill): the sample gave each query a
 // threshold key tau.  A workgroup scores its group against GT tiles of 32
-// entries per wave (kGroupTiles, or kGroupTilesShort for short rows).  Per lane and register block a score is the ReLU'd
-// head sum (as the score kernel forms it) compared with a float floor below
-// which no score can reach tau; the few that pass are staged per (wave,
-// query) in LDS with their exact keys, then one atomic per query reserves
-// the workgroup's span of the list and the waves copy their candidates out.
+// entries per wave (kGroupTiles, or kGroupTilesShort for short rows).  Per
+// lane and register block a score is the ReLU'd head sum (as the score
+// kernel forms it) compared with a float floor below which no score can
+// reach tau; the few that pass are staged per wave in LDS with their exact
+// scores, then one atomic per query reserves the workgroup's span of the
+// list and the waves copy their candidates out.
 // A query whose row fits the list whole (at most cap entries, tau = 0) takes
 // every visible entry at list slot = entry index instead.
 //
