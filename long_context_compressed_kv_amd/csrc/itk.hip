@@ -778,11 +778,16 @@ __device__ uint32_t bitmap_nth(const uint32_t* bm, int nwords, uint32_t n, uint3
   return *found;
 }
 
+// at most this many entries tied at the k-th key are resolved through a
+// short list (more: through the row's bitmap)
+constexpr int kTieList = 64;
 template <int NT>
 struct SelectLds {
   RadixLds<NT> rx;
   uint32_t wsum[NT / 64];
   uint32_t found;
+  uint32_t ntie;
+  uint32_t tie[kTieList];          // the entries tied at the k-th key (few ties)
   uint32_t hcount[kMaxWg];         // streaming: the filter workgroups' counts
   uint32_t hfloor, htot, hover;    // their largest threshold, total, overflow
 };
@@ -808,7 +813,27 @@ __device__ bool select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, i
   // of the entries tied at tau only the need lowest are kept: mark the tied
   // ones, find the need-th set bit of the row, start the bitmap again
   uint32_t iota = 0xffffffffu;
-  if (need < n_eq) {
+  if (need < n_eq && n_eq <= (uint32_t)kTieList) {
+    // few entries tie at tau: their indices into a short list, and the
+    // need-th lowest is the one with need - 1 lower ones (entries are distinct)
+    if (tid == 0) sh.ntie = 0;
+    __syncthreads();
+    visit([&](uint32_t key, uint32_t e) {
+      if (key == tau) {
+        const uint32_t j = atomicAdd(&sh.ntie, 1u);
+        if (j < (uint32_t)kTieList) sh.tie[j] = e;
+      }
+    });
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t mine = (uint32_t)tid < n_eq ? sh.tie[tid] : 0xffffffffu;
+      uint32_t below = 0;
+      for (uint32_t j = 0; j < n_eq; ++j) below += sh.tie[j] < mine ? 1u : 0u;
+      if ((uint32_t)tid < n_eq && below == need - 1) sh.found = mine;
+    }
+    __syncthreads();
+    iota = sh.found;
+  } else if (need < n_eq) {
     __syncthreads();
     visit([&](uint32_t key, uint32_t e) {
       if (key == tau) atomicOr(&bm[e >> 5], 1u << (e & 31));
