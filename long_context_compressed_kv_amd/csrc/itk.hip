@@ -794,14 +794,16 @@ struct SelectLds {
 
 // The exact top-k of a row whose keys visit(f) produces (f(key, entry), each
 // thread its share; every thread calls it): the k-th largest key tau by radix
-// select, ties to the lowest entries by a radix select over their
-// complemented indices, the chosen entries marked in the LDS bitmap (nwords
-// words, cleared here) and written in index order to out[0..k).  The keys
-// visited must include every key of the row at or above `floor`; if tau
-// turns out below it, entries that were not visited could belong to the
-// top-k: nothing is written and false is returned.
+// select, ties to the lowest entries (the needed one found in a short list
+// of the tied entries, or by its rank among them in the bitmap), the chosen
+// entries marked in the LDS bitmap (nwords words, cleared here) and written
+// in index order to out[0..k).  The keys visited must include every key of
+// the row at or above `floor`; if tau turns out below it, entries that were
+// not visited could belong to the top-k: nothing is written and false is
+// returned.  Always inlined: as a call, the visitor's captured state would
+// go through scratch memory.
 template <int KBITS, int NT, typename Visit>
-__device__ bool select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, int32_t* out,
+__device__ __forceinline__ bool select_row(SelectLds<NT>& sh, uint32_t* bm, int nwords, int k, int32_t* out,
                            Visit visit, uint32_t floor = 0) {
   const int tid = threadIdx.x;
   uint32_t need, n_eq;
