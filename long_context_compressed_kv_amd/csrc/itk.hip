@@ -1036,7 +1036,12 @@ csa_status launch_all(const ItkArgs& a, int64_t max_kv, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  if (a.n_q < 2 * (int64_t)cus) return launch_select<FMT, SBF16, 1024>(a, bm_bytes, s);
+  if (a.n_q < 2 * (int64_t)cus) {
+    // fp32 indexer queries and keys: the exact redo's fp32 query group does
+    // not fit the 128 registers of a 1024-lane workgroup, so 8 waves a row
+    if constexpr (FMT == CSA_F32) return launch_select<FMT, SBF16, 512>(a, bm_bytes, s);
+    else return launch_select<FMT, SBF16, 1024>(a, bm_bytes, s);
+  }
   // many short rows (at most 1024 entries, so every entry is a candidate and
   // the list fits one wave's registers): one wave a row, whose barriers cost
   // next to nothing, and four times the rows resident
